@@ -1,0 +1,29 @@
+"""CPU oracle of the speculative-decoding verify step — TEST INFRASTRUCTURE ONLY.
+
+A plain, slow, fp64 statement of what the verify step computes, written from
+the pages' definitions:
+
+* attention.py — the (1+D) verify positions of each sequence attend over the
+  sequence's KV cache under a causal mask, G query heads per KV head
+  ("Co-Designing AI Models Using Speculative Decoding for Faster LLM
+  Inference", translated page, section "Draft length and attention
+  performance").
+* accept.py — greedy first-mismatch acceptance, and min(1, p/q) acceptance
+  with residual resampling plus the extra target token ("How does speculative
+  decoding speed up LLM inference?", sections "Mechanism" and "Math
+  intuition"; the NVIDIA page's "What is speculative decoding?" for D and AL;
+  the LLM inference handbook's "How speculative decoding works").
+
+Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may import
+or call anything here.  The product path (the HIP library and its Python
+binding) never does, and this package imports nothing from it: the two share
+only the seeded input generators in ``workloads/``.
+"""
+
+from .attention import bf16_bits_to_f64, verify_attention, verify_attention_unit
+from .accept import accept_greedy, accept_stochastic, accept_reject, row_log_normalizer
+
+__all__ = [
+    "bf16_bits_to_f64", "verify_attention", "verify_attention_unit",
+    "accept_greedy", "accept_stochastic", "accept_reject", "row_log_normalizer",
+]
