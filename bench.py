@@ -1,0 +1,268 @@
+"""Benchmark of one speculative-decoding verify step on one MI355X.
+
+A step is one verify-attention call plus one accept/reject call over one batch
+of seeded synthetic inputs already resident in HBM (the two halves of
+sd_verify_step, timed separately with HIP events on the stream they run on).
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--draft D] [--alpha A]
+                    [--no-cpu-baseline] [--json-only]
+
+Prints one JSON line.  The default workload is 16 sequences x 8 KV heads x
+G=8 over a 32768-token paged bf16 cache with D=15 drafts (G*(1+D) = 128) and
+stochastic acceptance over a 131072-token vocabulary.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "verified tokens/s per verify step (B,G,D,KV sweep) + % HBM / MFMA roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+
+
+def algorithmic_attention(inp):
+    """Bytes and flops one attention call must move / do (masked keys and padding excluded)."""
+    import numpy as np
+    kv = inp.kv_len.cpu().numpy().astype(np.int64)
+    qs = inp.q_start.cpu().numpy().astype(np.int64)
+    D = np.diff(qs) - 1
+    sp = inp.spec
+    d, Hkv, G = sp.head_dim, sp.kv_heads, sp.group
+    T = int(qs[-1])
+    kv_bytes = int((kv * Hkv * d * 2 * 2).sum())
+    q_bytes = T * Hkv * G * d * 2
+    o_bytes = q_bytes
+    bt_bytes = int(((kv + sp.page_size - 1) // sp.page_size).sum()) * 4
+    visible = 0
+    for b in range(len(kv)):
+        i = np.arange(D[b] + 1)
+        visible += int(np.maximum(kv[b] - D[b] + i, 0).sum())
+    flops = 4 * d * Hkv * G * visible
+    return kv_bytes + q_bytes + o_bytes + bt_bytes, flops
+
+
+def algorithmic_accept(inp):
+    sp = inp.spec
+    T = inp.target_logits.shape[0]
+    B = inp.q_start.shape[0] - 1
+    V = sp.vocab
+    if sp.mode == "greedy":
+        return T * V * 4
+    return (2 * T - B) * V * 4 + 2 * B * V * 4   # one pass over all rows + the residual/bonus rows
+
+
+def cpu_baseline(inp, budget_units: int):
+    """Time the oracle on a bounded sample of the same workload on the host cores."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+    from oracle import accept_greedy, accept_stochastic, verify_attention_unit
+
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:        # pragma: no cover
+        threadpool_limits = None
+    sp = inp.spec
+    B, Hkv = sp.batch, sp.kv_heads
+    workers = max(1, min(16, os.cpu_count() or 1, budget_units))
+    rng = np.random.default_rng(1)
+    units = [(int(rng.integers(B)), int(rng.integers(Hkv))) for _ in range(workers)]
+
+    def bits(t):
+        import torch
+        return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    qs = inp.q_start.cpu().numpy()
+    kvl = inp.kv_len.cpu().numpy()
+    subs = []
+    for b, h in units:
+        n = int(kvl[b])
+        npg = (n + sp.page_size - 1) // sp.page_size
+        pages = inp.block_table[b, :npg].long()
+        t0, t1 = int(qs[b]), int(qs[b + 1])
+        subs.append(dict(q_bits=bits(inp.q[t0:t1]), k_bits=bits(inp.k_cache[pages]),
+                         v_bits=bits(inp.v_cache[pages]), block_table=np.arange(npg, dtype=np.int32)[None],
+                         kv_len=np.asarray([n], np.int32), q_start=np.asarray([0, t1 - t0], np.int32),
+                         group=sp.group, b=0, h=h))
+    ctx = threadpool_limits(1) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        t_start = time.perf_counter()
+        with ThreadPoolExecutor(workers) as ex:
+            list(ex.map(lambda s: verify_attention_unit(**s), subs))
+        t_attn = time.perf_counter() - t_start
+        # accept: one sequence per worker, the same parallelism
+        seqs = [int(rng.integers(B)) for _ in range(workers)]
+        tl = inp.target_logits
+        dl = inp.draft_logits
+        toks = inp.draft_tokens.cpu().numpy()
+        uni = inp.uniforms.cpu().numpy()
+        jobs = []
+        for b in seqs:
+            t0, t1 = int(qs[b]), int(qs[b + 1])
+            d0 = t0 - b
+            job = dict(target_logits=tl[t0:t1].cpu().numpy(), draft_tokens=toks[d0:d0 + t1 - t0 - 1],
+                       q_start=np.asarray([0, t1 - t0], np.int32))
+            if sp.mode == "stochastic":
+                job.update(draft_logits=dl[d0:d0 + t1 - t0 - 1].cpu().numpy(), uniforms=uni[t0:t1])
+            jobs.append(job)
+        t_start = time.perf_counter()
+        with ThreadPoolExecutor(workers) as ex:
+            if sp.mode == "stochastic":
+                list(ex.map(lambda j: accept_stochastic(**j), jobs))
+            else:
+                list(ex.map(lambda j: accept_greedy(j["target_logits"], j["draft_tokens"], j["q_start"]), jobs))
+        t_acc = time.perf_counter() - t_start
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    # scale the sample (workers units in parallel) to the whole step
+    step_s = t_attn * (B * Hkv) / workers + t_acc * B / workers
+    T = int(qs[-1])
+    return {"value": T / step_s, "unit": "verified tokens/s", "cores": workers, "kind": "oracle",
+            "sample": f"{workers} (sequence, KV head) attention units + {workers} sequences' accept/reject, "
+                      f"run on {workers} threads and scaled to {B * Hkv} units / {B} sequences",
+            "step_seconds_estimate": step_s, "sample_seconds": t_attn + t_acc}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="g8_kv32k_D15")
+    ap.add_argument("--draft", type=int, default=None, help="override D (every sequence)")
+    ap.add_argument("--alpha", type=float, default=None, help="fixed acceptance rate for the synthetic drafter")
+    ap.add_argument("--kv-chunk", type=int, default=0)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the verify step is built and timed on a single MI355X "
+              "(--gpus 1); multi-GPU runs are not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import speculative_decoding_verification_sd_amd as sdv
+    from workloads import generate, preset
+
+    over = {"seed": args.seed}
+    if args.draft is not None:
+        over["draft_len"] = args.draft
+    if args.alpha is not None:
+        over["alpha"] = args.alpha
+    sp = preset(args.workload, **over)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating {sp.name} on {dev}", file=sys.stderr, flush=True)
+    inp = generate(sp, device=dev)
+    torch.cuda.synchronize()
+    B = sp.batch
+    T = inp.q.shape[0]
+    out = torch.empty_like(inp.q)
+    al = torch.empty(B, dtype=torch.int32, device=dev)
+    tok = torch.empty(T, dtype=torch.int32, device=dev)
+    adesc = sdv.attn_desc(inp.q, inp.k_cache, inp.block_table, sp.group, inp.max_draft, kv_chunk=args.kv_chunk)
+    cdesc = sdv.accept_desc(B, sp.vocab, inp.max_draft, sp.mode)
+    ws_a = torch.empty(max(1, sdv.sd_verify_attention_workspace_size(adesc, T)), dtype=torch.uint8, device=dev)
+    ws_c = torch.empty(max(1, sdv.sd_accept_reject_workspace_size(cdesc, T)), dtype=torch.uint8, device=dev)
+    ws_s = torch.empty(max(1, sdv.sd_verify_step_workspace_size(adesc, cdesc, T)), dtype=torch.uint8, device=dev)
+
+    def attention():
+        sdv.sd_verify_attention(inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.kv_len, inp.q_start, out,
+                                group_size=sp.group, max_draft=inp.max_draft, kv_chunk=args.kv_chunk,
+                                workspace=ws_a)
+
+    def accept():
+        sdv.sd_accept_reject(inp.target_logits, inp.draft_logits, inp.draft_tokens, inp.q_start, inp.uniforms,
+                             al, tok, mode=sp.mode, max_draft=inp.max_draft, workspace=ws_c)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(max(1, args.warmup)):
+        sdv.sd_verify_step(inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.kv_len, inp.q_start, out,
+                           inp.target_logits, inp.draft_logits, inp.draft_tokens, inp.uniforms, al, tok,
+                           group_size=sp.group, max_draft=inp.max_draft, mode=sp.mode, kv_chunk=args.kv_chunk,
+                           workspace=ws_s)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for k in range(K):
+        ev[k][0].record()
+        attention()
+        ev[k][1].record()
+        accept()
+        ev[k][2].record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    attn_ms = np.asarray([ev[k][0].elapsed_time(ev[k][1]) for k in range(K)])
+    acc_ms = np.asarray([ev[k][1].elapsed_time(ev[k][2]) for k in range(K)])
+    total_ms = ev[0][0].elapsed_time(ev[K - 1][2])
+    ms_per_step = total_ms / K
+    print(f"[bench] {K} steps: {ms_per_step:.3f} ms/step (attention {attn_ms.mean():.3f} ms, "
+          f"accept {acc_ms.mean():.3f} ms)", file=sys.stderr, flush=True)
+
+    a_bytes, a_flops = algorithmic_attention(inp)
+    c_bytes = algorithmic_accept(inp)
+    t_attn = float(attn_ms.mean()) * 1e-3
+    achieved = a_bytes / t_attn / 1e9
+    mean_al = float(al.float().mean().item())
+
+    line = {
+        "metric": METRIC,
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "verified tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": sp.name, "batch": B, "kv_heads": sp.kv_heads, "group": sp.group, "head_dim": sp.head_dim,
+            "kv_len": sp.kv_len if not isinstance(sp.kv_len, tuple) else list(sp.kv_len),
+            "draft_len": sp.draft_len if not isinstance(sp.draft_len, tuple) else list(sp.draft_len),
+            "vocab": sp.vocab, "accept": sp.mode, "alpha": sp.alpha, "page_size": sp.page_size,
+            "verified_tokens_per_step": T, "seed": sp.seed,
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+            "kernel": "verify attention (plan + main + split-KV combine launches)",
+            "algorithmic_bytes_per_launch": a_bytes,
+            "mfma_tflops": a_flops / t_attn / 1e12, "mfma_frac": a_flops / t_attn / 1e12 / BF16_PEAK_TFLOPS,
+        },
+        "attention_ms": float(attn_ms.mean()),
+        "attention_ms_p10_p90": [float(np.percentile(attn_ms, 10)), float(np.percentile(attn_ms, 90))],
+        "accept_ms": float(acc_ms.mean()),
+        "accept_gbs": c_bytes / (float(acc_ms.mean()) * 1e-3) / 1e9,
+        "emitted_tokens_per_s": float(al.sum().item()) / (ms_per_step * 1e-3),
+        "mean_accept_len": mean_al,
+        "host_wall_s": t_wall,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(inp, budget_units=16)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,191 @@
+/*
+ * sd_verify.h — the target-model verify step of speculative decoding on
+ * AMD Instinct MI355X (gfx950), as a C ABI.
+ *
+ * The verify step has two parts:
+ *
+ *  1. Verify attention.  The 1+D_b positions of sequence b (the last emitted
+ *     token followed by D_b drafted tokens) attend over the sequence's paged
+ *     KV cache in one pass.  The speculated tokens reuse the same KV cache, so
+ *     each KV head serves G*(1+D_b) query rows ("Co-Designing AI Models Using
+ *     Speculative Decoding for Faster LLM Inference", translated page, section
+ *     "Draft length and attention performance").  Every verify position yields
+ *     its own next-token distribution in that pass ("How does speculative
+ *     decoding speed up LLM inference?", section "Mechanism", Verify step), so
+ *     position i sees keys up to its own position (a causal mask inside the
+ *     block).
+ *
+ *  2. Accept / reject over the vocabulary.  Greedy: accept drafts until the
+ *     first mismatch with the target's top token (the co-design page, "What is
+ *     speculative decoding?").  Stochastic: accept draft x with probability
+ *     min(1, p(x)/q(x)); at the first rejection resample from the normalised
+ *     residual max(0, p - q) ("How does speculative decoding speed up LLM
+ *     inference?", sections "Mechanism" and "Math intuition").  The target
+ *     always yields one more token, so the acceptance length AL is in
+ *     [1, 1+D_b] (the co-design page, "What is speculative decoding?").
+ *
+ * Conventions for every call:
+ *  - All array arguments are DEVICE pointers, allocated and owned by the
+ *    caller.  The library never allocates, frees or synchronises; each call
+ *    enqueues its kernels on `stream` (a hipStream_t, NULL = default stream)
+ *    and returns.  Outputs are valid once that stream has reached them.
+ *  - Host-checkable preconditions (sizes, supported shapes, non-NULL pointers,
+ *    workspace size) are validated before anything is enqueued; a violation
+ *    returns a non-zero sd_status, enqueues nothing, and sd_last_error()
+ *    describes it.  Nothing is thrown and nothing aborts across this ABI.
+ *  - Device-side contents are the caller's contract: page ids in range for
+ *    the pages a sequence uses, kv_len[b] <= max_pages_per_seq*page_size,
+ *    q_start non-decreasing with q_start[B] == total_q, finite or -inf
+ *    logits (no row entirely -inf), uniforms in [0, 1).  Kernels clamp
+ *    indices so that a violation cannot read or write out of bounds; the
+ *    values computed for an offending sequence are then unspecified.
+ *  - Results are deterministic: the same inputs give bit-identical outputs.
+ *  - Concurrent calls are safe when they use distinct workspaces and outputs.
+ *
+ * Sequence layout shared by both parts: sequence b owns the verify rows
+ * q_start[b] .. q_start[b+1]-1 (1+D_b rows, D_b >= 0); row q_start[b]+i is
+ * verify position i.  Its D_b draft rows and drafted tokens sit at
+ * (q_start[b]-b)+i, i < D_b (so there are T_d = total_q - B of them).
+ */
+#ifndef SD_VERIFY_H
+#define SD_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SD_OK = 0,
+  SD_ERR_INVALID_ARG = 1,   /* a host-side precondition failed */
+  SD_ERR_UNSUPPORTED = 2,   /* valid request outside the built kernel variants */
+  SD_ERR_WORKSPACE = 3,     /* workspace NULL or smaller than the *_workspace_size query */
+  SD_ERR_HIP = 4            /* the HIP runtime reported an error while enqueueing */
+} sd_status;
+
+typedef enum { SD_ACCEPT_GREEDY = 0, SD_ACCEPT_STOCHASTIC = 1 } sd_accept_mode;
+typedef enum { SD_OUT_BF16 = 0, SD_OUT_F32 = 1 } sd_out_dtype;
+
+/* Verify-attention problem description (host memory, read during the call). */
+typedef struct {
+  int32_t num_seqs;           /* B >= 0 */
+  int32_t num_kv_heads;       /* H_kv >= 1 */
+  int32_t group_size;         /* G >= 1: query heads per KV head; query head hq uses KV head hq / G */
+  int32_t head_dim;           /* d: 64 or 128 */
+  int32_t page_size;          /* keys per page: 16 */
+  int32_t max_pages_per_seq;  /* columns of block_table */
+  int32_t num_pages;          /* pages in each of the K and V pools */
+  int32_t max_draft;          /* upper bound on every D_b; G*(1+max_draft) <= 256 */
+  float softmax_scale;        /* scores are scale * q.k; 0 selects 1/sqrt(d) */
+  int32_t out_dtype;          /* sd_out_dtype */
+  int32_t kv_chunk;           /* keys per split-KV work item, a multiple of 64; 0 = chosen per call */
+} sd_attn_desc;
+
+/* Accept/reject problem description. */
+typedef struct {
+  int32_t num_seqs;           /* B >= 0 */
+  int32_t vocab;              /* V >= 1 */
+  int32_t max_draft;          /* upper bound on every D_b */
+  int32_t mode;               /* sd_accept_mode */
+} sd_accept_desc;
+
+/*
+ * Workspace bytes sd_verify_attention needs for this description and
+ * total_q = sum_b (1+D_b) verify rows.  Returns 0 for an invalid description.
+ */
+size_t sd_verify_attention_workspace_size(const sd_attn_desc* desc, int32_t total_q);
+
+/*
+ * Verify attention.  For sequence b with N = kv_len[b] keys, of which the
+ * last 1+D_b are its own verify positions, row i (absolute position
+ * P = N-(1+D_b)+i) of query head hq attends to keys 0..P of KV head hq/G:
+ *     o = sum_j softmax_j(scale * q.k_j) v_j,
+ * with key j stored at page block_table[b*max_pages_per_seq + j/page_size],
+ * slot j % page_size.  A row with P < 0 sees no key and its output is zero.
+ *
+ *   q            bf16 [total_q, H_kv*G, d]                 row-major
+ *   k_cache      bf16 [num_pages, H_kv, page_size, d]      row-major
+ *   v_cache      bf16 [num_pages, H_kv, page_size, d]      row-major
+ *   block_table  int32 [B, max_pages_per_seq]
+ *   kv_len       int32 [B]
+ *   q_start      int32 [B+1]
+ *   out          [total_q, H_kv*G, d], bf16 or fp32 per desc->out_dtype; written, not read
+ *   workspace    device scratch of at least sd_verify_attention_workspace_size bytes,
+ *                16-byte aligned; its contents on entry do not matter
+ *
+ * Scores, softmax and accumulation are fp32; bf16 output is rounded to
+ * nearest-even.
+ */
+sd_status sd_verify_attention(const sd_attn_desc* desc, int32_t total_q,
+                              const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* kv_len,
+                              const int32_t* q_start, void* out,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes sd_accept_reject needs.  Returns 0 for an invalid description. */
+size_t sd_accept_reject_workspace_size(const sd_accept_desc* desc, int32_t total_q);
+
+/*
+ * Accept / reject.  For sequence b with t0 = q_start[b], D = q_start[b+1]-t0-1
+ * and draft base d0 = t0 - b:
+ *   target row t0+i (i = 0..D) holds the target's logits after position i;
+ *   draft row d0+i (i < D) holds the logits draft_tokens[d0+i] = x_{i+1} was drawn from.
+ *
+ * Greedy (draft_logits and uniforms may be NULL): x_{i+1} passes iff it equals
+ *   the lowest-index maximum of target row t0+i (compared as fp32).
+ * Stochastic: with p = softmax(target row), q = softmax(draft row), x passes
+ *   iff (double)uniforms[t0+i] < exp((log p(x)) - (log q(x))), evaluated in
+ *   fp64 from the fp32 logits (q(x)=0<p(x) passes; p(x)=0 fails).
+ * In both modes a token outside [0, V) fails.  With n the number of leading
+ * passes: accept_len[b] = n+1; out_tokens[t0+k] = x_{k+1} for k < n; then
+ *   greedy:      out_tokens[t0+n] = the target's top token at row n;
+ *   stochastic:  out_tokens[t0+n] = smallest j with C_j > uniforms[t0+D] * Z,
+ *                where C is the inclusive prefix sum over ascending token ids of
+ *                w = max(0, p - q) at row n if n < D, else w = p at row D, and
+ *                Z = C_{V-1} (w = p if the residual sums to zero);
+ *   out_tokens[t0+k] = -1 for n < k <= D.
+ *
+ *   target_logits fp32 [total_q, V];  draft_logits fp32 [total_q - B, V]
+ *   draft_tokens int32 [total_q - B]; q_start int32 [B+1]; uniforms fp32 [total_q]
+ *   accept_len int32 [B] (written);  out_tokens int32 [total_q] (written)
+ *
+ * Row sums of exponentials are accumulated in fp64; the tests, the residual
+ * and the inverse-CDF scan are evaluated in fp64.
+ */
+sd_status sd_accept_reject(const sd_accept_desc* desc, int32_t total_q,
+                           const float* target_logits, const float* draft_logits,
+                           const int32_t* draft_tokens, const int32_t* q_start,
+                           const float* uniforms, int32_t* accept_len, int32_t* out_tokens,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace for sd_verify_step: one buffer holding both parts' scratch. */
+size_t sd_verify_step_workspace_size(const sd_attn_desc* attn, const sd_accept_desc* acc,
+                                     int32_t total_q);
+
+/*
+ * One verify step: sd_verify_attention followed by sd_accept_reject on the
+ * same stream, sharing one workspace.  attn->num_seqs must equal
+ * acc->num_seqs; arguments are as in the two calls above.
+ */
+sd_status sd_verify_step(const sd_attn_desc* attn, const sd_accept_desc* acc, int32_t total_q,
+                         const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_table, const int32_t* kv_len, const int32_t* q_start,
+                         void* attn_out,
+                         const float* target_logits, const float* draft_logits,
+                         const int32_t* draft_tokens, const float* uniforms,
+                         int32_t* accept_len, int32_t* out_tokens,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Message describing the last non-OK status returned on the calling thread. */
+const char* sd_last_error(void);
+
+/* Library version string. */
+const char* sd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SD_VERIFY_H */

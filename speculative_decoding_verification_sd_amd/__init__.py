@@ -1,0 +1,30 @@
+"""The speculative-decoding verify step on AMD Instinct MI355X (gfx950).
+
+Verify attention over a paged bf16 KV cache and vocab-parallel accept/reject,
+as hand-written HIP kernels behind a C ABI (``include/sd_verify.h``,
+``libsdverify.so``).  This package is the Python binding of that ABI: it
+marshals PyTorch device tensors and the current stream into the C calls.
+"""
+
+import torch  # noqa: F401  (load torch's HIP runtime before libsdverify.so)
+
+from .binding import (  # noqa: F401
+    SdError,
+    accept_desc,
+    attn_desc,
+    lib,
+    sd_accept_reject,
+    sd_accept_reject_workspace_size,
+    sd_last_error,
+    sd_verify_attention,
+    sd_verify_attention_workspace_size,
+    sd_verify_step,
+    sd_verify_step_workspace_size,
+    sd_version,
+)
+
+__all__ = [
+    "SdError", "accept_desc", "attn_desc", "lib", "sd_accept_reject", "sd_accept_reject_workspace_size",
+    "sd_last_error", "sd_verify_attention", "sd_verify_attention_workspace_size", "sd_verify_step",
+    "sd_verify_step_workspace_size", "sd_version",
+]

@@ -1,0 +1,243 @@
+"""Thin Python binding of libsdverify's C ABI (argument marshalling only).
+
+Every function here has the name of the C entry point it calls.  Tensors are
+PyTorch device tensors: PyTorch provides device memory and the stream, the
+HIP library does all of the computation.  There is no fallback: if the
+library is missing or a call fails, an exception is raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsdverify.so")
+
+SD_OK, SD_ERR_INVALID_ARG, SD_ERR_UNSUPPORTED, SD_ERR_WORKSPACE, SD_ERR_HIP = range(5)
+SD_ACCEPT_GREEDY, SD_ACCEPT_STOCHASTIC = 0, 1
+SD_OUT_BF16, SD_OUT_F32 = 0, 1
+MODES = {"greedy": SD_ACCEPT_GREEDY, "stochastic": SD_ACCEPT_STOCHASTIC}
+
+
+class SdError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"sd status {status}: {msg}")
+        self.status = status
+
+
+class sd_attn_desc(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("group_size", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("max_draft", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+        ("out_dtype", ctypes.c_int32),
+        ("kv_chunk", ctypes.c_int32),
+    ]
+
+
+class sd_accept_desc(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("vocab", ctypes.c_int32),
+        ("max_draft", ctypes.c_int32),
+        ("mode", ctypes.c_int32),
+    ]
+
+
+_lib: Optional[ctypes.CDLL] = None
+_P = ctypes.c_void_p
+_SZ = ctypes.c_size_t
+_I = ctypes.c_int32
+
+SIGNATURES = {
+    "sd_verify_attention_workspace_size": (_SZ, [ctypes.POINTER(sd_attn_desc), _I]),
+    "sd_verify_attention": (ctypes.c_int, [ctypes.POINTER(sd_attn_desc), _I, _P, _P, _P, _P, _P, _P, _P, _P,
+                                           _SZ, _P]),
+    "sd_accept_reject_workspace_size": (_SZ, [ctypes.POINTER(sd_accept_desc), _I]),
+    "sd_accept_reject": (ctypes.c_int, [ctypes.POINTER(sd_accept_desc), _I, _P, _P, _P, _P, _P, _P, _P, _P,
+                                        _SZ, _P]),
+    "sd_verify_step_workspace_size": (_SZ, [ctypes.POINTER(sd_attn_desc), ctypes.POINTER(sd_accept_desc), _I]),
+    "sd_verify_step": (ctypes.c_int, [ctypes.POINTER(sd_attn_desc), ctypes.POINTER(sd_accept_desc), _I,
+                                      _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "sd_last_error": (ctypes.c_char_p, []),
+    "sd_version": (ctypes.c_char_p, []),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load libsdverify.so (after torch, so both use the same HIP runtime)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m speculative_decoding_verification_sd_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(status: int):
+    if status != SD_OK:
+        raise SdError(status, lib().sd_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device, stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def attn_desc(q, k_cache, block_table, group_size: int, max_draft: int, softmax_scale: float = 0.0,
+              out_dtype=torch.bfloat16, kv_chunk: int = 0) -> sd_attn_desc:
+    num_pages, hkv, page, d = k_cache.shape
+    return sd_attn_desc(num_seqs=block_table.shape[0], num_kv_heads=hkv, group_size=group_size, head_dim=d,
+                        page_size=page, max_pages_per_seq=block_table.shape[1], num_pages=num_pages,
+                        max_draft=max_draft, softmax_scale=softmax_scale,
+                        out_dtype=SD_OUT_F32 if out_dtype == torch.float32 else SD_OUT_BF16,
+                        kv_chunk=kv_chunk)
+
+
+def accept_desc(num_seqs: int, vocab: int, max_draft: int, mode: str) -> sd_accept_desc:
+    return sd_accept_desc(num_seqs=num_seqs, vocab=vocab, max_draft=max_draft, mode=MODES[mode])
+
+
+def sd_verify_attention_workspace_size(desc: sd_attn_desc, total_q: int) -> int:
+    return int(lib().sd_verify_attention_workspace_size(ctypes.byref(desc), total_q))
+
+
+def sd_accept_reject_workspace_size(desc: sd_accept_desc, total_q: int) -> int:
+    return int(lib().sd_accept_reject_workspace_size(ctypes.byref(desc), total_q))
+
+
+def sd_verify_step_workspace_size(attn: sd_attn_desc, acc: sd_accept_desc, total_q: int) -> int:
+    return int(lib().sd_verify_step_workspace_size(ctypes.byref(attn), ctypes.byref(acc), total_q))
+
+
+def _workspace(nbytes: int, device, workspace):
+    if workspace is None:
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace of {workspace.numel() * workspace.element_size()} bytes < {nbytes}")
+    return workspace
+
+
+def _check_attention_args(q, k_cache, v_cache, block_table, kv_len, q_start, out):
+    dev = q.device
+    _need(q, "q", torch.bfloat16)
+    _need(k_cache, "k_cache", torch.bfloat16, dev)
+    _need(v_cache, "v_cache", torch.bfloat16, dev)
+    _need(block_table, "block_table", torch.int32, dev)
+    _need(kv_len, "kv_len", torch.int32, dev)
+    _need(q_start, "q_start", torch.int32, dev)
+    if out.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out must be bf16 or fp32")
+    _need(out, "out", out.dtype, dev)
+    if k_cache.shape != v_cache.shape or k_cache.dim() != 4:
+        raise ValueError("k_cache and v_cache must both be [pages, kv_heads, page_size, head_dim]")
+    if q.dim() != 3 or out.shape != q.shape:
+        raise ValueError("q and out must be [total_q, query_heads, head_dim]")
+    B = block_table.shape[0]
+    if kv_len.shape != (B,) or q_start.shape != (B + 1,):
+        raise ValueError("kv_len must be [B] and q_start [B+1]")
+
+
+def sd_verify_attention(q, k_cache, v_cache, block_table, kv_len, q_start, out, *, group_size: int,
+                        max_draft: int, softmax_scale: float = 0.0, kv_chunk: int = 0,
+                        workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    _check_attention_args(q, k_cache, v_cache, block_table, kv_len, q_start, out)
+    desc = attn_desc(q, k_cache, block_table, group_size, max_draft, softmax_scale, out.dtype, kv_chunk)
+    total_q = q.shape[0]
+    ws = _workspace(sd_verify_attention_workspace_size(desc, total_q), q.device, workspace)
+    _check(lib().sd_verify_attention(ctypes.byref(desc), total_q, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                     _ptr(block_table), _ptr(kv_len), _ptr(q_start), _ptr(out), _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(q.device, stream)))
+
+
+def _check_accept_args(target_logits, draft_logits, draft_tokens, q_start, uniforms, accept_len, out_tokens,
+                       mode):
+    dev = target_logits.device
+    _need(target_logits, "target_logits", torch.float32)
+    _need(draft_tokens, "draft_tokens", torch.int32, dev)
+    _need(q_start, "q_start", torch.int32, dev)
+    _need(accept_len, "accept_len", torch.int32, dev)
+    _need(out_tokens, "out_tokens", torch.int32, dev)
+    if mode == "stochastic":
+        _need(draft_logits, "draft_logits", torch.float32, dev)
+        _need(uniforms, "uniforms", torch.float32, dev)
+    B = q_start.shape[0] - 1
+    T, V = target_logits.shape
+    if accept_len.shape != (B,) or out_tokens.shape != (T,) or draft_tokens.shape != (T - B,):
+        raise ValueError("accept_len [B], out_tokens [T_q], draft_tokens [T_q - B] expected")
+    if mode == "stochastic" and (draft_logits.shape != (T - B, V) or uniforms.shape != (T,)):
+        raise ValueError("draft_logits [T_q - B, V] and uniforms [T_q] expected")
+
+
+def sd_accept_reject(target_logits, draft_logits, draft_tokens, q_start, uniforms, accept_len, out_tokens, *,
+                     mode: str, max_draft: int, workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    _check_accept_args(target_logits, draft_logits, draft_tokens, q_start, uniforms, accept_len, out_tokens, mode)
+    B = q_start.shape[0] - 1
+    T, V = target_logits.shape
+    desc = accept_desc(B, V, max_draft, mode)
+    ws = _workspace(sd_accept_reject_workspace_size(desc, T), target_logits.device, workspace)
+    stoch = mode == "stochastic"
+    _check(lib().sd_accept_reject(ctypes.byref(desc), T, _ptr(target_logits), _ptr(draft_logits if stoch else None),
+                                  _ptr(draft_tokens), _ptr(q_start), _ptr(uniforms if stoch else None),
+                                  _ptr(accept_len), _ptr(out_tokens), _ptr(ws), ws.numel() * ws.element_size(),
+                                  _stream(target_logits.device, stream)))
+
+
+def sd_verify_step(q, k_cache, v_cache, block_table, kv_len, q_start, attn_out, target_logits, draft_logits,
+                   draft_tokens, uniforms, accept_len, out_tokens, *, group_size: int, max_draft: int, mode: str,
+                   softmax_scale: float = 0.0, kv_chunk: int = 0, workspace: Optional[torch.Tensor] = None,
+                   stream=None) -> None:
+    _check_attention_args(q, k_cache, v_cache, block_table, kv_len, q_start, attn_out)
+    _check_accept_args(target_logits, draft_logits, draft_tokens, q_start, uniforms, accept_len, out_tokens, mode)
+    adesc = attn_desc(q, k_cache, block_table, group_size, max_draft, softmax_scale, attn_out.dtype, kv_chunk)
+    B = q_start.shape[0] - 1
+    T, V = target_logits.shape
+    cdesc = accept_desc(B, V, max_draft, mode)
+    ws = _workspace(sd_verify_step_workspace_size(adesc, cdesc, T), q.device, workspace)
+    stoch = mode == "stochastic"
+    _check(lib().sd_verify_step(ctypes.byref(adesc), ctypes.byref(cdesc), T, _ptr(q), _ptr(k_cache),
+                                _ptr(v_cache), _ptr(block_table), _ptr(kv_len), _ptr(q_start), _ptr(attn_out),
+                                _ptr(target_logits), _ptr(draft_logits if stoch else None), _ptr(draft_tokens),
+                                _ptr(uniforms if stoch else None), _ptr(accept_len), _ptr(out_tokens), _ptr(ws),
+                                ws.numel() * ws.element_size(), _stream(q.device, stream)))
+
+
+def sd_version() -> str:
+    return lib().sd_version().decode()
+
+
+def sd_last_error() -> str:
+    return lib().sd_last_error().decode()

@@ -1,0 +1,224 @@
+// C ABI of the verify step: argument validation, workspace sizing and
+// stream-ordered launches.  Nothing here allocates, frees or synchronises.
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string>
+
+#include "../../include/sd_verify.h"
+#include "common.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+sd_status fail(sd_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return s;
+}
+
+constexpr int kMaxRows = 256;   // G*(1+max_draft) handled by one workgroup
+
+sd_status check_attn(const sd_attn_desc* d, int32_t total_q) {
+  if (!d) return fail(SD_ERR_INVALID_ARG, "attention descriptor is NULL");
+  if (d->num_seqs < 0) return fail(SD_ERR_INVALID_ARG, "num_seqs=%d must be >= 0", d->num_seqs);
+  if (d->num_kv_heads < 1) return fail(SD_ERR_INVALID_ARG, "num_kv_heads=%d must be >= 1", d->num_kv_heads);
+  if (d->group_size < 1) return fail(SD_ERR_INVALID_ARG, "group_size=%d must be >= 1", d->group_size);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(SD_ERR_UNSUPPORTED, "head_dim=%d: supported values are 64 and 128", d->head_dim);
+  if (d->page_size != 16) return fail(SD_ERR_UNSUPPORTED, "page_size=%d: only 16 is supported", d->page_size);
+  if (d->max_pages_per_seq < 1) return fail(SD_ERR_INVALID_ARG, "max_pages_per_seq=%d must be >= 1", d->max_pages_per_seq);
+  if ((long long)d->max_pages_per_seq * d->page_size > (1LL << 30))
+    return fail(SD_ERR_UNSUPPORTED, "max_pages_per_seq*page_size exceeds 2^30 keys");
+  if (d->num_pages < 1) return fail(SD_ERR_INVALID_ARG, "num_pages=%d must be >= 1", d->num_pages);
+  if (d->max_draft < 0) return fail(SD_ERR_INVALID_ARG, "max_draft=%d must be >= 0", d->max_draft);
+  if ((long long)d->group_size * (1LL + d->max_draft) > kMaxRows)
+    return fail(SD_ERR_UNSUPPORTED, "group_size*(1+max_draft)=%lld exceeds %d rows per KV head",
+                (long long)d->group_size * (1LL + d->max_draft), kMaxRows);
+  if (!(d->softmax_scale >= 0.f) || !isfinite(d->softmax_scale))
+    return fail(SD_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
+  if (d->out_dtype != SD_OUT_BF16 && d->out_dtype != SD_OUT_F32)
+    return fail(SD_ERR_INVALID_ARG, "out_dtype=%d is not an sd_out_dtype", d->out_dtype);
+  if (d->kv_chunk < 0 || d->kv_chunk % 64 != 0)
+    return fail(SD_ERR_INVALID_ARG, "kv_chunk=%d must be 0 or a positive multiple of 64", d->kv_chunk);
+  if (total_q < d->num_seqs || (long long)total_q > (long long)d->num_seqs * (1LL + d->max_draft))
+    return fail(SD_ERR_INVALID_ARG, "total_q=%d must lie in [num_seqs, num_seqs*(1+max_draft)] = [%d, %lld]",
+                total_q, d->num_seqs, (long long)d->num_seqs * (1LL + d->max_draft));
+  return SD_OK;
+}
+
+sd_status check_accept(const sd_accept_desc* d, int32_t total_q) {
+  if (!d) return fail(SD_ERR_INVALID_ARG, "accept descriptor is NULL");
+  if (d->num_seqs < 0) return fail(SD_ERR_INVALID_ARG, "num_seqs=%d must be >= 0", d->num_seqs);
+  if (d->vocab < 1) return fail(SD_ERR_INVALID_ARG, "vocab=%d must be >= 1", d->vocab);
+  if (d->max_draft < 0) return fail(SD_ERR_INVALID_ARG, "max_draft=%d must be >= 0", d->max_draft);
+  if (d->max_draft > 4096) return fail(SD_ERR_UNSUPPORTED, "max_draft=%d exceeds 4096", d->max_draft);
+  if (d->mode != SD_ACCEPT_GREEDY && d->mode != SD_ACCEPT_STOCHASTIC)
+    return fail(SD_ERR_INVALID_ARG, "mode=%d is not an sd_accept_mode", d->mode);
+  if (total_q < d->num_seqs || (long long)total_q > (long long)d->num_seqs * (1LL + d->max_draft))
+    return fail(SD_ERR_INVALID_ARG, "total_q=%d must lie in [num_seqs, num_seqs*(1+max_draft)]", total_q);
+  const long long rows = d->mode == SD_ACCEPT_STOCHASTIC ? 2LL * total_q - d->num_seqs : total_q;
+  if (rows * ((d->vocab + 4095) / 4096) > 0x7fffffffLL)
+    return fail(SD_ERR_UNSUPPORTED, "rows x vocab chunks exceeds the launch grid");
+  return SD_OK;
+}
+
+size_t attn_ws(const sd_attn_desc* d) {
+  return sdv_attn_workspace_bytes(d->num_seqs, d->num_kv_heads, d->group_size, d->head_dim,
+                                  d->max_pages_per_seq, d->max_draft, d->kv_chunk);
+}
+
+size_t acc_ws(const sd_accept_desc* d, int32_t total_q) {
+  return sdv_accept_workspace_bytes(d->num_seqs, total_q, d->vocab, d->mode == SD_ACCEPT_STOCHASTIC);
+}
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+sd_status run_attention(const sd_attn_desc* d, int32_t total_q, const void* q, const void* k,
+                        const void* v, const int32_t* bt, const int32_t* kv_len, const int32_t* q_start,
+                        void* out, void* ws, size_t ws_bytes, void* stream) {
+  sd_status s = check_attn(d, total_q);
+  if (s != SD_OK) return s;
+  if (d->num_seqs == 0) return SD_OK;
+  if (!q || !k || !v || !bt || !kv_len || !q_start || !out)
+    return fail(SD_ERR_INVALID_ARG, "a required attention pointer is NULL");
+  const size_t need = attn_ws(d);
+  if (!ws || ws_bytes < need)
+    return fail(SD_ERR_WORKSPACE, "attention workspace %zu bytes < required %zu", ws_bytes, need);
+  if ((uintptr_t)ws % 16 || (uintptr_t)q % 16 || (uintptr_t)k % 16 || (uintptr_t)v % 16 || (uintptr_t)out % 16)
+    return fail(SD_ERR_INVALID_ARG, "q, caches, out and workspace must be 16-byte aligned");
+  SdAttnLaunch a;
+  a.q = q;
+  a.k_cache = k;
+  a.v_cache = v;
+  a.block_table = bt;
+  a.kv_len = kv_len;
+  a.q_start = q_start;
+  a.out = out;
+  a.workspace = ws;
+  a.B = d->num_seqs;
+  a.Hkv = d->num_kv_heads;
+  a.G = d->group_size;
+  a.head_dim = d->head_dim;
+  a.max_pages = d->max_pages_per_seq;
+  a.num_pages = d->num_pages;
+  a.max_draft = d->max_draft;
+  a.out_f32 = d->out_dtype == SD_OUT_F32;
+  a.kv_chunk = d->kv_chunk;
+  a.total_q = total_q;
+  a.softmax_scale = d->softmax_scale;
+  a.stream = (hipStream_t)stream;
+  hipError_t e = sdv_attn_launch(a);
+  if (e != hipSuccess) return fail(SD_ERR_HIP, "verify attention launch: %s", hipGetErrorString(e));
+  return SD_OK;
+}
+
+sd_status run_accept(const sd_accept_desc* d, int32_t total_q, const float* target, const float* draft,
+                     const int32_t* tokens, const int32_t* q_start, const float* uniforms, int32_t* al,
+                     int32_t* out_tokens, void* ws, size_t ws_bytes, void* stream) {
+  sd_status s = check_accept(d, total_q);
+  if (s != SD_OK) return s;
+  if (d->num_seqs == 0) return SD_OK;
+  const bool stoch = d->mode == SD_ACCEPT_STOCHASTIC;
+  const bool any_drafts = total_q > d->num_seqs;
+  if (!target || !q_start || !al || !out_tokens || (any_drafts && !tokens))
+    return fail(SD_ERR_INVALID_ARG, "a required accept pointer is NULL");
+  if (stoch && (!uniforms || (any_drafts && !draft)))
+    return fail(SD_ERR_INVALID_ARG, "stochastic acceptance needs draft_logits and uniforms");
+  const size_t need = acc_ws(d, total_q);
+  if (!ws || ws_bytes < need)
+    return fail(SD_ERR_WORKSPACE, "accept workspace %zu bytes < required %zu", ws_bytes, need);
+  if ((uintptr_t)ws % 16) return fail(SD_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  SdAccLaunch a;
+  a.target = target;
+  a.draft = draft;
+  a.tokens = tokens;
+  a.q_start = q_start;
+  a.uniforms = uniforms;
+  a.accept_len = al;
+  a.out_tokens = out_tokens;
+  a.workspace = ws;
+  a.B = d->num_seqs;
+  a.T = total_q;
+  a.V = d->vocab;
+  a.max_draft = d->max_draft;
+  a.stochastic = stoch;
+  a.stream = (hipStream_t)stream;
+  hipError_t e = sdv_accept_launch(a);
+  if (e != hipSuccess) return fail(SD_ERR_HIP, "accept/reject launch: %s", hipGetErrorString(e));
+  return SD_OK;
+}
+
+}  // namespace
+
+#define SD_EXPORT __attribute__((visibility("default")))
+
+extern "C" {
+
+SD_EXPORT size_t sd_verify_attention_workspace_size(const sd_attn_desc* desc, int32_t total_q) {
+  if (check_attn(desc, total_q) != SD_OK) return 0;
+  return attn_ws(desc);
+}
+
+SD_EXPORT sd_status sd_verify_attention(const sd_attn_desc* desc, int32_t total_q, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* block_table, const int32_t* kv_len,
+                              const int32_t* q_start, void* out, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  return run_attention(desc, total_q, q, k_cache, v_cache, block_table, kv_len, q_start, out, workspace,
+                       workspace_bytes, stream);
+}
+
+SD_EXPORT size_t sd_accept_reject_workspace_size(const sd_accept_desc* desc, int32_t total_q) {
+  if (check_accept(desc, total_q) != SD_OK) return 0;
+  return acc_ws(desc, total_q);
+}
+
+SD_EXPORT sd_status sd_accept_reject(const sd_accept_desc* desc, int32_t total_q, const float* target_logits,
+                           const float* draft_logits, const int32_t* draft_tokens, const int32_t* q_start,
+                           const float* uniforms, int32_t* accept_len, int32_t* out_tokens, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return run_accept(desc, total_q, target_logits, draft_logits, draft_tokens, q_start, uniforms, accept_len,
+                    out_tokens, workspace, workspace_bytes, stream);
+}
+
+SD_EXPORT size_t sd_verify_step_workspace_size(const sd_attn_desc* attn, const sd_accept_desc* acc, int32_t total_q) {
+  if (check_attn(attn, total_q) != SD_OK || check_accept(acc, total_q) != SD_OK) return 0;
+  if (attn->num_seqs != acc->num_seqs) return 0;
+  return align256(attn_ws(attn)) + acc_ws(acc, total_q);
+}
+
+SD_EXPORT sd_status sd_verify_step(const sd_attn_desc* attn, const sd_accept_desc* acc, int32_t total_q, const void* q,
+                         const void* k_cache, const void* v_cache, const int32_t* block_table,
+                         const int32_t* kv_len, const int32_t* q_start, void* attn_out,
+                         const float* target_logits, const float* draft_logits, const int32_t* draft_tokens,
+                         const float* uniforms, int32_t* accept_len, int32_t* out_tokens, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  sd_status s = check_attn(attn, total_q);
+  if (s != SD_OK) return s;
+  s = check_accept(acc, total_q);
+  if (s != SD_OK) return s;
+  if (attn->num_seqs != acc->num_seqs)
+    return fail(SD_ERR_INVALID_ARG, "attention num_seqs=%d differs from accept num_seqs=%d", attn->num_seqs,
+                acc->num_seqs);
+  const size_t a_bytes = align256(attn_ws(attn));
+  const size_t need = a_bytes + acc_ws(acc, total_q);
+  if (!workspace || workspace_bytes < need)
+    return fail(SD_ERR_WORKSPACE, "verify-step workspace %zu bytes < required %zu", workspace_bytes, need);
+  s = run_attention(attn, total_q, q, k_cache, v_cache, block_table, kv_len, q_start, attn_out, workspace,
+                    a_bytes, stream);
+  if (s != SD_OK) return s;
+  return run_accept(acc, total_q, target_logits, draft_logits, draft_tokens, q_start, uniforms, accept_len,
+                    out_tokens, (unsigned char*)workspace + a_bytes, workspace_bytes - a_bytes, stream);
+}
+
+SD_EXPORT const char* sd_last_error(void) { return g_error.c_str(); }
+
+SD_EXPORT const char* sd_version(void) { return "sdverify 0.1.0 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,139 @@
+"""The C ABI library loads, exports every function include/sd_verify.h
+declares, and rejects invalid host-side arguments before touching a GPU."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import speculative_decoding_verification_sd_amd as sdv
+from speculative_decoding_verification_sd_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sd_verify.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sd_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_three_calls_and_their_workspace_queries():
+    names = declared_functions()
+    for n in ("sd_verify_attention", "sd_accept_reject", "sd_verify_step", "sd_verify_attention_workspace_size",
+              "sd_accept_reject_workspace_size", "sd_verify_step_workspace_size", "sd_last_error", "sd_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_function():
+    lib = sdv.lib()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+        assert n in B.SIGNATURES, n
+    assert sdv.sd_version().startswith("sdverify")
+
+
+def _attn(**kw):
+    d = dict(num_seqs=2, num_kv_heads=2, group_size=4, head_dim=64, page_size=16, max_pages_per_seq=16,
+             num_pages=40, max_draft=3, softmax_scale=0.0, out_dtype=0, kv_chunk=0)
+    d.update(kw)
+    return B.sd_attn_desc(**d)
+
+
+def _acc(**kw):
+    d = dict(num_seqs=2, vocab=1000, max_draft=3, mode=1)
+    d.update(kw)
+    return B.sd_accept_desc(**d)
+
+
+def test_workspace_queries():
+    assert sdv.sd_verify_attention_workspace_size(_attn(), 8) > 0
+    assert sdv.sd_accept_reject_workspace_size(_acc(), 8) > 0
+    assert sdv.sd_verify_step_workspace_size(_attn(), _acc(), 8) >= \
+        sdv.sd_verify_attention_workspace_size(_attn(), 8) + sdv.sd_accept_reject_workspace_size(_acc(), 8)
+    # invalid descriptions report 0
+    assert sdv.sd_verify_attention_workspace_size(_attn(head_dim=96), 8) == 0
+    assert sdv.sd_verify_attention_workspace_size(_attn(group_size=8, max_draft=32), 8) == 0
+    assert sdv.sd_accept_reject_workspace_size(_acc(vocab=0), 8) == 0
+    assert sdv.sd_verify_step_workspace_size(_attn(num_seqs=3), _acc(), 8) == 0
+    # the largest supported rows per KV head is 256 = G*(1+D)
+    assert sdv.sd_verify_attention_workspace_size(_attn(group_size=8, max_draft=31, num_seqs=1), 32) > 0
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(head_dim=80), B.SD_ERR_UNSUPPORTED, "head_dim"),
+    (dict(page_size=32), B.SD_ERR_UNSUPPORTED, "page_size"),
+    (dict(group_size=0), B.SD_ERR_INVALID_ARG, "group_size"),
+    (dict(num_kv_heads=0), B.SD_ERR_INVALID_ARG, "num_kv_heads"),
+    (dict(group_size=16, max_draft=16), B.SD_ERR_UNSUPPORTED, "exceeds 256"),
+    (dict(kv_chunk=100), B.SD_ERR_INVALID_ARG, "kv_chunk"),
+    (dict(softmax_scale=float("nan")), B.SD_ERR_INVALID_ARG, "softmax_scale"),
+    (dict(out_dtype=7), B.SD_ERR_INVALID_ARG, "out_dtype"),
+])
+def test_attention_rejects_bad_descriptions(kw, status, needle):
+    lib = sdv.lib()
+    d = _attn(**kw)
+    st = lib.sd_verify_attention(ctypes.byref(d), 8, *([None] * 8), 0, None)
+    assert st == status
+    assert needle in sdv.sd_last_error()
+
+
+def test_attention_rejects_null_pointers_and_small_workspace():
+    lib = sdv.lib()
+    d = _attn()
+    dummy = ctypes.c_void_p(4096)
+    st = lib.sd_verify_attention(ctypes.byref(d), 8, None, dummy, dummy, dummy, dummy, dummy, dummy, dummy,
+                                 1 << 30, None)
+    assert st == B.SD_ERR_INVALID_ARG and "NULL" in sdv.sd_last_error()
+    st = lib.sd_verify_attention(ctypes.byref(d), 8, dummy, dummy, dummy, dummy, dummy, dummy, dummy, dummy, 16,
+                                 None)
+    assert st == B.SD_ERR_WORKSPACE
+    st = lib.sd_verify_attention(ctypes.byref(d), 100, dummy, dummy, dummy, dummy, dummy, dummy, dummy, dummy,
+                                 1 << 30, None)
+    assert st == B.SD_ERR_INVALID_ARG and "total_q" in sdv.sd_last_error()
+    st = lib.sd_verify_attention(None, 8, *([None] * 8), 0, None)
+    assert st == B.SD_ERR_INVALID_ARG
+
+
+def test_empty_batch_is_a_no_op():
+    lib = sdv.lib()
+    d = _attn(num_seqs=0)
+    assert lib.sd_verify_attention(ctypes.byref(d), 0, *([None] * 8), 0, None) == B.SD_OK
+    a = _acc(num_seqs=0)
+    assert lib.sd_accept_reject(ctypes.byref(a), 0, *([None] * 8), 0, None) == B.SD_OK
+
+
+def test_accept_rejects_bad_arguments():
+    lib = sdv.lib()
+    dummy = ctypes.c_void_p(4096)
+    a = _acc(mode=5)
+    assert lib.sd_accept_reject(ctypes.byref(a), 8, *([dummy] * 8), 1 << 30, None) == B.SD_ERR_INVALID_ARG
+    a = _acc()
+    # stochastic without uniforms
+    st = lib.sd_accept_reject(ctypes.byref(a), 8, dummy, dummy, dummy, dummy, None, dummy, dummy, dummy, 1 << 30,
+                              None)
+    assert st == B.SD_ERR_INVALID_ARG and "uniforms" in sdv.sd_last_error()
+    st = lib.sd_accept_reject(ctypes.byref(a), 8, dummy, dummy, dummy, dummy, dummy, dummy, dummy, dummy, 8, None)
+    assert st == B.SD_ERR_WORKSPACE
+    a = _acc(mode=0)
+    # greedy may omit draft logits and uniforms, but not the workspace
+    st = lib.sd_accept_reject(ctypes.byref(a), 8, dummy, None, dummy, dummy, None, dummy, dummy, None, 0, None)
+    assert st == B.SD_ERR_WORKSPACE
+
+
+def test_step_checks_consistency():
+    lib = sdv.lib()
+    d = _attn()
+    a = _acc(num_seqs=3)
+    st = lib.sd_verify_step(ctypes.byref(d), ctypes.byref(a), 8, *([None] * 14), 0, None)
+    assert st == B.SD_ERR_INVALID_ARG and "num_seqs" in sdv.sd_last_error()
+
+
+def test_binding_validates_tensors_on_cpu():
+    import torch
+    q = torch.zeros(8, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device tensor"):
+        sdv.sd_verify_attention(q, q, q, torch.zeros(2, 16, dtype=torch.int32), torch.zeros(2, dtype=torch.int32),
+                                torch.zeros(3, dtype=torch.int32), q, group_size=4, max_draft=3)

@@ -1,0 +1,123 @@
+"""GPU accept/reject against the oracle: accepted lengths and emitted tokens
+must be identical (same seeded uniforms), greedy and stochastic."""
+
+import numpy as np
+import pytest
+import torch
+
+from tests.gpu_util import gpu_accept, oracle_accept, say
+from workloads import WorkloadSpec, generate, preset
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(inp, mode=None):
+    m = {}
+    al_o, tok_o = oracle_accept(inp, mode, margins=m)
+    al_g, tok_g = gpu_accept(inp, mode)
+    if m.get("test") is not None and len(m["test"]):
+        say(f"  min test margin {m['test'].min():.2e}, min sample margin {m['sample'].min():.2e}")
+    bad = np.nonzero((al_o != al_g))[0]
+    assert bad.size == 0, f"accept_len differs at sequences {bad[:10]}: oracle {al_o[bad[:10]]} gpu {al_g[bad[:10]]}"
+    badt = np.nonzero(tok_o != tok_g)[0]
+    assert badt.size == 0, f"tokens differ at rows {badt[:10]}: oracle {tok_o[badt[:10]]} gpu {tok_g[badt[:10]]}"
+    return al_g
+
+
+def spec(**kw):
+    base = dict(name="acc_case", batch=24, kv_heads=1, group=1, head_dim=64, kv_len=64,
+                draft_len=(0, 1, 3, 7, 15), vocab=32000, mode="stochastic", target_std=3.0, draft_noise_std=1.0)
+    base.update(kw)
+    return WorkloadSpec(**base)
+
+
+@pytest.mark.parametrize("mode", ["stochastic", "greedy"])
+def test_tiny_workload(mode):
+    inp = generate(preset("tiny"))
+    say(f"case: tiny {mode}")
+    _check(inp, mode)
+
+
+@pytest.mark.parametrize("vocab", [32000, 1001, 4096, 5, 151936])
+@pytest.mark.parametrize("mode", ["stochastic", "greedy"])
+def test_vocab_sizes_and_ragged_drafts(vocab, mode):
+    inp = generate(spec(vocab=vocab, seed=vocab % 97))
+    say(f"case: V={vocab} {mode}")
+    _check(inp, mode)
+
+
+@pytest.mark.parametrize("alpha", [0.4, 0.6, 0.8])
+def test_fixed_acceptance_rate(alpha):
+    inp = generate(spec(batch=32, draft_len=15, alpha=alpha, seed=int(alpha * 10)))
+    say(f"case: alpha={alpha}")
+    al = _check(inp)
+    say(f"  mean AL {al.mean():.3f} vs tau {(1 - alpha ** 16) / (1 - alpha):.3f}")
+
+
+def test_greedy_argmax_drafts_accept_all_and_ties():
+    inp = generate(spec(batch=8, draft_len=7, vocab=5000, mode="greedy", draft_pick="argmax", draft_noise_std=0.0))
+    say("case: greedy, drafts = target argmax")
+    al = _check(inp, "greedy")
+    assert np.all(al == 8)
+    # ties: make two equal maxima in every target row; the lower id must win
+    t = inp.target_logits.clone()
+    top = t.max(dim=1).values + 1.0
+    t[:, 17] = top
+    t[:, 4000] = top
+    inp2 = inp.__class__(**{**inp.__dict__, "target_logits": t})
+    _check(inp2, "greedy")
+
+
+def test_infinite_logits_and_out_of_range_drafts():
+    inp = generate(spec(batch=6, draft_len=[4, 4, 4, 4, 4, 0], vocab=3000, seed=11))
+    t = inp.target_logits.clone()
+    d = inp.draft_logits.clone()
+    tok = inp.draft_tokens.clone()
+    qs = inp.q_start.tolist()
+    # seq 0: p(x1) = 0 -> reject at 0
+    t[qs[0], int(tok[0])] = -float("inf")
+    # seq 1: q(x1) = 0 < p(x1) -> accept at 0
+    d[4, int(tok[4])] = -float("inf")
+    # seq 2: out-of-range draft ids
+    tok[8] = -1
+    tok[9] = 3000
+    # seq 3: half the vocabulary impossible in the target
+    t[qs[3]:qs[4], ::2] = -float("inf")
+    inp2 = inp.__class__(**{**inp.__dict__, "target_logits": t, "draft_logits": d, "draft_tokens": tok})
+    say("case: -inf logits and out-of-range ids")
+    al = _check(inp2)
+    assert al[0] == 1 and al[1] >= 2 and al[2] == 1
+
+
+def test_identical_distributions_accept_everything():
+    inp = generate(spec(batch=8, draft_len=9, vocab=7000, seed=3))
+    qs = inp.q_start.tolist()
+    d = torch.cat([inp.target_logits[qs[b]:qs[b + 1] - 1] for b in range(8)])
+    inp2 = inp.__class__(**{**inp.__dict__, "draft_logits": d})
+    al = _check(inp2)
+    assert np.all(al == 10)
+
+
+def test_deterministic():
+    inp = generate(spec(seed=5))
+    a = gpu_accept(inp)
+    b = gpu_accept(inp)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("name", ["g8_kv32k_D15", "g32_kv128k_D3_greedy", "ragged_b64"])
+def test_full_size_workloads(name):
+    sp = preset(name)
+    say(f"case: full size accept {sp.name}")
+    # only the accept half is exercised here: shrink the KV side to one small head
+    inp = generate(sp.with_(kv_len=64, head_dim=64, kv_heads=1, group=1), device="cuda")
+    al = _check(inp)
+    say(f"  mean AL {al.mean():.3f}")
+
+
+def test_tile_sweep_alpha_full_size():
+    for alpha in (0.4, 0.8):
+        sp = preset("g8_kv32k_sweep", draft_len=31, alpha=alpha, kv_len=64, head_dim=64, kv_heads=1, group=1)
+        say(f"case: sweep accept D=31 alpha={alpha}")
+        inp = generate(sp, device="cuda")
+        _check(inp)

@@ -1,0 +1,121 @@
+"""GPU parity of verify attention against the fp64 oracle (|err| <= 2e-2 on
+bf16 outputs), through the C ABI.  Sizes span several 64-key tiles, ragged
+page tails, split-KV with the combine pass, every row-block variant
+(G*(1+D) up to 64, 128 and 256) and both head dims."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import verify_attention_unit
+from tests.gpu_util import ATTN_TOL, compare_attention, gpu_attention, say, unit_subproblem
+from workloads import WorkloadSpec, generate, preset
+
+pytestmark = pytest.mark.gpu
+
+
+def spec(**kw):
+    base = dict(name="attn_case", batch=3, kv_heads=2, group=8, head_dim=128, kv_len=[1000, 77, 2500],
+                draft_len=[15, 3, 7], vocab=64, mode="stochastic")
+    base.update(kw)
+    return WorkloadSpec(**base)
+
+
+def test_tiny_workload_full_parity():
+    inp = generate(preset("tiny"))
+    say("case: tiny d=64")
+    err = compare_attention(inp, gpu_attention(inp))
+    say(f"tiny max|err| = {err:.3e}")
+    assert err <= ATTN_TOL
+
+
+@pytest.mark.parametrize("kv_chunk", [0, 256, 64])
+def test_ragged_lengths_and_split_kv(kv_chunk):
+    inp = generate(spec())
+    say(f"case: ragged G=8 d=128 kv_chunk={kv_chunk}")
+    err = compare_attention(inp, gpu_attention(inp, kv_chunk=kv_chunk))
+    say(f"max|err| = {err:.3e}")
+    assert err <= ATTN_TOL
+
+
+@pytest.mark.parametrize("G,drafts,d", [
+    (8, [0, 0], 128),          # R = 8 (plain decode)
+    (4, [3, 2], 64),           # R = 16
+    (8, [3, 1], 128),          # R <= 64
+    (8, [15, 9], 128),         # R <= 128
+    (8, [31, 20], 128),        # R <= 256
+    (32, [3, 1], 128),         # G = 32, R = 128
+    (16, [15, 4], 64),         # R = 256, d = 64
+    (1, [0, 7], 128),          # G = 1
+])
+def test_row_block_variants(G, drafts, d):
+    inp = generate(spec(batch=2, group=G, head_dim=d, kv_len=[700, 1333], draft_len=drafts, seed=G + d))
+    say(f"case: G={G} drafts={drafts} d={d}")
+    err = compare_attention(inp, gpu_attention(inp, kv_chunk=256))
+    say(f"max|err| = {err:.3e}")
+    assert err <= ATTN_TOL
+    err = compare_attention(inp, gpu_attention(inp))
+    assert err <= ATTN_TOL
+
+
+def test_fp32_output_and_explicit_scale():
+    inp = generate(spec(seed=4))
+    say("case: fp32 output, scale 0.05")
+    from oracle import verify_attention
+    from tests.oracle_io import attention_args
+    ref = verify_attention(**attention_args(inp), scale=0.05)
+    out = gpu_attention(inp, out_dtype=torch.float32, softmax_scale=0.05).cpu().numpy()
+    err = float(np.abs(out - ref).max())
+    say(f"max|err| = {err:.3e}")
+    assert err <= 1e-2
+
+
+def test_nan_past_the_sequence_end_is_never_read():
+    inp = generate(spec(kv_len=[1001, 77, 35], seed=5), poison_tail=True)
+    say("case: NaN-poisoned page tails")
+    for chunk in (0, 64):
+        err = compare_attention(inp, gpu_attention(inp, kv_chunk=chunk))
+        assert err <= ATTN_TOL
+
+
+def test_sequence_shorter_than_its_block():
+    inp = generate(spec(batch=2, kv_len=[3, 16], draft_len=[5, 15], seed=6))
+    say("case: kv_len < 1+D")
+    out = gpu_attention(inp)
+    err = compare_attention(inp, out)
+    assert err <= ATTN_TOL
+    assert torch.all(out[0:3].float() == 0)
+
+
+def test_deterministic():
+    inp = generate(spec(seed=7))
+    a = gpu_attention(inp, kv_chunk=256)
+    b = gpu_attention(inp, kv_chunk=256)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("name,over", [
+    ("g8_kv32k_D15", {}),
+    ("g32_kv128k_D3_greedy", {}),
+    ("g8_kv32k_sweep", dict(draft_len=31)),
+    ("ragged_b64", {}),
+])
+def test_full_size_sampled_units(name, over):
+    """The benchmarked shapes and launch configuration; sampled (b, h) units
+    are recomputed by the oracle one by one."""
+    sp = preset(name, **over)
+    say(f"case: full size {sp.name}")
+    inp = generate(sp, device="cuda")
+    out = gpu_attention(inp)
+    rng = np.random.default_rng(0)
+    B, Hkv = sp.batch, sp.kv_heads
+    picks = {(0, 0), (B - 1, Hkv - 1)} | {(int(rng.integers(B)), int(rng.integers(Hkv))) for _ in range(3)}
+    worst = 0.0
+    for b, h in sorted(picks):
+        sub, (t0, t1) = unit_subproblem(inp, b)
+        ref = verify_attention_unit(**sub, b=0, h=h)                     # [1+D, G, d]
+        got = out[t0:t1, h * sp.group:(h + 1) * sp.group].float().cpu().numpy()
+        assert np.all(np.isfinite(got))
+        worst = max(worst, float(np.abs(got - ref).max()))
+    say(f"{sp.name}: max|err| over {len(picks)} units = {worst:.3e}")
+    assert worst <= ATTN_TOL

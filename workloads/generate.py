@@ -49,9 +49,10 @@ def _gen(seed: int, name: str, device: torch.device) -> torch.Generator:
 class WorkloadSpec:
     """Sizes and value distributions of one synthetic verify step.
 
-    ``kv_len`` is an int (every sequence) or ("lognormal", median, sigma, lo, hi).
-    ``draft_len`` is an int (every sequence) or a tuple of choices drawn
-    uniformly per sequence.  ``alpha`` switches the draft distribution to the
+    ``kv_len`` is an int (every sequence), a list (one per sequence) or
+    ("lognormal", median, sigma, lo, hi).  ``draft_len`` is an int (every
+    sequence), a list (one per sequence) or a tuple of choices drawn uniformly
+    per sequence.  ``alpha`` switches the draft distribution to the
     fixed-acceptance-rate construction q = (1-lam) p + lam/V (see generate()).
     """
 
@@ -124,6 +125,9 @@ def _structure(spec: WorkloadSpec):
     B = spec.batch
     if isinstance(spec.kv_len, int):
         kv = torch.full((B,), spec.kv_len, dtype=torch.int64)
+    elif isinstance(spec.kv_len, list):
+        kv = torch.tensor(spec.kv_len, dtype=torch.int64)
+        assert len(kv) == B
     else:
         kind, median, sigma, lo, hi = spec.kv_len
         assert kind == "lognormal"
@@ -131,6 +135,9 @@ def _structure(spec: WorkloadSpec):
         kv = torch.exp(math.log(median) + sigma * z).round().clamp(lo, hi).to(torch.int64)
     if isinstance(spec.draft_len, int):
         dl = torch.full((B,), spec.draft_len, dtype=torch.int64)
+    elif isinstance(spec.draft_len, list):
+        dl = torch.tensor(spec.draft_len, dtype=torch.int64)
+        assert len(dl) == B
     else:
         choices = torch.tensor(list(spec.draft_len), dtype=torch.int64)
         idx = torch.randint(len(choices), (B,), generator=_gen(spec.seed, "draft_len", torch.device("cpu")))
