@@ -80,7 +80,7 @@ typedef struct {
   int32_t max_draft;          /* upper bound on every D_b; G*(1+max_draft) <= 256 */
   float softmax_scale;        /* scores are scale * q.k; 0 selects 1/sqrt(d) */
   int32_t out_dtype;          /* sd_out_dtype */
-  int32_t kv_chunk;           /* keys per split-KV work item, a multiple of 64; 0 = chosen per call */
+  int32_t kv_chunk;           /* keys per split-KV work item: a multiple of 64, at most 8192; 0 = chosen per call */
 } sd_attn_desc;
 
 /* Accept/reject problem description. */

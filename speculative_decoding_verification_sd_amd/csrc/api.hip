@@ -47,6 +47,8 @@ sd_status check_attn(const sd_attn_desc* d, int32_t total_q) {
     return fail(SD_ERR_INVALID_ARG, "out_dtype=%d is not an sd_out_dtype", d->out_dtype);
   if (d->kv_chunk < 0 || d->kv_chunk % 64 != 0)
     return fail(SD_ERR_INVALID_ARG, "kv_chunk=%d must be 0 or a positive multiple of 64", d->kv_chunk);
+  if (d->kv_chunk > 8192)
+    return fail(SD_ERR_UNSUPPORTED, "kv_chunk=%d exceeds 8192 keys per work item", d->kv_chunk);
   if (total_q < d->num_seqs || (long long)total_q > (long long)d->num_seqs * (1LL + d->max_draft))
     return fail(SD_ERR_INVALID_ARG, "total_q=%d must lie in [num_seqs, num_seqs*(1+max_draft)] = [%d, %lld]",
                 total_q, d->num_seqs, (long long)d->num_seqs * (1LL + d->max_draft));

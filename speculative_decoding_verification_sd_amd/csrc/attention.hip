@@ -42,6 +42,7 @@ constexpr int kPage = 16;
 constexpr int kTileKeys = 64;
 constexpr int kThreads = 256;
 constexpr int kMinChunk = 256;
+constexpr int kMaxChunk = 8192;          // keys per work item; bounds the per-item page list in LDS
 constexpr int kTargetItems = 1024;
 constexpr int kPlanHeader = 4;
 
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(kThreads) void verify_attn_plan(AttnParams p, int f
       long long want = (red[0] * p.Hkv + kTargetItems - 1) / kTargetItems;
       want = (want + kTileKeys - 1) / kTileKeys * kTileKeys;
       const long long cap = ((long long)p.max_pages * kPage + kTileKeys - 1) / kTileKeys * kTileKeys;
-      chunk = (int)min(cap, max((long long)kMinChunk, want));
+      chunk = (int)min(min(cap, (long long)kMaxChunk), max((long long)kMinChunk, want));
     }
     s_chunk = chunk;
   }
@@ -119,27 +120,74 @@ __global__ __launch_bounds__(kThreads) void verify_attn_plan(AttnParams p, int f
   }
 }
 
-// XOR swizzle of the 8-byte slot (4 keys) inside a transposed V row (64 keys).
-__device__ __forceinline__ int v_swz(int d) { return (d & 15) ^ ((d >> 4) & 15); }
+// Wait until at most `n` vector-memory operations of this wave are in flight
+// (LDS-DMA loads count like any other vector load).
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // gfx9 s_waitcnt immediate: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
 
-template <int HD>
-struct Tile {
-  static constexpr int kDch = HD / 8;                 // 16-byte chunks per key row
-  static constexpr int kKPitch = HD * 2 + 16;          // padded K row in LDS (bytes)
-  static constexpr int kKBytes = kTileKeys * kKPitch;
-  static constexpr int kVBytes = HD * kTileKeys * 2;   // transposed V: HD rows of 64 keys
-  static constexpr int kStage = kKBytes + kVBytes;
-  static constexpr int kKLoads = kTileKeys * kDch / kThreads;
-  static constexpr int kVThreads = 16 * kDch;         // each loads 4 keys x 8 dims
+__device__ __forceinline__ void wait_lds() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+}
+
+// XOR swizzle of the 16-byte chunk index inside a K or V row of the LDS tile,
+// as a function of the key's position mod 16.  Eight consecutive keys read at
+// one logical chunk (K operand) and four consecutive keys read at two adjacent
+// chunks (transposed V reads) both land on distinct bank groups.
+__device__ __forceinline__ int chunk_swz(int k) {
+  return ((k & 3) << 1) ^ ((k >> 2) & 1) ^ (((k >> 3) & 1) << 3);
+}
+
+// One 16-byte-per-lane global->LDS DMA (global_load_lds_dwordx4): lane i's 16 bytes land
+// at LDS byte address lds_addr + 16*i (lds_addr is wave-uniform, passed in M0).  Issued as
+// inline asm so that the compiler does not pace LDS reads on these loads; the ring below
+// waits for them explicitly with s_waitcnt vmcnt before a barrier.
+__device__ __forceinline__ void dma16(const void* src, unsigned lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(src)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ void block_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int HD, int NRB>
+struct Ring {
+  static constexpr int kTile = 32;                       // keys per tile (two pages)
+  static constexpr int kRowB = HD * 2;                   // bytes per key row
+  static constexpr int kCpr = kRowB / 16;                // 16-byte chunks per row
+  static constexpr int kHalf = kTile * kRowB;            // K (or V) bytes per tile
+  static constexpr int kStageB = 2 * kHalf;
+  static constexpr int kStages = NRB >= 4 ? 8 : 4;       // ring depth
+  static constexpr int kLoadsPerWave = kHalf / 1024 / 4; // DMA instructions per wave for K (same for V)
+  static constexpr int kKeysPerLoad = 1024 / kRowB;      // key rows one wave instruction fills
 };
 
 // ---------------------------------------------------------------------------
 template <int HD, int NRB, int OUT_F32>
 __global__ __launch_bounds__(kThreads, (NRB >= 4 ? 1 : 2)) void verify_attn_main(AttnParams p) {
-  using T = Tile<HD>;
+  using RG = Ring<HD, NRB>;
   constexpr int NKC = HD / 32;   // MFMA k-steps over d for S
   constexpr int NDB = HD / 16;   // 16-wide d blocks of O
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * T::kStage];
+  constexpr int LPW = 2 * RG::kLoadsPerWave;
+  constexpr float kLazy = 8.f;   // rescale only when a row max grows by more than 2^8
+  // one LDS object: the K/V ring followed by the page ids of the current item
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[RG::kStages * RG::kStageB +
+                                                              (kMaxChunk / kPage + 2) * 4];
+  int* s_pages = (int*)(smem + RG::kStages * RG::kStageB);
+  __attribute__((address_space(3))) unsigned char* lds_smem = (__attribute__((address_space(3))) unsigned char*)smem;
+  const unsigned lds_base = (unsigned)(size_t)lds_smem;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -150,6 +198,13 @@ __global__ __launch_bounds__(kThreads, (NRB >= 4 ? 1 : 2)) void verify_attn_main
   const int total = min(p.plan[1], p.item_cap);
   const int* item_start = p.plan + kPlanHeader;
   const int Hq = p.Hkv * p.G;
+
+  // lane-constant LDS offsets
+  const int kswz = chunk_swz(l16) & (RG::kCpr - 1);                   // K operand: key = kb*16 + l16
+  const int vkey = g4 * 4 + (l16 >> 2);                               // transposed V read: key row
+  const int vswz = chunk_swz(vkey) & (RG::kCpr - 1);
+  const int vsub = (l16 & 3) >> 1;                                    // chunk within the 16-wide d block
+  const int vbyte = (l16 & 1) * 8;
 
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
     int lo = 0, hi = p.B;
@@ -170,6 +225,46 @@ __global__ __launch_bounds__(kThreads, (NRB >= 4 ? 1 : 2)) void verify_attn_main
     const int k_end = min(N, k_begin + chunk);
     const int* bt = p.block_table + (size_t)b * p.max_pages;
     const bool wave_active = wave * NRB * 16 < R;
+    const int ntiles = k_end > k_begin ? (k_end - k_begin + RG::kTile - 1) / RG::kTile : 0;
+    static_assert(kMaxChunk % RG::kTile == 0, "tiles never straddle an item");
+
+    // Issue this wave's share of the LDS-DMA loads of tile `tile` into its ring stage.
+    auto issue = [&](int tile) {
+      const int ts = k_begin + tile * RG::kTile;
+      unsigned char* st = smem + (tile % RG::kStages) * RG::kStageB;
+#pragma unroll
+      for (int kv = 0; kv < 2; ++kv) {
+        const uint16_t* cache = kv ? p.v : p.k;
+#pragma unroll
+        for (int i = 0; i < RG::kLoadsPerWave; ++i) {
+          // the rows one instruction fills lie in one page
+          const int row0 = (wave * RG::kLoadsPerWave + i) * RG::kKeysPerLoad;
+          const int pid = s_pages[tile * (RG::kTile / kPage) + row0 / kPage];
+          const int key = row0 + lane / RG::kCpr;
+          const int pc = lane % RG::kCpr;
+          const int lc = pc ^ (chunk_swz(key & 15) & (RG::kCpr - 1));
+          const int gk = ts + key;
+          // keys past the end read a valid dummy chunk and are zeroed in LDS before use
+          const uint16_t* src = gk < k_end
+              ? cache + (((size_t)pid * p.Hkv + h) * kPage + (gk & (kPage - 1))) * HD + lc * 8
+              : cache;
+          dma16(src, lds_base + (unsigned)((st - smem) + kv * RG::kHalf + row0 * RG::kRowB));
+        }
+      }
+    };
+    // Zero the key rows of tile `tile` at or past k_end that this wave loaded.
+    auto zero_tail = [&](int tile) {
+      const int ts = k_begin + tile * RG::kTile;
+      unsigned char* st = smem + (tile % RG::kStages) * RG::kStageB;
+#pragma unroll
+      for (int kv = 0; kv < 2; ++kv)
+#pragma unroll
+        for (int i = 0; i < RG::kLoadsPerWave; ++i) {
+          const int row0 = (wave * RG::kLoadsPerWave + i) * RG::kKeysPerLoad;
+          if (ts + row0 + lane / RG::kCpr >= k_end)
+            *(u32x4*)(st + kv * RG::kHalf + row0 * RG::kRowB + lane * 16) = u32x4{0, 0, 0, 0};
+        }
+    };
 
     // Query fragments (B operand of S^T = K Q^T): lane holds row l16, dims g4*8..+7 of each 32-wide step.
     bf16x8 qf[NRB][NKC];
@@ -200,85 +295,56 @@ __global__ __launch_bounds__(kThreads, (NRB >= 4 ? 1 : 2)) void verify_attn_main
       for (int db = 0; db < NDB; ++db) o[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    const int ntiles = k_end > k_begin ? (k_end - k_begin + kTileKeys - 1) / kTileKeys : 0;
-    u32x4 kreg[T::kKLoads];
-    u32x4 vreg[4];
-
-    auto page_block = [&](int key, const uint16_t* cache) -> const uint16_t* {
-      int pid = bt[key / kPage];
-      pid = min(max(pid, 0), p.num_pages - 1);
-      return cache + (((size_t)pid * p.Hkv + h) * kPage + (key & (kPage - 1))) * HD;
-    };
-    auto load_tile = [&](int tile) {
-      const int ts = k_begin + tile * kTileKeys;
+    // page ids of this item (clamped into the pool), then drain every load issued so far so
+    // that the ring's vmcnt accounting below only ever sees its own LDS-DMA loads
+    const int page0 = k_begin / kPage;
+    const int npages = (k_end + kPage - 1) / kPage - page0;
+    for (int j = tid; j < npages; j += kThreads) s_pages[j] = min(max(bt[page0 + j], 0), p.num_pages - 1);
+    wait_vmem<0>();
+    wait_lds();
+    block_sync();
 #pragma unroll
-      for (int j = 0; j < T::kKLoads; ++j) {
-        const int c = j * kThreads + tid;
-        const int key = ts + c / T::kDch;
-        const int dch = c % T::kDch;
-        kreg[j] = key < k_end ? *(const u32x4*)(page_block(key, p.k) + dch * 8) : u32x4{0, 0, 0, 0};
-      }
-      if (tid < T::kVThreads) {
-        const int dch = tid % T::kDch;
-        const int kq = tid / T::kDch;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = ts + kq * 4 + r;
-          vreg[r] = key < k_end ? *(const u32x4*)(page_block(key, p.v) + dch * 8) : u32x4{0, 0, 0, 0};
-        }
-      }
-    };
-    auto store_tile = [&](int stage) {
-      unsigned char* base = smem + stage * T::kStage;
-#pragma unroll
-      for (int j = 0; j < T::kKLoads; ++j) {
-        const int c = j * kThreads + tid;
-        *(u32x4*)(base + (c / T::kDch) * T::kKPitch + (c % T::kDch) * 16) = kreg[j];
-      }
-      if (tid < T::kVThreads) {
-        const int dch = tid % T::kDch;
-        const int kq = tid / T::kDch;
-        unsigned char* vt = base + T::kKBytes;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int w = e >> 1;
-          const int d = dch * 8 + e;
-          unsigned lo, hi;
-          if (e & 1) {
-            lo = (vreg[0][w] >> 16) | (vreg[1][w] & 0xFFFF0000u);
-            hi = (vreg[2][w] >> 16) | (vreg[3][w] & 0xFFFF0000u);
-          } else {
-            lo = (vreg[0][w] & 0xFFFFu) | (vreg[1][w] << 16);
-            hi = (vreg[2][w] & 0xFFFFu) | (vreg[3][w] << 16);
-          }
-          *(u32x2*)(vt + d * 128 + ((kq ^ v_swz(d)) * 8)) = u32x2{lo, hi};
-        }
-      }
-    };
-
-    if (ntiles > 0) {
-      load_tile(0);
-      store_tile(0);
-    }
-    __syncthreads();
+    for (int t = 0; t < RG::kStages - 1; ++t)
+      if (t < ntiles) issue(t);
 
     for (int tile = 0; tile < ntiles; ++tile) {
-      const bool more = tile + 1 < ntiles;
-      if (more) load_tile(tile + 1);
+      // tiles issued after this one: tile+1 .. min(ntiles-1, tile+kStages-2)
+      const int after = min(RG::kStages - 2, ntiles - 1 - tile);
+      if constexpr (RG::kStages == 4) {
+        if (after >= 2) wait_vmem<2 * LPW>();
+        else if (after == 1) wait_vmem<LPW>();
+        else wait_vmem<0>();
+      } else {
+        switch (after) {
+          case 6: wait_vmem<6 * LPW>(); break;
+          case 5: wait_vmem<5 * LPW>(); break;
+          case 4: wait_vmem<4 * LPW>(); break;
+          case 3: wait_vmem<3 * LPW>(); break;
+          case 2: wait_vmem<2 * LPW>(); break;
+          case 1: wait_vmem<LPW>(); break;
+          default: wait_vmem<0>(); break;
+        }
+      }
+      const int ts = k_begin + tile * RG::kTile;
+      if (ts + RG::kTile > k_end) {
+        zero_tail(tile);
+        wait_lds();
+      }
+      block_sync();
+      if (tile + RG::kStages - 1 < ntiles) issue(tile + RG::kStages - 1);
 
       if (wave_active) {
-        const unsigned char* Ks = smem + (tile & 1) * T::kStage;
-        const unsigned char* Vs = Ks + T::kKBytes;
-        const int ts = k_begin + tile * kTileKeys;
-        const bool need_mask = ts + kTileKeys > N - D;
+        const unsigned char* Ks = smem + (tile % RG::kStages) * RG::kStageB;
+        const unsigned char* Vs = Ks + RG::kHalf;
+        const bool need_mask = ts + RG::kTile > N - D;
 
-        f32x4 sc[4][NRB];
+        f32x4 sc[2][NRB];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
+        for (int kb = 0; kb < 2; ++kb) {
           bf16x8 kf[NKC];
+          const unsigned char* krow = Ks + (kb * 16 + l16) * RG::kRowB;
 #pragma unroll
-          for (int c = 0; c < NKC; ++c)
-            kf[c] = *(const bf16x8*)(Ks + (kb * 16 + l16) * T::kKPitch + c * 64 + g4 * 16);
+          for (int c = 0; c < NKC; ++c) kf[c] = *(const bf16x8*)(krow + (((c * 4 + g4) ^ kswz) * 16));
 #pragma unroll
           for (int rb = 0; rb < NRB; ++rb) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -289,71 +355,73 @@ __global__ __launch_bounds__(kThreads, (NRB >= 4 ? 1 : 2)) void verify_attn_main
           }
         }
 
-        bf16x8 pf[NRB][2];
+        // online softmax, one query row per lane; lazy rescale of the running max
+        float mt[NRB];
+        bool grow = false;
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
           if (need_mask) {
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
               for (int e = 0; e < 4; ++e)
                 if (ts + kb * 16 + g4 * 4 + e > pos[rb]) sc[kb][rb][e] = -INFINITY;
           }
-          float mt = sc[0][rb][0];
+          float m = fmaxf(fmaxf(sc[0][rb][0], sc[0][rb][1]), fmaxf(sc[0][rb][2], sc[0][rb][3]));
+          m = fmaxf(m, fmaxf(fmaxf(sc[1][rb][0], sc[1][rb][1]), fmaxf(sc[1][rb][2], sc[1][rb][3])));
+          m = fmaxf(m, __shfl_xor(m, 16));
+          m = fmaxf(m, __shfl_xor(m, 32));
+          mt[rb] = m * p.scale_log2;
+          grow |= mt[rb] > m_run[rb] + kLazy;
+        }
+        if (__any(grow)) {
 #pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
+          for (int rb = 0; rb < NRB; ++rb) {
+            if (mt[rb] > m_run[rb] + kLazy) {
+              const float alpha = fast_exp2(m_run[rb] - mt[rb]);
+              m_run[rb] = mt[rb];
+              l_run[rb] *= alpha;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) mt = fmaxf(mt, sc[kb][rb][e]);
-          mt = fmaxf(mt, __shfl_xor(mt, 16));
-          mt = fmaxf(mt, __shfl_xor(mt, 32));
-          const float m_new = fmaxf(m_run[rb], mt * p.scale_log2);
-          const float mc = m_new == -INFINITY ? 0.f : m_new;
-          const float alpha = fast_exp2(m_run[rb] - mc);
-          m_run[rb] = m_new;
-          float psum = 0.f;
-          float pv[4][4];
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              pv[kb][e] = fast_exp2(fmaf(sc[kb][rb][e], p.scale_log2, -mc));
-              psum += pv[kb][e];
+              for (int db = 0; db < NDB; ++db) o[rb][db] *= alpha;
             }
-          l_run[rb] = l_run[rb] * alpha + psum;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) o[rb][db] *= alpha;
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            bf16x8 t;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              t[e] = (__bf16)pv[2 * h2][e];
-              t[4 + e] = (__bf16)pv[2 * h2 + 1][e];
-            }
-            pf[rb][h2] = t;
           }
         }
+        bf16x8 pf[NRB];
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+          const float mc = m_run[rb] == -INFINITY ? 0.f : m_run[rb];
+          float psum = 0.f;
+          bf16x8 t;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float pv = fast_exp2(fmaf(sc[kb][rb][e], p.scale_log2, -mc));
+              psum += pv;
+              t[kb * 4 + e] = (__bf16)pv;
+            }
+          l_run[rb] += psum;
+          pf[rb] = t;
+        }
 
+        // O^T += V^T P^T: V read transposed from LDS, keys in the order of the S^T accumulators
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
+        for (int db = 0; db < NDB; ++db) {
+          const int pc = (db * 2 + vsub) ^ vswz;
+          const int voff = (tile % RG::kStages) * RG::kStageB + RG::kHalf + vkey * RG::kRowB + pc * 16 + vbyte;
+          const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_smem + voff));
+          const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_smem + voff + 16 * RG::kRowB));
+          const bf16x8 vf = __builtin_bit_cast(
+              bf16x8, u32x4{__builtin_bit_cast(u32x2, lo4)[0], __builtin_bit_cast(u32x2, lo4)[1],
+                            __builtin_bit_cast(u32x2, hi4)[0], __builtin_bit_cast(u32x2, hi4)[1]});
 #pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const int d = db * 16 + l16;
-            const int sw = v_swz(d);
-            const unsigned char* vrow = Vs + d * 128;
-            const u32x2 va = *(const u32x2*)(vrow + (((h2 * 8 + g4) ^ sw) * 8));
-            const u32x2 vb = *(const u32x2*)(vrow + (((h2 * 8 + 4 + g4) ^ sw) * 8));
-            const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{va[0], va[1], vb[0], vb[1]});
-#pragma unroll
-            for (int rb = 0; rb < NRB; ++rb)
-              o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[rb][h2], o[rb][db], 0, 0, 0);
-          }
+          for (int rb = 0; rb < NRB; ++rb)
+            o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[rb], o[rb][db], 0, 0, 0);
         }
       }
-
-      if (more) store_tile((tile + 1) & 1);
-      __syncthreads();
     }
+    // every wave is done with the ring before the next item's loads land in it
+    block_sync();
 
     if (wave_active) {
 #pragma unroll
@@ -464,7 +532,11 @@ static AttnLayout attn_layout(int B, int Hkv, int G, int HD, int max_pages, int 
   if (kv_chunk > 0) {
     cap = (long long)B * Hkv * ((max_keys + kv_chunk - 1) / kv_chunk);
   } else {
+    // auto chunk = clamp(ceil(keys*Hkv/target), kMinChunk, kMaxChunk): below the upper clamp the
+    // items number at most target + B*Hkv, at it at most B*Hkv*ceil(max_keys/kMaxChunk)
     cap = kTargetItems + (long long)B * Hkv;
+    const long long by_max = (long long)B * Hkv * ((max_keys + kMaxChunk - 1) / kMaxChunk);
+    cap = cap > by_max ? cap : by_max;
     const long long by_min = (long long)B * Hkv * ((max_keys + kMinChunk - 1) / kMinChunk);
     cap = cap < by_min ? cap : by_min;
   }
