@@ -15,7 +15,7 @@ from typing import Optional
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libsdverify.so")
+LIB_PATH = os.environ.get("SDVERIFY_LIB") or os.path.join(HERE, "libsdverify.so")
 
 SD_OK, SD_ERR_INVALID_ARG, SD_ERR_UNSUPPORTED, SD_ERR_WORKSPACE, SD_ERR_HIP = range(5)
 SD_ACCEPT_GREEDY, SD_ACCEPT_STOCHASTIC = 0, 1

@@ -23,6 +23,13 @@ LIB_NAME = "libsdverify.so"
 ARCH = "gfx950"
 
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Per-file flags.  Verify attention never carries NaN through its max/exp
+# chain (masked scores are -inf and unused LDS rows are zeroed), so its
+# translation unit drops NaN-quieting canonicalisations around fmax.  Its
+# LDS-DMA inline asm writes M0 (declared as clobbered); tests/test_attention_isa.py
+# checks on the generated ISA that nothing else in those kernels uses M0, so the
+# corresponding clang warning is silenced here.
+FILE_FLAGS = {"attention.hip": ["-fno-honor-nans", "-Wno-inline-asm"]}
 COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function", "-fvisibility=hidden",
                 "-I", INCLUDE, "-I", CSRC]
 
@@ -38,13 +45,14 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
+def build(verbose: bool = False, extra_flags=(), out: str = None) -> str:
     cc = hipcc()
-    out = os.path.join(HERE, LIB_NAME)
+    out = out or os.path.join(HERE, LIB_NAME)
     with tempfile.TemporaryDirectory(prefix="sdv_build_") as tmp:
         def compile_one(src):
             obj = os.path.join(tmp, os.path.basename(src) + ".o")
-            cmd = [cc, *COMMON_FLAGS, *DEVICE_FLAGS, *extra_flags, "-c", src, "-o", obj]
+            cmd = [cc, *COMMON_FLAGS, *DEVICE_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []),
+                   *extra_flags, "-c", src, "-o", obj]
             r = subprocess.run(cmd, capture_output=True, text=True)
             msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                              if "packed-fp32-ops" not in l)

@@ -1,0 +1,78 @@
+"""Checks on the generated gfx950 ISA of the verify-attention kernels (CPU only:
+hipcc cross-compiles the device code to assembly).
+
+* M0 is written only by the LDS-DMA sequence (s_mov_b32 m0 / s_nop / global_load_lds),
+  so the inline-asm DMA's M0 clobber cannot disturb anything the compiler keeps in M0.
+* No transposed V read (ds_read_b64_tr_b16) or K read (ds_read_b128) waits for every
+  vector load in flight: between a barrier and the LDS reads of a tile there is no
+  s_waitcnt vmcnt(0), which would drain the DMA ring on every tile.
+"""
+
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from speculative_decoding_verification_sd_amd import build as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "speculative_decoding_verification_sd_amd", "csrc", "attention.hip")
+
+
+@pytest.fixture(scope="module")
+def kernels(tmp_path_factory):
+    try:
+        cc = B.hipcc()
+    except RuntimeError:
+        pytest.skip("hipcc not available")
+    out = tmp_path_factory.mktemp("isa") / "attention.s"
+    cmd = [cc, *B.COMMON_FLAGS, *B.DEVICE_FLAGS, *B.FILE_FLAGS.get("attention.hip", []), "--cuda-device-only",
+           "-S", "-Wno-inline-asm", SRC, "-o", str(out)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-3000:]
+    text = out.read_text()
+    found = {}
+    for m in re.finditer(r"^(_Z\w*verify_attn_main\w*):[^\n]*\n(.*?)^\s*s_endpgm", text, re.M | re.S):
+        found[m.group(1)] = [l.strip() for l in m.group(2).split("\n")]
+    assert len(found) >= 6, "expected every verify_attn_main instantiation"
+    return found
+
+
+def _instrs(lines):
+    return [l for l in lines if l and not l.startswith((";", ".")) and not l.endswith(":")]
+
+
+def test_m0_written_only_by_the_dma_sequence(kernels):
+    for name, lines in kernels.items():
+        ins = _instrs(lines)
+        for i, l in enumerate(ins):
+            if re.search(r"\bm0\b", l):
+                assert l.startswith("s_mov_b32 m0, s"), (name, l)
+                assert ins[i + 1] == "s_nop 0" and ins[i + 2].startswith("global_load_lds_dwordx4"), (name, ins[i:i + 3])
+
+
+def test_no_full_vmem_drain_before_tile_reads(kernels):
+    for name, lines in kernels.items():
+        ins = _instrs(lines)
+        since_barrier = None
+        for l in ins:
+            if l.startswith("s_barrier"):
+                since_barrier = []
+                continue
+            if since_barrier is None:
+                continue
+            if l.startswith(("ds_read_b64_tr_b16", "ds_read_b128")):
+                assert not any(re.match(r"s_waitcnt .*vmcnt\(0\)", x) for x in since_barrier), (name, l)
+                since_barrier = None
+                continue
+            since_barrier.append(l)
+
+
+def test_dma_base_is_not_sign_extended(kernels):
+    """The scalar DMA base is built from two readfirstlane words; the low word must be
+    zero-extended (a sign-extending s_bfe_i64 there corrupts addresses whose low word
+    has bit 31 set)."""
+    for name, lines in kernels.items():
+        assert not any(l.startswith("s_bfe_i64") for l in _instrs(lines)), name
