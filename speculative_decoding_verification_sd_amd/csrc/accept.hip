@@ -10,37 +10,42 @@
 // ("How does speculative decoding speed up LLM inference?", sections
 // "Mechanism" and "Math intuition").
 //
-// Kernels (all vocab-parallel except the per-sequence decision):
-//   1. accept_rowstats   grid = rows x vocab chunks.  Per chunk of 4096 logits:
-//                        max, lowest-index argmax and sum of exp(x - max)
-//                        (fp32 exp, fp64 accumulation).  One pass over every
+// Kernels:
+//   1. accept_rowstats   grid = rows x vocab chunks (8192 logits each).  Chunk
+//                        max (greedy: lowest-index argmax; stochastic: sum of
+//                        exp(x - max) accumulated in fp64).  One pass over every
 //                        target (and draft) row: this is the step's HBM cost.
-//   2. accept_decide     one workgroup per sequence.  Merges the chunk
-//                        statistics into log-normalisers (fp64), runs the D_b
-//                        tests in parallel (fp64 ratios), finds the first
-//                        failure n, writes AL and the accepted tokens.
-//   3. accept_residual   grid = vocab chunks x sequences (stochastic only).
+//   2. accept_decide     one workgroup per sequence.  Loads the sequence's
+//                        chunk statistics into LDS, merges them into per-row
+//                        log-normalisers (fp64), runs the D_b tests in parallel
+//                        (fp64 ratios), finds the first failure n, writes AL
+//                        and the accepted tokens, and (stochastic) resets the
+//                        sequence's arrival counter for kernel 3.
+//   3. accept_sample     grid = vocab chunks x sequences (stochastic only).
 //                        fp64 chunk sums of the residual max(0, p - q) at row
-//                        n (or of p at row D when everything passed).
-//   4. accept_sample     one workgroup per sequence.  Finds the chunk holding
-//                        u*Z from the chunk sums, rebuilds that chunk's fp64
-//                        weights and scans them to the first prefix sum > u*Z.
+//                        n (of p at row D when every draft passed); the last
+//                        chunk of a sequence to finish then finds the chunk
+//                        holding u*Z and scans it in fp64 to the first prefix
+//                        sum > u*Z.
 
-#include <math.h>
 #include <limits.h>
+#include <math.h>
 
 #include "common.h"
 
 namespace sdv {
 
 constexpr int kAccThreads = 256;
-constexpr int kChunk = 4096;                      // logits per workgroup
-constexpr int kPerThread = kChunk / kAccThreads;  // 16
+constexpr int kChunk = 8192;                      // logits per row-statistics workgroup
+constexpr int kPerThread = kChunk / kAccThreads;  // 32
+constexpr int kSChunk = 4096;                     // logits per sampling workgroup
+constexpr int kSPerThread = kSChunk / kAccThreads;
+constexpr int kDecideSlots = 2048;                // chunk statistics staged in LDS per pass
 
 struct RowPart {
   float m;     // chunk max
-  int idx;     // lowest index attaining it
-  double s;    // sum of exp(x - m) over the chunk
+  int idx;     // lowest index attaining it (greedy)
+  double s;    // sum of exp(x - m) over the chunk (stochastic)
 };
 
 struct SeqState {
@@ -48,7 +53,8 @@ struct SeqState {
   int residual;     // 1: sample max(0, p - q) at row n; 0: sample p at row D
   double lse_p;     // log-normaliser of the target row n
   double lse_q;     // log-normaliser of the draft row n (residual only)
-  double pad;
+  unsigned arrived; // sampling workgroups done (reset by accept_decide)
+  int pad;
 };
 
 struct AccParams {
@@ -61,8 +67,8 @@ struct AccParams {
   int* out_tokens;
   RowPart* part;      // [rows, nchunk]
   SeqState* state;    // [B]
-  double* rsum;       // [B, nchunk, 2]  (residual, p) chunk sums
-  int B, T, V, nchunk, max_draft;
+  double* rsum;       // [B, nschunk, 2]  (residual, p) chunk sums
+  int B, T, V, nchunk, nschunk, max_draft;
 };
 
 __device__ __forceinline__ bool better(float m1, int i1, float m0, int i0) {
@@ -83,6 +89,17 @@ __device__ __forceinline__ void block_argmax(float& m, int& idx, float* sm, int*
   for (int k = 1; k < kAccThreads / 64; ++k)
     if (better(sm[k], si[k], m, idx)) { m = sm[k]; idx = si[k]; }
   __syncthreads();
+}
+
+__device__ __forceinline__ float block_max(float m, float* sm) {
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) sm[w] = m;
+  __syncthreads();
+  m = sm[0];
+  for (int k = 1; k < kAccThreads / 64; ++k) m = fmaxf(m, sm[k]);
+  __syncthreads();
+  return m;
 }
 
 __device__ __forceinline__ double block_sum(double v, double* sd) {
@@ -117,8 +134,9 @@ __global__ __launch_bounds__(kAccThreads) void accept_rowstats(AccParams p) {
   const int tid = threadIdx.x;
   const int j0 = c * kChunk;
 
+  // element k of this thread has index j0 + (k/4)*1024 + tid*4 + k%4 (VEC4) or
+  // j0 + k*256 + tid (scalar): increasing in k either way
   float x[kPerThread];
-  int jx[kPerThread];
   if (VEC4) {
 #pragma unroll
     for (int k = 0; k < kPerThread / 4; ++k) {
@@ -131,36 +149,57 @@ __global__ __launch_bounds__(kAccThreads) void accept_rowstats(AccParams p) {
         for (int e = 0; e < 4; ++e) v[e] = j + e < p.V ? src[j + e] : -INFINITY;
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) { x[k * 4 + e] = v[e]; jx[k * 4 + e] = j + e; }
+      for (int e = 0; e < 4; ++e) x[k * 4 + e] = v[e];
     }
   } else {
 #pragma unroll
     for (int k = 0; k < kPerThread; ++k) {
       const int j = j0 + k * kAccThreads + tid;
       x[k] = j < p.V ? src[j] : -INFINITY;
-      jx[k] = j;
     }
   }
-  // indices visited in increasing order: strict '>' keeps the lowest index on ties
-  float m = -INFINITY;
-  int idx = INT_MAX;
-#pragma unroll
-  for (int k = 0; k < kPerThread; ++k)
-    if (x[k] > m || (idx == INT_MAX && jx[k] < p.V && x[k] == m)) { m = x[k]; idx = jx[k]; }
-  block_argmax(m, idx, sm, si);
+  auto index_of = [&](int k) {
+    return VEC4 ? j0 + ((k >> 2) * kAccThreads + tid) * 4 + (k & 3) : j0 + k * kAccThreads + tid;
+  };
 
-  double s = 0.0;
-  if (STOCH && m != -INFINITY) {
+  if (!STOCH) {
+    // lowest-index maximum: strict '>' over increasing indices; a row of -inf
+    // still reports a real index (first element inside the vocabulary)
+    float m = -INFINITY;
+    int idx = INT_MAX;
 #pragma unroll
-    for (int k = 0; k < kPerThread; ++k) s += (double)expf(x[k] - m);
-    s = block_sum(s, sd);
-  }
-  if (tid == 0) {
-    RowPart r;
-    r.m = m;
-    r.idx = idx;
-    r.s = s;
-    p.part[(size_t)row * p.nchunk + c] = r;
+    for (int k = 0; k < kPerThread; ++k) {
+      const int j = index_of(k);
+      if (x[k] > m || (idx == INT_MAX && j < p.V)) { m = x[k]; idx = j; }
+    }
+    block_argmax(m, idx, sm, si);
+    if (tid == 0) {
+      RowPart r;
+      r.m = m;
+      r.idx = idx;
+      r.s = 0.0;
+      p.part[(size_t)row * p.nchunk + c] = r;
+    }
+  } else {
+    float m = x[0];
+#pragma unroll
+    for (int k = 1; k < kPerThread; ++k) m = fmaxf(m, x[k]);
+    m = block_max(m, sm);
+    double s = 0.0;
+    if (m != -INFINITY) {
+      // exp(x - m) as 2^((x - m) log2 e); fp32 terms, fp64 running sum
+      const float ml = m * 1.4426950408889634f;
+#pragma unroll
+      for (int k = 0; k < kPerThread; ++k) s += (double)fast_exp2(fmaf(x[k], 1.4426950408889634f, -ml));
+      s = block_sum(s, sd);
+    }
+    if (tid == 0) {
+      RowPart r;
+      r.m = m;
+      r.idx = 0;
+      r.s = s;
+      p.part[(size_t)row * p.nchunk + c] = r;
+    }
   }
 }
 
@@ -168,6 +207,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_rowstats(AccParams p) {
 template <int STOCH>
 __global__ __launch_bounds__(kAccThreads) void accept_decide(AccParams p) {
   extern __shared__ double dyn[];               // lse_p[D+1], lse_q[D], argmax[D+1]
+  __shared__ RowPart stage[kDecideSlots];
   __shared__ int first_fail;
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
@@ -177,29 +217,40 @@ __global__ __launch_bounds__(kAccThreads) void accept_decide(AccParams p) {
   double* lse_p = dyn;
   double* lse_q = dyn + (p.max_draft + 1);
   int* amax = (int*)(dyn + 2 * p.max_draft + 1);
-  const bool ok = seq_ok(p, t0, D, d0);
-  if (!ok) {
+  if (!seq_ok(p, t0, D, d0)) {
     if (tid == 0) p.accept_len[b] = 0;
     return;
   }
 
+  // rows: r <= D -> target row t0+r; r > D -> draft row d0+r-D-1
   const int nrows = STOCH ? 2 * D + 1 : D + 1;
-  for (int r = tid; r < nrows; r += kAccThreads) {
-    const int prow = r <= D ? t0 + r : p.T + d0 + (r - D - 1);
-    const RowPart* pr = p.part + (size_t)prow * p.nchunk;
-    float M = -INFINITY;
-    int ai = INT_MAX;
-    for (int c = 0; c < p.nchunk; ++c)
-      if (better(pr[c].m, pr[c].idx, M, ai)) { M = pr[c].m; ai = pr[c].idx; }
-    double lse = 0.0;
-    if (STOCH) {
-      double Z = 0.0;
-      for (int c = 0; c < p.nchunk; ++c)
-        if (pr[c].m != -INFINITY) Z += exp((double)pr[c].m - (double)M) * pr[c].s;
-      lse = (double)M + log(Z);
+  const int rows_per_pass = max(1, kDecideSlots / p.nchunk);
+  for (int r0 = 0; r0 < nrows; r0 += rows_per_pass) {
+    const int nr = min(rows_per_pass, nrows - r0);
+    __syncthreads();
+    for (int e = tid; e < nr * p.nchunk; e += kAccThreads) {
+      const int r = r0 + e / p.nchunk;
+      const int prow = r <= D ? t0 + r : p.T + d0 + (r - D - 1);
+      stage[e] = p.part[(size_t)prow * p.nchunk + (e % p.nchunk)];
     }
-    if (r <= D) { lse_p[r] = lse; amax[r] = ai; }
-    else lse_q[r - D - 1] = lse;
+    __syncthreads();
+    for (int rr = tid; rr < nr; rr += kAccThreads) {
+      const RowPart* pr = stage + rr * p.nchunk;
+      const int r = r0 + rr;
+      float M = -INFINITY;
+      int ai = INT_MAX;
+      for (int c = 0; c < p.nchunk; ++c)
+        if (better(pr[c].m, pr[c].idx, M, ai)) { M = pr[c].m; ai = pr[c].idx; }
+      double lse = 0.0;
+      if (STOCH) {
+        double Z = 0.0;
+        for (int c = 0; c < p.nchunk; ++c)
+          if (pr[c].m != -INFINITY) Z += exp((double)pr[c].m - (double)M) * pr[c].s;
+        lse = (double)M + log(Z);
+      }
+      if (r <= D) { lse_p[r] = lse; amax[r] = ai; }
+      else lse_q[r - D - 1] = lse;
+    }
   }
   if (tid == 0) first_fail = D;
   __syncthreads();
@@ -235,13 +286,14 @@ __global__ __launch_bounds__(kAccThreads) void accept_decide(AccParams p) {
       st.residual = n < D;
       st.lse_p = lse_p[n];
       st.lse_q = n < D ? lse_q[n] : 0.0;
-      st.pad = 0.0;
+      st.arrived = 0u;
+      st.pad = 0;
       p.state[b] = st;
     }
   }
 }
 
-// fp64 weight of token j for the sampling row of one sequence.
+// fp64 weights of token j for the sampling row of one sequence.
 __device__ __forceinline__ void sample_weights(const AccParams& p, const SeqState& st, int t0, int d0, int j,
                                                double& w, double& pj) {
   const double pt = exp((double)p.target[(size_t)(t0 + st.n) * p.V + j] - st.lse_p);
@@ -255,18 +307,25 @@ __device__ __forceinline__ void sample_weights(const AccParams& p, const SeqStat
 }
 
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kAccThreads) void accept_residual(AccParams p) {
+__global__ __launch_bounds__(kAccThreads) void accept_sample(AccParams p) {
   __shared__ double sd[4];
+  __shared__ double scan[kAccThreads];
+  __shared__ int s_last, s_chunk, s_usep, s_tok;
+  __shared__ double s_base, s_T;
   const int c = blockIdx.x;
   const int b = blockIdx.y;
+  const int tid = threadIdx.x;
   const int t0 = p.q_start[b];
+  const int D = seq_d(p, b);
   const int d0 = t0 - b;
-  if (!seq_ok(p, t0, seq_d(p, b), d0)) return;
-  const SeqState st = p.state[b];
+  if (!seq_ok(p, t0, D, d0)) return;
+  SeqState st = p.state[b];
+
+  // (1) this chunk's fp64 sums of the residual (or p) and of p
   double zw = 0.0, zp = 0.0;
 #pragma unroll 4
-  for (int k = 0; k < kPerThread; ++k) {
-    const int j = c * kChunk + k * kAccThreads + threadIdx.x;
+  for (int k = 0; k < kSPerThread; ++k) {
+    const int j = c * kSChunk + k * kAccThreads + tid;
     if (j < p.V) {
       double w, pj;
       sample_weights(p, st, t0, d0, j, w, pj);
@@ -276,61 +335,76 @@ __global__ __launch_bounds__(kAccThreads) void accept_residual(AccParams p) {
   }
   zw = block_sum(zw, sd);
   zp = block_sum(zp, sd);
-  if (threadIdx.x == 0) {
-    p.rsum[((size_t)b * p.nchunk + c) * 2 + 0] = zw;
-    p.rsum[((size_t)b * p.nchunk + c) * 2 + 1] = zp;
-  }
-}
-
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kAccThreads) void accept_sample(AccParams p) {
-  __shared__ double scan[kAccThreads];
-  __shared__ int s_chunk, s_usep, s_tok;
-  __shared__ double s_base, s_T;
-  const int b = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int t0 = p.q_start[b];
-  const int D = seq_d(p, b);
-  const int d0 = t0 - b;
-  if (!seq_ok(p, t0, D, d0)) return;
-  SeqState st = p.state[b];
-
   if (tid == 0) {
-    const double* rs = p.rsum + (size_t)b * p.nchunk * 2;
-    double Z = 0.0;
-    for (int c = 0; c < p.nchunk; ++c) Z += rs[2 * c];
-    int usep = 0;
-    if (!(Z > 0.0)) {
-      usep = 1;
-      Z = 0.0;
-      for (int c = 0; c < p.nchunk; ++c) Z += rs[2 * c + 1];
+    // Hand-off between workgroups of one sequence, possibly on different XCDs
+    // (separate L2s): the sums are agent-scope atomic stores, which are
+    // coherent across XCDs, and complete (vmcnt 0) before the arrival count.
+    // A release fence would do the same by writing back the whole L2.
+    double* dst = p.rsum + ((size_t)b * p.nschunk + c) * 2;
+    __hip_atomic_store(dst, zw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(dst + 1, zp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const unsigned prev = __hip_atomic_fetch_add(&p.state[b].arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == (unsigned)(p.nschunk - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+
+  // (2) last chunk to finish: find the chunk holding u*Z, then scan it.  The
+  // chunk sums are read once each, in parallel, and scanned in LDS.
+  double* rsb = p.rsum + (size_t)b * p.nschunk * 2;
+  auto rs_at = [&](int i) { return __hip_atomic_load(rsb + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+  zw = 0.0;
+  zp = 0.0;
+  for (int k = tid; k < p.nschunk; k += kAccThreads) {
+    zw += rs_at(2 * k);
+    zp += rs_at(2 * k + 1);
+  }
+  zw = block_sum(zw, sd);
+  zp = block_sum(zp, sd);
+  const int usep = !(zw > 0.0);                   // the residual has no mass: sample p
+  const double T = (double)p.uniforms[t0 + D] * (usep ? zp : zw);
+  if (tid == 0) {
+    s_chunk = INT_MAX;
+    s_tok = -1;                                   // last chunk with weight (rounding fallback)
+  }
+  double carry = 0.0;
+  for (int base = 0; base < p.nschunk; base += kAccThreads) {
+    const int k = base + tid;
+    const double v = k < p.nschunk ? rs_at(2 * k + usep) : 0.0;
+    scan[tid] = v;
+    __syncthreads();
+    for (int off = 1; off < kAccThreads; off <<= 1) {
+      const double add = tid >= off ? scan[tid - off] : 0.0;
+      __syncthreads();
+      scan[tid] += add;
+      __syncthreads();
     }
-    const double T = (double)p.uniforms[t0 + D] * Z;
-    double acc = 0.0;
-    int cs = -1;
-    for (int c = 0; c < p.nchunk; ++c) {
-      const double nxt = acc + rs[2 * c + usep];
-      if (nxt > T) { cs = c; break; }
-      acc = nxt;
+    const double incl = carry + scan[tid];
+    if (k < p.nschunk && incl > T) atomicMin(&s_chunk, k);
+    if (v > 0.0) atomicMax(&s_tok, k);
+    __syncthreads();
+    if (k == s_chunk) s_base = incl - v;
+    carry += scan[kAccThreads - 1];
+    __syncthreads();
+    if (s_chunk != INT_MAX) break;
+  }
+  if (tid == 0) {
+    if (s_chunk == INT_MAX) {                     // prefix never passed u*Z
+      s_chunk = max(s_tok, 0);
+      s_base = -INFINITY;                         // never satisfied below -> last positive weight
     }
-    if (cs < 0) {                     // rounding: fall back to the last chunk with weight
-      cs = 0;
-      for (int c = 0; c < p.nchunk; ++c) if (rs[2 * c + usep] > 0.0) cs = c;
-      acc = -INFINITY;                // never satisfied below -> last positive weight
-    }
-    s_chunk = cs;
-    s_base = acc;
     s_T = T;
     s_usep = usep;
     s_tok = INT_MAX;
   }
   __syncthreads();
   if (s_usep) st.residual = 0;
-  const int j0 = s_chunk * kChunk + tid * kPerThread;
-  double w[kPerThread];
+  const int j0 = s_chunk * kSChunk + tid * kSPerThread;
+  double w[kSPerThread];
   double tsum = 0.0;
 #pragma unroll
-  for (int e = 0; e < kPerThread; ++e) {
+  for (int e = 0; e < kSPerThread; ++e) {
     const int j = j0 + e;
     double pj;
     w[e] = 0.0;
@@ -350,7 +424,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_sample(AccParams p) {
   int cand = INT_MAX;
   int last_pos = -1;
 #pragma unroll
-  for (int e = 0; e < kPerThread; ++e) {
+  for (int e = 0; e < kSPerThread; ++e) {
     C += w[e];
     if (cand == INT_MAX && C > s_T) cand = j0 + e;
     if (w[e] > 0.0) last_pos = j0 + e;
@@ -363,7 +437,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_sample(AccParams p) {
     if (tid == 0) {
       int best = -1;
       for (int k = 0; k < kAccThreads; ++k) best = max(best, (int)scan[k]);
-      s_tok = best < 0 ? s_chunk * kChunk : best;
+      s_tok = best < 0 ? s_chunk * kSChunk : best;
     }
     __syncthreads();
   }
@@ -372,18 +446,19 @@ __global__ __launch_bounds__(kAccThreads) void accept_sample(AccParams p) {
 
 struct AccLayout {
   size_t part_off, state_off, rsum_off, total;
-  int nchunk;
+  int nchunk, nschunk;
 };
 
 static AccLayout acc_layout(int B, int T, int V, int stochastic) {
   AccLayout L;
   L.nchunk = (V + kChunk - 1) / kChunk;
+  L.nschunk = (V + kSChunk - 1) / kSChunk;
   const size_t rows = stochastic ? (size_t)T + (size_t)(T - B) : (size_t)T;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += (bytes + 255) / 256 * 256; return o; };
   L.part_off = take(rows * L.nchunk * sizeof(RowPart));
   L.state_off = take((size_t)B * sizeof(SeqState));
-  L.rsum_off = take((size_t)B * L.nchunk * 2 * sizeof(double));
+  L.rsum_off = take((size_t)B * L.nschunk * 2 * sizeof(double));
   L.total = off;
   return L;
 }
@@ -414,6 +489,7 @@ hipError_t sdv_accept_launch(const SdAccLaunch& a) {
   p.T = a.T;
   p.V = a.V;
   p.nchunk = L.nchunk;
+  p.nschunk = L.nschunk;
   p.max_draft = a.max_draft;
 
   const bool vec4 = (a.V % 4 == 0) && ((uintptr_t)a.target % 16 == 0) &&
@@ -425,8 +501,7 @@ hipError_t sdv_accept_launch(const SdAccLaunch& a) {
     if (vec4) accept_rowstats<1, 1><<<grid1, kAccThreads, 0, a.stream>>>(p);
     else accept_rowstats<1, 0><<<grid1, kAccThreads, 0, a.stream>>>(p);
     accept_decide<1><<<a.B, kAccThreads, dyn, a.stream>>>(p);
-    accept_residual<<<dim3(L.nchunk, a.B), kAccThreads, 0, a.stream>>>(p);
-    accept_sample<<<a.B, kAccThreads, 0, a.stream>>>(p);
+    accept_sample<<<dim3(L.nschunk, a.B), kAccThreads, 0, a.stream>>>(p);
   } else {
     if (vec4) accept_rowstats<0, 1><<<grid1, kAccThreads, 0, a.stream>>>(p);
     else accept_rowstats<0, 0><<<grid1, kAccThreads, 0, a.stream>>>(p);

@@ -6,7 +6,7 @@
 #include <stdio.h>
 #include <string>
 
-#include "../../include/sd_verify.h"
+#include "sd_verify.h"
 #include "common.h"
 
 namespace {
