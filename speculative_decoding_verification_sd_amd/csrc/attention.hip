@@ -37,6 +37,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 
@@ -48,13 +49,10 @@ constexpr int kMaxChunk = 16384;         // keys per work item; bounds the per-i
 constexpr int kPlanThreads = 256;
 constexpr int kPlanHeader = 4;
 
-// Ring depth (tiles resident in LDS per workgroup).  Build-time tunables: the
-// 4-wave variants run two workgroups per CU, the 8-wave one a single one.
-#ifndef SDV_RING_STAGES
-#define SDV_RING_STAGES 3
-#endif
-#ifndef SDV_RING_STAGES_WIDE
-#define SDV_RING_STAGES_WIDE 6
+// LDS bytes of the K/V rings of one CU (at most 8 tiles per workgroup),
+// shared by its resident workgroups.  Build-time tunable.
+#ifndef SDV_RING_BYTES_PER_CU
+#define SDV_RING_BYTES_PER_CU 131072
 #endif
 
 struct ItemDesc {
@@ -75,6 +73,7 @@ struct AttnParams {
   int* plan;        // [4 + B + 1]: chunk, total items, -, -, item_start[0..B]
   ItemDesc* items;  // [item_cap]
   int B, Hkv, G, max_pages, num_pages, max_draft, rpad, total_q, item_cap;
+  int nhalf;        // workgroups per item: 2 when a sequence can have more query rows than one holds
   float scale_log2;
 };
 
@@ -114,6 +113,9 @@ __global__ __launch_bounds__(kPlanThreads) void verify_attn_plan(AttnParams p, i
   __syncthreads();
   const int chunk = fixed_chunk > 0 ? fixed_chunk : s_best;
 
+  // descriptors: sequences in groups of kPlanThreads; the group's items are
+  // written by all threads, each finding its sequence by binary search over
+  // the inclusive scan of items per sequence
   int carry = 0;
   for (int base = 0; base < p.B; base += kPlanThreads) {
     const int b = base + tid;
@@ -124,6 +126,7 @@ __global__ __launch_bounds__(kPlanThreads) void verify_attn_plan(AttnParams p, i
       v = ns * p.Hkv;
     }
     scan[tid] = v;
+    s_keys[tid] = N;
     __syncthreads();
     for (int off = 1; off < kPlanThreads; off <<= 1) {
       const int add = tid >= off ? scan[tid - off] : 0;
@@ -131,27 +134,33 @@ __global__ __launch_bounds__(kPlanThreads) void verify_attn_plan(AttnParams p, i
       scan[tid] += add;
       __syncthreads();
     }
-    const int first = carry + scan[tid] - v;
-    if (b < p.B) {
-      p.plan[kPlanHeader + b] = first;
-      const int t0 = p.q_start[b];
-      const int D = seq_drafts(p, b);
-      for (int h = 0; h < p.Hkv; ++h)
-        for (int s = 0; s < ns; ++s) {
-          const int it = first + h * ns + s;
-          if (it < p.item_cap) {
-            ItemDesc d;
-            d.b = b;
-            d.h = h;
-            d.k_begin = s * chunk;
-            d.k_end = min(N, (s + 1) * chunk);
-            d.t0 = t0;
-            d.D = D;
-            d.N = N;
-            d.nsplit = ns;
-            p.items[it] = d;
-          }
-        }
+    if (b < p.B) p.plan[kPlanHeader + b] = carry + scan[tid] - v;
+    const int n = min(kPlanThreads, p.B - base);
+    const int group_items = scan[n - 1];
+    for (int e = tid; e < group_items; e += kPlanThreads) {
+      const int it = carry + e;
+      if (it >= p.item_cap) break;
+      int lo = 0, hi = n - 1;                 // first j with scan[j] > e
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (scan[mid] > e) hi = mid;
+        else lo = mid + 1;
+      }
+      const int bj = base + lo;
+      const int Nj = s_keys[lo];
+      const int nsj = max(1, (Nj + chunk - 1) / chunk);
+      const int r = e - (lo > 0 ? scan[lo - 1] : 0);
+      const int s = r % nsj;
+      ItemDesc d;
+      d.b = bj;
+      d.h = r / nsj;
+      d.k_begin = s * chunk;
+      d.k_end = min(Nj, (s + 1) * chunk);
+      d.t0 = p.q_start[bj];
+      d.D = seq_drafts(p, bj);
+      d.N = Nj;
+      d.nsplit = nsj;
+      p.items[it] = d;
     }
     carry += scan[kPlanThreads - 1];
     __syncthreads();
@@ -226,41 +235,61 @@ __device__ __forceinline__ float row_max4(float v) {
   auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
-__device__ __forceinline__ float row_sum4(float v) {
-  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
 
-template <int HD, int NW>
+template <int HD, int NW, int WPC>
 struct Ring {
   static constexpr int kTile = 32;                        // keys per tile (two pages)
   static constexpr int kRowB = HD * 2;                    // bytes per key row
   static constexpr int kCpr = kRowB / 16;                 // 16-byte chunks per row
   static constexpr int kHalf = kTile * kRowB;             // K (or V) bytes per tile
   static constexpr int kStageB = 2 * kHalf;
-  static constexpr int kStages = NW >= 8 ? SDV_RING_STAGES_WIDE : SDV_RING_STAGES;
+  static constexpr int kBudget = SDV_RING_BYTES_PER_CU / WPC;
+  // even, so that the unrolled tile loop alternates two score buffers statically
+  static constexpr int kStages = (kBudget / kStageB < 8 ? kBudget / kStageB : 8) & ~1;
   static constexpr int kLoadsKV = 2 * kHalf / 1024;       // 1 KB DMA instructions per tile (K and V)
   static constexpr int kLPW = kLoadsKV / NW;              // ... per wave
   static constexpr int kKeysPerLoad = 1024 / kRowB;       // key rows one instruction fills
-  static_assert(kStages >= 2 && kStages <= 8, "ring depth");
+  static_assert(kStages >= 4, "the pipelined tile loop needs four ring stages");
   static_assert(kLoadsKV % NW == 0 && kLPW >= 1, "DMA instructions divide evenly over the waves");
 };
 
+// Wait until at most `tiles` tiles' worth (LPW loads each, tiles <= 6) of this
+// wave's vector loads are in flight; the count must be an immediate, hence the
+// switch.
+template <int LPW>
+__device__ __forceinline__ void wait_tiles(int tiles) {
+  switch (tiles) {
+    case 6: wait_vmem<6 * LPW>(); break;
+    case 5: wait_vmem<5 * LPW>(); break;
+    case 4: wait_vmem<4 * LPW>(); break;
+    case 3: wait_vmem<3 * LPW>(); break;
+    case 2: wait_vmem<2 * LPW>(); break;
+    case 1: wait_vmem<LPW>(); break;
+    default: wait_vmem<0>(); break;
+  }
+}
+
+template <int V>
+using ic = std::integral_constant<int, V>;
+
 // ---------------------------------------------------------------------------
-template <int HD, int NRB, int NW, int OUT_F32>
-__global__ __launch_bounds__(64 * NW, (NW >= 8 ? 1 : 2)) void verify_attn_main(AttnParams p) {
-  using RG = Ring<HD, NW>;
+// NRB row blocks of 16 per wave, NW waves, WPC resident workgroups per CU.
+template <int HD, int NRB, int NW, int WPC, int OUT_F32>
+__global__ __launch_bounds__(64 * NW, WPC) void verify_attn_main(AttnParams p) {
+  using RG = Ring<HD, NW, WPC>;
+  constexpr int S = RG::kStages;
   constexpr int NKC = HD / 32;   // MFMA k-steps over d for S
   constexpr int NDB = HD / 16;   // 16-wide d blocks of O
   constexpr int LPW = RG::kLPW;
   constexpr int kPageB = kPage * HD * 2;   // bytes of one (page, head) block
-  constexpr float kLazy = 8.f;             // raise the running max only when it grows by more than 2^8
-  constexpr int kPageSlots = kMaxChunk / kPage + 2;
-  // one LDS object: the K/V ring followed by the page ids of the current item
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[RG::kStages * RG::kStageB + kPageSlots * 4];
-  int* s_pages = (int*)(smem + RG::kStages * RG::kStageB);
+  constexpr float kLazy = 8.f;             // safe pass: raise the running max only when it grows by more than 2^8
+  constexpr int kPageSlots = kMaxChunk / kPage + 2 * S;
+  static_assert(S - 2 <= 6 && (S - 2) * LPW < 64, "wait_tiles range");
+  // One LDS object: the K tiles of all ring stages, then the V tiles (so that a
+  // lane-constant base plus a 16-bit immediate reaches every stage), then the
+  // page ids of the current item.
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[S * RG::kStageB + kPageSlots * 4];
+  int* s_pages = (int*)(smem + S * RG::kStageB);
   lds_u8* lds_smem = (lds_u8*)smem;
   const unsigned lds_base = (unsigned)(size_t)lds_smem;
 
@@ -272,12 +301,21 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 1 : 2)) void verify_attn_main(A
   const int total = min(p.plan[1], p.item_cap);
   const int Hq = p.Hkv * p.G;
 
-  // lane-constant offsets
-  const int kswz = chunk_swz<HD>(l16) & (RG::kCpr - 1);                   // K operand: key = kb*16 + l16
-  const int vkey = g4 * 4 + (l16 >> 2);                               // transposed V read: key row
+  // Lane-constant LDS offsets inside a stage (the stage itself is an immediate
+  // in the unrolled tile loop).  K operand: key kb*16 + l16, logical chunk
+  // c*4 + g4.  Transposed V read: key row g4*4 + l16/4 (and +16), chunk pair db.
+  const int kswz = chunk_swz<HD>(l16) & (RG::kCpr - 1);
+  int koff[NKC];
+#pragma unroll
+  for (int c = 0; c < NKC; ++c) koff[c] = l16 * RG::kRowB + (((c * 4 + g4) ^ kswz) * 16);
+  const int vkey = g4 * 4 + (l16 >> 2);
   const int vswz = chunk_swz<HD>(vkey) & (RG::kCpr - 1);
-  const int vsub = (l16 & 3) >> 1;                                    // chunk within the 16-wide d block
-  const int vbyte = (l16 & 1) * 8;
+  const int vsub = (l16 & 3) >> 1;
+  int voffs[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+    voffs[db] = S * RG::kHalf + vkey * RG::kRowB + (l16 & 1) * 8 + (((db * 2 + vsub) ^ vswz) * 16);
+
   // DMA instruction j = wave + NW*i of a tile: K rows for j < kLoadsKV/2, V rows after
   unsigned dma_off[LPW];         // byte offset of this lane's 16 bytes inside the (page, head) block
   int dma_row[LPW];              // first key row (tile-relative) the instruction fills
@@ -291,29 +329,61 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 1 : 2)) void verify_attn_main(A
     const int lc = (lane % RG::kCpr) ^ (chunk_swz<HD>(key & 15) & (RG::kCpr - 1));
     dma_off[i] = (unsigned)(((key & 15) * HD + lc * 8) * 2);
   }
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
 
-  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+  // With two row halves per item, virtual items 16k..16k+7 are the first
+  // halves and 16k+8..16k+15 the second halves of items 8k..8k+7: workgroups
+  // are dealt round-robin over the eight XCDs, so both halves of an item run on
+  // one XCD and the second reads the item's pages from that XCD's L2.
+  constexpr int kRowsWG = NRB * NW * 16;
+  const int nvirt = p.nhalf == 1 ? total : (total + 7) / 8 * 16;
+  for (int vi = blockIdx.x; vi < nvirt; vi += gridDim.x) {
+    const int item = p.nhalf == 1 ? vi : (vi >> 4) * 8 + (vi & 7);
+    const int row0 = p.nhalf == 1 ? 0 : ((vi >> 3) & 1) * kRowsWG;
+    if (item >= total) continue;
     const ItemDesc d = p.items[item];
-    const int b = d.b, h = d.h, k_begin = d.k_begin, k_end = d.k_end;
-    const int t0 = d.t0, D = d.D, N = d.N, nsplit = d.nsplit;
+    // wave-uniform copies, so that everything derived from them (page bases,
+    // tile counts) stays in scalar registers
+    const int b = __builtin_amdgcn_readfirstlane(d.b), h = __builtin_amdgcn_readfirstlane(d.h);
+    const int k_begin = __builtin_amdgcn_readfirstlane(d.k_begin), k_end = __builtin_amdgcn_readfirstlane(d.k_end);
+    const int t0 = __builtin_amdgcn_readfirstlane(d.t0), D = __builtin_amdgcn_readfirstlane(d.D);
+    const int N = __builtin_amdgcn_readfirstlane(d.N), nsplit = __builtin_amdgcn_readfirstlane(d.nsplit);
     const int R = p.G * (1 + D);
+    if (row0 >= R) continue;     // the sequence's rows fit in the first half
     const int* bt = p.block_table + (size_t)b * p.max_pages;
-    const bool wave_active = wave * NRB * 16 < R;
+    const bool wave_active = row0 + wave * NRB * 16 < R;
     const int ntiles = k_end > k_begin ? (k_end - k_begin + RG::kTile - 1) / RG::kTile : 0;
+    const bool ragged_tail = k_begin + ntiles * RG::kTile > k_end;
     const unsigned char* kbase = (const unsigned char*)p.k + (size_t)h * kPageB;
     const unsigned char* vbase = (const unsigned char*)p.v + (size_t)h * kPageB;
-    const size_t page_stride = (size_t)p.Hkv * kPageB;
+    const uint64_t page_stride = (uint64_t)p.Hkv * kPageB;
 
-    // Issue this wave's share of the LDS-DMA loads of tile `tile` into its ring stage.
-    auto issue = [&](int tile) {
-      const unsigned st = lds_base + (unsigned)((tile % RG::kStages) * RG::kStageB);
+    // Page ids of a tile's two pages (wave-uniform) -> this wave's DMA loads of
+    // the tile into ring stage `st`.
+    auto tile_pages = [&](int tile) {
+      const u32x2 v = *(const u32x2*)(s_pages + tile * 2);
+      return u32x2{(unsigned)__builtin_amdgcn_readfirstlane(v[0]), (unsigned)__builtin_amdgcn_readfirstlane(v[1])};
+    };
+    auto issue = [&](u32x2 pids, int st) {
+      const uint64_t off0 = (uint64_t)pids[0] * page_stride;
+      const uint64_t off1 = (uint64_t)pids[1] * page_stride;
+      const unsigned sb = lds_base + (unsigned)(st * RG::kHalf);
 #pragma unroll
-      for (int i = 0; i < LPW; ++i) {
-        // the rows of one instruction lie in one page
-        const int pid = __builtin_amdgcn_readfirstlane(s_pages[tile * (RG::kTile / kPage) + dma_row[i] / kPage]);
-        dma16((dma_kv[i] ? vbase : kbase) + (size_t)pid * page_stride, dma_off[i],
-              st + (unsigned)(dma_kv[i] * RG::kHalf + dma_row[i] * RG::kRowB));
-      }
+      for (int i = 0; i < LPW; ++i)
+        dma16((dma_kv[i] ? vbase : kbase) + (dma_row[i] >= kPage ? off1 : off0), dma_off[i],
+              sb + (unsigned)(dma_kv[i] * S * RG::kHalf + dma_row[i] * RG::kRowB));
+    };
+    // zero the key rows at or past k_end that this wave loaded into stage st (last tile only)
+    auto zero_tail = [&](int tile, int st) {
+      unsigned char* sp = smem + st * RG::kHalf;
+      const int ts = k_begin + tile * RG::kTile;
+#pragma unroll
+      for (int i = 0; i < LPW; ++i)
+        if (ts + dma_row[i] + lane / RG::kCpr >= k_end)
+          *(u32x4*)(sp + dma_kv[i] * S * RG::kHalf + dma_row[i] * RG::kRowB + lane * 16) = u32x4{0, 0, 0, 0};
+      wait_lds();
     };
 
     // Query fragments (B operand of S^T = K Q^T): lane holds row l16, dims g4*8..+7 of each 32-wide step.
@@ -321,7 +391,7 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 1 : 2)) void verify_attn_main(A
     int pos[NRB];
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
-      const int row = (wave * NRB + rb) * 16 + l16;
+      const int row = row0 + (wave * NRB + rb) * 16 + l16;
       const int i0 = row / p.G;
       const bool valid = row < R && t0 >= 0 && t0 + i0 < p.total_q;
       const int i = valid ? i0 : 0;
@@ -335,12 +405,15 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 1 : 2)) void verify_attn_main(A
       }
     }
 
-    float m_run[NRB], l_run[NRB];
+    float m_run[NRB];
+    float m_off[NRB];              // -m_run, or 0 while m_run is -inf (exp2 argument offset)
+    f32x4 l_acc[NRB];              // row sums of P from an MFMA against ones (all four entries equal)
     f32x4 o[NRB][NDB];
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       m_run[rb] = -INFINITY;
-      l_run[rb] = 0.f;
+      m_off[rb] = 0.f;
+      l_acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int db = 0; db < NDB; ++db) o[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -356,127 +429,260 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 1 : 2)) void verify_attn_main(A
     wait_vmem<0>();
     wait_lds();
     block_sync();
-#pragma unroll
-    for (int t = 0; t < RG::kStages - 1; ++t)
-      if (t < ntiles) issue(t);
 
-    auto compute = [&](int tile) {
-      const unsigned char* Ks = smem + (tile % RG::kStages) * RG::kStageB;
+    // Scores of tile `tile`: causal mask (only tiles that reach the draft
+    // block need it) and row max.
+    f32x4 sc[2][2][NRB];           // scores of tiles of even / odd index
+    float mt[NRB];                 // row max of the newest scores (log2 units)
+    auto mask_scores = [&](f32x4 (&s)[2][NRB], int tile) {
       const int ts = k_begin + tile * RG::kTile;
-      const bool need_mask = ts + RG::kTile > N - D;
-
-      f32x4 sc[2][NRB];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        bf16x8 kf[NKC];
-        const unsigned char* krow = Ks + (kb * 16 + l16) * RG::kRowB;
-#pragma unroll
-        for (int c = 0; c < NKC; ++c) kf[c] = *(const bf16x8*)(krow + (((c * 4 + g4) ^ kswz) * 16));
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int c = 0; c < NKC; ++c)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[c], qf[rb][c], acc, 0, 0, 0);
-          sc[kb][rb] = acc;
-        }
-      }
-
-      // online softmax, one query row per lane; lazy rescale of the running max
-      float mt[NRB];
-      bool grow = false;
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) {
-        if (need_mask) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (ts + kb * 16 + g4 * 4 + e > pos[rb]) sc[kb][rb][e] = -INFINITY;
-        }
-        float m = fmaxf(fmaxf(sc[0][rb][0], sc[0][rb][1]), fmaxf(sc[0][rb][2], sc[0][rb][3]));
-        m = fmaxf(m, fmaxf(fmaxf(sc[1][rb][0], sc[1][rb][1]), fmaxf(sc[1][rb][2], sc[1][rb][3])));
-        mt[rb] = row_max4(m) * p.scale_log2;
-        grow |= mt[rb] > m_run[rb] + kLazy;
-      }
-      if (__any(grow)) {
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-          if (mt[rb] > m_run[rb] + kLazy) {
-            const float alpha = fast_exp2(m_run[rb] - mt[rb]);
-            m_run[rb] = mt[rb];
-            l_run[rb] *= alpha;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) o[rb][db] *= alpha;
-          }
-        }
-      }
-      bf16x8 pf[NRB];
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-        const float mc = m_run[rb] == -INFINITY ? 0.f : m_run[rb];
-        float psum = 0.f;
-        bf16x8 t;
+        const int lim = pos[rb] - ts - g4 * 4;   // key kb*16 + g4*4 + e is visible iff kb*16 + e <= lim
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float pv = fast_exp2(fmaf(sc[kb][rb][e], p.scale_log2, -mc));
-            psum += pv;
-            t[kb * 4 + e] = (__bf16)pv;
-          }
-        l_run[rb] += psum;
-        pf[rb] = t;
-      }
-
-      // O^T += V^T P^T: V read transposed from LDS, keys in the order of the S^T accumulators
-      const int vstage = (tile % RG::kStages) * RG::kStageB + RG::kHalf + vkey * RG::kRowB + vbyte;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int voff = vstage + (((db * 2 + vsub) ^ vswz) * 16);
-        const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_smem + voff));
-        const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_smem + voff + 16 * RG::kRowB));
-        const u32x2 lo = __builtin_bit_cast(u32x2, lo4);
-        const u32x2 hi = __builtin_bit_cast(u32x2, hi4);
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb)
-          o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[rb], o[rb][db], 0, 0, 0);
+          for (int e = 0; e < 4; ++e)
+            if (kb * 16 + e > lim) s[kb][rb][e] = -INFINITY;
       }
     };
-
-    // steady state: every iteration has kStages-2 younger tiles in flight and issues one more
-    const int nsteady = ntiles - (RG::kStages - 1);
-    int tile = 0;
-    for (; tile < nsteady; ++tile) {
-      wait_vmem<(RG::kStages - 2) * LPW>();
-      block_sync();
-      issue(tile + RG::kStages - 1);
-      if (wave_active) compute(tile);
-    }
-    // drain: the last kStages-1 tiles are all in flight already
-    for (; tile < ntiles; ++tile) {
-      switch (ntiles - 1 - tile) {
-        case 6: wait_vmem<6 * LPW>(); break;
-        case 5: wait_vmem<5 * LPW>(); break;
-        case 4: wait_vmem<4 * LPW>(); break;
-        case 3: wait_vmem<3 * LPW>(); break;
-        case 2: wait_vmem<2 * LPW>(); break;
-        case 1: wait_vmem<LPW>(); break;
-        default: wait_vmem<0>(); break;
-      }
-      if (k_begin + (tile + 1) * RG::kTile > k_end) {
-        // zero the key rows at or past k_end that this wave loaded (last tile only)
-        unsigned char* st = smem + (tile % RG::kStages) * RG::kStageB;
-        const int ts = k_begin + tile * RG::kTile;
+    // Sets mt; true if some row's max exceeds its running max by more than `slack`.
+    auto row_max = [&](const f32x4 (&s)[2][NRB], float slack) {
+      bool over = false;
 #pragma unroll
-        for (int i = 0; i < LPW; ++i)
-          if (ts + dma_row[i] + lane / RG::kCpr >= k_end)
-            *(u32x4*)(st + dma_kv[i] * RG::kHalf + dma_row[i] * RG::kRowB + lane * 16) = u32x4{0, 0, 0, 0};
-        wait_lds();
+      for (int rb = 0; rb < NRB; ++rb) {
+        float m = fmaxf(fmaxf(s[0][rb][0], s[0][rb][1]), fmaxf(s[0][rb][2], s[0][rb][3]));
+        m = fmaxf(m, fmaxf(fmaxf(s[1][rb][0], s[1][rb][1]), fmaxf(s[1][rb][2], s[1][rb][3])));
+        mt[rb] = row_max4(m) * p.scale_log2;
+        over |= mt[rb] > m_run[rb] + slack;
       }
+      return over;
+    };
+    // K operand fragments / transposed V fragments of the tile at byte offset
+    // `off` of the K (V) region; `off` folds into the instruction's immediate
+    // wherever it is a constant.
+    auto read_k = [&](int off, bf16x8 (&kf)[2][NKC]) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int c = 0; c < NKC; ++c)
+          kf[kb][c] = *(const bf16x8*)(smem + off + kb * 16 * RG::kRowB + koff[c]);
+    };
+    auto read_v = [&](int off, bf16x8 (&vf)[NDB]) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int va = off + voffs[db];
+        const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_smem + va));
+        const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_smem + va + 16 * RG::kRowB));
+        const u32x2 lo = __builtin_bit_cast(u32x2, lo4);
+        const u32x2 hi = __builtin_bit_cast(u32x2, hi4);
+        vf[db] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+      }
+    };
+    // the 2*NRB accumulation chains advance together (k-step outermost), so
+    // consecutive MFMAs never depend on each other
+    auto mfma_scores = [&](const bf16x8 (&kf)[2][NKC], f32x4 (&s)[2][NRB]) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) s[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NKC; ++c)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int rb = 0; rb < NRB; ++rb)
+            s[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][c], qf[rb][c], s[kb][rb], 0, 0, 0);
+    };
+    // P = 2^(S * scale * log2 e - m) in bf16, keys in the order of the S^T accumulators
+    auto probs = [&](const f32x4 (&s)[2][NRB], bf16x8 (&pf)[NRB]) {
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            pf[rb][kb * 4 + e] = (__bf16)fast_exp2(fmaf(s[kb][rb][e], p.scale_log2, m_off[rb]));
+    };
+    // O^T += V^T P^T; l += 1^T P^T
+    auto accumulate = [&](const bf16x8 (&vf)[NDB], const bf16x8 (&pf)[NRB]) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+          o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], pf[rb], o[rb][db], 0, 0, 0);
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb)
+        l_acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[rb], l_acc[rb], 0, 0, 0);
+    };
+
+    // ---- Fast pass.  Each row's reference max is fixed by the item's first
+    // tile and never moves, and later tiles take no row max at all: a score
+    // that rises far above the reference shows in the row sum l (it holds every
+    // P), and an item whose l ends above 2^kSlack (or is not finite) is
+    // recomputed by the safe pass below with a running max.  Below that bound
+    // o and l are far from fp32 overflow.
+    constexpr float kSlack = 64.f;
+    // Tiles 0..steady-1 run in the unrolled, pipelined loop: each has a next
+    // tile that needs no causal mask.  steady is a multiple of S, so that the
+    // loop carries no per-step guards and tile `steady` starts the tail with
+    // its scores in sc[0].
+    const int plain = max(0, min(ntiles - 1, (N - D - k_begin) / RG::kTile - 1));
+    const int steady = plain - plain % S;
+
+    // Tile t (ring stage t % S), pipelined: P of tile t on the vector ALUs
+    // while the matrix cores compute the scores of tile t+1, then P V of tile t
+    // on the matrix cores while the vector ALUs take the row max of tile t+1.
+    auto body = [&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      bf16x8 kf[2][NKC];
+      read_k(((u + 1) % S) * RG::kHalf, kf);
+      bf16x8 vf[NDB];
+      read_v(u * RG::kHalf, vf);
+      bf16x8 pf[NRB];
+      probs(sc[u & 1], pf);
+      mfma_scores(kf, sc[(u + 1) & 1]);
+      accumulate(vf, pf);
+      // interleave: LDS reads first, then one MFMA per few VALU ops
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * NKC, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * NRB * NKC; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        if (i < NDB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, NRB * (NDB + 1), 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 8 * NRB, 0);   // the new scores leave the accumulators last
+    };
+
+    // The whole tile loop in two copies, for waves with and without query
+    // rows in this item, so that no branch inside it merges accumulators.
+    auto fast_pass = [&](auto activec) {
+      constexpr bool ACTIVE = decltype(activec)::value;
+#pragma unroll
+      for (int t = 0; t < S - 1; ++t)
+        if (t < ntiles) issue(tile_pages(t), t);
+      u32x2 pids_next = {0u, 0u};    // page ids of the next tile to issue (tile S-1 first)
+      if (S - 1 < ntiles) pids_next = tile_pages(S - 1);
+      if (ntiles == 0) return;
+      wait_tiles<LPW>(min(S - 2, ntiles - 1));
+      if (ntiles == 1 && ragged_tail) zero_tail(0, 0);
       block_sync();
-      if (wave_active) compute(tile);
+      if constexpr (ACTIVE) {
+        bf16x8 kf[2][NKC];
+        read_k(0, kf);
+        mfma_scores(kf, sc[0]);
+        if (k_begin + RG::kTile > N - D) mask_scores(sc[0], 0);
+        row_max(sc[0], 0.f);
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+          m_run[rb] = mt[rb];
+          m_off[rb] = mt[rb] == -INFINITY ? 0.f : -mt[rb];
+        }
+      }
+      // wait for tile t+1, barrier, refill the stage tile t-1 used with tile t+S-1
+      auto advance = [&](int t, int st_issue) {
+        wait_tiles<LPW>(min(S - 3, ntiles - 2 - t));
+        if (t + 1 == ntiles - 1 && ragged_tail) zero_tail(t + 1, (t + 1) % S);
+        block_sync();
+        if (t + S - 1 < ntiles) {
+          issue(pids_next, st_issue);
+          if (t + S < ntiles) pids_next = tile_pages(t + S);
+        }
+      };
+      for (int tb = 0; tb < steady; tb += S) {
+        auto step = [&](auto uc) {
+          constexpr int u = decltype(uc)::value;
+          advance(tb + u, (u + S - 1) % S);
+          if constexpr (ACTIVE) body(uc);
+        };
+        step(ic<0>{});
+        step(ic<1>{});
+        step(ic<2>{});
+        step(ic<3>{});
+        if constexpr (S > 4) step(ic<4>{});
+        if constexpr (S > 5) step(ic<5>{});
+        if constexpr (S > 6) step(ic<6>{});
+        if constexpr (S > 7) step(ic<7>{});
+      }
+      // tail: the last plain tiles, the masked ones and the last one, one at a
+      // time with run-time ring stages
+      for (int t = steady; t < ntiles; ++t) {
+        const bool has_next = t + 1 < ntiles;
+        if (has_next) {
+          advance(t, (t + S - 1) % S);
+        } else {
+          block_sync();
+        }
+        if constexpr (ACTIVE) {
+          bf16x8 pf[NRB];
+          probs(sc[0], pf);
+          bf16x8 vf[NDB];
+          read_v((t % S) * RG::kHalf, vf);
+          accumulate(vf, pf);
+          if (has_next) {
+            bf16x8 kf[2][NKC];
+            read_k(((t + 1) % S) * RG::kHalf, kf);
+            mfma_scores(kf, sc[0]);
+            if (k_begin + (t + 2) * RG::kTile > N - D) mask_scores(sc[0], t + 1);
+          }
+        }
+      }
+    };
+    if (wave_active) fast_pass(std::true_type{});
+    else fast_pass(std::false_type{});
+    // every load of the fast pass has landed (the last tile waited for vmcnt 0)
+    bool over = false;
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) over |= !(l_acc[rb][0] <= 0x1p64f);
+    over &= wave_active;
+
+    // ---- Safe pass (only if some row's max outgrew the fast pass): the same
+    // tiles again, one at a time, with a running max raised lazily (when it
+    // grows by more than 2^kLazy) and the accumulators rescaled.
+    if (__syncthreads_or(over ? 1 : 0)) {
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        m_run[rb] = -INFINITY;
+        m_off[rb] = 0.f;
+        l_acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int t = 0; t < S - 1; ++t)
+        if (t < ntiles) issue(tile_pages(t), t);
+      for (int t = 0; t < ntiles; ++t) {
+        wait_tiles<LPW>(min(S - 2, ntiles - 1 - t));
+        if (t == ntiles - 1 && ragged_tail) zero_tail(t, t % S);
+        block_sync();
+        if (t + S - 1 < ntiles) issue(tile_pages(t + S - 1), (t + S - 1) % S);
+        if (wave_active) {
+          const int off = (t % S) * RG::kHalf;
+          bf16x8 kf[2][NKC];
+          read_k(off, kf);
+          mfma_scores(kf, sc[0]);
+          if (k_begin + (t + 1) * RG::kTile > N - D) mask_scores(sc[0], t);
+          if (__any(row_max(sc[0], kLazy))) {
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb) {
+              if (mt[rb] > m_run[rb] + kLazy) {
+                const float alpha = fast_exp2(m_run[rb] - mt[rb]);
+                m_run[rb] = mt[rb];
+                m_off[rb] = -mt[rb];
+                l_acc[rb] *= alpha;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) o[rb][db] *= alpha;
+              }
+            }
+          }
+          bf16x8 pf[NRB];
+          probs(sc[0], pf);
+          bf16x8 vf[NDB];
+          read_v(off, vf);
+          accumulate(vf, pf);
+        }
+      }
     }
     // every wave is done with the ring before the next item's loads land in it
     block_sync();
@@ -484,8 +690,8 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 1 : 2)) void verify_attn_main(A
     if (wave_active) {
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) {
-        const float lt = row_sum4(l_run[rb]);
-        const int row = (wave * NRB + rb) * 16 + l16;
+        const float lt = l_acc[rb][0];
+        const int row = row0 + (wave * NRB + rb) * 16 + l16;
         if (row >= R || t0 < 0 || t0 + row / p.G >= p.total_q) continue;
         if (nsplit == 1) {
           const int i = row / p.G;
@@ -514,6 +720,374 @@ __global__ __launch_bounds__(64 * NW, (NW >= 8 ? 1 : 2)) void verify_attn_main(A
         }
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Verify attention with 32x32x16 MFMAs for blocks of more than 64 query rows:
+// a workgroup of 8 waves, two per SIMD, over 128 query rows.  The waves form
+// two sets of four (32 rows per wave); set 0 takes the even tiles of the item
+// and set 1 the odd ones, both from one LDS-DMA ring, and the two partial
+// results are merged through LDS at the end of the item.  Two waves per SIMD
+// hide each other's LDS, barrier and MFMA-dependency latencies.  Operands:
+//   * S^T = K Q^T per 32-key tile: A = K (lane: key row l%32, dims
+//     c*16 + (l/32)*8..+7), B = Q^T (lane: query row l%32, same dims), so each
+//     lane holds one query row and keys (e/4)*8 + (l/32)*4 + e%4, e < 16.
+//   * O^T += V^T P^T per 16-key step ks: A = V^T read transposed, keys in the
+//     accumulator's order (ks*16 + (l/32)*4 + 0..3, then +8); B = P^T, which is
+//     entries 8ks..8ks+7 of the score accumulator converted to bf16.
+// Reference maxima, the overflow check and the safe pass follow
+// verify_attn_main.
+
+// XOR swizzle of the 16-byte chunks of a K or V row in LDS for this kernel, a
+// function of the key's position mod 16 (64 banks of 4 bytes): sixteen
+// consecutive key rows read at one logical chunk (the K operand) land on
+// distinct banks, and so do four consecutive key rows times an aligned run of
+// four chunks (one transposed V read of 32 lanes).
+template <int HD>
+__device__ __forceinline__ int wide_swz(int k) {
+  if constexpr (HD == 128) return ((k & 3) << 2) | ((k >> 2) & 3);
+  else return (((k >> 1) & 1) << 2) | ((k >> 2) & 3);
+}
+
+template <int HD, int OUT_F32>
+__global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
+  constexpr int NW = 8;
+  using RG = Ring<HD, NW, 1>;
+  constexpr int S = RG::kStages;
+  constexpr int NKS = HD / 16;   // 16-wide d steps of S^T
+  constexpr int NMB = HD / 32;   // 32-wide d blocks of O^T
+  constexpr int LPW = RG::kLPW;
+  constexpr int kPageB = kPage * HD * 2;
+  constexpr float kLazy = 8.f;   // safe pass: raise the running max only when it grows by more than 2^8
+  constexpr float kSlack = 64.f;
+  constexpr int kPageSlots = kMaxChunk / kPage + 2 * S;
+  constexpr int kMergeF = 16 * NMB + 2;        // floats per lane handed from set 1 to set 0
+  static_assert(S % 2 == 0 && S >= 6 && (S - 4) <= 6 && (S - 4) * LPW < 64, "ring depth");
+  static_assert(4 * kMergeF * 64 * 4 <= S * RG::kStageB, "merge buffer fits in the ring");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[S * RG::kStageB + kPageSlots * 4];
+  int* s_pages = (int*)(smem + S * RG::kStageB);
+  lds_u8* lds_smem = (lds_u8*)smem;
+  const unsigned lds_base = (unsigned)(size_t)lds_smem;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int set = wave >> 2, w4 = wave & 3;
+  const int r32 = lane & 31, hh = lane >> 5, j16 = lane & 15, grp = lane >> 4;
+  const int total = min(p.plan[1], p.item_cap);
+  const int Hq = p.Hkv * p.G;
+
+  // Lane-constant LDS offsets, including the set's stage parity: in step k the
+  // set reads tile 2k + set, whose stage is (2k + set) % S.
+  int koff[NKS];                 // K operand: key row r32, logical chunk 2c + hh
+#pragma unroll
+  for (int c = 0; c < NKS; ++c)
+    koff[c] = set * RG::kHalf + r32 * RG::kRowB + (((c * 2 + hh) ^ wide_swz<HD>(r32)) * 16);
+  int voffs[NMB][2];             // transposed V read: key row 4*(grp/2) + j16/4 (+8), dims mb*32 + (grp%2)*16 + 4*(j16%4)
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int key = 4 * (grp >> 1) + (j16 >> 2) + 8 * hi;
+      const int d0 = mb * 32 + (grp & 1) * 16 + 4 * (j16 & 3);
+      voffs[mb][hi] = set * RG::kHalf + S * RG::kHalf + key * RG::kRowB +
+                      (((d0 >> 3) ^ wide_swz<HD>(key)) * 16) + (d0 & 7) * 2;
+    }
+  unsigned dma_off[LPW];
+  int dma_row[LPW];
+  int dma_kv[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int j = wave + NW * i;
+    dma_kv[i] = j >= RG::kLoadsKV / 2;
+    dma_row[i] = (j % (RG::kLoadsKV / 2)) * RG::kKeysPerLoad;
+    const int key = dma_row[i] + lane / RG::kCpr;
+    const int lc = (lane % RG::kCpr) ^ wide_swz<HD>(key & 15);
+    dma_off[i] = (unsigned)(((key & 15) * HD + lc * 8) * 2);
+  }
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
+
+  constexpr int kRowsWG = 4 * 32;
+  const int nvirt = p.nhalf == 1 ? total : (total + 7) / 8 * 16;
+  for (int vi = blockIdx.x; vi < nvirt; vi += gridDim.x) {
+    const int item = p.nhalf == 1 ? vi : (vi >> 4) * 8 + (vi & 7);
+    const int row0 = p.nhalf == 1 ? 0 : ((vi >> 3) & 1) * kRowsWG;
+    if (item >= total) continue;
+    const ItemDesc d = p.items[item];
+    const int b = __builtin_amdgcn_readfirstlane(d.b), h = __builtin_amdgcn_readfirstlane(d.h);
+    const int k_begin = __builtin_amdgcn_readfirstlane(d.k_begin), k_end = __builtin_amdgcn_readfirstlane(d.k_end);
+    const int t0 = __builtin_amdgcn_readfirstlane(d.t0), D = __builtin_amdgcn_readfirstlane(d.D);
+    const int N = __builtin_amdgcn_readfirstlane(d.N), nsplit = __builtin_amdgcn_readfirstlane(d.nsplit);
+    const int R = p.G * (1 + D);
+    if (row0 >= R) continue;
+    const int* bt = p.block_table + (size_t)b * p.max_pages;
+    const bool wave_active = row0 + w4 * 32 < R;
+    const int ntiles = k_end > k_begin ? (k_end - k_begin + RG::kTile - 1) / RG::kTile : 0;
+    const int nsteps = (ntiles + 1) / 2;
+    const bool ragged_tail = k_begin + ntiles * RG::kTile > k_end;
+    const unsigned char* kbase = (const unsigned char*)p.k + (size_t)h * kPageB;
+    const unsigned char* vbase = (const unsigned char*)p.v + (size_t)h * kPageB;
+    const uint64_t page_stride = (uint64_t)p.Hkv * kPageB;
+
+    auto tile_pages = [&](int tile) {
+      const u32x2 v = *(const u32x2*)(s_pages + tile * 2);
+      return u32x2{(unsigned)__builtin_amdgcn_readfirstlane(v[0]), (unsigned)__builtin_amdgcn_readfirstlane(v[1])};
+    };
+    auto issue = [&](u32x2 pids, int st) {
+      const uint64_t off0 = (uint64_t)pids[0] * page_stride;
+      const uint64_t off1 = (uint64_t)pids[1] * page_stride;
+      const unsigned sb = lds_base + (unsigned)(st * RG::kHalf);
+#pragma unroll
+      for (int i = 0; i < LPW; ++i)
+        dma16((dma_kv[i] ? vbase : kbase) + (dma_row[i] >= kPage ? off1 : off0), dma_off[i],
+              sb + (unsigned)(dma_kv[i] * S * RG::kHalf + dma_row[i] * RG::kRowB));
+    };
+    auto zero_tail = [&](int tile) {
+      unsigned char* sp = smem + (tile % S) * RG::kHalf;
+      const int ts = k_begin + tile * RG::kTile;
+#pragma unroll
+      for (int i = 0; i < LPW; ++i)
+        if (ts + dma_row[i] + lane / RG::kCpr >= k_end)
+          *(u32x4*)(sp + dma_kv[i] * S * RG::kHalf + dma_row[i] * RG::kRowB + lane * 16) = u32x4{0, 0, 0, 0};
+      wait_lds();
+    };
+
+    // Query fragments (B operand of S^T): lane holds row r32, dims c*16 + hh*8..+7.
+    const int row = row0 + w4 * 32 + r32;
+    const int i0 = row / p.G;
+    const bool valid = row < R && t0 >= 0 && t0 + i0 < p.total_q;
+    const int qi = valid ? i0 : 0;
+    const int qg = valid ? row - qi * p.G : 0;
+    const int pos = valid ? N - 1 - D + qi : -1;
+    bf16x8 qf[NKS];
+    {
+      const uint16_t* qp = p.q + ((size_t)(t0 + qi) * Hq + (size_t)h * p.G + qg) * HD + hh * 8;
+#pragma unroll
+      for (int c = 0; c < NKS; ++c) {
+        u32x4 raw = valid ? *(const u32x4*)(qp + c * 16) : u32x4{0, 0, 0, 0};
+        qf[c] = __builtin_bit_cast(bf16x8, raw);
+      }
+    }
+    float m_run = -INFINITY;
+    float m_off = 0.f;
+    f32x16 l_acc;
+    f32x16 o[NMB];
+    auto clear = [&]() {
+      m_run = -INFINITY;
+      m_off = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) l_acc[e] = 0.f;
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[mb][e] = 0.f;
+    };
+    clear();
+
+    const int page0 = k_begin / kPage;
+    const int last_page = (k_end - 1) / kPage;
+    for (int j = tid; j < ntiles * (RG::kTile / kPage); j += 64 * NW)
+      s_pages[j] = min(max(bt[min(page0 + j, last_page)], 0), p.num_pages - 1);
+    wait_vmem<0>();
+    wait_lds();
+    block_sync();
+
+    f32x16 sc;
+    float mt = -INFINITY;
+    auto mask_scores = [&](int tile) {
+      const int lim = pos - (k_begin + tile * RG::kTile) - 4 * hh;   // key (e/4)*8 + 4hh + e%4 is visible iff (e/4)*8 + e%4 <= lim
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if ((e >> 2) * 8 + (e & 3) > lim) sc[e] = -INFINITY;
+    };
+    auto row_max = [&](float slack) {
+      float m = sc[0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) m = fmaxf(m, sc[e]);
+      auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+      mt = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1])) * p.scale_log2;
+      return mt > m_run + slack;
+    };
+    // S^T of the set's tile at stage offset `off` (two accumulation chains)
+    auto scores = [&](int off) {
+      f32x16 s0, s1;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) { s0[e] = 0.f; s1[e] = 0.f; }
+#pragma unroll
+      for (int c = 0; c < NKS; c += 2) {
+        const bf16x8 k0 = *(const bf16x8*)(smem + off + koff[c]);
+        const bf16x8 k1 = *(const bf16x8*)(smem + off + koff[c + 1]);
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[c], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[c + 1], s1, 0, 0, 0);
+      }
+      sc = s0 + s1;
+    };
+    // P from the scores, then O^T += V^T P^T and l += 1^T P^T at stage offset `off`
+    auto accumulate = [&](int off) {
+      bf16x8 pf[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pf[ks][e] = (__bf16)fast_exp2(fmaf(sc[ks * 8 + e], p.scale_log2, m_off));
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+          const int va = off + ks * 16 * RG::kRowB;
+          const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_smem + va + voffs[mb][0]));
+          const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_smem + va + voffs[mb][1]));
+          const u32x2 lo = __builtin_bit_cast(u32x2, lo4);
+          const u32x2 hi = __builtin_bit_cast(u32x2, hi4);
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+          o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[mb], 0, 0, 0);
+        }
+        l_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pf[ks], l_acc, 0, 0, 0);
+      }
+    };
+    auto rescale = [&]() {
+      if (mt > m_run + kLazy) {
+        const float alpha = fast_exp2(m_run - mt);
+        m_run = mt;
+        m_off = -mt;
+        l_acc *= alpha;
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) o[mb] *= alpha;
+      }
+    };
+
+    // Step k: tiles 2k (set 0) and 2k+1 (set 1).  Wait for both, barrier,
+    // refill the stages of tiles 2k-2 and 2k-1 with tiles 2k+S-2 and 2k+S-1.
+    auto advance = [&](int k, int st0) {
+      wait_tiles<LPW>(max(0, min(S - 4, ntiles - 2 - 2 * k)));
+      if (ragged_tail && (ntiles - 1) / 2 == k) zero_tail(ntiles - 1);
+      block_sync();
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int tt = 2 * k + S - 2 + q;
+        if (tt < ntiles) issue(tile_pages(tt), (st0 + q) % S);
+      }
+    };
+    // Generic step (first, masked, last, and every step of the safe pass):
+    // run-time stages; SAFE raises the running max lazily.
+    auto step_generic = [&](int k, auto safec) {
+      constexpr bool SAFE = decltype(safec)::value;
+      advance(k, (2 * k + S - 2) % S);
+      const int tt = 2 * k + set;
+      if (wave_active && tt < ntiles) {
+        const int off = (2 * k % S) * RG::kHalf;   // the set's parity is in koff / voffs
+        scores(off);
+        if (k_begin + (tt + 1) * RG::kTile > N - D) mask_scores(tt);
+        if constexpr (SAFE) {
+          if (__any(row_max(kLazy))) rescale();
+        } else if (k == 0) {
+          row_max(0.f);
+          m_run = mt;
+          m_off = mt == -INFINITY ? 0.f : -mt;
+        }
+        accumulate(off);
+      }
+    };
+
+    // ---- Fast pass: step 0 (reference maxima), unrolled plain steps, then the rest.
+#pragma unroll
+    for (int t = 0; t < S - 2; ++t)
+      if (t < ntiles) issue(tile_pages(t), t);
+    // plain steps: both tiles exist and need no causal mask
+    const int plain = max(1, min(ntiles / 2, (N - D - k_begin) / (2 * RG::kTile)));
+    const int ngroups = (plain - 1) / (S / 2);
+    if (nsteps > 0) step_generic(0, std::false_type{});
+    auto fast_steady = [&](auto activec) {
+      constexpr bool ACTIVE = decltype(activec)::value;
+      for (int g = 0; g < ngroups; ++g) {
+        const int kb = 1 + g * (S / 2);
+        auto step = [&](auto uc) {
+          constexpr int u = decltype(uc)::value;
+          constexpr int st = (2 * (1 + u)) % S;         // stage of tile 2k (k = kb + u; kb - 1 is a multiple of S/2)
+          advance(kb + u, (st + S - 2) % S);
+          if constexpr (ACTIVE) {
+            scores(st * RG::kHalf);
+            accumulate(st * RG::kHalf);
+          }
+        };
+        step(ic<0>{});
+        step(ic<1>{});
+        step(ic<2>{});
+        if constexpr (S > 6) step(ic<3>{});
+      }
+    };
+    if (wave_active) fast_steady(std::true_type{});
+    else fast_steady(std::false_type{});
+    for (int k = 1 + ngroups * (S / 2); k < nsteps; ++k) step_generic(k, std::false_type{});
+    const bool over = wave_active && !(l_acc[0] <= 0x1p64f);
+
+    // ---- Safe pass (only if some row's max outgrew its reference): the same
+    // steps again with a running max.
+    if (__syncthreads_or(over ? 1 : 0)) {
+      clear();
+#pragma unroll
+      for (int t = 0; t < S - 2; ++t)
+        if (t < ntiles) issue(tile_pages(t), t);
+      for (int k = 0; k < nsteps; ++k) step_generic(k, std::true_type{});
+    }
+    block_sync();   // every wave is done with the ring (all loads landed: the last step waited for vmcnt 0)
+
+    // ---- Merge the two sets' partials (set 1 hands (O, l, m) to set 0 through LDS).
+    float* xch = (float*)smem + (size_t)w4 * kMergeF * 64 + lane;
+    if (set == 1 && wave_active) {
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) xch[(mb * 16 + e) * 64] = o[mb][e];
+      xch[(16 * NMB) * 64] = l_acc[0];
+      xch[(16 * NMB + 1) * 64] = m_run;
+    }
+    block_sync();
+    if (set == 0 && wave_active && valid) {
+      const float lb = xch[(16 * NMB) * 64];
+      const float mb_ = xch[(16 * NMB + 1) * 64];
+      const float M = fmaxf(m_run, mb_);
+      const float wa = M == -INFINITY ? 0.f : fast_exp2(m_run - M);
+      const float wb = M == -INFINITY ? 0.f : fast_exp2(mb_ - M);
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[mb][e] = o[mb][e] * wa + xch[(mb * 16 + e) * 64] * wb;
+      const float lt = l_acc[0] * wa + lb * wb;
+      // O^T accumulator: lane holds query row r32 and dims mb*32 + q*8 + 4hh + 0..3 in entries 4q..4q+3.
+      if (nsplit == 1) {
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        const size_t obase = ((size_t)(t0 + qi) * Hq + (size_t)h * p.G + qg) * HD + hh * 4;
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 v = f32x4{o[mb][4 * q], o[mb][4 * q + 1], o[mb][4 * q + 2], o[mb][4 * q + 3]} * inv;
+            const int dd = mb * 32 + q * 8;
+            if (OUT_F32) {
+              *(f32x4*)((float*)p.out + obase + dd) = v;
+            } else {
+              const bf16x4 t = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+              *(u32x2*)((uint16_t*)p.out + obase + dd) = __builtin_bit_cast(u32x2, t);
+            }
+          }
+      } else {
+        float* slab = p.part_o + ((size_t)item * p.rpad + row) * HD + hh * 4;
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            *(f32x4*)(slab + mb * 32 + q * 8) = f32x4{o[mb][4 * q], o[mb][4 * q + 1], o[mb][4 * q + 2], o[mb][4 * q + 3]};
+        if (hh == 0) {
+          float* ml = p.part_ml + ((size_t)item * p.rpad + row) * 2;
+          ml[0] = M;
+          ml[1] = lt;
+        }
+      }
+    }
+    block_sync();   // the merge buffer is part of the ring
   }
 }
 
@@ -575,13 +1149,17 @@ __global__ __launch_bounds__(256) void verify_attn_combine(AttnParams p) {
 // Host side: variant choice, workspace layout, launches.
 struct AttnLayout {
   size_t plan_off, items_off, ml_off, o_off, total;
-  int rpad, item_cap, variant;   // variant 0: 1 row block x 4 waves, 1: 2 x 4, 2: 2 x 8
+  int rpad, item_cap, variant, nhalf;
+  // variant 0: 4 waves x 1 row block (64 rows), two workgroups per CU;
+  // variant 1: 4 waves x 2 row blocks (128 rows), one workgroup per CU, two
+  // workgroups per item (row halves) when a sequence can have more rows
 };
 
-static int attn_variant(int rmax) { return rmax <= 64 ? 0 : (rmax <= 128 ? 1 : 2); }
+static int attn_variant(int rmax) { return rmax <= 64 ? 0 : 1; }
+static int attn_halves(int rmax) { return rmax <= 128 ? 1 : 2; }
 
-// Resident workgroups of the persistent grid per CU (the plan targets that many items).
-static int attn_slots(int cus, int variant) { return cus * (variant == 2 ? 1 : 2); }
+// Resident workgroups of the persistent grid per CU.
+static int attn_slots(int cus, int variant) { return cus * (variant == 0 ? 2 : 1); }
 
 // The item cap (and so the workspace size) depends on the CU count; it is
 // computed for the largest CU count of a gfx950 part so that the size query
@@ -592,10 +1170,11 @@ static AttnLayout attn_layout(int B, int Hkv, int G, int HD, int max_pages, int 
   AttnLayout L;
   const int rmax = G * (1 + max_draft);
   L.variant = attn_variant(rmax);
+  L.nhalf = attn_halves(rmax);
   L.rpad = (rmax + 15) / 16 * 16;
   const long long max_keys = (long long)max_pages * kPage;
   const long long units = (long long)B * Hkv;
-  const long long slots = attn_slots(kMaxCus, L.variant);
+  const long long slots = attn_slots(kMaxCus, L.variant) / L.nhalf;   // items the plan aims for
   long long cap;
   if (kv_chunk > 0) {
     cap = units * ((max_keys + kv_chunk - 1) / kv_chunk);
@@ -628,9 +1207,8 @@ size_t sdv_attn_workspace_bytes(int B, int Hkv, int G, int head_dim, int max_pag
 
 template <int HD, int OUTF>
 static void launch_main(int variant, const AttnParams& p, int grid, hipStream_t st) {
-  if (variant == 0) verify_attn_main<HD, 1, 4, OUTF><<<grid, 256, 0, st>>>(p);
-  else if (variant == 1) verify_attn_main<HD, 2, 4, OUTF><<<grid, 256, 0, st>>>(p);
-  else verify_attn_main<HD, 2, 8, OUTF><<<grid, 512, 0, st>>>(p);
+  if (variant == 0) verify_attn_main<HD, 1, 4, 2, OUTF><<<grid, 256, 0, st>>>(p);
+  else verify_attn_wide<HD, OUTF><<<grid, 512, 0, st>>>(p);
 }
 
 hipError_t sdv_attn_launch(const SdAttnLaunch& a) {
@@ -641,7 +1219,10 @@ hipError_t sdv_attn_launch(const SdAttnLaunch& a) {
   if (e != hipSuccess) return e;
   cus = std::max(1, std::min(cus, kMaxCus));
   const AttnLayout L = attn_layout(a.B, a.Hkv, a.G, a.head_dim, a.max_pages, a.max_draft, a.kv_chunk);
-  const int slots = (int)std::min<long long>(attn_slots(cus, L.variant), L.item_cap);
+  const int wgs = attn_slots(cus, L.variant);
+  const int slots = std::max(1, wgs / L.nhalf);   // items the plan aims for
+  const int grid = (int)std::min<long long>(wgs, L.nhalf == 1 ? (long long)L.item_cap
+                                                               : ((long long)L.item_cap + 7) / 8 * 16);
   unsigned char* ws = (unsigned char*)a.workspace;
   AttnParams p;
   p.q = (const uint16_t*)a.q;
@@ -664,16 +1245,17 @@ hipError_t sdv_attn_launch(const SdAttnLaunch& a) {
   p.rpad = L.rpad;
   p.total_q = a.total_q;
   p.item_cap = L.item_cap;
+  p.nhalf = L.nhalf;
   const float scale = a.softmax_scale > 0.f ? a.softmax_scale : 1.f / sqrtf((float)a.head_dim);
   p.scale_log2 = scale * 1.4426950408889634f;
 
   verify_attn_plan<<<1, kPlanThreads, 0, a.stream>>>(p, a.kv_chunk, slots);
   if (a.head_dim == 128) {
-    if (a.out_f32) launch_main<128, 1>(L.variant, p, slots, a.stream);
-    else launch_main<128, 0>(L.variant, p, slots, a.stream);
+    if (a.out_f32) launch_main<128, 1>(L.variant, p, grid, a.stream);
+    else launch_main<128, 0>(L.variant, p, grid, a.stream);
   } else {
-    if (a.out_f32) launch_main<64, 1>(L.variant, p, slots, a.stream);
-    else launch_main<64, 0>(L.variant, p, slots, a.stream);
+    if (a.out_f32) launch_main<64, 1>(L.variant, p, grid, a.stream);
+    else launch_main<64, 0>(L.variant, p, grid, a.stream);
   }
   const int cgrid = a.B * a.Hkv * (L.rpad / 8);
   if (a.head_dim == 128) {

@@ -34,9 +34,9 @@ def kernels(tmp_path_factory):
     assert r.returncode == 0, r.stderr[-3000:]
     text = out.read_text()
     found = {}
-    for m in re.finditer(r"^(_Z\w*verify_attn_main\w*):[^\n]*\n(.*?)^\s*s_endpgm", text, re.M | re.S):
+    for m in re.finditer(r"^(_Z\w*verify_attn_(?:main|wide)\w*):[^\n]*\n(.*?)^\s*s_endpgm", text, re.M | re.S):
         found[m.group(1)] = [l.strip() for l in m.group(2).split("\n")]
-    assert len(found) >= 6, "expected every verify_attn_main instantiation"
+    assert len(found) >= 8, "expected every verify_attn_main and verify_attn_wide instantiation"
     return found
 
 
@@ -76,3 +76,10 @@ def test_dma_base_is_not_sign_extended(kernels):
     has bit 31 set)."""
     for name, lines in kernels.items():
         assert not any(l.startswith("s_bfe_i64") for l in _instrs(lines)), name
+
+
+def test_no_scratch_in_tile_loop(kernels):
+    """No register spills: scratch loads and stores are vector-memory operations and
+    would count against the vmcnt waits that pace the LDS-DMA ring."""
+    for name, lines in kernels.items():
+        assert not any(l.startswith(("scratch_", "buffer_store", "buffer_load")) for l in _instrs(lines)), name

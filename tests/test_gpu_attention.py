@@ -119,3 +119,33 @@ def test_full_size_sampled_units(name, over):
         worst = max(worst, float(np.abs(got - ref).max()))
     say(f"{sp.name}: max|err| over {len(picks)} units = {worst:.3e}")
     assert worst <= ATTN_TOL
+
+
+def _plant_dominant_key(inp, b, h, key, scale=5.0, negative_prefix=0):
+    """All queries of KV head h get one vector v; key `key` of sequence b becomes
+    scale*v (a score far above anything before it), optionally after a prefix of
+    keys pointing away from v (scores far below)."""
+    G = inp.group
+    g = torch.Generator().manual_seed(1234 + key)
+    v = torch.randn(inp.q.shape[-1], generator=g).to(torch.bfloat16)
+    inp.q[:, h * G:(h + 1) * G, :] = v
+    bt = inp.block_table[b].cpu()
+    ps = inp.spec.page_size
+    inp.k_cache[int(bt[key // ps]), h, key % ps, :] = (scale * v.float()).to(torch.bfloat16)
+    for j in range(negative_prefix):
+        inp.k_cache[int(bt[j // ps]), h, j % ps, :] = (-scale * v.float()).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("key,prefix,kv_chunk", [
+    (2000, 0, 0),       # late dominant key, one item per sequence
+    (2000, 0, 256),     # ... in a later split
+    (2497, 0, 0),       # inside the draft block (visible to the last rows only)
+    (1500, 32, 0),      # first tile far below everything after it
+])
+def test_score_far_above_the_first_tile_max(key, prefix, kv_chunk):
+    inp = generate(spec(batch=1, kv_len=[2500], draft_len=[7], seed=5))
+    _plant_dominant_key(inp, 0, 1, key, negative_prefix=prefix)
+    say(f"case: dominant key {key} prefix {prefix} kv_chunk={kv_chunk}")
+    err = compare_attention(inp, gpu_attention(inp, kv_chunk=kv_chunk))
+    say(f"max|err| = {err:.3e}")
+    assert err <= ATTN_TOL
