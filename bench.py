@@ -193,6 +193,90 @@ def stored_traffic(workload: str):
         return None
 
 
+def _rocprof_csv(d: str, kind: str):
+    import csv
+    import glob
+    hits = glob.glob(os.path.join(d, f"*{kind}.csv"))
+    if not hits:
+        raise SystemExit(f"no *{kind}.csv under {d}")
+    with open(hits[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def _per_dispatch(d: str):
+    """{dispatch id: (kernel name, summed counter value)} of one rocprofv3 --pmc run."""
+    per = {}
+    for r in _rocprof_csv(d, "counter_collection"):
+        name, v = per.get(r["Dispatch_Id"], (r["Kernel_Name"], 0.0))
+        per[r["Dispatch_Id"]] = (name, v + float(r["Counter_Value"]))
+    return per
+
+
+def write_profiles(bench_json: str, kt_dir: str, fetch_dir: str, write_dir: str, copy_bytes: int):
+    """Write the kernel-time and HBM-traffic summaries under profiles/ from one
+    bench.py JSON line and three rocprofv3 runs of bench.py (kernel trace with
+    --stats, FETCH_SIZE pass, WRITE_SIZE pass; the counter passes ran with
+    --calibrate-copy `copy_bytes`)."""
+    import statistics
+    with open(bench_json) as f:
+        line = json.loads(f.read().strip().splitlines()[-1])
+    cfg = line["config"]
+    wl = cfg["workload"]
+    from workloads import PRESETS
+    key = next((k for k, v in PRESETS.items() if v.name == wl), None)
+    args = "--no-cpu-baseline" + ("" if key in (None, "g8_kv32k_D15") else f" --workload {key}")
+    # kernel-time summary: the library's kernels only
+    stats = [r for r in _rocprof_csv(kt_dir, "kernel_stats") if "sdv::" in r["Name"]]
+    calls = int(stats[0]["Calls"]) if stats else 0
+    main = max(stats, key=lambda r: float(r["TotalDurationNs"]))
+    prof = os.path.join(ROOT, "profiles")
+    with open(os.path.join(prof, f"verify_step_{wl}_kernel_stats.txt"), "w") as f:
+        f.write(f"# rocprofv3 kernel-trace summary of the library's kernels, workload {wl}:\n"
+                "# one verify step = verify attention (plan, main, split-KV combine) + accept/reject.\n"
+                f"# {calls} calls per kernel = warmup + timed steps.  Durations in ns.\n"
+                f"$ cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d REPO/gpurun_out/kt "
+                f"-o run --output-format csv -- python3 REPO/bench.py {args}\n")
+        f.write("Name,Calls,TotalDurationNs,AverageNs,Percentage,MinNs,MaxNs,StdDev\n")
+        for r in stats:
+            f.write(",".join([r["Name"], r["Calls"], r["TotalDurationNs"], r["AverageNs"], r["Percentage"],
+                              r["MinNs"], r["MaxNs"], r["StdDev"]]) + "\n")
+        f.write(f"bench.py in the same call: attention {line['attention_ms'] * 1e3:.1f} us/step (HIP events), "
+                f"accept {line['accept_ms'] * 1e3:.1f} us/step, {line['value']:.0f} verified tokens/s\n")
+    # traffic summary of the dominant kernel
+    kname = main["Name"]
+    fetch, write = _per_dispatch(fetch_dir), _per_dispatch(write_dir)
+    fk = statistics.median(v for n, v in fetch.values() if n == kname)
+    wk = statistics.median(v for n, v in write.values() if n == kname)
+    nk = sum(1 for n, _ in fetch.values() if n == kname)
+    copy_w = [v for n, v in write.values() if "copyBuffer" in n and abs(v * 1024 - copy_bytes) < 1024]
+    copy_f = sorted((v for n, v in fetch.values() if "copyBuffer" in n), reverse=True)[:len(copy_w)]
+    if not copy_w or not copy_f:
+        raise SystemExit("no calibration copy found in the counter runs")
+    cw, cf = statistics.median(copy_w), statistics.median(copy_f)
+    fscale, wscale = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+    hbm = fk * 1024 * fscale + wk * 1024 * wscale
+    alg = line["roofline"]["algorithmic_bytes_per_launch"]
+    short = kname.replace("void ", "").split("(")[0].replace("sdv::", "")
+    with open(os.path.join(prof, f"verify_attn_traffic_{wl}.txt"), "w") as f:
+        f.write(f"# HBM traffic per launch of the dominant kernel ({short}) on workload {wl}, from two\n"
+                f"# rocprofv3 counter passes (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch, median of {nk}\n"
+                f"# launches).  Each pass also runs a plain {copy_bytes >> 20} MiB device-to-device copy\n"
+                "# (__amd_rocclr_copyBuffer) whose counter readings give the scale from counter KiB to bytes.\n")
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            f.write(f"$ cd /tmp && export TMPDIR=/tmp && timeout -s KILL 90 rocprofv3 --pmc {c} --kernel-trace "
+                    f"-d REPO/gpurun_out/pmc_{c.split('_')[0].lower()} -o run --output-format csv -- python3 "
+                    f"REPO/bench.py {args} --steps 5 --warmup 2 --calibrate-copy {copy_bytes}\n")
+        f.write(f"kernel: {short}\n"
+                f"attention_source_sha256: {attention_source_digest()}\n"
+                f"fetch_kib_per_launch: {fk:.1f}\nwrite_kib_per_launch: {wk:.1f}\n"
+                f"copy_bytes: {copy_bytes}\ncopy_fetch_kib: {cf:.1f}\ncopy_write_kib: {cw:.1f}\n"
+                f"fetch_scale: {fscale:.5f}\nwrite_scale: {wscale:.5f}\n"
+                f"hbm_bytes_per_launch: {hbm:.0f}\nalgorithmic_bytes_per_launch: {alg}\n"
+                f"traffic_over_algorithmic: {hbm / alg:.4f}\n"
+                f"kernel_average_ns (kernel trace): {float(main['AverageNs']):.0f}\n")
+    print(f"wrote profiles for {wl}: {short} {float(main['AverageNs']) / 1e3:.1f} us, traffic {hbm / alg:.4f}x")
+
+
 def copy_calibration(nbytes: int, reps: int = 3):
     """A plain device-to-device copy of `nbytes` (torch's elementwise copy), for
     scaling the FETCH_SIZE / WRITE_SIZE counters to bytes."""
@@ -218,7 +302,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="after the timed steps, copy BYTES device-to-device (counter calibration)")
+    ap.add_argument("--write-profiles", nargs=4, metavar=("BENCH_JSON", "KT_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write the profiles/ summaries from a bench line and three rocprofv3 runs (no GPU)")
     args = ap.parse_args()
+    if args.write_profiles:
+        write_profiles(*args.write_profiles, copy_bytes=args.calibrate_copy or (1 << 30))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -275,15 +364,17 @@ def main():
     a_bytes, a_flops = algorithmic_attention(inp)
     c_bytes = algorithmic_accept(inp)
     # A step whose working set fits the 256 MB Infinity Cache would be served from it on the next
-    # step: then a 1 GiB scratch write between steps (outside the timed events) evicts it.
+    # step: then a 1 GiB scratch read between steps (outside the timed events) evicts it.  A read,
+    # not a write, so that no dirty lines are left to be written back inside the timed step.
     flush = (a_bytes + c_bytes) < (1 << 30)
-    scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev) if flush else None
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device=dev) if flush else None
+    sink = torch.empty(1, dtype=torch.float32, device=dev)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     for k in range(K):
         if flush:
-            scratch.fill_(float(k))
+            torch.amax(scratch, dim=0, keepdim=True, out=sink)
         ev[k][0].record()
         attention()
         ev[k][1].record()
@@ -338,7 +429,7 @@ def main():
         "emitted_tokens_per_s": float(al.sum().item()) / (ms_per_step * 1e-3),
         "mean_accept_len": mean_al,
         "host_wall_s": t_wall,
-        "cache_flush": "1 GiB scratch write between steps, outside the timed events" if flush else None,
+        "cache_flush": "1 GiB scratch read between steps, outside the timed events" if flush else None,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)

@@ -107,7 +107,9 @@ size_t sd_verify_attention_workspace_size(const sd_attn_desc* desc, int32_t tota
  *
  *   q            bf16 [total_q, H_kv*G, d]                 row-major
  *   k_cache      bf16 [num_pages, H_kv, page_size, d]      row-major
- *   v_cache      bf16 [num_pages, H_kv, page_size, d]      row-major
+ *   v_cache      bf16 [num_pages, H_kv, d, page_size]      row-major: each page of V
+ *                stored d-major (the transpose of its page_size x d block), so
+ *                that the keys a P.V product contracts over are contiguous
  *   block_table  int32 [B, max_pages_per_seq]
  *   kv_len       int32 [B]
  *   q_start      int32 [B+1]

@@ -39,9 +39,11 @@ def bf16_bits_to_f64(bits) -> np.ndarray:
 
 
 def _check(q_bits, k_bits, v_bits, block_table, kv_len, q_start, group):
-    if q_bits.ndim != 3 or k_bits.ndim != 4 or v_bits.shape != k_bits.shape:
-        raise ValueError("q [T, Hq, d], k/v [P, Hkv, page, d] expected")
+    if q_bits.ndim != 3 or k_bits.ndim != 4 or v_bits.ndim != 4:
+        raise ValueError("q [T, Hq, d], k [P, Hkv, page, d], v [P, Hkv, d, page] expected")
     P, Hkv, ps, d = k_bits.shape
+    if v_bits.shape != (P, Hkv, d, ps):
+        raise ValueError("v must be [P, Hkv, d, page]: each page stored d-major")
     if q_bits.shape[1] != Hkv * group or q_bits.shape[2] != d:
         raise ValueError("q heads must be Hkv*G with the cache's head_dim")
     B = len(kv_len)
@@ -61,11 +63,21 @@ def _check(q_bits, k_bits, v_bits, block_table, kv_len, q_start, group):
 
 
 def _sequence_keys(cache_bits, table_row, n, h):
-    """Keys (or values) 0..n-1 of one sequence and KV head, in position order."""
+    """Keys 0..n-1 of one sequence and KV head from a [P, Hkv, page, d] cache, in
+    position order: [n, d]."""
     ps = cache_bits.shape[2]
     j = np.arange(n)
     pages = table_row[j // ps]
     return bf16_bits_to_f64(cache_bits[pages, h, j % ps, :])
+
+
+def _sequence_values(cache_bits, table_row, n, h):
+    """Values 0..n-1 of one sequence and KV head from a [P, Hkv, d, page] cache
+    (pages stored d-major), in position order: [n, d]."""
+    ps = cache_bits.shape[3]
+    j = np.arange(n)
+    pages = table_row[j // ps]
+    return bf16_bits_to_f64(cache_bits[pages, h, :, j % ps])
 
 
 def verify_attention_unit(q_bits, k_bits, v_bits, block_table, kv_len, q_start, group,
@@ -78,7 +90,7 @@ def verify_attention_unit(q_bits, k_bits, v_bits, block_table, kv_len, q_start, 
     t0 = int(q_start[b])
     rows = int(q_start[b + 1]) - t0            # 1 + D_b
     K = _sequence_keys(k_bits, block_table[b], n, h)
-    V = _sequence_keys(v_bits, block_table[b], n, h)
+    V = _sequence_values(v_bits, block_table[b], n, h)
     out = np.zeros((rows, group, d), dtype=np.float64)
     for i in range(rows):
         P = n - rows + i

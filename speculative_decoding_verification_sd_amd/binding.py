@@ -162,8 +162,10 @@ def _check_attention_args(q, k_cache, v_cache, block_table, kv_len, q_start, out
     if out.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("out must be bf16 or fp32")
     _need(out, "out", out.dtype, dev)
-    if k_cache.shape != v_cache.shape or k_cache.dim() != 4:
-        raise ValueError("k_cache and v_cache must both be [pages, kv_heads, page_size, head_dim]")
+    if k_cache.dim() != 4 or v_cache.dim() != 4 or \
+            tuple(v_cache.shape) != (k_cache.shape[0], k_cache.shape[1], k_cache.shape[3], k_cache.shape[2]):
+        raise ValueError("k_cache must be [pages, kv_heads, page_size, head_dim] and v_cache "
+                         "[pages, kv_heads, head_dim, page_size] (pages stored d-major)")
     if q.dim() != 3 or out.shape != q.shape:
         raise ValueError("q and out must be [total_q, query_heads, head_dim]")
     B = block_table.shape[0]

@@ -186,15 +186,15 @@ __device__ __forceinline__ void wait_lds() {
   __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
 }
 
-// XOR swizzle of the 16-byte chunk index inside a K or V row of the LDS tile,
-// as a function of the key's position mod 16, for 64 banks of 4 bytes: the
-// 16 lanes of a ds_read_b128 (K operand, sixteen keys at one logical chunk)
-// and the 32 lanes of a ds_read_b64_tr_b16 (eight keys, two adjacent chunks)
-// each touch every bank at most once.
+// XOR swizzle of the 16-byte chunks of a K row in LDS for verify_attn_main, a
+// function of the key's position in the 32-key tile (64 banks of 4 bytes): the
+// sixteen key rows one ds_read_b128 reads together ((r/4)*8 + kb*4 + r%4,
+// r < 16) land on distinct banks.  Bit 2 of the key (kb) is not used, so the
+// rows of the second block sit a constant four rows further.
 template <int HD>
-__device__ __forceinline__ int chunk_swz(int k) {
-  if constexpr (HD == 128) return ((k & 7) << 1) | ((k >> 3) & 1);
-  else return (((k >> 1) & 3) << 1) | ((k >> 3) & 1);
+__device__ __forceinline__ int key_swz(int k) {
+  if constexpr (HD == 128) return (k & 3) | (((k >> 3) & 3) << 2);
+  else return ((k >> 1) & 1) | (((k >> 3) & 3) << 1);
 }
 
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
@@ -253,6 +253,68 @@ struct Ring {
   static_assert(kLoadsKV % NW == 0 && kLPW >= 1, "DMA instructions divide evenly over the waves");
 };
 
+// One LDS-DMA instruction of a tile as seen by one lane: it moves 1 KiB (16
+// bytes per lane) of one (page, head) block into a ring stage.
+//   K: kKeysPerLoad key rows in key order; the lane's 16 bytes are logical
+//      chunk (lane % kCpr) ^ swz(key) of its key row.
+//   V: 32 d-rows of one d-major V page (16 keys x 2 bytes per d); LDS half h
+//      of d-row d holds keys ((h ^ bit 3 of d) * 8)..+7, so that sixteen
+//      consecutive d-rows read at one key half land on distinct banks.
+struct DmaSlot {
+  unsigned src;   // lane's byte offset inside the (page, head) block
+  int dst;        // byte offset of the instruction's 1 KiB inside the stage's K (or V) tile
+  int page;       // page of the tile (0 or 1)
+  int kv;         // 0: K, 1: V
+  int key0;       // tile-relative key of the lane's first element
+};
+
+template <int HD, class RG, class SWZ>
+__device__ __forceinline__ DmaSlot dma_slot(int j, int lane, SWZ swz) {
+  DmaSlot s;
+  if (j < RG::kLoadsKV / 2) {
+    const int row0 = j * RG::kKeysPerLoad;
+    const int key = row0 + lane / RG::kCpr;
+    const int lc = (lane % RG::kCpr) ^ swz(key);
+    s.src = (unsigned)(((key & 15) * HD + lc * 8) * 2);
+    s.dst = row0 * RG::kRowB;
+    s.page = row0 / kPage;
+    s.kv = 0;
+    s.key0 = key;
+  } else {
+    constexpr int kPerPage = HD / 32;             // instructions per V page (32 d-rows of 32 bytes)
+    const int jv = j - RG::kLoadsKV / 2;
+    const int page = jv / kPerPage;
+    const int d = (jv % kPerPage) * 32 + lane / 2;
+    const int half = (lane & 1) ^ ((d >> 3) & 1);
+    s.src = (unsigned)(d * 32 + half * 16);
+    s.dst = page * HD * 32 + (jv % kPerPage) * 1024;
+    s.page = page;
+    s.kv = 1;
+    s.key0 = page * kPage + half * 8;
+  }
+  return s;
+}
+
+// Zero the elements of this wave's DMA loads of stage `sp` whose keys lie at or
+// past `lim` (tile-relative): whole K rows, single entries of the V pages.
+template <int LPW, class RG, int S>
+__device__ __forceinline__ void zero_keys_past(unsigned char* sp, const DmaSlot (&dma)[LPW], int lane, int lim) {
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    if (dma[i].kv == 0) {
+      if (dma[i].key0 >= lim) *(u32x4*)(sp + dma[i].dst + lane * 16) = u32x4{0, 0, 0, 0};
+    } else if (dma[i].key0 + 7 >= lim) {
+      unsigned short* e = (unsigned short*)(sp + S * RG::kHalf + dma[i].dst + lane * 16);
+      u32x4 x = *(u32x4*)e;
+      unsigned short* xs = (unsigned short*)&x;
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (dma[i].key0 + q >= lim) xs[q] = 0;
+      *(u32x4*)e = x;
+    }
+  }
+}
+
 // Wait until at most `tiles` tiles' worth (LPW loads each, tiles <= 6) of this
 // wave's vector loads are in flight; the count must be an immediate, hence the
 // switch.
@@ -302,33 +364,25 @@ __global__ __launch_bounds__(64 * NW, WPC) void verify_attn_main(AttnParams p) {
   const int Hq = p.Hkv * p.G;
 
   // Lane-constant LDS offsets inside a stage (the stage itself is an immediate
-  // in the unrolled tile loop).  K operand: key kb*16 + l16, logical chunk
-  // c*4 + g4.  Transposed V read: key row g4*4 + l16/4 (and +16), chunk pair db.
-  const int kswz = chunk_swz<HD>(l16) & (RG::kCpr - 1);
+  // in the unrolled tile loop).  S^T block kb takes key (r/4)*8 + kb*4 + r%4
+  // as its MFMA row r, so that lane group g4 holds the eight consecutive keys
+  // g4*8..+7 of the tile: K operand row key(0, l16) (+4 rows for kb = 1),
+  // logical chunk c*4 + g4; V^T operand d-row db*16 + l16, keys g4*8..+7.
+  const int kkey = (l16 >> 2) * 8 + (l16 & 3);
   int koff[NKC];
 #pragma unroll
-  for (int c = 0; c < NKC; ++c) koff[c] = l16 * RG::kRowB + (((c * 4 + g4) ^ kswz) * 16);
-  const int vkey = g4 * 4 + (l16 >> 2);
-  const int vswz = chunk_swz<HD>(vkey) & (RG::kCpr - 1);
-  const int vsub = (l16 & 3) >> 1;
+  for (int c = 0; c < NKC; ++c) koff[c] = kkey * RG::kRowB + (((c * 4 + g4) ^ key_swz<HD>(kkey)) * 16);
   int voffs[NDB];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
-    voffs[db] = S * RG::kHalf + vkey * RG::kRowB + (l16 & 1) * 8 + (((db * 2 + vsub) ^ vswz) * 16);
-
-  // DMA instruction j = wave + NW*i of a tile: K rows for j < kLoadsKV/2, V rows after
-  unsigned dma_off[LPW];         // byte offset of this lane's 16 bytes inside the (page, head) block
-  int dma_row[LPW];              // first key row (tile-relative) the instruction fills
-  int dma_kv[LPW];
-#pragma unroll
-  for (int i = 0; i < LPW; ++i) {
-    const int j = wave + NW * i;
-    dma_kv[i] = j >= RG::kLoadsKV / 2;
-    dma_row[i] = (j % (RG::kLoadsKV / 2)) * RG::kKeysPerLoad;
-    const int key = dma_row[i] + lane / RG::kCpr;
-    const int lc = (lane % RG::kCpr) ^ (chunk_swz<HD>(key & 15) & (RG::kCpr - 1));
-    dma_off[i] = (unsigned)(((key & 15) * HD + lc * 8) * 2);
+  for (int db = 0; db < NDB; ++db) {
+    const int dd = db * 16 + l16;
+    voffs[db] = S * RG::kHalf + (g4 >> 1) * HD * 32 + dd * 32 + (((g4 & 1) ^ ((dd >> 3) & 1)) * 16);
   }
+
+  // DMA instruction j = wave + NW*i of a tile: K rows for j < kLoadsKV/2, V pages after
+  DmaSlot dma[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) dma[i] = dma_slot<HD, RG>(wave + NW * i, lane, [](int k) { return key_swz<HD>(k); });
   bf16x8 ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
@@ -372,17 +426,12 @@ __global__ __launch_bounds__(64 * NW, WPC) void verify_attn_main(AttnParams p) {
       const unsigned sb = lds_base + (unsigned)(st * RG::kHalf);
 #pragma unroll
       for (int i = 0; i < LPW; ++i)
-        dma16((dma_kv[i] ? vbase : kbase) + (dma_row[i] >= kPage ? off1 : off0), dma_off[i],
-              sb + (unsigned)(dma_kv[i] * S * RG::kHalf + dma_row[i] * RG::kRowB));
+        dma16((dma[i].kv ? vbase : kbase) + (dma[i].page ? off1 : off0), dma[i].src,
+              sb + (unsigned)(dma[i].kv * S * RG::kHalf + dma[i].dst));
     };
-    // zero the key rows at or past k_end that this wave loaded into stage st (last tile only)
+    // zero what this wave loaded into stage st for keys at or past k_end (last tile only)
     auto zero_tail = [&](int tile, int st) {
-      unsigned char* sp = smem + st * RG::kHalf;
-      const int ts = k_begin + tile * RG::kTile;
-#pragma unroll
-      for (int i = 0; i < LPW; ++i)
-        if (ts + dma_row[i] + lane / RG::kCpr >= k_end)
-          *(u32x4*)(sp + dma_kv[i] * S * RG::kHalf + dma_row[i] * RG::kRowB + lane * 16) = u32x4{0, 0, 0, 0};
+      zero_keys_past<LPW, RG, S>(smem + st * RG::kHalf, dma, lane, k_end - (k_begin + tile * RG::kTile));
       wait_lds();
     };
 
@@ -438,12 +487,12 @@ __global__ __launch_bounds__(64 * NW, WPC) void verify_attn_main(AttnParams p) {
       const int ts = k_begin + tile * RG::kTile;
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) {
-        const int lim = pos[rb] - ts - g4 * 4;   // key kb*16 + g4*4 + e is visible iff kb*16 + e <= lim
+        const int lim = pos[rb] - ts - g4 * 8;   // key g4*8 + kb*4 + e is visible iff kb*4 + e <= lim
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (kb * 16 + e > lim) s[kb][rb][e] = -INFINITY;
+            if (kb * 4 + e > lim) s[kb][rb][e] = -INFINITY;
       }
     };
     // Sets mt; true if some row's max exceeds its running max by more than `slack`.
@@ -466,18 +515,11 @@ __global__ __launch_bounds__(64 * NW, WPC) void verify_attn_main(AttnParams p) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int c = 0; c < NKC; ++c)
-          kf[kb][c] = *(const bf16x8*)(smem + off + kb * 16 * RG::kRowB + koff[c]);
+          kf[kb][c] = *(const bf16x8*)(smem + off + kb * 4 * RG::kRowB + koff[c]);
     };
     auto read_v = [&](int off, bf16x8 (&vf)[NDB]) {
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int va = off + voffs[db];
-        const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_smem + va));
-        const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_smem + va + 16 * RG::kRowB));
-        const u32x2 lo = __builtin_bit_cast(u32x2, lo4);
-        const u32x2 hi = __builtin_bit_cast(u32x2, hi4);
-        vf[db] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-      }
+      for (int db = 0; db < NDB; ++db) vf[db] = *(const bf16x8*)(smem + off + voffs[db]);
     };
     // the 2*NRB accumulation chains advance together (k-step outermost), so
     // consecutive MFMAs never depend on each other
@@ -519,10 +561,10 @@ __global__ __launch_bounds__(64 * NW, WPC) void verify_attn_main(AttnParams p) {
     // ---- Fast pass.  Each row's reference max is fixed by the item's first
     // tile and never moves, and later tiles take no row max at all: a score
     // that rises far above the reference shows in the row sum l (it holds every
-    // P), and an item whose l ends above 2^kSlack (or is not finite) is
+    // P), and an item whose l ends above kOverflow (or is not finite) is
     // recomputed by the safe pass below with a running max.  Below that bound
     // o and l are far from fp32 overflow.
-    constexpr float kSlack = 64.f;
+    constexpr float kOverflow = 0x1p64f;   // row sums above this redo the item
     // Tiles 0..steady-1 run in the unrolled, pipelined loop: each has a next
     // tile that needs no causal mask.  steady is a multiple of S, so that the
     // loop carries no per-step guards and tile `steady` starts the tail with
@@ -634,7 +676,7 @@ __global__ __launch_bounds__(64 * NW, WPC) void verify_attn_main(AttnParams p) {
     // every load of the fast pass has landed (the last tile waited for vmcnt 0)
     bool over = false;
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) over |= !(l_acc[rb][0] <= 0x1p64f);
+    for (int rb = 0; rb < NRB; ++rb) over |= !(l_acc[rb][0] <= kOverflow);
     over &= wave_active;
 
     // ---- Safe pass (only if some row's max outgrew the fast pass): the same
@@ -760,7 +802,7 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
   constexpr int LPW = RG::kLPW;
   constexpr int kPageB = kPage * HD * 2;
   constexpr float kLazy = 8.f;   // safe pass: raise the running max only when it grows by more than 2^8
-  constexpr float kSlack = 64.f;
+  constexpr float kOverflow = 0x1p64f;   // row sums above this redo the item
   constexpr int kPageSlots = kMaxChunk / kPage + 2 * S;
   constexpr int kMergeF = 16 * NMB + 2;        // floats per lane handed from set 1 to set 0
   static_assert(S % 2 == 0 && S >= 6 && (S - 4) <= 6 && (S - 4) * LPW < 64, "ring depth");
@@ -774,38 +816,29 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int set = wave >> 2, w4 = wave & 3;
-  const int r32 = lane & 31, hh = lane >> 5, j16 = lane & 15, grp = lane >> 4;
+  const int r32 = lane & 31, hh = lane >> 5;
   const int total = min(p.plan[1], p.item_cap);
   const int Hq = p.Hkv * p.G;
 
   // Lane-constant LDS offsets, including the set's stage parity: in step k the
   // set reads tile 2k + set, whose stage is (2k + set) % S.
-  int koff[NKS];                 // K operand: key row r32, logical chunk 2c + hh
+  // S^T takes key pi(r) = (r/16)*16 + ((r/4)%2)*8 + ((r/8)%2)*4 + r%4 as its MFMA
+  // row r, so that score entry e of a lane holds key (e/8)*16 + 8hh + e%8 and
+  // each 16-key step of P V reads eight consecutive keys per lane.
+  const int kkey = (r32 >> 4) * 16 + ((r32 >> 2) & 1) * 8 + ((r32 >> 3) & 1) * 4 + (r32 & 3);
+  int koff[NKS];                 // K operand: key row kkey, logical chunk 2c + hh
 #pragma unroll
   for (int c = 0; c < NKS; ++c)
-    koff[c] = set * RG::kHalf + r32 * RG::kRowB + (((c * 2 + hh) ^ wide_swz<HD>(r32)) * 16);
-  int voffs[NMB][2];             // transposed V read: key row 4*(grp/2) + j16/4 (+8), dims mb*32 + (grp%2)*16 + 4*(j16%4)
+    koff[c] = set * RG::kHalf + kkey * RG::kRowB + (((c * 2 + hh) ^ wide_swz<HD>(kkey)) * 16);
+  int voffs[NMB];                // V^T operand: d-row mb*32 + r32, keys ks*16 + 8hh..+7 (page ks)
 #pragma unroll
-  for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-    for (int hi = 0; hi < 2; ++hi) {
-      const int key = 4 * (grp >> 1) + (j16 >> 2) + 8 * hi;
-      const int d0 = mb * 32 + (grp & 1) * 16 + 4 * (j16 & 3);
-      voffs[mb][hi] = set * RG::kHalf + S * RG::kHalf + key * RG::kRowB +
-                      (((d0 >> 3) ^ wide_swz<HD>(key)) * 16) + (d0 & 7) * 2;
-    }
-  unsigned dma_off[LPW];
-  int dma_row[LPW];
-  int dma_kv[LPW];
-#pragma unroll
-  for (int i = 0; i < LPW; ++i) {
-    const int j = wave + NW * i;
-    dma_kv[i] = j >= RG::kLoadsKV / 2;
-    dma_row[i] = (j % (RG::kLoadsKV / 2)) * RG::kKeysPerLoad;
-    const int key = dma_row[i] + lane / RG::kCpr;
-    const int lc = (lane % RG::kCpr) ^ wide_swz<HD>(key & 15);
-    dma_off[i] = (unsigned)(((key & 15) * HD + lc * 8) * 2);
+  for (int mb = 0; mb < NMB; ++mb) {
+    const int dd = mb * 32 + r32;
+    voffs[mb] = set * RG::kHalf + S * RG::kHalf + dd * 32 + ((hh ^ ((dd >> 3) & 1)) * 16);
   }
+  DmaSlot dma[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) dma[i] = dma_slot<HD, RG>(wave + NW * i, lane, [](int k) { return wide_swz<HD>(k & 15); });
   bf16x8 ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
@@ -842,16 +875,11 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
       const unsigned sb = lds_base + (unsigned)(st * RG::kHalf);
 #pragma unroll
       for (int i = 0; i < LPW; ++i)
-        dma16((dma_kv[i] ? vbase : kbase) + (dma_row[i] >= kPage ? off1 : off0), dma_off[i],
-              sb + (unsigned)(dma_kv[i] * S * RG::kHalf + dma_row[i] * RG::kRowB));
+        dma16((dma[i].kv ? vbase : kbase) + (dma[i].page ? off1 : off0), dma[i].src,
+              sb + (unsigned)(dma[i].kv * S * RG::kHalf + dma[i].dst));
     };
     auto zero_tail = [&](int tile) {
-      unsigned char* sp = smem + (tile % S) * RG::kHalf;
-      const int ts = k_begin + tile * RG::kTile;
-#pragma unroll
-      for (int i = 0; i < LPW; ++i)
-        if (ts + dma_row[i] + lane / RG::kCpr >= k_end)
-          *(u32x4*)(sp + dma_kv[i] * S * RG::kHalf + dma_row[i] * RG::kRowB + lane * 16) = u32x4{0, 0, 0, 0};
+      zero_keys_past<LPW, RG, S>(smem + (tile % S) * RG::kHalf, dma, lane, k_end - (k_begin + tile * RG::kTile));
       wait_lds();
     };
 
@@ -873,7 +901,7 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
     }
     float m_run = -INFINITY;
     float m_off = 0.f;
-    f32x16 l_acc;
+    f32x16 l_acc;                  // row sums (every entry of a lane holds its query row's sum)
     f32x16 o[NMB];
     auto clear = [&]() {
       m_run = -INFINITY;
@@ -898,10 +926,10 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
     f32x16 sc;
     float mt = -INFINITY;
     auto mask_scores = [&](int tile) {
-      const int lim = pos - (k_begin + tile * RG::kTile) - 4 * hh;   // key (e/4)*8 + 4hh + e%4 is visible iff (e/4)*8 + e%4 <= lim
+      const int lim = pos - (k_begin + tile * RG::kTile) - 8 * hh;   // key (e/8)*16 + 8hh + e%8 is visible iff (e/8)*16 + e%8 <= lim
 #pragma unroll
       for (int e = 0; e < 16; ++e)
-        if ((e >> 2) * 8 + (e & 3) > lim) sc[e] = -INFINITY;
+        if ((e >> 3) * 16 + (e & 7) > lim) sc[e] = -INFINITY;
     };
     auto row_max = [&](float slack) {
       float m = sc[0];
@@ -936,12 +964,7 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
       for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) {
-          const int va = off + ks * 16 * RG::kRowB;
-          const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_smem + va + voffs[mb][0]));
-          const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_smem + va + voffs[mb][1]));
-          const u32x2 lo = __builtin_bit_cast(u32x2, lo4);
-          const u32x2 hi = __builtin_bit_cast(u32x2, hi4);
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+          const bf16x8 vf = *(const bf16x8*)(smem + off + ks * HD * 32 + voffs[mb]);
           o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[mb], 0, 0, 0);
         }
         l_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pf[ks], l_acc, 0, 0, 0);
@@ -1021,7 +1044,7 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
     if (wave_active) fast_steady(std::true_type{});
     else fast_steady(std::false_type{});
     for (int k = 1 + ngroups * (S / 2); k < nsteps; ++k) step_generic(k, std::false_type{});
-    const bool over = wave_active && !(l_acc[0] <= 0x1p64f);
+    const bool over = wave_active && !(l_acc[0] <= kOverflow);
 
     // ---- Safe pass (only if some row's max outgrew its reference): the same
     // steps again with a running max.

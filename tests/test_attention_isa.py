@@ -54,20 +54,20 @@ def test_m0_written_only_by_the_dma_sequence(kernels):
 
 
 def test_no_full_vmem_drain_before_tile_reads(kernels):
+    """No K/V tile read (ds_read_b128 / ds_read_b64_tr_b16) is preceded, within its
+    basic block, by an s_waitcnt vmcnt(0): the compiler must not drain the DMA ring
+    in front of the tile reads (the ring's own waits are explicit and counted)."""
     for name, lines in kernels.items():
-        ins = _instrs(lines)
-        since_barrier = None
-        for l in ins:
-            if l.startswith("s_barrier"):
-                since_barrier = []
+        block = []
+        for l in lines:
+            if not l or l.startswith(";"):
                 continue
-            if since_barrier is None:
+            if l.endswith(":") or l.startswith(".LBB") or l.startswith("s_barrier"):
+                block = []
                 continue
             if l.startswith(("ds_read_b64_tr_b16", "ds_read_b128")):
-                assert not any(re.match(r"s_waitcnt .*vmcnt\(0\)", x) for x in since_barrier), (name, l)
-                since_barrier = None
-                continue
-            since_barrier.append(l)
+                assert not any(re.match(r"s_waitcnt .*vmcnt\(0\)", x) for x in block), (name, l)
+            block.append(l)
 
 
 def test_dma_base_is_not_sign_extended(kernels):

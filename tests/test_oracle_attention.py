@@ -28,7 +28,7 @@ def _paged_from_dense(dense_k, dense_v, page, rng, extra_pages=3):
     pool = sum(npages) + extra_pages
     perm = rng.permutation(pool)
     kc = rng.integers(0, 1 << 16, size=(pool, Hkv, page, d), dtype=np.uint16)   # junk everywhere
-    vc = rng.integers(0, 1 << 16, size=(pool, Hkv, page, d), dtype=np.uint16)
+    vc = rng.integers(0, 1 << 16, size=(pool, Hkv, d, page), dtype=np.uint16)   # pages stored d-major
     # keep junk finite so that it cannot hide behind NaN arithmetic
     kc &= np.uint16(0x3FFF)
     vc &= np.uint16(0x3FFF)
@@ -41,7 +41,7 @@ def _paged_from_dense(dense_k, dense_v, page, rng, extra_pages=3):
             bt[b, pg] = phys
             lo, hi = pg * page, min((pg + 1) * page, dense_k[b].shape[1])
             kc[phys, :, : hi - lo, :] = dense_k[b][:, lo:hi, :]
-            vc[phys, :, : hi - lo, :] = dense_v[b][:, lo:hi, :]
+            vc[phys, :, :, : hi - lo] = dense_v[b][:, lo:hi, :].transpose(0, 2, 1)
     return kc, vc, bt
 
 
@@ -113,7 +113,7 @@ def test_constant_values_and_dominant_key():
     c = _case(rng, [40], [3], Hkv=1, G=2, d=16)
     vconst = _rand_bits(rng, (16,))
     vc = c["vc"].copy()
-    vc[:, 0, :, :] = vconst
+    vc[:, 0, :, :] = vconst[:, None]     # every key's value row is vconst (pages are d-major)
     out = verify_attention(c["q"], c["kc"], vc, c["bt"], c["kv_len"], c["q_start"], 2)
     np.testing.assert_allclose(out[0], np.broadcast_to(bf16_bits_to_f64(vconst), out[0].shape),
                                rtol=0, atol=1e-14)
@@ -124,7 +124,7 @@ def test_constant_values_and_dominant_key():
     page, slot = c["bt"][0, 5 // 16], 5 % 16
     kc[page, 0, slot, :] = k5.view(np.uint16)
     out = verify_attention(c["q"], kc, c["vc"], c["bt"], c["kv_len"], c["q_start"], 2)
-    v5 = bf16_bits_to_f64(c["vc"][page, 0, slot])
+    v5 = bf16_bits_to_f64(c["vc"][page, 0, :, slot])
     np.testing.assert_allclose(out[0, 0], v5, rtol=0, atol=1e-9)
 
 
