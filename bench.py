@@ -300,6 +300,8 @@ def main():
     ap.add_argument("--kv-chunk", type=int, default=0)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--settle-s", type=float, default=1.0,
+                    help="before the warmup, run steps for this many seconds so the GPU clock settles")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="after the timed steps, copy BYTES device-to-device (counter calibration)")
     ap.add_argument("--write-profiles", nargs=4, metavar=("BENCH_JSON", "KT_DIR", "FETCH_DIR", "WRITE_DIR"),
@@ -352,12 +354,25 @@ def main():
         sdv.sd_accept_reject(inp.target_logits, inp.draft_logits, inp.draft_tokens, inp.q_start, inp.uniforms,
                              al, tok, mode=sp.mode, max_draft=inp.max_draft, workspace=ws_c)
 
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(max(1, args.warmup)):
+    def step():
         sdv.sd_verify_step(inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.kv_len, inp.q_start, out,
                            inp.target_logits, inp.draft_logits, inp.draft_tokens, inp.uniforms, al, tok,
                            group_size=sp.group, max_draft=inp.max_draft, mode=sp.mode, kv_chunk=args.kv_chunk,
                            workspace=ws_s)
+
+    # From idle the GPU takes tens of milliseconds to reach its steady clock under this load (at the
+    # power limit for the attention); a few warmup steps alone would time that ramp.
+    settle_steps = 0
+    t_end = time.perf_counter() + max(0.0, args.settle_s)
+    while time.perf_counter() < t_end:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+        settle_steps += 10
+    print(f"[bench] clock settle: {settle_steps} steps in {args.settle_s:.1f} s; warmup {args.warmup}",
+          file=sys.stderr, flush=True)
+    for _ in range(max(1, args.warmup)):
+        step()
     torch.cuda.synchronize()
 
     K = args.steps
@@ -429,6 +444,7 @@ def main():
         "emitted_tokens_per_s": float(al.sum().item()) / (ms_per_step * 1e-3),
         "mean_accept_len": mean_al,
         "host_wall_s": t_wall,
+        "clock_settle": {"seconds": args.settle_s, "steps": settle_steps},
         "cache_flush": "1 GiB scratch read between steps, outside the timed events" if flush else None,
     }
     if not args.no_cpu_baseline:

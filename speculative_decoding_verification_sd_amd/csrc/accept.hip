@@ -15,18 +15,21 @@
 //                        max (greedy: lowest-index argmax; stochastic: sum of
 //                        exp(x - max) accumulated in fp64).  One pass over every
 //                        target (and draft) row: this is the step's HBM cost.
-//   2. accept_decide     one workgroup per sequence.  Loads the sequence's
-//                        chunk statistics into LDS, merges them into per-row
-//                        log-normalisers (fp64), runs the D_b tests in parallel
-//                        (fp64 ratios), finds the first failure n, writes AL
-//                        and the accepted tokens, and (stochastic) resets the
-//                        sequence's arrival counter for kernel 3.
-//   3. accept_sample     grid = vocab chunks x sequences (stochastic only).
-//                        fp64 chunk sums of the residual max(0, p - q) at row
-//                        n (of p at row D when every draft passed); the last
-//                        chunk of a sequence to finish then finds the chunk
-//                        holding u*Z and scans it in fp64 to the first prefix
-//                        sum > u*Z.
+//                        (Stochastic: also clears the per-sequence arrival
+//                        counters used by kernel 2b.)
+//   2a. accept_decide    greedy: one workgroup per sequence merges the chunk
+//                        argmaxes of its 1+D rows, compares the drafts, and
+//                        writes AL, the accepted tokens and the correction.
+//   2b. accept_finish    stochastic: grid = vocab chunks x sequences.  Every
+//                        workgroup takes the sequence's decision itself (fp64
+//                        log-normalisers merged from the chunk statistics, the
+//                        D tests in fp64, the first failure n); workgroup 0
+//                        writes AL and the accepted tokens.  Each workgroup
+//                        then sums its chunk of the residual max(0, p - q) at
+//                        row n (of p at row D when every draft passed) in fp64,
+//                        per thread (16 consecutive tokens) and per chunk; the
+//                        last to finish finds the first prefix sum > u*Z by
+//                        chunk, then 16-token slice, then token.
 
 #include <limits.h>
 #include <math.h>
@@ -39,7 +42,8 @@ constexpr int kAccThreads = 256;
 constexpr int kChunk = 8192;                      // logits per row-statistics workgroup
 constexpr int kPerThread = kChunk / kAccThreads;  // 32
 constexpr int kSChunk = 4096;                     // logits per sampling workgroup
-constexpr int kSPerThread = kSChunk / kAccThreads;
+constexpr int kSPerThread = kSChunk / kAccThreads;  // 16: one slice of the sampling search per thread
+static_assert(kSPerThread % 4 == 0 && kSPerThread <= 64, "a slice is scanned by one wave");
 constexpr int kDecideSlots = 2048;                // chunk statistics staged in LDS per pass
 
 struct RowPart {
@@ -48,13 +52,12 @@ struct RowPart {
   double s;    // sum of exp(x - m) over the chunk (stochastic)
 };
 
+// The decision a sampling workgroup works from.
 struct SeqState {
   int n;            // leading passes
   int residual;     // 1: sample max(0, p - q) at row n; 0: sample p at row D
   double lse_p;     // log-normaliser of the target row n
   double lse_q;     // log-normaliser of the draft row n (residual only)
-  unsigned arrived; // sampling workgroups done (reset by accept_decide)
-  int pad;
 };
 
 struct AccParams {
@@ -66,9 +69,10 @@ struct AccParams {
   int* accept_len;
   int* out_tokens;
   RowPart* part;      // [rows, nchunk]
-  SeqState* state;    // [B]
+  unsigned* arrived;  // [B] sampling workgroups done (cleared by accept_rowstats)
   double* rsum;       // [B, nschunk, 2]  (residual, p) chunk sums
-  int B, T, V, nchunk, nschunk, max_draft;
+  double* rsub;       // [B, nschunk, 256, 2]  (residual, p) sums of each thread's 16 tokens
+  int B, T, V, nchunk, nschunk, max_draft, vec4;
 };
 
 __device__ __forceinline__ bool better(float m1, int i1, float m0, int i0) {
@@ -130,6 +134,8 @@ __global__ __launch_bounds__(kAccThreads) void accept_rowstats(AccParams p) {
   __shared__ double sd[4];
   const int row = blockIdx.x / p.nchunk;
   const int c = blockIdx.x - row * p.nchunk;
+  if (STOCH && blockIdx.x == 0)
+    for (int i = threadIdx.x; i < p.B; i += kAccThreads) p.arrived[i] = 0u;
   const float* src = row < p.T ? p.target + (size_t)row * p.V : p.draft + (size_t)(row - p.T) * p.V;
   const int tid = threadIdx.x;
   const int j0 = c * kChunk;
@@ -204,9 +210,8 @@ __global__ __launch_bounds__(kAccThreads) void accept_rowstats(AccParams p) {
 }
 
 // ---------------------------------------------------------------------------
-template <int STOCH>
 __global__ __launch_bounds__(kAccThreads) void accept_decide(AccParams p) {
-  extern __shared__ double dyn[];               // lse_p[D+1], lse_q[D], argmax[D+1]
+  extern __shared__ int amax[];                 // [D+1] row argmaxes
   __shared__ RowPart stage[kDecideSlots];
   __shared__ int first_fail;
   const int b = blockIdx.x;
@@ -214,42 +219,26 @@ __global__ __launch_bounds__(kAccThreads) void accept_decide(AccParams p) {
   const int t0 = p.q_start[b];
   const int D = seq_d(p, b);
   const int d0 = t0 - b;
-  double* lse_p = dyn;
-  double* lse_q = dyn + (p.max_draft + 1);
-  int* amax = (int*)(dyn + 2 * p.max_draft + 1);
   if (!seq_ok(p, t0, D, d0)) {
     if (tid == 0) p.accept_len[b] = 0;
     return;
   }
 
-  // rows: r <= D -> target row t0+r; r > D -> draft row d0+r-D-1
-  const int nrows = STOCH ? 2 * D + 1 : D + 1;
+  const int nrows = D + 1;                      // target rows t0 .. t0+D
   const int rows_per_pass = max(1, kDecideSlots / p.nchunk);
   for (int r0 = 0; r0 < nrows; r0 += rows_per_pass) {
     const int nr = min(rows_per_pass, nrows - r0);
     __syncthreads();
-    for (int e = tid; e < nr * p.nchunk; e += kAccThreads) {
-      const int r = r0 + e / p.nchunk;
-      const int prow = r <= D ? t0 + r : p.T + d0 + (r - D - 1);
-      stage[e] = p.part[(size_t)prow * p.nchunk + (e % p.nchunk)];
-    }
+    for (int e = tid; e < nr * p.nchunk; e += kAccThreads)
+      stage[e] = p.part[(size_t)(t0 + r0 + e / p.nchunk) * p.nchunk + (e % p.nchunk)];
     __syncthreads();
     for (int rr = tid; rr < nr; rr += kAccThreads) {
       const RowPart* pr = stage + rr * p.nchunk;
-      const int r = r0 + rr;
       float M = -INFINITY;
       int ai = INT_MAX;
       for (int c = 0; c < p.nchunk; ++c)
         if (better(pr[c].m, pr[c].idx, M, ai)) { M = pr[c].m; ai = pr[c].idx; }
-      double lse = 0.0;
-      if (STOCH) {
-        double Z = 0.0;
-        for (int c = 0; c < p.nchunk; ++c)
-          if (pr[c].m != -INFINITY) Z += exp((double)pr[c].m - (double)M) * pr[c].s;
-        lse = (double)M + log(Z);
-      }
-      if (r <= D) { lse_p[r] = lse; amax[r] = ai; }
-      else lse_q[r - D - 1] = lse;
+      amax[r0 + rr] = ai;
     }
   }
   if (tid == 0) first_fail = D;
@@ -257,195 +246,264 @@ __global__ __launch_bounds__(kAccThreads) void accept_decide(AccParams p) {
 
   for (int i = tid; i < D; i += kAccThreads) {
     const int x = p.tokens[d0 + i];
-    bool pass = false;
-    if (x >= 0 && x < p.V) {
-      if (!STOCH) {
-        pass = x == amax[i];
-      } else {
-        const double lp = (double)p.target[(size_t)(t0 + i) * p.V + x] - lse_p[i];
-        const double lq = (double)p.draft[(size_t)(d0 + i) * p.V + x] - lse_q[i];
-        const double r = exp(lp - lq);
-        pass = (double)p.uniforms[t0 + i] < r;
-      }
-    }
-    if (!pass) atomicMin(&first_fail, i);
+    if (!(x >= 0 && x < p.V && x == amax[i])) atomicMin(&first_fail, i);
   }
   __syncthreads();
   const int n = first_fail;
-  for (int k = tid; k <= D; k += kAccThreads) {
-    int tok = -1;
-    if (k < n) tok = p.tokens[d0 + k];
-    else if (k == n && !STOCH) tok = amax[n];
-    p.out_tokens[t0 + k] = tok;
-  }
-  if (tid == 0) {
-    p.accept_len[b] = n + 1;
-    if (STOCH) {
-      SeqState st;
-      st.n = n;
-      st.residual = n < D;
-      st.lse_p = lse_p[n];
-      st.lse_q = n < D ? lse_q[n] : 0.0;
-      st.arrived = 0u;
-      st.pad = 0;
-      p.state[b] = st;
-    }
-  }
+  for (int k = tid; k <= D; k += kAccThreads) p.out_tokens[t0 + k] = k < n ? p.tokens[d0 + k] : k == n ? amax[n] : -1;
+  if (tid == 0) p.accept_len[b] = n + 1;
 }
 
-// fp64 weights of token j for the sampling row of one sequence.
-__device__ __forceinline__ void sample_weights(const AccParams& p, const SeqState& st, int t0, int d0, int j,
-                                               double& w, double& pj) {
-  const double pt = exp((double)p.target[(size_t)(t0 + st.n) * p.V + j] - st.lse_p);
-  pj = pt;
-  if (st.residual) {
-    const double qt = exp((double)p.draft[(size_t)(d0 + st.n) * p.V + j] - st.lse_q);
-    w = fmax(0.0, pt - qt);
-  } else {
-    w = pt;
+// fp64 weights of one token of the sampling row from its target logit tl and
+// draft logit dl: pj = p(j); w = max(0, p(j) - q(j)) at a rejection, p(j) when
+// every draft passed.  A token past the vocabulary comes in as -inf (weight 0).
+__device__ __forceinline__ void sample_weight(float tl, float dl, const SeqState& st, double& w, double& pj) {
+  pj = exp((double)tl - st.lse_p);
+  w = st.residual ? fmax(0.0, pj - exp((double)dl - st.lse_q)) : pj;
+}
+
+// inclusive prefix sum over the 64 lanes of a wave
+__device__ __forceinline__ double wave_incl_scan(double v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double u = __shfl_up(v, off);
+    if (lane >= off) v += u;
   }
+  return v;
+}
+
+// log-normaliser log(sum_x exp(l_x)) of row `prow` from its chunk statistics,
+// merged by the 16 lanes of a group (lane k takes chunks k, k+16, ...): the row
+// max M over the chunk maxima, then log(sum_c exp(m_c - M) s_c) + M in fp64.
+// Every lane of the group must call it; each gets the result.
+__device__ __forceinline__ double row_lse16(const AccParams& p, int prow, int lane16) {
+  const RowPart* pr = p.part + (size_t)prow * p.nchunk;
+  RowPart a0, a1;
+  a0.m = a1.m = -INFINITY;
+  a0.s = a1.s = 0.0;
+  if (lane16 < p.nchunk) a0 = pr[lane16];
+  if (lane16 + 16 < p.nchunk) a1 = pr[lane16 + 16];
+  float M = fmaxf(a0.m, a1.m);
+  for (int k = lane16 + 32; k < p.nchunk; k += 16) M = fmaxf(M, pr[k].m);
+#pragma unroll
+  for (int off = 8; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  double Z = 0.0;
+  if (a0.m != -INFINITY) Z += exp((double)a0.m - (double)M) * a0.s;
+  if (a1.m != -INFINITY) Z += exp((double)a1.m - (double)M) * a1.s;
+  for (int k = lane16 + 32; k < p.nchunk; k += 16) {
+    const RowPart q = pr[k];
+    if (q.m != -INFINITY) Z += exp((double)q.m - (double)M) * q.s;
+  }
+#pragma unroll
+  for (int off = 8; off > 0; off >>= 1) Z += __shfl_xor(Z, off);
+  return (double)M + log(Z);
 }
 
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kAccThreads) void accept_sample(AccParams p) {
-  __shared__ double sd[4];
-  __shared__ double scan[kAccThreads];
-  __shared__ int s_last, s_chunk, s_usep, s_tok;
-  __shared__ double s_base, s_T;
+__global__ __launch_bounds__(kAccThreads) void accept_finish(AccParams p) {
+  __shared__ double sd[4], s_wtot[4];
+  __shared__ int s_fail, s_have, s_last, s_chunk, s_usep, s_slice, s_slice_last;
+  __shared__ double s_lp, s_lq, s_base, s_slice_base, s_T;
   const int c = blockIdx.x;
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
   const int t0 = p.q_start[b];
   const int D = seq_d(p, b);
   const int d0 = t0 - b;
-  if (!seq_ok(p, t0, D, d0)) return;
-  SeqState st = p.state[b];
+  if (!seq_ok(p, t0, D, d0)) {
+    if (c == 0 && tid == 0) p.accept_len[b] = 0;
+    return;
+  }
 
-  // (1) this chunk's fp64 sums of the residual (or p) and of p
-  double zw = 0.0, zp = 0.0;
-#pragma unroll 4
-  for (int k = 0; k < kSPerThread; ++k) {
-    const int j = c * kSChunk + k * kAccThreads + tid;
-    if (j < p.V) {
-      double w, pj;
-      sample_weights(p, st, t0, d0, j, w, pj);
-      zw += w;
-      zp += pj;
+  // (0) the decision.  Group g (16 lanes) takes draft position i = r0 + g of
+  // each pass: the log-normalisers of target row i and draft row i, then (lane
+  // 0) the test of draft i: it passes when u_i < p(x_i) / q(x_i), evaluated as
+  // exp((l_p - LSE_p) - (l_q - LSE_q)) in fp64.  Row D has no draft row.
+  const int lane16 = tid & 15, grp = tid >> 4;
+  if (tid == 0) { s_fail = D; s_have = 0; }
+  __syncthreads();
+  double my_lp = 0.0, my_lq = 0.0;
+  int my_i = -1;
+  for (int r0 = 0; r0 <= D; r0 += kAccThreads / 16) {
+    const int i = r0 + grp;
+    const bool live = i <= D;
+    const bool test = i < D && lane16 == 0;
+    int x = -1;
+    float ut = 0.f;
+    if (test) { x = p.tokens[d0 + i]; ut = p.uniforms[t0 + i]; }
+    const bool inv = x >= 0 && x < p.V;
+    float tl = 0.f, dl = 0.f;
+    if (test && inv) { tl = p.target[(size_t)(t0 + i) * p.V + x]; dl = p.draft[(size_t)(d0 + i) * p.V + x]; }
+    const double lp = row_lse16(p, t0 + (live ? i : 0), lane16);
+    // (draft rows d0 .. d0+D-1 exist only for D > 0, a condition uniform over the workgroup)
+    const double lq = D > 0 ? row_lse16(p, p.T + d0 + min(i, D - 1), lane16) : 0.0;
+    if (live) { my_lp = lp; my_lq = lq; my_i = i; }
+    if (test) {
+      const double r = exp(((double)tl - lp) - ((double)dl - lq));
+      if (!(inv && (double)ut < r)) atomicMin(&s_fail, i);
     }
   }
-  zw = block_sum(zw, sd);
-  zp = block_sum(zp, sd);
+  __syncthreads();
+  const int n = s_fail;
+  if (my_i == n && lane16 == 0) { s_lp = my_lp; s_lq = my_lq; s_have = 1; }
+  __syncthreads();
+  if (!s_have && grp == 0) {           // n fell in an earlier pass: merge its rows again
+    const double lp = row_lse16(p, t0 + n, lane16);
+    const double lq = n < D ? row_lse16(p, p.T + d0 + n, lane16) : 0.0;
+    if (lane16 == 0) { s_lp = lp; s_lq = lq; }
+  }
+  if (c == 0) {
+    for (int k = tid; k <= D; k += kAccThreads)
+      if (k != n) p.out_tokens[t0 + k] = k < n ? p.tokens[d0 + k] : -1;   // k == n: the sample, below
+    if (tid == 0) p.accept_len[b] = n + 1;
+  }
+  __syncthreads();
+  SeqState st;
+  st.n = n;
+  st.residual = n < D;
+  st.lse_p = s_lp;
+  st.lse_q = n < D ? s_lq : 0.0;
+
+  // (1) this chunk's fp64 sums.  Thread t takes the 16 consecutive logits
+  // j0 .. j0+15 (all loaded before any arithmetic): the weight of token j is
+  // max(0, p_j - q_j) at a rejection, p_j when every draft passed.  The thread
+  // publishes its own sums (residual, p) and the workgroup the chunk's.
+  const float* prow = p.target + (size_t)(t0 + n) * p.V;
+  const float* qrow = p.draft + (size_t)(d0 + (n < D ? n : 0)) * p.V;
+  const int j0 = c * kSChunk + tid * kSPerThread;
+  float tl[kSPerThread], dl[kSPerThread];
+  if (p.vec4 && j0 + kSPerThread <= p.V) {
+#pragma unroll
+    for (int k = 0; k < kSPerThread / 4; ++k) {
+      const f32x4 v = *(const f32x4*)(prow + j0 + 4 * k);
+      const f32x4 u = st.residual ? *(const f32x4*)(qrow + j0 + 4 * k) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { tl[4 * k + e] = v[e]; dl[4 * k + e] = u[e]; }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kSPerThread; ++e) {
+      const bool in = j0 + e < p.V;
+      tl[e] = in ? prow[j0 + e] : -INFINITY;
+      dl[e] = in && st.residual ? qrow[j0 + e] : -INFINITY;
+    }
+  }
+  double tw = 0.0, tp = 0.0;
+#pragma unroll
+  for (int e = 0; e < kSPerThread; ++e) {
+    double w, pj;
+    sample_weight(tl[e], dl[e], st, w, pj);
+    tw += w;
+    tp += pj;
+  }
+  // Hand-off between workgroups of one sequence, possibly on different XCDs
+  // (separate L2s): the sums are agent-scope atomic stores, which are coherent
+  // across XCDs, and each is complete (vmcnt 0) before the arrival count.  A
+  // release fence would do the same by writing back the whole L2.
+  {
+    double* dst = p.rsub + (((size_t)b * p.nschunk + c) * kAccThreads + tid) * 2;
+    __hip_atomic_store(dst, tw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(dst + 1, tp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  const double zw = block_sum(tw, sd);
+  const double zp = block_sum(tp, sd);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
   if (tid == 0) {
-    // Hand-off between workgroups of one sequence, possibly on different XCDs
-    // (separate L2s): the sums are agent-scope atomic stores, which are
-    // coherent across XCDs, and complete (vmcnt 0) before the arrival count.
-    // A release fence would do the same by writing back the whole L2.
     double* dst = p.rsum + ((size_t)b * p.nschunk + c) * 2;
     __hip_atomic_store(dst, zw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(dst + 1, zp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    const unsigned prev = __hip_atomic_fetch_add(&p.state[b].arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned prev = __hip_atomic_fetch_add(&p.arrived[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = prev == (unsigned)(p.nschunk - 1);
   }
   __syncthreads();
   if (!s_last) return;
 
-  // (2) last chunk to finish: find the chunk holding u*Z, then scan it.  The
-  // chunk sums are read once each, in parallel, and scanned in LDS.
-  double* rsb = p.rsum + (size_t)b * p.nschunk * 2;
-  auto rs_at = [&](int i) { return __hip_atomic_load(rsb + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
-  zw = 0.0;
-  zp = 0.0;
-  for (int k = tid; k < p.nschunk; k += kAccThreads) {
-    zw += rs_at(2 * k);
-    zp += rs_at(2 * k + 1);
-  }
-  zw = block_sum(zw, sd);
-  zp = block_sum(zp, sd);
-  const int usep = !(zw > 0.0);                   // the residual has no mass: sample p
-  const double T = (double)p.uniforms[t0 + D] * (usep ? zp : zw);
-  if (tid == 0) {
-    s_chunk = INT_MAX;
-    s_tok = -1;                                   // last chunk with weight (rounding fallback)
-  }
-  double carry = 0.0;
-  for (int base = 0; base < p.nschunk; base += kAccThreads) {
-    const int k = base + tid;
-    const double v = k < p.nschunk ? rs_at(2 * k + usep) : 0.0;
-    scan[tid] = v;
-    __syncthreads();
-    for (int off = 1; off < kAccThreads; off <<= 1) {
-      const double add = tid >= off ? scan[tid - off] : 0.0;
-      __syncthreads();
-      scan[tid] += add;
-      __syncthreads();
-    }
-    const double incl = carry + scan[tid];
-    if (k < p.nschunk && incl > T) atomicMin(&s_chunk, k);
-    if (v > 0.0) atomicMax(&s_tok, k);
-    __syncthreads();
-    if (k == s_chunk) s_base = incl - v;
-    carry += scan[kAccThreads - 1];
-    __syncthreads();
-    if (s_chunk != INT_MAX) break;
-  }
-  if (tid == 0) {
-    if (s_chunk == INT_MAX) {                     // prefix never passed u*Z
-      s_chunk = max(s_tok, 0);
-      s_base = -INFINITY;                         // never satisfied below -> last positive weight
-    }
-    s_T = T;
-    s_usep = usep;
-    s_tok = INT_MAX;
-  }
-  __syncthreads();
-  if (s_usep) st.residual = 0;
-  const int j0 = s_chunk * kSChunk + tid * kSPerThread;
-  double w[kSPerThread];
-  double tsum = 0.0;
+  // (2) the last workgroup of the sequence draws the token: the first token
+  // whose inclusive prefix sum of weights exceeds T = u * Z, found in three
+  // levels (chunk, 16-token slice, token).  Where rounding leaves T past every
+  // prefix of a level, the level takes its last element with weight > 0.
+  const int lane = tid & 63, wave = tid >> 6;
+  auto ld = [](const double* a) { return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+  if (wave == 0) {
+    // level 1 (one wave): totals, T, and the chunk
+    const double* rs = p.rsum + (size_t)b * p.nschunk * 2;
+    double vw0 = 0.0, vp0 = 0.0;
+    if (lane < p.nschunk) { vw0 = ld(rs + 2 * lane); vp0 = ld(rs + 2 * lane + 1); }
+    double sw = vw0, sp = vp0;
+    for (int k = lane + 64; k < p.nschunk; k += 64) { sw += ld(rs + 2 * k); sp += ld(rs + 2 * k + 1); }
 #pragma unroll
-  for (int e = 0; e < kSPerThread; ++e) {
-    const int j = j0 + e;
-    double pj;
-    w[e] = 0.0;
-    if (j < p.V) sample_weights(p, st, t0, d0, j, w[e], pj);
-    tsum += w[e];
-  }
-  // inclusive scan of the per-thread sums (ascending token order)
-  scan[tid] = tsum;
-  __syncthreads();
-  for (int off = 1; off < kAccThreads; off <<= 1) {
-    const double add = tid >= off ? scan[tid - off] : 0.0;
-    __syncthreads();
-    scan[tid] += add;
-    __syncthreads();
-  }
-  double C = s_base + (scan[tid] - tsum);
-  int cand = INT_MAX;
-  int last_pos = -1;
-#pragma unroll
-  for (int e = 0; e < kSPerThread; ++e) {
-    C += w[e];
-    if (cand == INT_MAX && C > s_T) cand = j0 + e;
-    if (w[e] > 0.0) last_pos = j0 + e;
-  }
-  if (cand != INT_MAX) atomicMin(&s_tok, cand);
-  __syncthreads();
-  if (s_tok == INT_MAX) {             // rounding left u*Z past this chunk's scan
-    scan[tid] = (double)last_pos;
-    __syncthreads();
-    if (tid == 0) {
-      int best = -1;
-      for (int k = 0; k < kAccThreads; ++k) best = max(best, (int)scan[k]);
-      s_tok = best < 0 ? s_chunk * kSChunk : best;
+    for (int off = 32; off > 0; off >>= 1) { sw += __shfl_xor(sw, off); sp += __shfl_xor(sp, off); }
+    const int usep = !(sw > 0.0);                 // the residual has no mass: sample p
+    const double T = (double)p.uniforms[t0 + D] * (usep ? sp : sw);
+    double carry = 0.0, base = -INFINITY;
+    int chunk = -1, lastpos = -1;
+    for (int kb = 0; kb < p.nschunk; kb += 64) {
+      const int k = kb + lane;
+      const double v = kb == 0 ? (usep ? vp0 : vw0) : (k < p.nschunk ? ld(rs + 2 * k + usep) : 0.0);
+      const double incl = wave_incl_scan(v);
+      double excl = __shfl_up(incl, 1);
+      if (lane == 0) excl = 0.0;
+      const unsigned long long hit = __ballot(k < p.nschunk && carry + incl > T);
+      const unsigned long long pos = __ballot(v > 0.0);
+      if (pos) lastpos = kb + 63 - __clzll(pos);
+      if (hit) {
+        const int l = __ffsll(hit) - 1;
+        chunk = kb + l;
+        base = carry + __shfl(excl, l);
+        break;
+      }
+      carry += __shfl(incl, 63);
     }
-    __syncthreads();
+    if (chunk < 0) chunk = max(lastpos, 0);       // base stays -inf: every later level falls back
+    if (lane == 0) { s_chunk = chunk; s_base = base; s_T = T; s_usep = usep; s_slice = INT_MAX; s_slice_last = -1; }
   }
-  if (tid == 0) p.out_tokens[t0 + st.n] = s_tok;
+  __syncthreads();
+  // level 2 (four waves): the 16-token slice inside the chunk, from the published thread sums
+  const int chunk = s_chunk;
+  const double T = s_T;
+  {
+    const double v = ld(p.rsub + (((size_t)b * p.nschunk + chunk) * kAccThreads + tid) * 2 + s_usep);
+    const double incl = wave_incl_scan(v);
+    if (lane == 63) s_wtot[wave] = incl;
+    __syncthreads();
+    double carry = s_base;
+    for (int w = 0; w < wave; ++w) carry += s_wtot[w];
+    if (carry + incl > T) atomicMin(&s_slice, tid);
+    if (v > 0.0) atomicMax(&s_slice_last, tid);
+    __syncthreads();
+    if (tid == s_slice) s_slice_base = carry + (incl - v);
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // level 3 (one wave): the token inside the slice, by a sequential prefix sum
+    const int slice = s_slice != INT_MAX ? s_slice : max(s_slice_last, 0);
+    const double base = s_slice != INT_MAX ? s_slice_base : -INFINITY;
+    if (s_usep) st.residual = 0;
+    const int js = chunk * kSChunk + slice * kSPerThread;
+    double w = 0.0;
+    if (lane < kSPerThread && js + lane < p.V) {
+      double pj;
+      sample_weight(prow[js + lane], st.residual ? qrow[js + lane] : -INFINITY, st, w, pj);
+    }
+    double C = base;
+    int tok = -1, last = -1;
+#pragma unroll
+    for (int e = 0; e < kSPerThread; ++e) {
+      const double we = __shfl(w, e);
+      C += we;
+      if (tok < 0 && C > T) tok = js + e;
+      if (we > 0.0) last = js + e;
+    }
+    if (tok < 0) tok = last >= 0 ? last : js;
+    if (lane == 0) p.out_tokens[t0 + n] = tok;
+  }
 }
 
 struct AccLayout {
-  size_t part_off, state_off, rsum_off, total;
+  size_t part_off, arrived_off, rsum_off, rsub_off, total;
   int nchunk, nschunk;
 };
 
@@ -457,8 +515,9 @@ static AccLayout acc_layout(int B, int T, int V, int stochastic) {
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += (bytes + 255) / 256 * 256; return o; };
   L.part_off = take(rows * L.nchunk * sizeof(RowPart));
-  L.state_off = take((size_t)B * sizeof(SeqState));
+  L.arrived_off = take((size_t)B * sizeof(unsigned));
   L.rsum_off = take((size_t)B * L.nschunk * 2 * sizeof(double));
+  L.rsub_off = take(stochastic ? (size_t)B * L.nschunk * kAccThreads * 2 * sizeof(double) : 0);
   L.total = off;
   return L;
 }
@@ -483,8 +542,9 @@ hipError_t sdv_accept_launch(const SdAccLaunch& a) {
   p.accept_len = a.accept_len;
   p.out_tokens = a.out_tokens;
   p.part = (RowPart*)(ws + L.part_off);
-  p.state = (SeqState*)(ws + L.state_off);
+  p.arrived = (unsigned*)(ws + L.arrived_off);
   p.rsum = (double*)(ws + L.rsum_off);
+  p.rsub = (double*)(ws + L.rsub_off);
   p.B = a.B;
   p.T = a.T;
   p.V = a.V;
@@ -494,18 +554,17 @@ hipError_t sdv_accept_launch(const SdAccLaunch& a) {
 
   const bool vec4 = (a.V % 4 == 0) && ((uintptr_t)a.target % 16 == 0) &&
                     (!a.stochastic || (uintptr_t)a.draft % 16 == 0);
+  p.vec4 = vec4;
   const size_t rows = a.stochastic ? (size_t)a.T + (size_t)(a.T - a.B) : (size_t)a.T;
   const unsigned grid1 = (unsigned)(rows * L.nchunk);
-  const size_t dyn = (size_t)(2 * a.max_draft + 1) * sizeof(double) + (size_t)(a.max_draft + 1) * sizeof(int);
   if (a.stochastic) {
     if (vec4) accept_rowstats<1, 1><<<grid1, kAccThreads, 0, a.stream>>>(p);
     else accept_rowstats<1, 0><<<grid1, kAccThreads, 0, a.stream>>>(p);
-    accept_decide<1><<<a.B, kAccThreads, dyn, a.stream>>>(p);
-    accept_sample<<<dim3(L.nschunk, a.B), kAccThreads, 0, a.stream>>>(p);
+    accept_finish<<<dim3(L.nschunk, a.B), kAccThreads, 0, a.stream>>>(p);
   } else {
     if (vec4) accept_rowstats<0, 1><<<grid1, kAccThreads, 0, a.stream>>>(p);
     else accept_rowstats<0, 0><<<grid1, kAccThreads, 0, a.stream>>>(p);
-    accept_decide<0><<<a.B, kAccThreads, dyn, a.stream>>>(p);
+    accept_decide<<<a.B, kAccThreads, (size_t)(a.max_draft + 1) * sizeof(int), a.stream>>>(p);
   }
   return hipGetLastError();
 }
