@@ -839,9 +839,6 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
   DmaSlot dma[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) dma[i] = dma_slot<HD, RG>(wave + NW * i, lane, [](int k) { return wide_swz<HD>(k & 15); });
-  bf16x8 ones;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
 
   constexpr int kRowsWG = 4 * 32;
   const int nvirt = p.nhalf == 1 ? total : (total + 7) / 8 * 16;
@@ -901,13 +898,13 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
     }
     float m_run = -INFINITY;
     float m_off = 0.f;
-    f32x16 l_acc;                  // row sums (every entry of a lane holds its query row's sum)
+    float l_run;                   // this lane's share of its row sum (its 16 of each tile's 32 keys);
+                                   // the row's sum adds the partner lane l ^ 32
     f32x16 o[NMB];
     auto clear = [&]() {
       m_run = -INFINITY;
       m_off = 0.f;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) l_acc[e] = 0.f;
+      l_run = 0.f;
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
@@ -953,7 +950,8 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
       }
       sc = s0 + s1;
     };
-    // P from the scores, then O^T += V^T P^T and l += 1^T P^T at stage offset `off`
+    // P from the scores, then O^T += V^T P^T at stage offset `off`, and the
+    // lane's share of l from the same bf16 P (dot products with (1, 1))
     auto accumulate = [&](int off) {
       bf16x8 pf[2];
 #pragma unroll
@@ -961,21 +959,29 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) pf[ks][e] = (__bf16)fast_exp2(fmaf(sc[ks * 8 + e], p.scale_log2, m_off));
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) {
           const bf16x8 vf = *(const bf16x8*)(smem + off + ks * HD * 32 + voffs[mb]);
           o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[mb], 0, 0, 0);
         }
-        l_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pf[ks], l_acc, 0, 0, 0);
-      }
+      const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[ks][2 * q], pf[ks][2 * q + 1]}, one2, l_run, false);
+    };
+    auto row_sum = [&]() {
+      auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+      return __uint_as_float(a[0]) + __uint_as_float(a[1]);
     };
     auto rescale = [&]() {
       if (mt > m_run + kLazy) {
         const float alpha = fast_exp2(m_run - mt);
         m_run = mt;
         m_off = -mt;
-        l_acc *= alpha;
+        l_run *= alpha;
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) o[mb] *= alpha;
       }
@@ -1044,7 +1050,7 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
     if (wave_active) fast_steady(std::true_type{});
     else fast_steady(std::false_type{});
     for (int k = 1 + ngroups * (S / 2); k < nsteps; ++k) step_generic(k, std::false_type{});
-    const bool over = wave_active && !(l_acc[0] <= kOverflow);
+    const bool over = wave_active && !(row_sum() <= kOverflow);
 
     // ---- Safe pass (only if some row's max outgrew its reference): the same
     // steps again with a running max.
@@ -1064,7 +1070,7 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
       for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) xch[(mb * 16 + e) * 64] = o[mb][e];
-      xch[(16 * NMB) * 64] = l_acc[0];
+      xch[(16 * NMB) * 64] = row_sum();
       xch[(16 * NMB + 1) * 64] = m_run;
     }
     block_sync();
@@ -1078,7 +1084,7 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
       for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[mb][e] = o[mb][e] * wa + xch[(mb * 16 + e) * 64] * wb;
-      const float lt = l_acc[0] * wa + lb * wb;
+      const float lt = row_sum() * wa + lb * wb;
       // O^T accumulator: lane holds query row r32 and dims mb*32 + q*8 + 4hh + 0..3 in entries 4q..4q+3.
       if (nsplit == 1) {
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
