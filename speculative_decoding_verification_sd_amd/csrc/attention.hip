@@ -11,25 +11,26 @@
 //
 // Work decomposition (split-KV).  A sequence's keys are cut into chunks of
 // `chunk` keys; a work item is (sequence, KV head, chunk).  A one-workgroup
-// plan kernel picks the smallest chunk (a multiple of 64 keys) whose item
-// count fits the resident workgroups of the grid, so that every item runs
-// concurrently, and writes one descriptor per item.  A persistent grid walks
-// the items.
+// plan kernel picks the chunk (a multiple of 64 keys) from a bound on the
+// schedule's length, lists the items longest first and writes one descriptor
+// per item; a persistent grid walks the list.
 //
-// Per item, a workgroup of NW waves runs over 32-key tiles (two 16-key pages):
+// Per item, a workgroup runs over 32-key tiles (two 16-key pages):
 //   * K and V tiles travel global -> LDS with global_load_lds_dwordx4 (no
-//     registers) into a ring of kStages tiles, paced by explicit vmcnt waits
-//     and a bare s_barrier, so kStages-1 tiles are in flight per workgroup.
+//     registers) into a ring of tiles, paced by explicit vmcnt waits and a bare
+//     s_barrier.  K pages are key-major and V pages d-major ([d][16 keys]);
 //     LDS rows are XOR-swizzled in 16-byte chunks against bank conflicts.
-//   * Each wave owns NRB blocks of 16 query rows.  S^T = K * Q^T is computed
-//     with v_mfma_f32_16x16x32_bf16 (Q stays in registers), so each lane holds
-//     one query row: the online softmax reduces across four lanes with
-//     v_permlane32_swap / v_permlane16_swap, and the running max is raised
-//     lazily (only when it grows by more than 2^8), which leaves the output
-//     rescale out of almost every tile.
-//   * P (bf16) is taken straight from the S^T accumulators as the B operand
-//     of O^T = V^T * P^T; V is read transposed with ds_read_b64_tr_b16 in the
-//     same key order.
+//   * S^T = K * Q^T with Q held in registers, so each lane holds one query row
+//     and the row reductions stay within a lane pair (v_permlane32_swap).
+//     verify_attn_wide (more than 64 rows) uses v_mfma_f32_32x32x16_bf16 with
+//     8 waves in two sets that take alternate tiles; verify_attn_main (up to
+//     64 rows) uses v_mfma_f32_16x16x32_bf16.
+//   * Softmax: each row's reference max is fixed by the item's first tile, so
+//     later tiles need neither a row max nor a rescale; an item whose row sum
+//     ends above 2^64 (a score far above its reference) is computed again with
+//     a running max.
+//   * P (bf16) is taken straight from the S^T accumulators as the B operand of
+//     O^T = V^T * P^T, and V^T comes from the d-major pages with ds_read_b128.
 // Items that cover a whole sequence write the output; otherwise the
 // unnormalised partial (O, m, l) goes to the workspace and a combine kernel
 // merges the splits with their log-sum-exp weights.
@@ -47,7 +48,9 @@ constexpr int kPage = 16;
 constexpr int kMinChunk = 256;
 constexpr int kMaxChunk = 16384;         // keys per work item; bounds the per-item page list in LDS
 constexpr int kPlanThreads = 256;
-constexpr int kPlanHeader = 4;
+constexpr int kItemsPerSlot = 4;         // work items per resident workgroup the workspace admits
+constexpr int kItemOverheadBytes = 192 * 1024;   // an item's fixed cost (set-up, partials) in bytes of K/V
+constexpr int kPlanHeader = 16;
 
 // LDS bytes of the K/V rings of one CU (at most 8 tiles per workgroup),
 // shared by its resident workgroups.  Build-time tunable.
@@ -70,7 +73,7 @@ struct AttnParams {
   void* out;
   float* part_o;    // [item_cap, rpad, d]   unnormalised partial outputs
   float* part_ml;   // [item_cap, rpad, 2]   (running max in log2 units, sum)
-  int* plan;        // [4 + B + 1]: chunk, total items, -, -, item_start[0..B]
+  int* plan;        // [16 + 2B + 1]: chunk, total items, full items, work counters, item_start, tail_pos
   ItemDesc* items;  // [item_cap]
   int B, Hkv, G, max_pages, num_pages, max_draft, rpad, total_q, item_cap;
   int nhalf;        // workgroups per item: 2 when a sequence can have more query rows than one holds
@@ -86,60 +89,165 @@ __device__ __forceinline__ int seq_drafts(const AttnParams& p, int b) {
 }
 
 // ---------------------------------------------------------------------------
-// Plan (one workgroup).  Chunk: `fixed_chunk` if non-zero, else the smallest
-// multiple of 64 in [kMinChunk, kMaxChunk] whose item count
-// Hkv * sum_b max(1, ceil(N_b / chunk)) fits `slots` (thread t evaluates
-// chunk kMinChunk + 64 t).  Then the exclusive prefix of items per sequence
-// and one descriptor per item.
-__global__ __launch_bounds__(kPlanThreads) void verify_attn_plan(AttnParams p, int fixed_chunk, int slots) {
+// Plan (one workgroup).
+//
+// Chunk: `fixed_chunk` if non-zero.  Otherwise thread t evaluates chunk
+// kMinChunk + 64 t (at most the longest sequence, rounded up to 64, and at
+// most kMaxChunk): with items(c) = Hkv * sum_b max(1, ceil(N_b / c)), the
+// schedule of the persistent grid takes at least the average load per slot,
+// (Hkv * sum_b N_b + ovh * items(c)) / slots keys (ovh: fixed cost of an item
+// in keys), and at least the longest item, min(c, max_b N_b).  The plan takes
+// the chunk with the smallest of these bounds (the largest chunk on ties)
+// among those whose items fit the workspace (the smaller chunk on ties).
+//
+// Order: items go to the workgroups in a longest-first order, which keeps the
+// tail of the schedule short when sequence lengths differ: when some items are
+// shorter than the chunk and there are more items than workgroups, the grid
+// takes the items after its first round from eight counters (workgroup w uses
+// counter w % 8 and the items i with i % 8 == w % 8) as workgroups finish.  Every full-chunk item comes
+// first; then the one shorter item of each (sequence, head), by its length in
+// kLenBuckets buckets, longest bucket first.  Split-KV partials stay addressed
+// by the natural index item_start[b] + h * nsplit_b + split.
+//
+// plan[]: [0] chunk, [1] items, [2] full-chunk items, [8..15] work counters
+// (cleared here), then item_start[0..B] and tail_pos[0..B-1] (scheduled index
+// of head 0's shorter item of sequence b; kept in LDS for the first
+// kPlanCacheSeqs sequences) from kPlanHeader on.
+constexpr int kLenBuckets = 64;
+constexpr int kPlanCacheSeqs = 2048;     // sequences whose key count and tail index the plan keeps in LDS
+
+__global__ __launch_bounds__(kPlanThreads) void verify_attn_plan(AttnParams p, int fixed_chunk, int slots,
+                                                                 int ovh_keys) {
   __shared__ int s_keys[kPlanThreads];
   __shared__ int scan[kPlanThreads];
-  __shared__ int s_best;
+  __shared__ int fscan[kPlanThreads];
+  __shared__ int s_bucket[kLenBuckets];
+  __shared__ unsigned long long s_best;
+  __shared__ long long s_ksum, s_full;
+  __shared__ int s_nmax;
+  __shared__ int s_n[kPlanCacheSeqs];      // N_b
+  __shared__ int s_tail[kPlanCacheSeqs];   // tail_pos[b]
   const int tid = threadIdx.x;
   const int max_keys = p.max_pages * kPage;
   const int cap_chunk = max(kMinChunk, min(kMaxChunk, (max_keys + 63) / 64 * 64));
   const int my_chunk = min(kMinChunk + 64 * tid, cap_chunk);
-  long long my_items = 0;
+  int* tail_pos = p.plan + kPlanHeader + p.B + 1;
+  auto keys_of = [&](int b) { return b < kPlanCacheSeqs ? s_n[b] : seq_keys(p, b); };
+
+  // (1) the chunk
+  if (tid == 0) { s_best = ~0ull; s_ksum = 0; s_full = 0; s_nmax = 0; }
+  if (tid < kLenBuckets) s_bucket[tid] = 0;
+  long long my_items = 0, ksum = 0;
+  int nmax = 0;
   for (int base = 0; base < p.B; base += kPlanThreads) {
     __syncthreads();
-    s_keys[tid] = base + tid < p.B ? seq_keys(p, base + tid) : 0;
+    const int nb = base + tid < p.B ? seq_keys(p, base + tid) : 0;
+    s_keys[tid] = nb;
+    if (base + tid < kPlanCacheSeqs) s_n[base + tid] = nb;
+    ksum += nb;
+    nmax = max(nmax, nb);
     __syncthreads();
     const int n = min(kPlanThreads, p.B - base);
     for (int j = 0; j < n; ++j) my_items += max(1, (s_keys[j] + my_chunk - 1) / my_chunk);
   }
-  if (tid == 0) s_best = cap_chunk;
+  // (block reductions: a wave reduction, then one LDS atomic per wave)
+  const int lane = tid & 63;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    ksum += __shfl_xor(ksum, off);
+    nmax = max(nmax, __shfl_xor(nmax, off));
+  }
   __syncthreads();
-  if (my_items * p.Hkv <= slots) atomicMin(&s_best, my_chunk);
+  if (lane == 0) {
+    atomicAdd((unsigned long long*)&s_ksum, (unsigned long long)ksum);
+    atomicMax(&s_nmax, nmax);
+  }
   __syncthreads();
-  const int chunk = fixed_chunk > 0 ? fixed_chunk : s_best;
+  const long long items_c = my_items * p.Hkv;
+  unsigned long long key = ~0ull;
+  if (items_c <= p.item_cap) {
+    const long long load = (s_ksum * p.Hkv + (long long)ovh_keys * items_c + slots - 1) / slots;
+    const long long est = max(load, (long long)min(my_chunk, s_nmax));
+    key = ((unsigned long long)est << 9) | (unsigned long long)tid;   // ties: the smaller chunk
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) key = min(key, (unsigned long long)__shfl_xor(key, off));
+  if (lane == 0) atomicMin(&s_best, key);
+  __syncthreads();
+  int chunk = cap_chunk;
+  if (fixed_chunk > 0) chunk = fixed_chunk;
+  else if (s_best != ~0ull) chunk = min(kMinChunk + 64 * (int)(s_best & 511), cap_chunk);
 
-  // descriptors: sequences in groups of kPlanThreads; the group's items are
-  // written by all threads, each finding its sequence by binary search over
-  // the inclusive scan of items per sequence
-  int carry = 0;
+  // (2) the shorter items: count per length bucket (bucket 0 = longest), and
+  // the number of full-chunk items
+  auto split_of = [&](int N, int& full, int& tail_len) {   // full chunks, and the shorter item's length (-1: none)
+    full = N / chunk;
+    tail_len = (N % chunk != 0 || N == 0) ? N - full * chunk : -1;
+  };
+  auto bucket_of = [&](int len) {
+    return kLenBuckets - 1 - (int)(((long long)len * kLenBuckets) / ((long long)chunk + 1));
+  };
+  long long nfull = 0;
+  for (int b = tid; b < p.B; b += kPlanThreads) {
+    int full, tl;
+    split_of(keys_of(b), full, tl);
+    nfull += (long long)full * p.Hkv;
+    if (tl >= 0) atomicAdd(&s_bucket[bucket_of(tl)], 1);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) nfull += __shfl_xor(nfull, off);
+  if (lane == 0) atomicAdd((unsigned long long*)&s_full, (unsigned long long)nfull);
+  __syncthreads();
+  static_assert(kLenBuckets == 64, "one lane of wave 0 per bucket");
+  if (tid < 64) {                                  // bucket counts -> exclusive prefix (running cursors)
+    const int c = s_bucket[tid];
+    int incl = c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(incl, off);
+      if (tid >= off) incl += t;
+    }
+    s_bucket[tid] = incl - c;
+  }
+  __syncthreads();
+  for (int b = tid; b < p.B; b += kPlanThreads) {
+    int full, tl;
+    split_of(keys_of(b), full, tl);
+    const int tp = tl >= 0 ? (int)(s_full + (long long)atomicAdd(&s_bucket[bucket_of(tl)], 1) * p.Hkv) : -1;
+    if (b < kPlanCacheSeqs) s_tail[b] = tp;
+    else tail_pos[b] = tp;
+  }
+  __syncthreads();
+
+  // (3) descriptors: sequences in groups of kPlanThreads.  Natural index e of
+  // the group's items -> (sequence by binary search over the inclusive scan of
+  // items per sequence, head, split) -> scheduled index.
+  int carry = 0, fcarry = 0;
   for (int base = 0; base < p.B; base += kPlanThreads) {
     const int b = base + tid;
-    int v = 0, N = 0, ns = 1;
+    int v = 0, N = 0, ns = 1, full = 0, tl = -1;
     if (b < p.B) {
-      N = seq_keys(p, b);
+      N = keys_of(b);
       ns = max(1, (N + chunk - 1) / chunk);
       v = ns * p.Hkv;
+      split_of(N, full, tl);
     }
     scan[tid] = v;
+    fscan[tid] = b < p.B ? full * p.Hkv : 0;
     s_keys[tid] = N;
     __syncthreads();
     for (int off = 1; off < kPlanThreads; off <<= 1) {
       const int add = tid >= off ? scan[tid - off] : 0;
+      const int fadd = tid >= off ? fscan[tid - off] : 0;
       __syncthreads();
       scan[tid] += add;
+      fscan[tid] += fadd;
       __syncthreads();
     }
     if (b < p.B) p.plan[kPlanHeader + b] = carry + scan[tid] - v;
     const int n = min(kPlanThreads, p.B - base);
     const int group_items = scan[n - 1];
     for (int e = tid; e < group_items; e += kPlanThreads) {
-      const int it = carry + e;
-      if (it >= p.item_cap) break;
       int lo = 0, hi = n - 1;                 // first j with scan[j] > e
       while (lo < hi) {
         const int mid = (lo + hi) >> 1;
@@ -149,25 +257,32 @@ __global__ __launch_bounds__(kPlanThreads) void verify_attn_plan(AttnParams p, i
       const int bj = base + lo;
       const int Nj = s_keys[lo];
       const int nsj = max(1, (Nj + chunk - 1) / chunk);
+      const int fj = Nj / chunk;
       const int r = e - (lo > 0 ? scan[lo - 1] : 0);
-      const int s = r % nsj;
+      const int hj = r / nsj, sj = r % nsj;
+      const int pos = sj < fj ? fcarry + (lo > 0 ? fscan[lo - 1] : 0) + hj * fj + sj
+                              : (bj < kPlanCacheSeqs ? s_tail[bj] : tail_pos[bj]) + hj;
+      if (pos < 0 || pos >= p.item_cap) continue;
       ItemDesc d;
       d.b = bj;
-      d.h = r / nsj;
-      d.k_begin = s * chunk;
-      d.k_end = min(Nj, (s + 1) * chunk);
+      d.h = hj;
+      d.k_begin = sj * chunk;
+      d.k_end = min(Nj, (sj + 1) * chunk);
       d.t0 = p.q_start[bj];
       d.D = seq_drafts(p, bj);
       d.N = Nj;
       d.nsplit = nsj;
-      p.items[it] = d;
+      p.items[pos] = d;
     }
     carry += scan[kPlanThreads - 1];
+    fcarry += fscan[kPlanThreads - 1];
     __syncthreads();
   }
+  if (tid < 8) p.plan[8 + tid] = 0;
   if (tid == 0) {
     p.plan[0] = chunk;
     p.plan[1] = carry;
+    p.plan[2] = (int)s_full;
     p.plan[kPlanHeader + p.B] = carry;
   }
 }
@@ -393,7 +508,24 @@ __global__ __launch_bounds__(64 * NW, WPC) void verify_attn_main(AttnParams p) {
   // one XCD and the second reads the item's pages from that XCD's L2.
   constexpr int kRowsWG = NRB * NW * 16;
   const int nvirt = p.nhalf == 1 ? total : (total + 7) / 8 * 16;
-  for (int vi = blockIdx.x; vi < nvirt; vi += gridDim.x) {
+  // Items after the first round.  When the plan's list (longest first) holds
+  // items shorter than the chunk and more items than workgroups, the next item
+  // of this workgroup's class (index = blockIdx % 8 modulo 8) as workgroups
+  // finish, from the class's counter; otherwise (and with row halves, whose
+  // stride keeps both halves of an item on one XCD) a fixed stride.
+  __shared__ int s_next;
+  const int chunk = p.plan[0];
+  const bool dyn = p.nhalf == 1 && gridDim.x >= 8 && total > (int)gridDim.x && p.plan[2] < total;
+  const int cls = blockIdx.x & 7;
+  const int first_dyn = (int)gridDim.x + ((cls - (int)(gridDim.x & 7)) & 7);
+  auto next_item = [&](int vi) {
+    if (!dyn) return vi + (int)gridDim.x;
+    block_sync();
+    if (threadIdx.x == 0) s_next = first_dyn + 8 * atomicAdd(p.plan + 8 + cls, 1);
+    block_sync();
+    return s_next;
+  };
+  for (int vi = blockIdx.x; vi < nvirt; vi = next_item(vi)) {
     const int item = p.nhalf == 1 ? vi : (vi >> 4) * 8 + (vi & 7);
     const int row0 = p.nhalf == 1 ? 0 : ((vi >> 3) & 1) * kRowsWG;
     if (item >= total) continue;
@@ -404,6 +536,12 @@ __global__ __launch_bounds__(64 * NW, WPC) void verify_attn_main(AttnParams p) {
     const int k_begin = __builtin_amdgcn_readfirstlane(d.k_begin), k_end = __builtin_amdgcn_readfirstlane(d.k_end);
     const int t0 = __builtin_amdgcn_readfirstlane(d.t0), D = __builtin_amdgcn_readfirstlane(d.D);
     const int N = __builtin_amdgcn_readfirstlane(d.N), nsplit = __builtin_amdgcn_readfirstlane(d.nsplit);
+    // (a descriptor outside the inputs is skipped rather than followed)
+    if (b < 0 || b >= p.B || h < 0 || h >= p.Hkv || k_begin < 0 || k_end < k_begin ||
+        k_end > p.max_pages * kPage || nsplit < 1 || chunk < 64)
+      continue;
+    const int pslot = p.plan[kPlanHeader + b] + h * nsplit + k_begin / chunk;   // natural index: partials
+    if (pslot < 0 || pslot >= p.item_cap) continue;
     const int R = p.G * (1 + D);
     if (row0 >= R) continue;     // the sequence's rows fit in the first half
     const int* bt = p.block_table + (size_t)b * p.max_pages;
@@ -751,11 +889,11 @@ __global__ __launch_bounds__(64 * NW, WPC) void verify_attn_main(AttnParams p) {
             }
           }
         } else {
-          float* slab = p.part_o + ((size_t)item * p.rpad + row) * HD + g4 * 4;
+          float* slab = p.part_o + ((size_t)pslot * p.rpad + row) * HD + g4 * 4;
 #pragma unroll
           for (int db = 0; db < NDB; ++db) *(f32x4*)(slab + db * 16) = o[rb][db];
           if (g4 == 0) {
-            float* ml = p.part_ml + ((size_t)item * p.rpad + row) * 2;
+            float* ml = p.part_ml + ((size_t)pslot * p.rpad + row) * 2;
             ml[0] = m_run[rb];
             ml[1] = lt;
           }
@@ -842,7 +980,24 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
 
   constexpr int kRowsWG = 4 * 32;
   const int nvirt = p.nhalf == 1 ? total : (total + 7) / 8 * 16;
-  for (int vi = blockIdx.x; vi < nvirt; vi += gridDim.x) {
+  // Items after the first round.  When the plan's list (longest first) holds
+  // items shorter than the chunk and more items than workgroups, the next item
+  // of this workgroup's class (index = blockIdx % 8 modulo 8) as workgroups
+  // finish, from the class's counter; otherwise (and with row halves, whose
+  // stride keeps both halves of an item on one XCD) a fixed stride.
+  __shared__ int s_next;
+  const int chunk = p.plan[0];
+  const bool dyn = p.nhalf == 1 && gridDim.x >= 8 && total > (int)gridDim.x && p.plan[2] < total;
+  const int cls = blockIdx.x & 7;
+  const int first_dyn = (int)gridDim.x + ((cls - (int)(gridDim.x & 7)) & 7);
+  auto next_item = [&](int vi) {
+    if (!dyn) return vi + (int)gridDim.x;
+    block_sync();
+    if (threadIdx.x == 0) s_next = first_dyn + 8 * atomicAdd(p.plan + 8 + cls, 1);
+    block_sync();
+    return s_next;
+  };
+  for (int vi = blockIdx.x; vi < nvirt; vi = next_item(vi)) {
     const int item = p.nhalf == 1 ? vi : (vi >> 4) * 8 + (vi & 7);
     const int row0 = p.nhalf == 1 ? 0 : ((vi >> 3) & 1) * kRowsWG;
     if (item >= total) continue;
@@ -851,6 +1006,12 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
     const int k_begin = __builtin_amdgcn_readfirstlane(d.k_begin), k_end = __builtin_amdgcn_readfirstlane(d.k_end);
     const int t0 = __builtin_amdgcn_readfirstlane(d.t0), D = __builtin_amdgcn_readfirstlane(d.D);
     const int N = __builtin_amdgcn_readfirstlane(d.N), nsplit = __builtin_amdgcn_readfirstlane(d.nsplit);
+    // (a descriptor outside the inputs is skipped rather than followed)
+    if (b < 0 || b >= p.B || h < 0 || h >= p.Hkv || k_begin < 0 || k_end < k_begin ||
+        k_end > p.max_pages * kPage || nsplit < 1 || chunk < 64)
+      continue;
+    const int pslot = p.plan[kPlanHeader + b] + h * nsplit + k_begin / chunk;   // natural index: partials
+    if (pslot < 0 || pslot >= p.item_cap) continue;
     const int R = p.G * (1 + D);
     if (row0 >= R) continue;
     const int* bt = p.block_table + (size_t)b * p.max_pages;
@@ -1103,14 +1264,14 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
             }
           }
       } else {
-        float* slab = p.part_o + ((size_t)item * p.rpad + row) * HD + hh * 4;
+        float* slab = p.part_o + ((size_t)pslot * p.rpad + row) * HD + hh * 4;
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
           for (int q = 0; q < 4; ++q)
             *(f32x4*)(slab + mb * 32 + q * 8) = f32x4{o[mb][4 * q], o[mb][4 * q + 1], o[mb][4 * q + 2], o[mb][4 * q + 3]};
         if (hh == 0) {
-          float* ml = p.part_ml + ((size_t)item * p.rpad + row) * 2;
+          float* ml = p.part_ml + ((size_t)pslot * p.rpad + row) * 2;
           ml[0] = M;
           ml[1] = lt;
         }
@@ -1156,6 +1317,8 @@ __global__ __launch_bounds__(256) void verify_attn_combine(AttnParams p) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float L = 0.f;
     if (M != -INFINITY) {
+      // (unrolled so that the loads of several splits are in flight together)
+#pragma unroll 8
       for (int s = 0; s < nsplit; ++s) {
         const size_t slot = (size_t)(item0 + s) * p.rpad + row;
         const float ms = p.part_ml[slot * 2];
@@ -1208,16 +1371,17 @@ static AttnLayout attn_layout(int B, int Hkv, int G, int HD, int max_pages, int 
   if (kv_chunk > 0) {
     cap = units * ((max_keys + kv_chunk - 1) / kv_chunk);
   } else {
-    // the plan picks the smallest chunk with at most `slots` items, else kMaxChunk
+    // the plan takes a chunk whose items fit this cap: up to kItemsPerSlot per
+    // slot, and always kMaxChunk
     const long long at_max = units * ((max_keys + kMaxChunk - 1) / kMaxChunk);
     const long long at_min = units * ((max_keys + kMinChunk - 1) / kMinChunk);
-    cap = std::min(at_min, std::max(slots, at_max));
+    cap = std::min(at_min, std::max(slots * kItemsPerSlot, at_max));
   }
   if (cap < 1) cap = 1;
   L.item_cap = (int)cap;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += (bytes + 255) / 256 * 256; return o; };
-  L.plan_off = take((size_t)(kPlanHeader + B + 1) * 4);
+  L.plan_off = take((size_t)(kPlanHeader + 2 * B + 1) * 4);
   L.items_off = take((size_t)cap * sizeof(ItemDesc));
   L.ml_off = take((size_t)cap * L.rpad * 2 * 4);
   L.o_off = take((size_t)cap * L.rpad * HD * 4);
@@ -1278,7 +1442,7 @@ hipError_t sdv_attn_launch(const SdAttnLaunch& a) {
   const float scale = a.softmax_scale > 0.f ? a.softmax_scale : 1.f / sqrtf((float)a.head_dim);
   p.scale_log2 = scale * 1.4426950408889634f;
 
-  verify_attn_plan<<<1, kPlanThreads, 0, a.stream>>>(p, a.kv_chunk, slots);
+  verify_attn_plan<<<1, kPlanThreads, 0, a.stream>>>(p, a.kv_chunk, slots, kItemOverheadBytes / (4 * a.head_dim));
   if (a.head_dim == 128) {
     if (a.out_f32) launch_main<128, 1>(L.variant, p, grid, a.stream);
     else launch_main<128, 0>(L.variant, p, grid, a.stream);

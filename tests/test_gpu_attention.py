@@ -58,6 +58,23 @@ def test_row_block_variants(G, drafts, d):
     assert err <= ATTN_TOL
 
 
+@pytest.mark.parametrize("kv_chunk", [0, 256])
+def test_many_sequences_mixed_lengths(kv_chunk):
+    """More sequences than the plan keeps in LDS (2048), lengths 1..900 plus one
+    long sequence: the plan's global path, items shorter than the chunk in
+    longest-first order, and workgroups taking items from the counters."""
+    rng = np.random.default_rng(21)
+    B = 2100
+    kv = [int(x) for x in rng.integers(1, 900, size=B)]
+    kv[0] = 20000
+    dr = [int(x) for x in rng.integers(0, 4, size=B)]
+    inp = generate(spec(batch=B, kv_heads=1, group=2, head_dim=64, kv_len=kv, draft_len=dr, seed=21))
+    say(f"case: B={B} mixed lengths kv_chunk={kv_chunk}")
+    err = compare_attention(inp, gpu_attention(inp, kv_chunk=kv_chunk))
+    say(f"max|err| = {err:.3e}")
+    assert err <= ATTN_TOL
+
+
 def test_fp32_output_and_explicit_scale():
     inp = generate(spec(seed=4))
     say("case: fp32 output, scale 0.05")
