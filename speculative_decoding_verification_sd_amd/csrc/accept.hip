@@ -32,6 +32,7 @@
 //                        chunk, then 16-token slice, then token.
 
 #include <limits.h>
+#include <algorithm>
 #include <math.h>
 
 #include "common.h"
@@ -44,7 +45,8 @@ constexpr int kPerThread = kChunk / kAccThreads;  // 32
 constexpr int kSChunk = 4096;                     // logits per sampling workgroup
 constexpr int kSPerThread = kSChunk / kAccThreads;  // 16: one slice of the sampling search per thread
 static_assert(kSPerThread % 4 == 0 && kSPerThread <= 64, "a slice is scanned by one wave");
-constexpr int kDecideSlots = 2048;                // chunk statistics staged in LDS per pass
+constexpr int kDecideSlots = 2048;
+constexpr int kFinishWGs = 1024;                  // accept_finish workgroups in flight at once (4 per CU)                // chunk statistics staged in LDS per pass
 
 struct RowPart {
   float m;     // chunk max
@@ -365,58 +367,60 @@ __global__ __launch_bounds__(kAccThreads) void accept_finish(AccParams p) {
   st.lse_p = s_lp;
   st.lse_q = n < D ? s_lq : 0.0;
 
-  // (1) this chunk's fp64 sums.  Thread t takes the 16 consecutive logits
-  // j0 .. j0+15 (all loaded before any arithmetic): the weight of token j is
-  // max(0, p_j - q_j) at a rejection, p_j when every draft passed.  The thread
-  // publishes its own sums (residual, p) and the workgroup the chunk's.
+  // (1) fp64 sums of the workgroup's chunks (c = blockIdx.x, + gridDim.x, ...).
+  // Thread t takes the 16 consecutive logits j0 .. j0+15 of a chunk (all
+  // loaded before any arithmetic): the weight of token j is max(0, p_j - q_j)
+  // at a rejection, p_j when every draft passed.  The thread publishes its own
+  // sums (residual, p) and the workgroup the chunk's.  Hand-off between
+  // workgroups of one sequence, possibly on different XCDs (separate L2s): the
+  // sums are agent-scope atomic stores, which are coherent across XCDs, and
+  // each is complete (vmcnt 0) before the arrival count.  A release fence would
+  // do the same by writing back the whole L2.
   const float* prow = p.target + (size_t)(t0 + n) * p.V;
   const float* qrow = p.draft + (size_t)(d0 + (n < D ? n : 0)) * p.V;
-  const int j0 = c * kSChunk + tid * kSPerThread;
-  float tl[kSPerThread], dl[kSPerThread];
-  if (p.vec4 && j0 + kSPerThread <= p.V) {
+  for (int c = blockIdx.x; c < p.nschunk; c += gridDim.x) {
+    const int j0 = c * kSChunk + tid * kSPerThread;
+    float tl[kSPerThread], dl[kSPerThread];
+    if (p.vec4 && j0 + kSPerThread <= p.V) {
 #pragma unroll
-    for (int k = 0; k < kSPerThread / 4; ++k) {
-      const f32x4 v = *(const f32x4*)(prow + j0 + 4 * k);
-      const f32x4 u = st.residual ? *(const f32x4*)(qrow + j0 + 4 * k) : f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int k = 0; k < kSPerThread / 4; ++k) {
+        const f32x4 v = *(const f32x4*)(prow + j0 + 4 * k);
+        const f32x4 u = st.residual ? *(const f32x4*)(qrow + j0 + 4 * k) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) { tl[4 * k + e] = v[e]; dl[4 * k + e] = u[e]; }
+        for (int e = 0; e < 4; ++e) { tl[4 * k + e] = v[e]; dl[4 * k + e] = u[e]; }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < kSPerThread; ++e) {
+        const bool in = j0 + e < p.V;
+        tl[e] = in ? prow[j0 + e] : -INFINITY;
+        dl[e] = in && st.residual ? qrow[j0 + e] : -INFINITY;
+      }
     }
-  } else {
+    double tw = 0.0, tp = 0.0;
 #pragma unroll
     for (int e = 0; e < kSPerThread; ++e) {
-      const bool in = j0 + e < p.V;
-      tl[e] = in ? prow[j0 + e] : -INFINITY;
-      dl[e] = in && st.residual ? qrow[j0 + e] : -INFINITY;
+      double w, pj;
+      sample_weight(tl[e], dl[e], st, w, pj);
+      tw += w;
+      tp += pj;
     }
-  }
-  double tw = 0.0, tp = 0.0;
-#pragma unroll
-  for (int e = 0; e < kSPerThread; ++e) {
-    double w, pj;
-    sample_weight(tl[e], dl[e], st, w, pj);
-    tw += w;
-    tp += pj;
-  }
-  // Hand-off between workgroups of one sequence, possibly on different XCDs
-  // (separate L2s): the sums are agent-scope atomic stores, which are coherent
-  // across XCDs, and each is complete (vmcnt 0) before the arrival count.  A
-  // release fence would do the same by writing back the whole L2.
-  {
     double* dst = p.rsub + (((size_t)b * p.nschunk + c) * kAccThreads + tid) * 2;
     __hip_atomic_store(dst, tw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(dst + 1, tp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const double zw = block_sum(tw, sd);
+    const double zp = block_sum(tp, sd);
+    if (tid == 0) {
+      double* cs = p.rsum + ((size_t)b * p.nschunk + c) * 2;
+      __hip_atomic_store(cs, zw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(cs + 1, zp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
-  const double zw = block_sum(tw, sd);
-  const double zp = block_sum(tp, sd);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (tid == 0) {
-    double* dst = p.rsum + ((size_t)b * p.nschunk + c) * 2;
-    __hip_atomic_store(dst, zw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(dst + 1, zp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     const unsigned prev = __hip_atomic_fetch_add(&p.arrived[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = prev == (unsigned)(p.nschunk - 1);
+    s_last = prev == gridDim.x - 1;
   }
   __syncthreads();
   if (!s_last) return;
@@ -560,7 +564,10 @@ hipError_t sdv_accept_launch(const SdAccLaunch& a) {
   if (a.stochastic) {
     if (vec4) accept_rowstats<1, 1><<<grid1, kAccThreads, 0, a.stream>>>(p);
     else accept_rowstats<1, 0><<<grid1, kAccThreads, 0, a.stream>>>(p);
-    accept_finish<<<dim3(L.nschunk, a.B), kAccThreads, 0, a.stream>>>(p);
+    // workgroups per sequence: all chunks, or about kFinishWGs / B in all when
+    // that is fewer (each then takes several chunks)
+    const int per_seq = std::max(1, std::min(L.nschunk, (kFinishWGs + a.B - 1) / std::max(a.B, 1)));
+    accept_finish<<<dim3(per_seq, a.B), kAccThreads, 0, a.stream>>>(p);
   } else {
     if (vec4) accept_rowstats<0, 1><<<grid1, kAccThreads, 0, a.stream>>>(p);
     else accept_rowstats<0, 0><<<grid1, kAccThreads, 0, a.stream>>>(p);
