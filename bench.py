@@ -277,6 +277,104 @@ def write_profiles(bench_json: str, kt_dir: str, fetch_dir: str, write_dir: str,
     print(f"wrote profiles for {wl}: {short} {float(main['AverageNs']) / 1e3:.1f} us, traffic {hbm / alg:.4f}x")
 
 
+SWEEP_PRESET = "g8_kv32k_sweep"
+
+
+def run_sweep(args):
+    """Verify attention (and accept) time per draft length D on the tile-boundary
+    sweep workload (B=32, H_kv=8, G=8, d=128, 32768-token cache, V=32000,
+    synthetic acceptance rate alpha), one JSON line with one point per D."""
+    import numpy as np
+    import torch
+
+    import speculative_decoding_verification_sd_amd as sdv
+    from workloads import generate, preset
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    points = []
+    alpha = args.alpha if args.alpha is not None else 0.6
+    for D in args.sweep:
+        sp = preset(SWEEP_PRESET, draft_len=D, alpha=alpha, seed=args.seed)
+        print(f"[bench] sweep D={D}: generating {sp.name}", file=sys.stderr, flush=True)
+        inp = generate(sp, device=dev)
+        B, T = sp.batch, inp.q.shape[0]
+        out = torch.empty_like(inp.q)
+        al = torch.empty(B, dtype=torch.int32, device=dev)
+        tok = torch.empty(T, dtype=torch.int32, device=dev)
+        adesc = sdv.attn_desc(inp.q, inp.k_cache, inp.block_table, sp.group, inp.max_draft)
+        cdesc = sdv.accept_desc(B, sp.vocab, inp.max_draft, sp.mode)
+        ws_a = torch.empty(max(1, sdv.sd_verify_attention_workspace_size(adesc, T)), dtype=torch.uint8, device=dev)
+        ws_c = torch.empty(max(1, sdv.sd_accept_reject_workspace_size(cdesc, T)), dtype=torch.uint8, device=dev)
+
+        def attention():
+            sdv.sd_verify_attention(inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.kv_len, inp.q_start,
+                                    out, group_size=sp.group, max_draft=inp.max_draft, workspace=ws_a)
+
+        def accept():
+            sdv.sd_accept_reject(inp.target_logits, inp.draft_logits, inp.draft_tokens, inp.q_start,
+                                 inp.uniforms, al, tok, mode=sp.mode, max_draft=inp.max_draft, workspace=ws_c)
+
+        t_end = time.perf_counter() + max(0.0, args.settle_s)
+        while time.perf_counter() < t_end:
+            for _ in range(5):
+                attention()
+                accept()
+            torch.cuda.synchronize()
+        for _ in range(max(1, args.warmup)):
+            attention()
+            accept()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        for k in range(args.steps):
+            ev[k][0].record()
+            attention()
+            ev[k][1].record()
+            accept()
+            ev[k][2].record()
+        torch.cuda.synchronize()
+        a_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+        c_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+        a_bytes, a_flops = algorithmic_attention(inp)
+        points.append({"D": D, "rows_per_kv_head": sp.group * (1 + D), "attention_ms": a_ms, "accept_ms": c_ms,
+                       "verified_tokens_per_s": T / ((a_ms + c_ms) * 1e-3),
+                       "mean_accept_len": float(al.float().mean().item()),
+                       "hbm_frac": a_bytes / (a_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                       "mfma_frac": a_flops / (a_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS})
+        print(f"[bench] sweep D={D}: attention {a_ms * 1e3:.1f} us, accept {c_ms * 1e3:.1f} us", file=sys.stderr,
+              flush=True)
+        del inp, out, ws_a, ws_c
+        torch.cuda.empty_cache()
+    sp = preset(SWEEP_PRESET)
+    print(json.dumps({"metric": "verify attention time per draft length (tile-boundary sweep)", "unit": "ms",
+                      "higher_is_better": False, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                      "dtype": "bf16", "data": "synthetic",
+                      "config": {"workload": sp.name.replace("_sweep", ""), "batch": sp.batch,
+                                 "kv_heads": sp.kv_heads, "group": sp.group, "head_dim": sp.head_dim,
+                                 "kv_len": sp.kv_len, "vocab": sp.vocab, "alpha": alpha, "seed": args.seed},
+                      "clock_settle_s_per_point": args.settle_s, "sweep": points}), flush=True)
+
+
+def write_sweep_profile(sweep_json: str):
+    """Text table of a --sweep line under profiles/."""
+    with open(sweep_json) as f:
+        line = json.loads(f.read().strip().splitlines()[-1])
+    cfg = line["config"]
+    path = os.path.join(ROOT, "profiles", f"verify_attn_sweep_{cfg['workload']}.txt")
+    with open(path, "w") as f:
+        f.write(f"# Verify attention per draft length D on {cfg['workload']} (one MI355X, HIP events, "
+                f"{line['steps']} timed calls per point after {line['clock_settle_s_per_point']} s of clock settle).\n"
+                "# G*(1+D) query rows share each KV head; the kernel variant changes at 64 rows (16x16 MFMA ->\n"
+                "# 32x32 MFMA) and the workgroups per item at 128 rows (one -> two row halves).\n"
+                "$ python3 REPO/bench.py --sweep\n")
+        f.write("D,rows_per_kv_head,attention_us,accept_us,hbm_frac,mfma_frac,verified_tokens_per_s,mean_AL\n")
+        for pt in line["sweep"]:
+            f.write(f"{pt['D']},{pt['rows_per_kv_head']},{pt['attention_ms'] * 1e3:.1f},{pt['accept_ms'] * 1e3:.1f},"
+                    f"{pt['hbm_frac']:.3f},{pt['mfma_frac']:.3f},{pt['verified_tokens_per_s']:.0f},"
+                    f"{pt['mean_accept_len']:.2f}\n")
+    print(f"wrote {path}")
+
+
 def copy_calibration(nbytes: int, reps: int = 3):
     """A plain device-to-device copy of `nbytes` (torch's elementwise copy), for
     scaling the FETCH_SIZE / WRITE_SIZE counters to bytes."""
@@ -304,11 +402,17 @@ def main():
                     help="before the warmup, run steps for this many seconds so the GPU clock settles")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="after the timed steps, copy BYTES device-to-device (counter calibration)")
+    ap.add_argument("--sweep", nargs="*", type=int, default=None, metavar="D",
+                    help="attention time per draft length on the sweep workload (default D = 0..31)")
+    ap.add_argument("--write-sweep-profile", metavar="SWEEP_JSON", help="write the profiles/ table of a --sweep line")
     ap.add_argument("--write-profiles", nargs=4, metavar=("BENCH_JSON", "KT_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write the profiles/ summaries from a bench line and three rocprofv3 runs (no GPU)")
     args = ap.parse_args()
     if args.write_profiles:
         write_profiles(*args.write_profiles, copy_bytes=args.calibrate_copy or (1 << 30))
+        return
+    if args.write_sweep_profile:
+        write_sweep_profile(args.write_sweep_profile)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -316,6 +420,13 @@ def main():
         print("bench.py measures one GPU only: the verify step is built and timed on a single MI355X "
               "(--gpus 1); multi-GPU runs are not part of this build.", file=sys.stderr)
         sys.exit(2)
+    if args.sweep is not None:
+        args.sweep = args.sweep or list(range(32))
+        if args.steps == 20 and args.warmup == 5:
+            args.steps, args.warmup = 10, 3
+        args.settle_s = min(args.settle_s, 0.3)
+        run_sweep(args)
+        return
 
     import numpy as np
     import torch

@@ -76,7 +76,6 @@ struct AttnParams {
   int* plan;        // [16 + 2B + 1]: chunk, total items, full items, work counters, item_start, tail_pos
   ItemDesc* items;  // [item_cap]
   int B, Hkv, G, max_pages, num_pages, max_draft, rpad, total_q, item_cap;
-  int nhalf;        // workgroups per item: 2 when a sequence can have more query rows than one holds
   float scale_log2;
 };
 
@@ -502,20 +501,13 @@ __global__ __launch_bounds__(64 * NW, WPC) void verify_attn_main(AttnParams p) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
 
-  // With two row halves per item, virtual items 16k..16k+7 are the first
-  // halves and 16k+8..16k+15 the second halves of items 8k..8k+7: workgroups
-  // are dealt round-robin over the eight XCDs, so both halves of an item run on
-  // one XCD and the second reads the item's pages from that XCD's L2.
-  constexpr int kRowsWG = NRB * NW * 16;
-  const int nvirt = p.nhalf == 1 ? total : (total + 7) / 8 * 16;
   // Items after the first round.  When the plan's list (longest first) holds
   // items shorter than the chunk and more items than workgroups, the next item
   // of this workgroup's class (index = blockIdx % 8 modulo 8) as workgroups
-  // finish, from the class's counter; otherwise (and with row halves, whose
-  // stride keeps both halves of an item on one XCD) a fixed stride.
+  // finish, from the class's counter; otherwise a fixed stride.
   __shared__ int s_next;
   const int chunk = p.plan[0];
-  const bool dyn = p.nhalf == 1 && gridDim.x >= 8 && total > (int)gridDim.x && p.plan[2] < total;
+  const bool dyn = gridDim.x >= 8 && total > (int)gridDim.x && p.plan[2] < total;
   const int cls = blockIdx.x & 7;
   const int first_dyn = (int)gridDim.x + ((cls - (int)(gridDim.x & 7)) & 7);
   auto next_item = [&](int vi) {
@@ -525,10 +517,8 @@ __global__ __launch_bounds__(64 * NW, WPC) void verify_attn_main(AttnParams p) {
     block_sync();
     return s_next;
   };
-  for (int vi = blockIdx.x; vi < nvirt; vi = next_item(vi)) {
-    const int item = p.nhalf == 1 ? vi : (vi >> 4) * 8 + (vi & 7);
-    const int row0 = p.nhalf == 1 ? 0 : ((vi >> 3) & 1) * kRowsWG;
-    if (item >= total) continue;
+  constexpr int row0 = 0;
+  for (int item = blockIdx.x; item < total; item = next_item(item)) {
     const ItemDesc d = p.items[item];
     // wave-uniform copies, so that everything derived from them (page bases,
     // tile counts) stays in scalar registers
@@ -543,7 +533,6 @@ __global__ __launch_bounds__(64 * NW, WPC) void verify_attn_main(AttnParams p) {
     const int pslot = p.plan[kPlanHeader + b] + h * nsplit + k_begin / chunk;   // natural index: partials
     if (pslot < 0 || pslot >= p.item_cap) continue;
     const int R = p.G * (1 + D);
-    if (row0 >= R) continue;     // the sequence's rows fit in the first half
     const int* bt = p.block_table + (size_t)b * p.max_pages;
     const bool wave_active = row0 + wave * NRB * 16 < R;
     const int ntiles = k_end > k_begin ? (k_end - k_begin + RG::kTile - 1) / RG::kTile : 0;
@@ -905,11 +894,13 @@ __global__ __launch_bounds__(64 * NW, WPC) void verify_attn_main(AttnParams p) {
 
 // ---------------------------------------------------------------------------
 // Verify attention with 32x32x16 MFMAs for blocks of more than 64 query rows:
-// a workgroup of 8 waves, two per SIMD, over 128 query rows.  The waves form
-// two sets of four (32 rows per wave); set 0 takes the even tiles of the item
-// and set 1 the odd ones, both from one LDS-DMA ring, and the two partial
-// results are merged through LDS at the end of the item.  Two waves per SIMD
-// hide each other's LDS, barrier and MFMA-dependency latencies.  Operands:
+// a workgroup of 8 waves, two per SIMD, in two sets of four (32 rows per
+// wave), both fed from one LDS-DMA ring.  Up to 128 rows (RS false), set 0
+// takes the even tiles of the item and set 1 the odd ones over the same 128
+// rows, and the two partial results are merged through LDS at the end of the
+// item.  Up to 256 rows (RS true), set s takes rows 128s .. 128s+127 over every
+// tile, so the item's pages are streamed once for all its rows.  Two waves per
+// SIMD hide each other's LDS, barrier and MFMA-dependency latencies.  Operands:
 //   * S^T = K Q^T per 32-key tile: A = K (lane: key row l%32, dims
 //     c*16 + (l/32)*8..+7), B = Q^T (lane: query row l%32, same dims), so each
 //     lane holds one query row and keys (e/4)*8 + (l/32)*4 + e%4, e < 16.
@@ -930,7 +921,7 @@ __device__ __forceinline__ int wide_swz(int k) {
   else return (((k >> 1) & 1) << 2) | ((k >> 2) & 3);
 }
 
-template <int HD, int OUT_F32>
+template <int HD, int OUT_F32, bool RS>
 __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
   constexpr int NW = 8;
   using RG = Ring<HD, NW, 1>;
@@ -958,8 +949,9 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
   const int total = min(p.plan[1], p.item_cap);
   const int Hq = p.Hkv * p.G;
 
-  // Lane-constant LDS offsets, including the set's stage parity: in step k the
-  // set reads tile 2k + set, whose stage is (2k + set) % S.
+  // Lane-constant LDS offsets, including (RS false) the set's stage parity: in
+  // step k the set reads tile 2k + set, whose stage is (2k + set) % S.  With RS
+  // both sets read both tiles of the step.
   // S^T takes key pi(r) = (r/16)*16 + ((r/4)%2)*8 + ((r/8)%2)*4 + r%4 as its MFMA
   // row r, so that score entry e of a lane holds key (e/8)*16 + 8hh + e%8 and
   // each 16-key step of P V reads eight consecutive keys per lane.
@@ -967,27 +959,25 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
   int koff[NKS];                 // K operand: key row kkey, logical chunk 2c + hh
 #pragma unroll
   for (int c = 0; c < NKS; ++c)
-    koff[c] = set * RG::kHalf + kkey * RG::kRowB + (((c * 2 + hh) ^ wide_swz<HD>(kkey)) * 16);
+    koff[c] = (RS ? 0 : set * RG::kHalf) + kkey * RG::kRowB + (((c * 2 + hh) ^ wide_swz<HD>(kkey)) * 16);
   int voffs[NMB];                // V^T operand: d-row mb*32 + r32, keys ks*16 + 8hh..+7 (page ks)
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) {
     const int dd = mb * 32 + r32;
-    voffs[mb] = set * RG::kHalf + S * RG::kHalf + dd * 32 + ((hh ^ ((dd >> 3) & 1)) * 16);
+    voffs[mb] = (RS ? 0 : set * RG::kHalf) + S * RG::kHalf + dd * 32 + ((hh ^ ((dd >> 3) & 1)) * 16);
   }
   DmaSlot dma[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) dma[i] = dma_slot<HD, RG>(wave + NW * i, lane, [](int k) { return wide_swz<HD>(k & 15); });
 
-  constexpr int kRowsWG = 4 * 32;
-  const int nvirt = p.nhalf == 1 ? total : (total + 7) / 8 * 16;
+  const int row0 = RS ? set * 128 : 0;   // first row of the set
   // Items after the first round.  When the plan's list (longest first) holds
   // items shorter than the chunk and more items than workgroups, the next item
   // of this workgroup's class (index = blockIdx % 8 modulo 8) as workgroups
-  // finish, from the class's counter; otherwise (and with row halves, whose
-  // stride keeps both halves of an item on one XCD) a fixed stride.
+  // finish, from the class's counter; otherwise a fixed stride.
   __shared__ int s_next;
   const int chunk = p.plan[0];
-  const bool dyn = p.nhalf == 1 && gridDim.x >= 8 && total > (int)gridDim.x && p.plan[2] < total;
+  const bool dyn = gridDim.x >= 8 && total > (int)gridDim.x && p.plan[2] < total;
   const int cls = blockIdx.x & 7;
   const int first_dyn = (int)gridDim.x + ((cls - (int)(gridDim.x & 7)) & 7);
   auto next_item = [&](int vi) {
@@ -997,10 +987,7 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
     block_sync();
     return s_next;
   };
-  for (int vi = blockIdx.x; vi < nvirt; vi = next_item(vi)) {
-    const int item = p.nhalf == 1 ? vi : (vi >> 4) * 8 + (vi & 7);
-    const int row0 = p.nhalf == 1 ? 0 : ((vi >> 3) & 1) * kRowsWG;
-    if (item >= total) continue;
+  for (int item = blockIdx.x; item < total; item = next_item(item)) {
     const ItemDesc d = p.items[item];
     const int b = __builtin_amdgcn_readfirstlane(d.b), h = __builtin_amdgcn_readfirstlane(d.h);
     const int k_begin = __builtin_amdgcn_readfirstlane(d.k_begin), k_end = __builtin_amdgcn_readfirstlane(d.k_end);
@@ -1013,7 +1000,6 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
     const int pslot = p.plan[kPlanHeader + b] + h * nsplit + k_begin / chunk;   // natural index: partials
     if (pslot < 0 || pslot >= p.item_cap) continue;
     const int R = p.G * (1 + D);
-    if (row0 >= R) continue;
     const int* bt = p.block_table + (size_t)b * p.max_pages;
     const bool wave_active = row0 + w4 * 32 < R;
     const int ntiles = k_end > k_begin ? (k_end - k_begin + RG::kTile - 1) / RG::kTile : 0;
@@ -1148,8 +1134,9 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
       }
     };
 
-    // Step k: tiles 2k (set 0) and 2k+1 (set 1).  Wait for both, barrier,
-    // refill the stages of tiles 2k-2 and 2k-1 with tiles 2k+S-2 and 2k+S-1.
+    // Step k: tiles 2k (set 0; RS: both sets) and 2k+1 (set 1; RS: both sets).
+    // Wait for both, barrier, refill the stages of tiles 2k-2 and 2k-1 with
+    // tiles 2k+S-2 and 2k+S-1.
     auto advance = [&](int k, int st0) {
       wait_tiles<LPW>(max(0, min(S - 4, ntiles - 2 - 2 * k)));
       if (ragged_tail && (ntiles - 1) / 2 == k) zero_tail(ntiles - 1);
@@ -1162,22 +1149,28 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
     };
     // Generic step (first, masked, last, and every step of the safe pass):
     // run-time stages; SAFE raises the running max lazily.
-    auto step_generic = [&](int k, auto safec) {
+    auto tile_generic = [&](int k, int tt, int off, auto safec) {
       constexpr bool SAFE = decltype(safec)::value;
-      advance(k, (2 * k + S - 2) % S);
-      const int tt = 2 * k + set;
       if (wave_active && tt < ntiles) {
-        const int off = (2 * k % S) * RG::kHalf;   // the set's parity is in koff / voffs
         scores(off);
         if (k_begin + (tt + 1) * RG::kTile > N - D) mask_scores(tt);
         if constexpr (SAFE) {
           if (__any(row_max(kLazy))) rescale();
-        } else if (k == 0) {
+        } else if (k == 0 && (!RS || tt == 0)) {
           row_max(0.f);
           m_run = mt;
           m_off = mt == -INFINITY ? 0.f : -mt;
         }
         accumulate(off);
+      }
+    };
+    auto step_generic = [&](int k, auto safec) {
+      advance(k, (2 * k + S - 2) % S);
+      if constexpr (RS) {
+        tile_generic(k, 2 * k, (2 * k % S) * RG::kHalf, safec);
+        tile_generic(k, 2 * k + 1, ((2 * k + 1) % S) * RG::kHalf, safec);
+      } else {
+        tile_generic(k, 2 * k + set, (2 * k % S) * RG::kHalf, safec);   // the set's parity is in koff / voffs
       }
     };
 
@@ -1200,6 +1193,10 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
           if constexpr (ACTIVE) {
             scores(st * RG::kHalf);
             accumulate(st * RG::kHalf);
+            if constexpr (RS) {
+              scores((st + 1) * RG::kHalf);
+              accumulate((st + 1) * RG::kHalf);
+            }
           }
         };
         step(ic<0>{});
@@ -1224,28 +1221,35 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
     }
     block_sync();   // every wave is done with the ring (all loads landed: the last step waited for vmcnt 0)
 
-    // ---- Merge the two sets' partials (set 1 hands (O, l, m) to set 0 through LDS).
-    float* xch = (float*)smem + (size_t)w4 * kMergeF * 64 + lane;
-    if (set == 1 && wave_active) {
+    // ---- Merge the two sets' partials (RS false: set 1 hands (O, l, m) to set 0
+    // through LDS; RS true: each set owns its rows).
+    float M = m_run;
+    float lt = row_sum();
+    if constexpr (!RS) {
+      float* xch = (float*)smem + (size_t)w4 * kMergeF * 64 + lane;
+      if (set == 1 && wave_active) {
 #pragma unroll
-      for (int mb = 0; mb < NMB; ++mb)
+        for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) xch[(mb * 16 + e) * 64] = o[mb][e];
-      xch[(16 * NMB) * 64] = row_sum();
-      xch[(16 * NMB + 1) * 64] = m_run;
+          for (int e = 0; e < 16; ++e) xch[(mb * 16 + e) * 64] = o[mb][e];
+        xch[(16 * NMB) * 64] = lt;
+        xch[(16 * NMB + 1) * 64] = m_run;
+      }
+      block_sync();
+      if (set == 0 && wave_active && valid) {
+        const float lb = xch[(16 * NMB) * 64];
+        const float mb_ = xch[(16 * NMB + 1) * 64];
+        M = fmaxf(m_run, mb_);
+        const float wa = M == -INFINITY ? 0.f : fast_exp2(m_run - M);
+        const float wb = M == -INFINITY ? 0.f : fast_exp2(mb_ - M);
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[mb][e] = o[mb][e] * wa + xch[(mb * 16 + e) * 64] * wb;
+        lt = lt * wa + lb * wb;
+      }
     }
-    block_sync();
-    if (set == 0 && wave_active && valid) {
-      const float lb = xch[(16 * NMB) * 64];
-      const float mb_ = xch[(16 * NMB + 1) * 64];
-      const float M = fmaxf(m_run, mb_);
-      const float wa = M == -INFINITY ? 0.f : fast_exp2(m_run - M);
-      const float wb = M == -INFINITY ? 0.f : fast_exp2(mb_ - M);
-#pragma unroll
-      for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[mb][e] = o[mb][e] * wa + xch[(mb * 16 + e) * 64] * wb;
-      const float lt = row_sum() * wa + lb * wb;
+    if ((RS || set == 0) && wave_active && valid) {
       // O^T accumulator: lane holds query row r32 and dims mb*32 + q*8 + 4hh + 0..3 in entries 4q..4q+3.
       if (nsplit == 1) {
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
@@ -1341,14 +1345,14 @@ __global__ __launch_bounds__(256) void verify_attn_combine(AttnParams p) {
 // Host side: variant choice, workspace layout, launches.
 struct AttnLayout {
   size_t plan_off, items_off, ml_off, o_off, total;
-  int rpad, item_cap, variant, nhalf;
-  // variant 0: 4 waves x 1 row block (64 rows), two workgroups per CU;
-  // variant 1: 4 waves x 2 row blocks (128 rows), one workgroup per CU, two
-  // workgroups per item (row halves) when a sequence can have more rows
+  int rpad, item_cap, variant;
+  // variant 0: verify_attn_main, 4 waves x 16 rows (64 rows), two workgroups per CU;
+  // variant 1: verify_attn_wide, 8 waves, up to 128 rows (the sets split the tiles);
+  // variant 2: verify_attn_wide, 8 waves, up to 256 rows (the sets split the rows);
+  // one workgroup per CU for variants 1 and 2
 };
 
-static int attn_variant(int rmax) { return rmax <= 64 ? 0 : 1; }
-static int attn_halves(int rmax) { return rmax <= 128 ? 1 : 2; }
+static int attn_variant(int rmax) { return rmax <= 64 ? 0 : rmax <= 128 ? 1 : 2; }
 
 // Resident workgroups of the persistent grid per CU.
 static int attn_slots(int cus, int variant) { return cus * (variant == 0 ? 2 : 1); }
@@ -1362,11 +1366,10 @@ static AttnLayout attn_layout(int B, int Hkv, int G, int HD, int max_pages, int 
   AttnLayout L;
   const int rmax = G * (1 + max_draft);
   L.variant = attn_variant(rmax);
-  L.nhalf = attn_halves(rmax);
   L.rpad = (rmax + 15) / 16 * 16;
   const long long max_keys = (long long)max_pages * kPage;
   const long long units = (long long)B * Hkv;
-  const long long slots = attn_slots(kMaxCus, L.variant) / L.nhalf;   // items the plan aims for
+  const long long slots = attn_slots(kMaxCus, L.variant);   // items the plan aims for
   long long cap;
   if (kv_chunk > 0) {
     cap = units * ((max_keys + kv_chunk - 1) / kv_chunk);
@@ -1401,7 +1404,8 @@ size_t sdv_attn_workspace_bytes(int B, int Hkv, int G, int head_dim, int max_pag
 template <int HD, int OUTF>
 static void launch_main(int variant, const AttnParams& p, int grid, hipStream_t st) {
   if (variant == 0) verify_attn_main<HD, 1, 4, 2, OUTF><<<grid, 256, 0, st>>>(p);
-  else verify_attn_wide<HD, OUTF><<<grid, 512, 0, st>>>(p);
+  else if (variant == 1) verify_attn_wide<HD, OUTF, false><<<grid, 512, 0, st>>>(p);
+  else verify_attn_wide<HD, OUTF, true><<<grid, 512, 0, st>>>(p);
 }
 
 hipError_t sdv_attn_launch(const SdAttnLaunch& a) {
@@ -1413,9 +1417,8 @@ hipError_t sdv_attn_launch(const SdAttnLaunch& a) {
   cus = std::max(1, std::min(cus, kMaxCus));
   const AttnLayout L = attn_layout(a.B, a.Hkv, a.G, a.head_dim, a.max_pages, a.max_draft, a.kv_chunk);
   const int wgs = attn_slots(cus, L.variant);
-  const int slots = std::max(1, wgs / L.nhalf);   // items the plan aims for
-  const int grid = (int)std::min<long long>(wgs, L.nhalf == 1 ? (long long)L.item_cap
-                                                               : ((long long)L.item_cap + 7) / 8 * 16);
+  const int slots = std::max(1, wgs);   // items the plan aims for
+  const int grid = (int)std::min<long long>(wgs, (long long)L.item_cap);
   unsigned char* ws = (unsigned char*)a.workspace;
   AttnParams p;
   p.q = (const uint16_t*)a.q;
@@ -1438,7 +1441,6 @@ hipError_t sdv_attn_launch(const SdAttnLaunch& a) {
   p.rpad = L.rpad;
   p.total_q = a.total_q;
   p.item_cap = L.item_cap;
-  p.nhalf = L.nhalf;
   const float scale = a.softmax_scale > 0.f ? a.softmax_scale : 1.f / sqrtf((float)a.head_dim);
   p.scale_log2 = scale * 1.4426950408889634f;
 
