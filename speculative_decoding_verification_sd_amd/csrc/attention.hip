@@ -1118,6 +1118,48 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[ks][2 * q], pf[ks][2 * q + 1]}, one2, l_run, false);
+      asm volatile("" ::"v"(l_run));   // keep the sums here: sunk past later tiles they hold P live
+    };
+    // The two halves of accumulate(), for the row-split step's pipeline.
+    auto make_p = [&](bf16x8* pf) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pf[ks][e] = (__bf16)fast_exp2(fmaf(sc[ks * 8 + e], p.scale_log2, m_off));
+      const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[ks][2 * q], pf[ks][2 * q + 1]}, one2, l_run, false);
+      asm volatile("" ::"v"(l_run));   // keep the sums here: sunk past later tiles they hold P live
+    };
+    auto pv = [&](int off, const bf16x8* pf) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+          const bf16x8 vf = *(const bf16x8*)(smem + off + ks * HD * 32 + voffs[mb]);
+          o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[mb], 0, 0, 0);
+        }
+    };
+    // Row-split steady step over the tiles at `off0` and `off1`: P of the first
+    // tile is formed (VALU) while the scores of the second accumulate (MFMA,
+    // one chain), then P V of the first, then the second tile.
+    auto rs_pair = [&](int off0, int off1) {
+      scores(off0);
+      bf16x8 pf[2];
+      make_p(pf);
+      f32x16 s1;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s1[e] = 0.f;
+#pragma unroll
+      for (int c = 0; c < NKS; ++c)
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(smem + off1 + koff[c]), qf[c], s1, 0, 0, 0);
+      pv(off0, pf);
+      sc = s1;
+      make_p(pf);
+      pv(off1, pf);
     };
     auto row_sum = [&]() {
       auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
@@ -1191,11 +1233,11 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
           constexpr int st = (2 * (1 + u)) % S;         // stage of tile 2k (k = kb + u; kb - 1 is a multiple of S/2)
           advance(kb + u, (st + S - 2) % S);
           if constexpr (ACTIVE) {
-            scores(st * RG::kHalf);
-            accumulate(st * RG::kHalf);
             if constexpr (RS) {
-              scores((st + 1) * RG::kHalf);
-              accumulate((st + 1) * RG::kHalf);
+              rs_pair(st * RG::kHalf, (st + 1) * RG::kHalf);
+            } else {
+              scores(st * RG::kHalf);
+              accumulate(st * RG::kHalf);
             }
           }
         };
