@@ -233,13 +233,15 @@ def write_profiles(bench_json: str, kt_dir: str, fetch_dir: str, write_dir: str,
     with open(os.path.join(prof, f"verify_step_{wl}_kernel_stats.txt"), "w") as f:
         f.write(f"# rocprofv3 kernel-trace summary of the library's kernels, workload {wl}:\n"
                 "# one verify step = verify attention (plan, main, split-KV combine) + accept/reject.\n"
-                f"# {calls} calls per kernel = warmup + timed steps.  Durations in ns.\n"
+                f"# {calls} calls per kernel = clock-settle + warmup + timed steps.  Durations in ns.\n"
                 f"$ cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d REPO/gpurun_out/kt "
                 f"-o run --output-format csv -- python3 REPO/bench.py {args}\n")
         f.write("Name,Calls,TotalDurationNs,AverageNs,Percentage,MinNs,MaxNs,StdDev\n")
         for r in stats:
             f.write(",".join([r["Name"], r["Calls"], r["TotalDurationNs"], r["AverageNs"], r["Percentage"],
                               r["MinNs"], r["MaxNs"], r["StdDev"]]) + "\n")
+        attn = sum(float(r["AverageNs"]) for r in stats if "verify_attn" in r["Name"]) / 1e3
+        f.write(f"attention call (plan + main + combine averages): {attn:.1f} us\n")
         f.write(f"bench.py in the same call: attention {line['attention_ms'] * 1e3:.1f} us/step (HIP events), "
                 f"accept {line['accept_ms'] * 1e3:.1f} us/step, {line['value']:.0f} verified tokens/s\n")
     # traffic summary of the dominant kernel
@@ -365,7 +367,8 @@ def write_sweep_profile(sweep_json: str):
         f.write(f"# Verify attention per draft length D on {cfg['workload']} (one MI355X, HIP events, "
                 f"{line['steps']} timed calls per point after {line['clock_settle_s_per_point']} s of clock settle).\n"
                 "# G*(1+D) query rows share each KV head; the kernel variant changes at 64 rows (16x16 MFMA ->\n"
-                "# 32x32 MFMA) and the workgroups per item at 128 rows (one -> two row halves).\n"
+                "# 32x32 MFMA, the wave sets split the tiles) and at 128 rows (the wave sets split the rows, so\n"
+                "# every wave takes both tiles of a step).\n"
                 "$ python3 REPO/bench.py --sweep\n")
         f.write("D,rows_per_kv_head,attention_us,accept_us,hbm_frac,mfma_frac,verified_tokens_per_s,mean_AL\n")
         for pt in line["sweep"]:
