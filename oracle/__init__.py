@@ -13,6 +13,9 @@ the pages' definitions:
   decoding speed up LLM inference?", sections "Mechanism" and "Math
   intuition"; the NVIDIA page's "What is speculative decoding?" for D and AL;
   the LLM inference handbook's "How speculative decoding works").
+* gemm.py — the verify-shaped linear layer y = x W^T whose GEMM-M grows to
+  M*(1+D) under speculation (the co-design page, section "Draft length and
+  performance of linear layers").
 
 Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may import
 or call anything here.  The product path (the HIP library and its Python
@@ -22,8 +25,10 @@ only the seeded input generators in ``workloads/``.
 
 from .attention import bf16_bits_to_f64, verify_attention, verify_attention_unit
 from .accept import accept_greedy, accept_stochastic, accept_reject, row_log_normalizer
+from .gemm import linear_abs_sum, verify_linear
 
 __all__ = [
     "bf16_bits_to_f64", "verify_attention", "verify_attention_unit",
     "accept_greedy", "accept_stochastic", "accept_reject", "row_log_normalizer",
+    "verify_linear", "linear_abs_sum",
 ]
