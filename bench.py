@@ -378,6 +378,91 @@ def write_sweep_profile(sweep_json: str):
     print(f"wrote {path}")
 
 
+def run_linear_sweep(args):
+    """The verify-shaped linear layer y = x W^T at N = K = 6144 (the expert GEMM
+    of the co-design page's Figure 3) for M = batch * (1+D): TFLOP/s per batch
+    and draft length, one JSON line.  W (75 MB) fits the Infinity Cache, so a
+    1 GiB read evicts it before every timed call."""
+    import numpy as np
+    import torch
+
+    import speculative_decoding_verification_sd_amd as sdv
+    from workloads import EXPERT_K, EXPERT_N, linear_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    N = K = EXPERT_N
+    drafts = [0, 1, 3, 7, 15]
+    batches = [1, 2, 4, 8, 16, 32, 64, 128, 256, 512]
+    m_max = max(b * (1 + d) for b in batches for d in drafts)
+    xs, w = linear_inputs(m_max, N, K, seed=args.seed, device=dev)
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    sink = torch.empty(1, dtype=torch.float32, device=dev)
+    ys = torch.empty(m_max, N, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(1, max(sdv.sd_verify_linear_workspace_size(sdv.linear_desc(b * (1 + d), N, K))
+                                for b in batches for d in drafts)), dtype=torch.uint8, device=dev)
+    t_end = time.perf_counter() + max(0.0, args.settle_s)
+    while time.perf_counter() < t_end:
+        sdv.sd_verify_linear(xs[:512], w, ys[:512], workspace=ws)
+        torch.cuda.synchronize()
+    points = []
+    for d in drafts:
+        for b in batches:
+            m = b * (1 + d)
+            x, y = xs[:m], ys[:m]
+            for _ in range(3):
+                sdv.sd_verify_linear(x, w, y, workspace=ws)
+            times = []
+            for _ in range(args.steps):
+                torch.amax(scratch, dim=0, keepdim=True, out=sink)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                sdv.sd_verify_linear(x, w, y, workspace=ws)
+                e1.record()
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1))
+            t = float(np.median(times)) * 1e-3
+            flops = 2.0 * m * N * K
+            nbytes = 2.0 * (m * K + N * K + m * N)
+            points.append({"D": d, "batch": b, "m": m, "us": t * 1e6, "tflops": flops / t / 1e12,
+                           "mfma_frac": flops / t / 1e12 / BF16_PEAK_TFLOPS,
+                           "hbm_frac": nbytes / t / 1e9 / HBM_PEAK_GBS})
+            print(f"[bench] linear D={d} batch={b} m={m}: {t * 1e6:.1f} us, {flops / t / 1e12:.1f} TFLOP/s",
+                  file=sys.stderr, flush=True)
+    base = next(p["tflops"] for p in points if p["D"] == 0 and p["batch"] == 1)
+    for p in points:
+        p["tflops_vs_D0_batch1"] = p["tflops"] / base
+    print(json.dumps({"metric": "verify-shaped linear layer TFLOP/s per batch and draft length (N = K = 6144)",
+                      "unit": "TFLOP/s", "higher_is_better": True, "n_gpus": 1, "steps": args.steps,
+                      "dtype": "bf16", "data": "synthetic",
+                      "config": {"workload": "linear_n6144_k6144", "n": N, "k": K, "drafts": drafts,
+                                 "batches": batches, "seed": args.seed},
+                      "cache_flush": "1 GiB scratch read before every timed call", "sweep": points}), flush=True)
+
+
+def write_linear_profile(sweep_json: str):
+    """Text table of a --linear-sweep line under profiles/."""
+    with open(sweep_json) as f:
+        line = json.loads(f.read().strip().splitlines()[-1])
+    pts = line["sweep"]
+    drafts = line["config"]["drafts"]
+    batches = line["config"]["batches"]
+    path = os.path.join(ROOT, "profiles", "verify_linear_sweep_n6144_k6144.txt")
+    with open(path, "w") as f:
+        f.write("# Verify-shaped linear layer y = x W^T, N = K = 6144, M = batch * (1+D), bf16 in / fp32 accumulate,\n"
+                f"# one MI355X, median of {line['steps']} HIP-event-timed calls, each after a 1 GiB cache-evicting read.\n"
+                "$ python3 REPO/bench.py --linear-sweep\n")
+        f.write("TFLOP/s\nbatch," + ",".join(f"D={d}" for d in drafts) + "\n")
+        for b in batches:
+            f.write(f"{b}," + ",".join(f"{next(p['tflops'] for p in pts if p['D'] == d and p['batch'] == b):.1f}"
+                                       for d in drafts) + "\n")
+        f.write("time us\nbatch," + ",".join(f"D={d}" for d in drafts) + "\n")
+        for b in batches:
+            f.write(f"{b}," + ",".join(f"{next(p['us'] for p in pts if p['D'] == d and p['batch'] == b):.1f}"
+                                       for d in drafts) + "\n")
+    print(f"wrote {path}")
+
+
 def copy_calibration(nbytes: int, reps: int = 3):
     """A plain device-to-device copy of `nbytes` (torch's elementwise copy), for
     scaling the FETCH_SIZE / WRITE_SIZE counters to bytes."""
@@ -408,6 +493,10 @@ def main():
     ap.add_argument("--sweep", nargs="*", type=int, default=None, metavar="D",
                     help="attention time per draft length on the sweep workload (default D = 0..31)")
     ap.add_argument("--write-sweep-profile", metavar="SWEEP_JSON", help="write the profiles/ table of a --sweep line")
+    ap.add_argument("--linear-sweep", action="store_true",
+                    help="the verify-shaped linear layer (N = K = 6144) over batch and draft length")
+    ap.add_argument("--write-linear-profile", metavar="SWEEP_JSON",
+                    help="write the profiles/ table of a --linear-sweep line")
     ap.add_argument("--write-profiles", nargs=4, metavar=("BENCH_JSON", "KT_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write the profiles/ summaries from a bench line and three rocprofv3 runs (no GPU)")
     args = ap.parse_args()
@@ -417,12 +506,19 @@ def main():
     if args.write_sweep_profile:
         write_sweep_profile(args.write_sweep_profile)
         return
+    if args.write_linear_profile:
+        write_linear_profile(args.write_linear_profile)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the verify step is built and timed on a single MI355X "
               "(--gpus 1); multi-GPU runs are not part of this build.", file=sys.stderr)
         sys.exit(2)
+    if args.linear_sweep:
+        args.settle_s = min(args.settle_s, 0.5)
+        run_linear_sweep(args)
+        return
     if args.sweep is not None:
         args.sweep = args.sweep or list(range(32))
         if args.steps == 20 and args.warmup == 5:

@@ -180,6 +180,39 @@ sd_status sd_verify_step(const sd_attn_desc* attn, const sd_accept_desc* acc, in
                          int32_t* accept_len, int32_t* out_tokens,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Verify-shaped linear layer (an extension next to the verify step proper).
+ * With speculation every linear layer of the target sees M*(1+D) rows in the
+ * verify pass instead of M, against the same weight: the GEMM-M grows by the
+ * factor 1+D while the bytes of W stay the same ("Co-Designing AI Models Using
+ * Speculative Decoding for Faster LLM Inference", translated page, section
+ * "Draft length and performance of linear layers", Figure 3, for an expert
+ * GEMM of N = K = 6144).
+ */
+typedef struct {
+  int32_t m;   /* rows of x and y (the verify rows, M*(1+D)), >= 0 */
+  int32_t n;   /* output features (rows of W): a positive multiple of 128 */
+  int32_t k;   /* input features: a positive multiple of 64; m*n, n*k, m*k < 2^31 */
+} sd_linear_desc;
+
+/* Workspace bytes sd_verify_linear needs (0 is a valid answer: then workspace may be NULL). */
+size_t sd_verify_linear_workspace_size(const sd_linear_desc* desc);
+
+/*
+ * y = x W^T:  y[m][n] = sum_k x[m][k] * w[n][k], fp32 accumulation, bf16 output
+ * rounded to nearest-even.
+ *
+ *   x          bf16 [m, k]   row-major
+ *   w          bf16 [n, k]   row-major (one row per output feature)
+ *   y          bf16 [m, n]   row-major; written, not read
+ *   workspace  device scratch of at least sd_verify_linear_workspace_size bytes, 16-byte
+ *              aligned (fp32 partial sums when K is split); its contents on entry do not matter
+ *
+ * Deterministic: partial sums over K ranges are added in a fixed order.
+ */
+sd_status sd_verify_linear(const sd_linear_desc* desc, const void* x, const void* w, void* y,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* Message describing the last non-OK status returned on the calling thread. */
 const char* sd_last_error(void);
 

@@ -54,6 +54,14 @@ class sd_accept_desc(ctypes.Structure):
     ]
 
 
+class sd_linear_desc(ctypes.Structure):
+    _fields_ = [
+        ("m", ctypes.c_int32),
+        ("n", ctypes.c_int32),
+        ("k", ctypes.c_int32),
+    ]
+
+
 _lib: Optional[ctypes.CDLL] = None
 _P = ctypes.c_void_p
 _SZ = ctypes.c_size_t
@@ -69,6 +77,8 @@ SIGNATURES = {
     "sd_verify_step_workspace_size": (_SZ, [ctypes.POINTER(sd_attn_desc), ctypes.POINTER(sd_accept_desc), _I]),
     "sd_verify_step": (ctypes.c_int, [ctypes.POINTER(sd_attn_desc), ctypes.POINTER(sd_accept_desc), _I,
                                       _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "sd_verify_linear_workspace_size": (_SZ, [ctypes.POINTER(sd_linear_desc)]),
+    "sd_verify_linear": (ctypes.c_int, [ctypes.POINTER(sd_linear_desc), _P, _P, _P, _P, _SZ, _P]),
     "sd_last_error": (ctypes.c_char_p, []),
     "sd_version": (ctypes.c_char_p, []),
 }
@@ -235,6 +245,32 @@ def sd_verify_step(q, k_cache, v_cache, block_table, kv_len, q_start, attn_out, 
                                 _ptr(target_logits), _ptr(draft_logits if stoch else None), _ptr(draft_tokens),
                                 _ptr(uniforms if stoch else None), _ptr(accept_len), _ptr(out_tokens), _ptr(ws),
                                 ws.numel() * ws.element_size(), _stream(q.device, stream)))
+
+
+def linear_desc(m: int, n: int, k: int) -> sd_linear_desc:
+    return sd_linear_desc(int(m), int(n), int(k))
+
+
+def sd_verify_linear_workspace_size(desc: sd_linear_desc) -> int:
+    return int(lib().sd_verify_linear_workspace_size(ctypes.byref(desc)))
+
+
+def sd_verify_linear(x, w, y, *, workspace=None, stream=None):
+    """y = x w^T for bf16 x [m, k], w [n, k] into bf16 y [m, n]."""
+    _need(x, "x", torch.bfloat16)
+    _need(w, "w", torch.bfloat16, x.device)
+    _need(y, "y", torch.bfloat16, x.device)
+    if x.dim() != 2 or w.dim() != 2 or y.dim() != 2:
+        raise ValueError("x, w and y must be 2-d")
+    m, k = x.shape
+    n = w.shape[0]
+    if w.shape[1] != k or tuple(y.shape) != (m, n):
+        raise ValueError(f"shapes x {tuple(x.shape)}, w {tuple(w.shape)}, y {tuple(y.shape)} do not match")
+    desc = linear_desc(m, n, k)
+    need = sd_verify_linear_workspace_size(desc)
+    ws = _workspace(need, x.device, workspace)
+    _check(lib().sd_verify_linear(ctypes.byref(desc), _ptr(x), _ptr(w), _ptr(y), _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(x.device, stream)))
 
 
 def sd_version() -> str:

@@ -157,6 +157,18 @@ sd_status run_accept(const sd_accept_desc* d, int32_t total_q, const float* targ
   return SD_OK;
 }
 
+sd_status check_gemm(const sd_linear_desc* d) {
+  if (!d) return fail(SD_ERR_INVALID_ARG, "linear-layer descriptor is NULL");
+  if (d->m < 0) return fail(SD_ERR_INVALID_ARG, "m=%d must be >= 0", d->m);
+  if (d->n < 1 || d->k < 1) return fail(SD_ERR_INVALID_ARG, "n=%d and k=%d must be >= 1", d->n, d->k);
+  if (d->n % 128 != 0) return fail(SD_ERR_UNSUPPORTED, "n=%d: only multiples of 128 are supported", d->n);
+  if (d->k % 64 != 0) return fail(SD_ERR_UNSUPPORTED, "k=%d: only multiples of 64 are supported", d->k);
+  if ((long long)d->m * d->n > 0x7fffffffLL || (long long)d->n * d->k > 0x7fffffffLL ||
+      (long long)d->m * d->k > 0x7fffffffLL)
+    return fail(SD_ERR_UNSUPPORTED, "m*n, n*k and m*k must each be below 2^31");
+  return SD_OK;
+}
+
 }  // namespace
 
 #define SD_EXPORT __attribute__((visibility("default")))
@@ -217,6 +229,37 @@ SD_EXPORT sd_status sd_verify_step(const sd_attn_desc* attn, const sd_accept_des
   if (s != SD_OK) return s;
   return run_accept(acc, total_q, target_logits, draft_logits, draft_tokens, q_start, uniforms, accept_len,
                     out_tokens, (unsigned char*)workspace + a_bytes, workspace_bytes - a_bytes, stream);
+}
+
+SD_EXPORT size_t sd_verify_linear_workspace_size(const sd_linear_desc* desc) {
+  if (check_gemm(desc) != SD_OK) return 0;
+  return sdv_gemm_workspace_bytes(desc->m, desc->n, desc->k);
+}
+
+SD_EXPORT sd_status sd_verify_linear(const sd_linear_desc* desc, const void* x, const void* w, void* y, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  sd_status s = check_gemm(desc);
+  if (s != SD_OK) return s;
+  if (desc->m == 0) return SD_OK;
+  if (!x || !w || !y) return fail(SD_ERR_INVALID_ARG, "x, w and y must not be NULL");
+  if ((uintptr_t)x % 16 || (uintptr_t)w % 16 || (uintptr_t)y % 16 || (uintptr_t)workspace % 16)
+    return fail(SD_ERR_INVALID_ARG, "x, w, y and workspace must be 16-byte aligned");
+  const size_t need = sdv_gemm_workspace_bytes(desc->m, desc->n, desc->k);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(SD_ERR_WORKSPACE, "linear-layer workspace %zu bytes < required %zu", workspace_bytes, need);
+  SdGemmLaunch a;
+  a.x = x;
+  a.w = w;
+  a.y = y;
+  a.workspace = workspace;
+  a.workspace_bytes = workspace_bytes;
+  a.m = desc->m;
+  a.n = desc->n;
+  a.k = desc->k;
+  a.stream = (hipStream_t)stream;
+  hipError_t e = sdv_gemm_launch(a);
+  if (e != hipSuccess) return fail(SD_ERR_HIP, "verify linear launch: %s", hipGetErrorString(e));
+  return SD_OK;
 }
 
 SD_EXPORT const char* sd_last_error(void) { return g_error.c_str(); }

@@ -287,18 +287,6 @@ __global__ __launch_bounds__(kPlanThreads) void verify_attn_plan(AttnParams p, i
 }
 
 // ---------------------------------------------------------------------------
-// Wait until at most N vector-memory operations of this wave are in flight
-// (LDS-DMA loads count like any other vector load).
-template <int N>
-__device__ __forceinline__ void wait_vmem() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  // gfx9 s_waitcnt immediate: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-__device__ __forceinline__ void wait_lds() {
-  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
-}
 
 // XOR swizzle of the 16-byte chunks of a K row in LDS for verify_attn_main, a
 // function of the key's position in the 32-key tile (64 banks of 4 bytes): the
@@ -313,34 +301,9 @@ __device__ __forceinline__ int key_swz(int k) {
 
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
-// One 16-byte-per-lane global->LDS DMA (global_load_lds_dwordx4, scalar-base
-// form): lane i reads base + voff_i and its 16 bytes land at LDS byte address
-// lds_addr + 16*i; base and lds_addr are wave-uniform (lds_addr goes to M0).
-// Issued as inline asm so that the compiler's waitcount logic does not pace
-// every later LDS read on these loads (it cannot tell ring stages apart and
-// would wait for all of them); the ring waits for them explicitly with
-// s_waitcnt vmcnt before its barrier.  M0 is written only here in this
-// kernel, which a build test checks on the generated ISA.
-__device__ __forceinline__ void dma16(const unsigned char* base, unsigned voff, unsigned lds_addr) {
-  // readfirstlane returns int: go through unsigned so the low word is zero-extended
-  const uint64_t b = (uint64_t)base;
-  const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(b >> 32));
-  const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)b);
-  const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :
-               : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(sb)
-               : "memory", "m0");
-}
-
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-__device__ __forceinline__ void block_sync() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 // Reductions over the four lanes {l, l^16, l^32, l^48} that hold one query row.
 __device__ __forceinline__ float row_max4(float v) {

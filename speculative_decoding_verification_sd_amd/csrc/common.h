@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 namespace sdv {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -22,6 +24,46 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Wait until at most N vector-memory operations of this wave are in flight
+// (LDS-DMA loads count like any other vector load).
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // gfx9 s_waitcnt immediate: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+__device__ __forceinline__ void wait_lds() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+}
+
+__device__ __forceinline__ void block_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One 16-byte-per-lane global->LDS DMA (global_load_lds_dwordx4, scalar-base
+// form): lane i reads base + voff_i and its 16 bytes land at LDS byte address
+// lds_addr + 16*i; base and lds_addr are wave-uniform (lds_addr goes to M0).
+// Issued as inline asm so that the compiler's waitcount logic does not pace
+// every later LDS read on these loads (it cannot tell ring stages apart and
+// would wait for all of them); the ring waits for them explicitly with
+// s_waitcnt vmcnt before its barrier.  M0 is written only here in the
+// kernels that use it, which a build test checks on the generated ISA.
+__device__ __forceinline__ void dma16(const unsigned char* base, unsigned voff, unsigned lds_addr) {
+  // readfirstlane returns int: go through unsigned so the low word is zero-extended
+  const uint64_t b = (uint64_t)base;
+  const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(b >> 32));
+  const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)b);
+  const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(sb)
+               : "memory", "m0");
+}
+
 
 }  // namespace sdv
 
@@ -58,3 +100,16 @@ size_t sdv_attn_workspace_bytes(int B, int Hkv, int G, int head_dim, int max_pag
 hipError_t sdv_attn_launch(const SdAttnLaunch& a);
 size_t sdv_accept_workspace_bytes(int B, int T, int V, int stochastic);
 hipError_t sdv_accept_launch(const SdAccLaunch& a);
+
+struct SdGemmLaunch {
+  const void* x;
+  const void* w;
+  void* y;
+  void* workspace;
+  size_t workspace_bytes;
+  int m, n, k;
+  hipStream_t stream;
+};
+
+size_t sdv_gemm_workspace_bytes(int m, int n, int k);
+hipError_t sdv_gemm_launch(const SdGemmLaunch& a);

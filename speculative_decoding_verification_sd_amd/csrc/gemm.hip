@@ -1,0 +1,237 @@
+// Verify-shaped linear layer on gfx950: y = x W^T.
+//
+// With speculation every linear layer of the target sees M*(1+D) rows in the
+// verify pass instead of M, against the same weight ("Co-Designing AI Models
+// Using Speculative Decoding for Faster LLM Inference", translated page,
+// section "Draft length and performance of linear layers", Figure 3: an
+// expert GEMM of N = K = 6144).  With few rows the product is bound by reading
+// W (N*K*2 bytes); from about 312 rows on (2.5 PFLOP/s over 8 TB/s) it is
+// bound by the bf16 MFMA rate.
+//
+// A workgroup of 4 waves computes a BM x 128 tile of y (BM = 32, 64 or 128,
+// chosen by M) over a range of K.  x and W tiles of 64 k travel global -> LDS
+// with global_load_lds_dwordx4 into a ring of kGemmStages stages, and each wave
+// multiplies 32x32 blocks with v_mfma_f32_32x32x16_bf16 (A = rows of x, B =
+// rows of W, both read from LDS as 16-byte chunks).  When M gives too few tiles
+// to fill the GPU, K is split: each split writes an fp32 partial and a second
+// kernel adds the partials in split order (the result does not depend on
+// timing) and rounds to bf16.
+
+#include "common.h"
+
+namespace sdv {
+
+constexpr int kGemmBN = 128;             // output columns per workgroup
+constexpr int kGemmBK = 64;              // k per ring stage
+constexpr int kGemmStages = 3;
+constexpr int kGemmRowB = kGemmBK * 2;   // bytes of one tile row in LDS: 8 chunks of 16 bytes
+
+struct GemmParams {
+  const unsigned char* x;   // bf16 [m, k]
+  const unsigned char* w;   // bf16 [n, k]
+  uint16_t* y;              // bf16 [m, n]
+  float* part;              // fp32 [ksplit, m, n] when ksplit > 1
+  int m, n, k, kchunk, ksplit;
+};
+
+// The 16-byte chunk c of tile row r sits at physical chunk c ^ ((r / 2) % 8).
+// An MFMA operand read takes 32 consecutive rows at one logical chunk; in each
+// group of 16 lanes the rows then cover all 64 banks once.
+__device__ __forceinline__ int gemm_swz(int r) { return (r >> 1) & 7; }
+
+template <int BM>
+struct GemmShape {
+  static constexpr int WM = BM >= 64 ? 2 : 1;            // 32-row blocks per wave
+  static constexpr int WAVES_M = BM / (32 * WM);
+  static constexpr int WAVES_N = 4 / WAVES_M;
+  static constexpr int WN = (kGemmBN / 32) / WAVES_N;    // 32-column blocks per wave
+  static constexpr int A_BYTES = BM * kGemmRowB;
+  static constexpr int STAGE = A_BYTES + kGemmBN * kGemmRowB;
+  static constexpr int A_LOADS = A_BYTES / 1024;         // one wave-wide DMA instruction moves 1 KB (8 rows)
+  static constexpr int B_LOADS = kGemmBN * kGemmRowB / 1024;
+  static constexpr int LPW = (A_LOADS + B_LOADS) / 4;    // DMA instructions per wave per stage
+  static_assert(WAVES_M * WAVES_N == 4 && WN >= 1 && (A_LOADS + B_LOADS) % 4 == 0, "tile shape");
+};
+
+template <int BM>
+__global__ __launch_bounds__(256) void verify_gemm(GemmParams p) {
+  using SH = GemmShape<BM>;
+  constexpr int S = kGemmStages;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[S * SH::STAGE];
+  const unsigned lds_base = (unsigned)(size_t)(__attribute__((address_space(3))) unsigned char*)smem;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / SH::WAVES_N, wn = wave % SH::WAVES_N;
+  const int r32 = lane & 31, hh = lane >> 5;
+  const int m0 = blockIdx.x * BM;
+  const int n0 = blockIdx.y * kGemmBN;
+  const int kz = blockIdx.z;
+  const int kb0 = kz * p.kchunk;
+  const int kb1 = min(p.k, kb0 + p.kchunk);
+  const int nst = (kb1 - kb0) / kGemmBK;
+  const size_t rowg = (size_t)p.k * 2;   // bytes of one row of x or W
+
+  // DMA slots of this wave: instruction j (= wave + 4i) fills rows 8j'..8j'+7
+  // of the A tile (j < A_LOADS) or of the B tile; lane l takes row 8j' + l/8
+  // and physical chunk l % 8, i.e. logical chunk (l % 8) ^ swz(row).
+  unsigned src[SH::LPW], dst[SH::LPW];
+  bool isb[SH::LPW];
+#pragma unroll
+  for (int i = 0; i < SH::LPW; ++i) {
+    const int j = wave + 4 * i;
+    isb[i] = j >= SH::A_LOADS;
+    const int jr = isb[i] ? j - SH::A_LOADS : j;
+    const int row = 8 * jr + lane / 8;
+    const int lc = (lane & 7) ^ gemm_swz(row);
+    // rows past the matrix read its last row (their products are never stored)
+    const int grow = isb[i] ? min(n0 + row, p.n - 1) - n0 : min(m0 + row, p.m - 1) - m0;
+    src[i] = (unsigned)((size_t)grow * rowg + lc * 16);
+    dst[i] = (unsigned)((isb[i] ? SH::A_BYTES : 0) + 8 * jr * kGemmRowB);
+  }
+  const unsigned char* xt = p.x + (size_t)m0 * rowg;
+  const unsigned char* wt = p.w + (size_t)n0 * rowg;
+  auto issue = [&](int st, int slot) {
+    const size_t kofs = (size_t)(kb0 + st * kGemmBK) * 2;
+#pragma unroll
+    for (int i = 0; i < SH::LPW; ++i)
+      dma16((isb[i] ? wt : xt) + kofs, src[i], lds_base + (unsigned)(slot * SH::STAGE) + dst[i]);
+  };
+
+  // operand offsets: lane reads row r32 of a 32-row block at logical chunk 2ks + hh
+  int opoff[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) opoff[ks] = r32 * kGemmRowB + (((2 * ks + hh) ^ gemm_swz(r32)) * 16);
+
+  f32x16 acc[SH::WM][SH::WN];
+#pragma unroll
+  for (int i = 0; i < SH::WM; ++i)
+#pragma unroll
+    for (int j = 0; j < SH::WN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+#pragma unroll
+  for (int st = 0; st < S - 1; ++st)
+    if (st < nst) issue(st, st);
+  for (int st = 0; st < nst; ++st) {
+    // stage st has landed when at most the later stages already issued are in flight
+    if (st + 1 < nst) wait_vmem<SH::LPW>();
+    else wait_vmem<0>();
+    block_sync();
+    if (st + S - 1 < nst) issue(st + S - 1, (st + S - 1) % S);
+    const unsigned char* base = smem + (st % S) * SH::STAGE;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8 a[SH::WM], b[SH::WN];
+#pragma unroll
+      for (int i = 0; i < SH::WM; ++i)
+        a[i] = *(const bf16x8*)(base + (wm * SH::WM + i) * 32 * kGemmRowB + opoff[ks]);
+#pragma unroll
+      for (int j = 0; j < SH::WN; ++j)
+        b[j] = *(const bf16x8*)(base + SH::A_BYTES + (wn * SH::WN + j) * 32 * kGemmRowB + opoff[ks]);
+#pragma unroll
+      for (int i = 0; i < SH::WM; ++i)
+#pragma unroll
+        for (int j = 0; j < SH::WN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // D layout: lane l, entry e -> column l % 32, row (e/4)*8 + (l/32)*4 + e%4 of the block
+#pragma unroll
+  for (int i = 0; i < SH::WM; ++i)
+#pragma unroll
+    for (int j = 0; j < SH::WN; ++j) {
+      const int n = n0 + (wn * SH::WN + j) * 32 + r32;
+      if (n >= p.n) continue;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + (wm * SH::WM + i) * 32 + (e >> 2) * 8 + hh * 4 + (e & 3);
+        if (m >= p.m) continue;
+        if (p.ksplit == 1) {
+          const __bf16 v = (__bf16)acc[i][j][e];
+          p.y[(size_t)m * p.n + n] = __builtin_bit_cast(uint16_t, v);
+        } else {
+          p.part[((size_t)kz * p.m + m) * p.n + n] = acc[i][j][e];
+        }
+      }
+    }
+}
+
+// y = bf16(sum over splits, in split order, of the fp32 partials); 4 columns per thread.
+__global__ __launch_bounds__(256) void verify_gemm_reduce(GemmParams p) {
+  const size_t q = (size_t)blockIdx.x * 256 + threadIdx.x;   // index of a 4-column group
+  const size_t total = (size_t)p.m * p.n / 4;
+  if (q >= total) return;
+  const size_t mn = (size_t)p.m * p.n;
+  f32x4 s = *(const f32x4*)(p.part + q * 4);
+  for (int z = 1; z < p.ksplit; ++z) s += *(const f32x4*)(p.part + (size_t)z * mn + q * 4);
+  const bf16x4 t = {(__bf16)s[0], (__bf16)s[1], (__bf16)s[2], (__bf16)s[3]};
+  *(u32x2*)(p.y + q * 4) = __builtin_bit_cast(u32x2, t);
+}
+
+struct GemmPlan {
+  int bm, ksplit, kchunk;
+};
+
+// Tile height by M; K split so that small M still gives about two workgroups
+// per CU, as long as the fp32 partials (written and read once) stay below a
+// quarter of the bytes of W.
+static GemmPlan gemm_plan(int m, int n, int k, int cus) {
+  GemmPlan g;
+  g.bm = m <= 32 ? 32 : m <= 256 ? 64 : 128;
+  const long long tiles = (long long)((m + g.bm - 1) / g.bm) * (n / kGemmBN);
+  const long long target = (long long)cus * (g.bm == 128 ? 1 : 2);
+  const int kblocks = k / kGemmBK;
+  long long ks = (target + tiles - 1) / std::max(1LL, tiles);
+  ks = std::min<long long>(ks, std::max(1, kblocks / 4));
+  ks = std::min<long long>(ks, std::max<long long>(1, (long long)k / (16LL * std::max(1, m))));
+  ks = std::max<long long>(1, ks);
+  const int per = (int)((kblocks + ks - 1) / ks);
+  g.kchunk = per * kGemmBK;
+  g.ksplit = (kblocks + per - 1) / per;
+  return g;
+}
+
+}  // namespace sdv
+
+using namespace sdv;
+
+size_t sdv_gemm_workspace_bytes(int m, int n, int k) {
+  const GemmPlan g = gemm_plan(m, n, k, 256);
+  return g.ksplit > 1 ? (size_t)g.ksplit * m * n * sizeof(float) : 0;
+}
+
+hipError_t sdv_gemm_launch(const SdGemmLaunch& a) {
+  int dev = 0, cus = 256;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  GemmPlan g = gemm_plan(a.m, a.n, a.k, std::min(cus, 256));
+  if (g.ksplit > 1 && (size_t)g.ksplit * a.m * a.n * sizeof(float) > a.workspace_bytes) {
+    // the workspace was sized for the largest CU count: fewer CUs never need more splits
+    return hipErrorInvalidValue;
+  }
+  GemmParams p;
+  p.x = (const unsigned char*)a.x;
+  p.w = (const unsigned char*)a.w;
+  p.y = (uint16_t*)a.y;
+  p.part = (float*)a.workspace;
+  p.m = a.m;
+  p.n = a.n;
+  p.k = a.k;
+  p.kchunk = g.kchunk;
+  p.ksplit = g.ksplit;
+  const dim3 grid((a.m + g.bm - 1) / g.bm, a.n / kGemmBN, g.ksplit);
+  if (g.bm == 32) verify_gemm<32><<<grid, 256, 0, a.stream>>>(p);
+  else if (g.bm == 64) verify_gemm<64><<<grid, 256, 0, a.stream>>>(p);
+  else verify_gemm<128><<<grid, 256, 0, a.stream>>>(p);
+  if (g.ksplit > 1) {
+    const size_t groups = (size_t)a.m * a.n / 4;
+    verify_gemm_reduce<<<(unsigned)((groups + 255) / 256), 256, 0, a.stream>>>(p);
+  }
+  return hipGetLastError();
+}

@@ -137,3 +137,28 @@ def test_binding_validates_tensors_on_cpu():
     with pytest.raises(ValueError, match="device tensor"):
         sdv.sd_verify_attention(q, q, q, torch.zeros(2, 16, dtype=torch.int32), torch.zeros(2, dtype=torch.int32),
                                 torch.zeros(3, dtype=torch.int32), q, group_size=4, max_draft=3)
+
+
+def test_linear_workspace_and_rejections():
+    lib = sdv.lib()
+    # small m splits K (fp32 partials in the workspace); a large m needs none
+    assert sdv.sd_verify_linear_workspace_size(sdv.linear_desc(8, 6144, 6144)) > 0
+    assert sdv.sd_verify_linear_workspace_size(sdv.linear_desc(4096, 6144, 6144)) == 0
+    for (m, n, k), status, needle in [((8, 100, 64), B.SD_ERR_UNSUPPORTED, "n="),
+                                      ((8, 128, 100), B.SD_ERR_UNSUPPORTED, "k="),
+                                      ((-1, 128, 64), B.SD_ERR_INVALID_ARG, "m="),
+                                      ((8, 0, 64), B.SD_ERR_INVALID_ARG, "n=")]:
+        d = sdv.linear_desc(m, n, k)
+        assert sdv.sd_verify_linear_workspace_size(d) == 0
+        assert lib.sd_verify_linear(ctypes.byref(d), None, None, None, None, 0, None) == status
+        assert needle in sdv.sd_last_error()
+    dummy = ctypes.c_void_p(4096)
+    d = sdv.linear_desc(8, 6144, 6144)
+    assert lib.sd_verify_linear(ctypes.byref(d), None, dummy, dummy, dummy, 1 << 30, None) == B.SD_ERR_INVALID_ARG
+    assert lib.sd_verify_linear(ctypes.byref(d), dummy, dummy, dummy, dummy, 16, None) == B.SD_ERR_WORKSPACE
+    assert lib.sd_verify_linear(ctypes.byref(d), ctypes.c_void_p(4100), dummy, dummy, dummy, 1 << 30,
+                                None) == B.SD_ERR_INVALID_ARG
+    assert lib.sd_verify_linear(None, None, None, None, None, 0, None) == B.SD_ERR_INVALID_ARG
+    # m = 0 is a no-op
+    d = sdv.linear_desc(0, 128, 64)
+    assert lib.sd_verify_linear(ctypes.byref(d), None, None, None, None, 0, None) == B.SD_OK
