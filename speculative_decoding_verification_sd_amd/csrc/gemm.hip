@@ -8,12 +8,12 @@
 // W (N*K*2 bytes); from about 312 rows on (2.5 PFLOP/s over 8 TB/s) it is
 // bound by the bf16 MFMA rate.
 //
-// A workgroup of 4 waves computes a BM x 128 tile of y (BM = 32, 64 or 128,
-// chosen by M) over a range of K.  x and W tiles of 64 k travel global -> LDS
-// with global_load_lds_dwordx4 into a ring of kGemmStages stages, and each wave
-// multiplies 32x32 blocks with v_mfma_f32_32x32x16_bf16 (A = rows of x, B =
-// rows of W, both read from LDS as 16-byte chunks).  When M gives too few tiles
-// to fill the GPU, K is split: each split writes an fp32 partial and a second
+// A workgroup of 4 waves computes a BM x BN tile of y (BM = 32, 64 or 128 and
+// BN = 128 or 256, chosen by M) over a range of K.  x and W tiles of 64 k
+// travel global -> LDS with global_load_lds_dwordx4 into a ring of S stages,
+// and each wave multiplies 32x32 blocks with v_mfma_f32_32x32x16_bf16 (A =
+// rows of x, B = rows of W, both read from LDS as 16-byte chunks).  When M
+// gives too few tiles to fill the GPU, K is split: each split writes an fp32 partial and a second
 // kernel adds the partials in split order (the result does not depend on
 // timing) and rounds to bf16.
 
@@ -21,9 +21,7 @@
 
 namespace sdv {
 
-constexpr int kGemmBN = 128;             // output columns per workgroup
 constexpr int kGemmBK = 64;              // k per ring stage
-constexpr int kGemmStages = 3;
 constexpr int kGemmRowB = kGemmBK * 2;   // bytes of one tile row in LDS: 8 chunks of 16 bytes
 
 struct GemmParams {
@@ -32,31 +30,55 @@ struct GemmParams {
   uint16_t* y;              // bf16 [m, n]
   float* part;              // fp32 [ksplit, m, n] when ksplit > 1
   int m, n, k, kchunk, ksplit;
+  int mt, nt;               // tiles along m and n
+  int per_xcd;              // tiles (of mt * nt * ksplit) each of the 8 XCD classes takes
 };
+
+// Tile of the workgroup.  Workgroups are dealt round-robin over the 8 XCDs
+// (each with its own L2), so class c = id % 8 takes the c-th contiguous run
+// of a tile order that walks kGemmGroupM m-tiles across every n-tile before
+// the next group: the workgroups that run together on one XCD then share
+// their x and W slices through its L2.  Returns false past the last tile.
+constexpr int kGemmGroupM = 4;
+__device__ __forceinline__ bool gemm_tile(const GemmParams& p, int& mt, int& nt, int& kz) {
+  const int id = blockIdx.x;
+  const int t = (id & 7) * p.per_xcd + (id >> 3);
+  const int total = p.mt * p.nt * p.ksplit;
+  if ((id >> 3) >= p.per_xcd || t >= total) return false;
+  kz = t / (p.mt * p.nt);
+  const int r = t - kz * (p.mt * p.nt);
+  const int gsz = kGemmGroupM * p.nt;
+  const int g = r / gsz;
+  const int gm = min(kGemmGroupM, p.mt - g * kGemmGroupM);   // m-tiles in this group
+  const int q = r - g * gsz;
+  mt = g * kGemmGroupM + q % gm;
+  nt = q / gm;
+  return true;
+}
 
 // The 16-byte chunk c of tile row r sits at physical chunk c ^ ((r / 2) % 8).
 // An MFMA operand read takes 32 consecutive rows at one logical chunk; in each
 // group of 16 lanes the rows then cover all 64 banks once.
 __device__ __forceinline__ int gemm_swz(int r) { return (r >> 1) & 7; }
 
-template <int BM>
+template <int BM, int BN>
 struct GemmShape {
-  static constexpr int WM = BM >= 64 ? 2 : 1;            // 32-row blocks per wave
-  static constexpr int WAVES_M = BM / (32 * WM);
+  static constexpr int WAVES_M = BM >= 128 ? 2 : 1;      // the 4 waves as WAVES_M x WAVES_N
   static constexpr int WAVES_N = 4 / WAVES_M;
-  static constexpr int WN = (kGemmBN / 32) / WAVES_N;    // 32-column blocks per wave
+  static constexpr int WM = BM / (32 * WAVES_M);         // 32-row blocks per wave
+  static constexpr int WN = BN / (32 * WAVES_N);         // 32-column blocks per wave
   static constexpr int A_BYTES = BM * kGemmRowB;
-  static constexpr int STAGE = A_BYTES + kGemmBN * kGemmRowB;
+  static constexpr int STAGE = A_BYTES + BN * kGemmRowB;
   static constexpr int A_LOADS = A_BYTES / 1024;         // one wave-wide DMA instruction moves 1 KB (8 rows)
-  static constexpr int B_LOADS = kGemmBN * kGemmRowB / 1024;
+  static constexpr int B_LOADS = BN * kGemmRowB / 1024;
   static constexpr int LPW = (A_LOADS + B_LOADS) / 4;    // DMA instructions per wave per stage
-  static_assert(WAVES_M * WAVES_N == 4 && WN >= 1 && (A_LOADS + B_LOADS) % 4 == 0, "tile shape");
+  static_assert(WM >= 1 && WN >= 1 && (A_LOADS + B_LOADS) % 4 == 0, "tile shape");
 };
 
-template <int BM>
+template <int BM, int BN, int S>
 __global__ __launch_bounds__(256) void verify_gemm(GemmParams p) {
-  using SH = GemmShape<BM>;
-  constexpr int S = kGemmStages;
+  using SH = GemmShape<BM, BN>;
+  static_assert(S >= 2 && S <= 4 && (S - 2) * SH::LPW < 64, "ring depth");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[S * SH::STAGE];
   const unsigned lds_base = (unsigned)(size_t)(__attribute__((address_space(3))) unsigned char*)smem;
 
@@ -65,9 +87,10 @@ __global__ __launch_bounds__(256) void verify_gemm(GemmParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / SH::WAVES_N, wn = wave % SH::WAVES_N;
   const int r32 = lane & 31, hh = lane >> 5;
-  const int m0 = blockIdx.x * BM;
-  const int n0 = blockIdx.y * kGemmBN;
-  const int kz = blockIdx.z;
+  int mt, nt, kz;
+  if (!gemm_tile(p, mt, nt, kz)) return;
+  const int m0 = mt * BM;
+  const int n0 = nt * BN;
   const int kb0 = kz * p.kchunk;
   const int kb1 = min(p.k, kb0 + p.kchunk);
   const int nst = (kb1 - kb0) / kGemmBK;
@@ -117,7 +140,9 @@ __global__ __launch_bounds__(256) void verify_gemm(GemmParams p) {
     if (st < nst) issue(st, st);
   for (int st = 0; st < nst; ++st) {
     // stage st has landed when at most the later stages already issued are in flight
-    if (st + 1 < nst) wait_vmem<SH::LPW>();
+    const int later = min(nst - st - 1, S - 2);
+    if (later >= S - 2) wait_vmem<(S - 2) * SH::LPW>();
+    else if (later >= 1) wait_vmem<SH::LPW>();
     else wait_vmem<0>();
     block_sync();
     if (st + S - 1 < nst) issue(st + S - 1, (st + S - 1) % S);
@@ -173,21 +198,23 @@ __global__ __launch_bounds__(256) void verify_gemm_reduce(GemmParams p) {
 }
 
 struct GemmPlan {
-  int bm, ksplit, kchunk;
+  int bm, bn, ksplit, kchunk;
 };
 
-// Tile height by M; K split so that small M still gives about two workgroups
-// per CU, as long as the fp32 partials (written and read once) stay below a
-// quarter of the bytes of W.
+// Tile by M (128 x 256 when that still gives two rounds of workgroups); K
+// split so that small M still fills about two workgroups per CU in one round,
+// as long as the fp32 partials (written and read once) stay below the bytes
+// of W.
 static GemmPlan gemm_plan(int m, int n, int k, int cus) {
   GemmPlan g;
   g.bm = m <= 32 ? 32 : m <= 256 ? 64 : 128;
-  const long long tiles = (long long)((m + g.bm - 1) / g.bm) * (n / kGemmBN);
+  g.bn = (g.bm == 128 && n % 256 == 0 && (long long)((m + 127) / 128) * (n / 256) >= 2LL * cus) ? 256 : 128;
+  const long long tiles = (long long)((m + g.bm - 1) / g.bm) * (n / g.bn);
   const long long target = (long long)cus * (g.bm == 128 ? 1 : 2);
   const int kblocks = k / kGemmBK;
-  long long ks = (target + tiles - 1) / std::max(1LL, tiles);
+  long long ks = target / std::max(1LL, tiles);
   ks = std::min<long long>(ks, std::max(1, kblocks / 4));
-  ks = std::min<long long>(ks, std::max<long long>(1, (long long)k / (16LL * std::max(1, m))));
+  ks = std::min<long long>(ks, std::max<long long>(1, (long long)k / (4LL * std::max(1, m))));
   ks = std::max<long long>(1, ks);
   const int per = (int)((kblocks + ks - 1) / ks);
   g.kchunk = per * kGemmBK;
@@ -225,10 +252,15 @@ hipError_t sdv_gemm_launch(const SdGemmLaunch& a) {
   p.k = a.k;
   p.kchunk = g.kchunk;
   p.ksplit = g.ksplit;
-  const dim3 grid((a.m + g.bm - 1) / g.bm, a.n / kGemmBN, g.ksplit);
-  if (g.bm == 32) verify_gemm<32><<<grid, 256, 0, a.stream>>>(p);
-  else if (g.bm == 64) verify_gemm<64><<<grid, 256, 0, a.stream>>>(p);
-  else verify_gemm<128><<<grid, 256, 0, a.stream>>>(p);
+  p.mt = (a.m + g.bm - 1) / g.bm;
+  p.nt = a.n / g.bn;
+  const long long tiles = (long long)p.mt * p.nt * g.ksplit;
+  p.per_xcd = (int)((tiles + 7) / 8);
+  const dim3 grid((unsigned)(8LL * p.per_xcd));
+  if (g.bm == 32) verify_gemm<32, 128, 4><<<grid, 256, 0, a.stream>>>(p);
+  else if (g.bm == 64) verify_gemm<64, 128, 3><<<grid, 256, 0, a.stream>>>(p);
+  else if (g.bn == 128) verify_gemm<128, 128, 4><<<grid, 256, 0, a.stream>>>(p);
+  else verify_gemm<128, 256, 3><<<grid, 256, 0, a.stream>>>(p);
   if (g.ksplit > 1) {
     const size_t groups = (size_t)a.m * a.n / 4;
     verify_gemm_reduce<<<(unsigned)((groups + 255) / 256), 256, 0, a.stream>>>(p);
