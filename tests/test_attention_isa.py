@@ -1,5 +1,6 @@
-"""Checks on the generated gfx950 ISA of the verify-attention kernels (CPU only:
-hipcc cross-compiles the device code to assembly).
+"""Checks on the generated gfx950 ISA of the verify-attention and verify-linear
+kernels, the ones that use the LDS-DMA ring (CPU only: hipcc cross-compiles the
+device code to assembly).
 
 * M0 is written only by the LDS-DMA sequence (s_mov_b32 m0 / s_nop / global_load_lds),
   so the inline-asm DMA's M0 clobber cannot disturb anything the compiler keeps in M0.
@@ -18,26 +19,46 @@ import pytest
 from speculative_decoding_verification_sd_amd import build as B
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SRC = os.path.join(ROOT, "speculative_decoding_verification_sd_amd", "csrc", "attention.hip")
+CSRC = os.path.join(ROOT, "speculative_decoding_verification_sd_amd", "csrc")
+# translation unit, kernels that use the DMA ring, minimum instantiations
+UNITS = {
+    "attention": ("attention.hip", r"verify_attn_(?:main|wide)", 8),
+    "gemm": ("gemm.hip", r"verify_gemmI", 4),
+}
 
 
-@pytest.fixture(scope="module")
-def kernels(tmp_path_factory):
+def _compile(tmp_path_factory, unit):
     try:
         cc = B.hipcc()
     except RuntimeError:
         pytest.skip("hipcc not available")
-    out = tmp_path_factory.mktemp("isa") / "attention.s"
-    cmd = [cc, *B.COMMON_FLAGS, *B.DEVICE_FLAGS, *B.FILE_FLAGS.get("attention.hip", []), "--cuda-device-only",
-           "-S", "-Wno-inline-asm", SRC, "-o", str(out)]
+    fname, pattern, least = UNITS[unit]
+    out = tmp_path_factory.mktemp("isa") / (unit + ".s")
+    cmd = [cc, *B.COMMON_FLAGS, *B.DEVICE_FLAGS, *B.FILE_FLAGS.get(fname, []), "--cuda-device-only",
+           "-S", "-Wno-inline-asm", os.path.join(CSRC, fname), "-o", str(out)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-3000:]
     text = out.read_text()
     found = {}
-    for m in re.finditer(r"^(_Z\w*verify_attn_(?:main|wide)\w*):[^\n]*\n(.*?)^\s*s_endpgm", text, re.M | re.S):
+    for m in re.finditer(r"^(_Z\w*" + pattern + r"\w*):[^\n]*\n(.*?)^\s*s_endpgm", text, re.M | re.S):
         found[m.group(1)] = [l.strip() for l in m.group(2).split("\n")]
-    assert len(found) >= 8, "expected every verify_attn_main and verify_attn_wide instantiation"
+    assert len(found) >= least, f"expected every instantiation of the {unit} kernels"
     return found
+
+
+@pytest.fixture(scope="module")
+def attention_kernels(tmp_path_factory):
+    return _compile(tmp_path_factory, "attention")
+
+
+@pytest.fixture(scope="module")
+def gemm_kernels(tmp_path_factory):
+    return _compile(tmp_path_factory, "gemm")
+
+
+@pytest.fixture(params=["attention", "gemm"])
+def kernels(request):
+    return request.getfixturevalue(request.param + "_kernels")
 
 
 def _instrs(lines):
