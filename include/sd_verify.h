@@ -181,6 +181,56 @@ sd_status sd_verify_step(const sd_attn_desc* attn, const sd_accept_desc* acc, in
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Tree verification (an extension next to the verify step proper).  The drafts
+ * of a sequence may form a tree instead of one chain: the target scores the
+ * whole tree in one pass with an attention mask that keeps the causal order
+ * inside each branch, and the longest accepted candidate prefix moves on (the
+ * LLM inference handbook, section "Medusa").
+ *
+ * Layout, as for the linear block: sequence b has 1+T_b tree nodes at verify
+ * rows q_start[b] .. q_start[b+1]-1, node 0 being the root (the last emitted
+ * token) and nodes 1..T_b drafted tokens, numbered so that every parent comes
+ * before its children.  With d0 = q_start[b]-b, parents[d0+i-1] in [0, i) is
+ * the parent of node i and tree_tokens[d0+i-1] its token.  The nodes' keys and
+ * values are the last 1+T_b positions of the sequence's cache, in node order.
+ */
+
+/*
+ * Attention under the tree mask: node i attends to the keys before the tree
+ * and to the nodes on its root path (its ancestors and itself); otherwise as
+ * sd_verify_attention, with the same workspace size query.  At most 64 nodes
+ * per tree (desc->max_draft <= 63).  A parent outside [0, i) is taken as the
+ * root.  parents int32 [total_q - B] (may be NULL when total_q == B).
+ */
+sd_status sd_verify_tree_attention(const sd_attn_desc* desc, int32_t total_q,
+                                   const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* block_table, const int32_t* kv_len,
+                                   const int32_t* q_start, const int32_t* parents, void* out,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes sd_tree_accept needs (desc->mode must be SD_ACCEPT_GREEDY); 0 if invalid. */
+size_t sd_tree_accept_workspace_size(const sd_accept_desc* desc, int32_t total_q);
+
+/*
+ * Greedy acceptance of a draft tree.  The root is accepted; node c is accepted
+ * iff its parent p is, and its token lies in [0, V) and equals the lowest-index
+ * maximum of target row q_start[b]+p.  The accepted node of largest depth (the
+ * lowest index among equal depths) ends the path of L nodes below the root:
+ *   accept_len[b] = L+1;
+ *   out_tokens[t0+k] = the token of the path's node at depth k+1 (k < L),
+ *   out_tokens[t0+L] = the target's top token at the path's last node,
+ *   out_nodes[t0+k] = the index of the path's node at depth k+1 (k < L);
+ * other entries up to t0+T_b are -1.  desc->mode must be SD_ACCEPT_GREEDY.
+ *
+ *   target_logits fp32 [total_q, V];  tree_tokens, parents int32 [total_q - B]
+ *   accept_len int32 [B]; out_tokens, out_nodes int32 [total_q] (written)
+ */
+sd_status sd_tree_accept(const sd_accept_desc* desc, int32_t total_q, const float* target_logits,
+                         const int32_t* tree_tokens, const int32_t* q_start, const int32_t* parents,
+                         int32_t* accept_len, int32_t* out_tokens, int32_t* out_nodes,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Verify-shaped linear layer (an extension next to the verify step proper).
  * With speculation every linear layer of the target sees M*(1+D) rows in the
  * verify pass instead of M, against the same weight: the GEMM-M grows by the

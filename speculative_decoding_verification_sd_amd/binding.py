@@ -77,6 +77,10 @@ SIGNATURES = {
     "sd_verify_step_workspace_size": (_SZ, [ctypes.POINTER(sd_attn_desc), ctypes.POINTER(sd_accept_desc), _I]),
     "sd_verify_step": (ctypes.c_int, [ctypes.POINTER(sd_attn_desc), ctypes.POINTER(sd_accept_desc), _I,
                                       _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "sd_verify_tree_attention": (ctypes.c_int, [ctypes.POINTER(sd_attn_desc), _I, _P, _P, _P, _P, _P, _P, _P, _P,
+                                                _P, _SZ, _P]),
+    "sd_tree_accept_workspace_size": (_SZ, [ctypes.POINTER(sd_accept_desc), _I]),
+    "sd_tree_accept": (ctypes.c_int, [ctypes.POINTER(sd_accept_desc), _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "sd_verify_linear_workspace_size": (_SZ, [ctypes.POINTER(sd_linear_desc)]),
     "sd_verify_linear": (ctypes.c_int, [ctypes.POINTER(sd_linear_desc), _P, _P, _P, _P, _SZ, _P]),
     "sd_last_error": (ctypes.c_char_p, []),
@@ -245,6 +249,48 @@ def sd_verify_step(q, k_cache, v_cache, block_table, kv_len, q_start, attn_out, 
                                 _ptr(target_logits), _ptr(draft_logits if stoch else None), _ptr(draft_tokens),
                                 _ptr(uniforms if stoch else None), _ptr(accept_len), _ptr(out_tokens), _ptr(ws),
                                 ws.numel() * ws.element_size(), _stream(q.device, stream)))
+
+
+def sd_verify_tree_attention(q, k_cache, v_cache, block_table, kv_len, q_start, parents, out, *, group_size: int,
+                             max_draft: int, softmax_scale: float = 0.0, kv_chunk: int = 0,
+                             workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Verify attention under the ancestor masks of per-sequence draft trees
+    (parents int32 [total_q - B]: parent of node i of sequence b at (q_start[b]-b)+i-1)."""
+    _check_attention_args(q, k_cache, v_cache, block_table, kv_len, q_start, out)
+    B = block_table.shape[0]
+    _need(parents, "parents", torch.int32, q.device)
+    if parents.shape != (q.shape[0] - B,):
+        raise ValueError("parents must be [total_q - B]")
+    desc = attn_desc(q, k_cache, block_table, group_size, max_draft, softmax_scale, out.dtype, kv_chunk)
+    total_q = q.shape[0]
+    ws = _workspace(sd_verify_attention_workspace_size(desc, total_q), q.device, workspace)
+    _check(lib().sd_verify_tree_attention(ctypes.byref(desc), total_q, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                          _ptr(block_table), _ptr(kv_len), _ptr(q_start), _ptr(parents), _ptr(out),
+                                          _ptr(ws), ws.numel() * ws.element_size(), _stream(q.device, stream)))
+
+
+def sd_tree_accept_workspace_size(desc: sd_accept_desc, total_q: int) -> int:
+    return int(lib().sd_tree_accept_workspace_size(ctypes.byref(desc), total_q))
+
+
+def sd_tree_accept(target_logits, tree_tokens, q_start, parents, accept_len, out_tokens, out_nodes, *,
+                   max_draft: int, workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Greedy acceptance of per-sequence draft trees (see the C header)."""
+    dev = target_logits.device
+    _need(target_logits, "target_logits", torch.float32)
+    for t, name in ((tree_tokens, "tree_tokens"), (q_start, "q_start"), (parents, "parents"),
+                    (accept_len, "accept_len"), (out_tokens, "out_tokens"), (out_nodes, "out_nodes")):
+        _need(t, name, torch.int32, dev)
+    B = q_start.shape[0] - 1
+    T, V = target_logits.shape
+    if tree_tokens.shape != (T - B,) or parents.shape != (T - B,) or accept_len.shape != (B,) or \
+            out_tokens.shape != (T,) or out_nodes.shape != (T,):
+        raise ValueError("tree_tokens, parents [T_q - B]; accept_len [B]; out_tokens, out_nodes [T_q] expected")
+    desc = accept_desc(B, V, max_draft, "greedy")
+    ws = _workspace(sd_tree_accept_workspace_size(desc, T), dev, workspace)
+    _check(lib().sd_tree_accept(ctypes.byref(desc), T, _ptr(target_logits), _ptr(tree_tokens), _ptr(q_start),
+                                _ptr(parents), _ptr(accept_len), _ptr(out_tokens), _ptr(out_nodes), _ptr(ws),
+                                ws.numel() * ws.element_size(), _stream(dev, stream)))
 
 
 def linear_desc(m: int, n: int, k: int) -> sd_linear_desc:

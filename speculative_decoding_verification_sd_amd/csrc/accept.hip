@@ -256,6 +256,78 @@ __global__ __launch_bounds__(kAccThreads) void accept_decide(AccParams p) {
   if (tid == 0) p.accept_len[b] = n + 1;
 }
 
+// ---------------------------------------------------------------------------
+// Greedy acceptance of a draft tree (one workgroup per sequence).  Node i of
+// sequence b (i = 0..T, node 0 the root) is verify row t0+i; nodes 1..T carry
+// tokens[d0+i-1] and parents[d0+i-1] < i.  Node c is accepted iff its parent p
+// is, and its token equals the top token of row p; the deepest accepted node
+// (the lowest index among equal depths) ends the path, which is emitted with
+// the target's top token at that node after it (the LLM inference handbook,
+// section "Medusa": the longest accepted candidate prefix moves on).
+__global__ __launch_bounds__(kAccThreads) void accept_tree(AccParams p, const int* parents, int* out_nodes) {
+  extern __shared__ int tdyn[];                  // amax[T+1], depth[T+1], par[T+1]
+  __shared__ RowPart stage[kDecideSlots];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int t0 = p.q_start[b];
+  const int T = seq_d(p, b);
+  const int d0 = t0 - b;
+  if (!seq_ok(p, t0, T, d0)) {
+    if (tid == 0) p.accept_len[b] = 0;
+    return;
+  }
+  int* amax = tdyn;
+  int* depth = tdyn + (p.max_draft + 1);
+  int* par = tdyn + 2 * (p.max_draft + 1);
+
+  const int nrows = T + 1;
+  const int rows_per_pass = max(1, kDecideSlots / p.nchunk);
+  for (int r0 = 0; r0 < nrows; r0 += rows_per_pass) {
+    const int nr = min(rows_per_pass, nrows - r0);
+    __syncthreads();
+    for (int e = tid; e < nr * p.nchunk; e += kAccThreads)
+      stage[e] = p.part[(size_t)(t0 + r0 + e / p.nchunk) * p.nchunk + (e % p.nchunk)];
+    __syncthreads();
+    for (int rr = tid; rr < nr; rr += kAccThreads) {
+      const RowPart* pr = stage + rr * p.nchunk;
+      float M = -INFINITY;
+      int ai = INT_MAX;
+      for (int c = 0; c < p.nchunk; ++c)
+        if (better(pr[c].m, pr[c].idx, M, ai)) { M = pr[c].m; ai = pr[c].idx; }
+      amax[r0 + rr] = ai;
+    }
+  }
+  // parents out of order are taken as the root (so that every walk below ends)
+  for (int i = 1 + tid; i <= T; i += kAccThreads) {
+    const int q = parents[d0 + i - 1];
+    par[i] = (q >= 0 && q < i) ? q : 0;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    // depth[i] >= 0: accepted at that depth; -1: not accepted
+    depth[0] = 0;
+    int best = 0;
+    for (int i = 1; i <= T; ++i) {
+      const int q = par[i];
+      const int x = p.tokens[d0 + i - 1];
+      depth[i] = (depth[q] >= 0 && x >= 0 && x < p.V && x == amax[q]) ? depth[q] + 1 : -1;
+      if (depth[i] > depth[best]) best = i;
+    }
+    const int L = depth[best];
+    for (int i = best, k = L - 1; i != 0; i = par[i], --k) {
+      p.out_tokens[t0 + k] = p.tokens[d0 + i - 1];
+      out_nodes[t0 + k] = i;
+    }
+    p.out_tokens[t0 + L] = amax[best];
+    p.accept_len[b] = L + 1;
+    depth[0] = L;                                // hand L to the other threads
+  }
+  __syncthreads();
+  const int L = depth[0];
+  for (int k = L + 1 + tid; k <= T; k += kAccThreads) p.out_tokens[t0 + k] = -1;
+  for (int k = L + tid; k <= T; k += kAccThreads) out_nodes[t0 + k] = -1;
+}
+
 // fp64 weights of one token of the sampling row from its target logit tl and
 // draft logit dl: pj = p(j); w = max(0, p(j) - q(j)) at a rejection, p(j) when
 // every draft passed.  A token past the vocabulary comes in as -inf (weight 0).
@@ -573,5 +645,35 @@ hipError_t sdv_accept_launch(const SdAccLaunch& a) {
     else accept_rowstats<0, 0><<<grid1, kAccThreads, 0, a.stream>>>(p);
     accept_decide<<<a.B, kAccThreads, (size_t)(a.max_draft + 1) * sizeof(int), a.stream>>>(p);
   }
+  return hipGetLastError();
+}
+
+hipError_t sdv_tree_accept_launch(const SdAccLaunch& a, const int32_t* parents, int32_t* out_nodes) {
+  const AccLayout L = acc_layout(a.B, a.T, a.V, 0);
+  unsigned char* ws = (unsigned char*)a.workspace;
+  AccParams p;
+  p.target = a.target;
+  p.draft = nullptr;
+  p.tokens = a.tokens;
+  p.q_start = a.q_start;
+  p.uniforms = nullptr;
+  p.accept_len = a.accept_len;
+  p.out_tokens = a.out_tokens;
+  p.part = (RowPart*)(ws + L.part_off);
+  p.arrived = (unsigned*)(ws + L.arrived_off);
+  p.rsum = nullptr;
+  p.rsub = nullptr;
+  p.B = a.B;
+  p.T = a.T;
+  p.V = a.V;
+  p.nchunk = L.nchunk;
+  p.nschunk = L.nschunk;
+  p.max_draft = a.max_draft;
+  const bool vec4 = (a.V % 4 == 0) && ((uintptr_t)a.target % 16 == 0);
+  p.vec4 = vec4;
+  const unsigned grid1 = (unsigned)((size_t)a.T * L.nchunk);
+  if (vec4) accept_rowstats<0, 1><<<grid1, kAccThreads, 0, a.stream>>>(p);
+  else accept_rowstats<0, 0><<<grid1, kAccThreads, 0, a.stream>>>(p);
+  accept_tree<<<a.B, kAccThreads, (size_t)3 * (a.max_draft + 1) * sizeof(int), a.stream>>>(p, parents, out_nodes);
   return hipGetLastError();
 }

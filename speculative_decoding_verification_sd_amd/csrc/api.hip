@@ -84,7 +84,7 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 sd_status run_attention(const sd_attn_desc* d, int32_t total_q, const void* q, const void* k,
                         const void* v, const int32_t* bt, const int32_t* kv_len, const int32_t* q_start,
-                        void* out, void* ws, size_t ws_bytes, void* stream) {
+                        void* out, void* ws, size_t ws_bytes, void* stream, const int32_t* parents = nullptr) {
   sd_status s = check_attn(d, total_q);
   if (s != SD_OK) return s;
   if (d->num_seqs == 0) return SD_OK;
@@ -102,6 +102,7 @@ sd_status run_attention(const sd_attn_desc* d, int32_t total_q, const void* q, c
   a.block_table = bt;
   a.kv_len = kv_len;
   a.q_start = q_start;
+  a.parents = parents;
   a.out = out;
   a.workspace = ws;
   a.B = d->num_seqs;
@@ -229,6 +230,60 @@ SD_EXPORT sd_status sd_verify_step(const sd_attn_desc* attn, const sd_accept_des
   if (s != SD_OK) return s;
   return run_accept(acc, total_q, target_logits, draft_logits, draft_tokens, q_start, uniforms, accept_len,
                     out_tokens, (unsigned char*)workspace + a_bytes, workspace_bytes - a_bytes, stream);
+}
+
+SD_EXPORT sd_status sd_verify_tree_attention(const sd_attn_desc* desc, int32_t total_q, const void* q,
+                                             const void* k_cache, const void* v_cache, const int32_t* block_table,
+                                             const int32_t* kv_len, const int32_t* q_start, const int32_t* parents,
+                                             void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  sd_status s = check_attn(desc, total_q);
+  if (s != SD_OK) return s;
+  if (desc->max_draft > 63) return fail(SD_ERR_UNSUPPORTED, "max_draft=%d: a draft tree has at most 64 nodes", desc->max_draft);
+  if (desc->num_seqs > 0 && total_q > desc->num_seqs && !parents)
+    return fail(SD_ERR_INVALID_ARG, "parents must not be NULL");
+  // (without drafts every row is a root, which the causal path computes alike)
+  return run_attention(desc, total_q, q, k_cache, v_cache, block_table, kv_len, q_start, out, workspace,
+                       workspace_bytes, stream, parents);
+}
+
+SD_EXPORT size_t sd_tree_accept_workspace_size(const sd_accept_desc* desc, int32_t total_q) {
+  if (check_accept(desc, total_q) != SD_OK || desc->mode != SD_ACCEPT_GREEDY) return 0;
+  return acc_ws(desc, total_q);
+}
+
+SD_EXPORT sd_status sd_tree_accept(const sd_accept_desc* d, int32_t total_q, const float* target_logits,
+                                   const int32_t* tree_tokens, const int32_t* q_start, const int32_t* parents,
+                                   int32_t* accept_len, int32_t* out_tokens, int32_t* out_nodes, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  sd_status s = check_accept(d, total_q);
+  if (s != SD_OK) return s;
+  if (d->mode != SD_ACCEPT_GREEDY) return fail(SD_ERR_UNSUPPORTED, "draft trees are accepted greedily only");
+  if (d->num_seqs == 0) return SD_OK;
+  const bool any = total_q > d->num_seqs;
+  if (!target_logits || !q_start || !accept_len || !out_tokens || !out_nodes || (any && (!tree_tokens || !parents)))
+    return fail(SD_ERR_INVALID_ARG, "a required tree-accept pointer is NULL");
+  const size_t need = acc_ws(d, total_q);
+  if (!workspace || workspace_bytes < need)
+    return fail(SD_ERR_WORKSPACE, "tree-accept workspace %zu bytes < required %zu", workspace_bytes, need);
+  if ((uintptr_t)workspace % 16) return fail(SD_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  SdAccLaunch a;
+  a.target = target_logits;
+  a.draft = nullptr;
+  a.tokens = tree_tokens;
+  a.q_start = q_start;
+  a.uniforms = nullptr;
+  a.accept_len = accept_len;
+  a.out_tokens = out_tokens;
+  a.workspace = workspace;
+  a.B = d->num_seqs;
+  a.T = total_q;
+  a.V = d->vocab;
+  a.max_draft = d->max_draft;
+  a.stochastic = 0;
+  a.stream = (hipStream_t)stream;
+  hipError_t e = sdv_tree_accept_launch(a, parents, out_nodes);   // (parents is read only for drafted nodes)
+  if (e != hipSuccess) return fail(SD_ERR_HIP, "tree accept launch: %s", hipGetErrorString(e));
+  return SD_OK;
 }
 
 SD_EXPORT size_t sd_verify_linear_workspace_size(const sd_linear_desc* desc) {

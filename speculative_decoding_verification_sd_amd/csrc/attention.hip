@@ -74,6 +74,7 @@ struct AttnParams {
   float* part_o;    // [item_cap, rpad, d]   unnormalised partial outputs
   float* part_ml;   // [item_cap, rpad, 2]   (running max in log2 units, sum)
   int* plan;        // [16 + 2B + 1]: chunk, total items, full items, work counters, item_start, tail_pos
+  const unsigned long long* tmask;   // NULL: causal block; else per verify row, the nodes of its draft tree it sees
   ItemDesc* items;  // [item_cap]
   int B, Hkv, G, max_pages, num_pages, max_draft, rpad, total_q, item_cap;
   float scale_log2;
@@ -85,6 +86,28 @@ __device__ __forceinline__ int seq_keys(const AttnParams& p, int b) {
 
 __device__ __forceinline__ int seq_drafts(const AttnParams& p, int b) {
   return min(max(p.q_start[b + 1] - p.q_start[b] - 1, 0), p.max_draft);
+}
+
+// ---------------------------------------------------------------------------
+// Draft-tree masks (one thread per sequence): node i of sequence b sees its
+// root path, mask(i) = mask(parent(i)) | bit i with mask(root) = bit 0, where
+// parents[(q_start[b]-b) + i-1] < i (the LLM inference handbook, section
+// "Medusa": tree attention keeps the causal order inside each branch).  A
+// parent out of that range is taken as the root.  At most 64 nodes per tree.
+__global__ __launch_bounds__(256) void verify_tree_masks(AttnParams p, const int* parents,
+                                                         unsigned long long* masks) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b >= p.B) return;
+  const int t0 = p.q_start[b];
+  const int T = min(seq_drafts(p, b), 63);
+  const int d0 = t0 - b;
+  if (t0 < 0 || t0 + T >= p.total_q || d0 < 0 || d0 + T > p.total_q - p.B) return;
+  masks[t0] = 1ull;
+  for (int i = 1; i <= T; ++i) {
+    int q = parents[d0 + i - 1];
+    q = (q >= 0 && q < i) ? q : 0;
+    masks[t0 + i] = masks[t0 + q] | (1ull << i);   // (the parent's mask was written above by this thread)
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -413,7 +436,7 @@ using ic = std::integral_constant<int, V>;
 
 // ---------------------------------------------------------------------------
 // NRB row blocks of 16 per wave, NW waves, WPC resident workgroups per CU.
-template <int HD, int NRB, int NW, int WPC, int OUT_F32>
+template <int HD, int NRB, int NW, int WPC, int OUT_F32, bool TREE>
 __global__ __launch_bounds__(64 * NW, WPC) void verify_attn_main(AttnParams p) {
   using RG = Ring<HD, NW, WPC>;
   constexpr int S = RG::kStages;
@@ -528,6 +551,7 @@ __global__ __launch_bounds__(64 * NW, WPC) void verify_attn_main(AttnParams p) {
     // Query fragments (B operand of S^T = K Q^T): lane holds row l16, dims g4*8..+7 of each 32-wide step.
     bf16x8 qf[NRB][NKC];
     int pos[NRB];
+    unsigned long long tm[NRB];    // draft tree: the nodes row rb sees (bit j: node j of the block)
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       const int row = row0 + (wave * NRB + rb) * 16 + l16;
@@ -536,6 +560,8 @@ __global__ __launch_bounds__(64 * NW, WPC) void verify_attn_main(AttnParams p) {
       const int i = valid ? i0 : 0;
       const int g = valid ? row - i * p.G : 0;
       pos[rb] = valid ? N - 1 - D + i : -1;
+      tm[rb] = 0ull;
+      if constexpr (TREE) tm[rb] = valid ? p.tmask[t0 + i] : 0ull;
       const uint16_t* qp = p.q + ((size_t)(t0 + i) * Hq + (size_t)h * p.G + g) * HD + g4 * 8;
 #pragma unroll
       for (int c = 0; c < NKC; ++c) {
@@ -569,20 +595,31 @@ __global__ __launch_bounds__(64 * NW, WPC) void verify_attn_main(AttnParams p) {
     wait_lds();
     block_sync();
 
-    // Scores of tile `tile`: causal mask (only tiles that reach the draft
-    // block need it) and row max.
+    // Scores of tile `tile`: causal (or draft-tree) mask, only for tiles that
+    // reach the draft block, and row max.
     f32x4 sc[2][2][NRB];           // scores of tiles of even / odd index
     float mt[NRB];                 // row max of the newest scores (log2 units)
     auto mask_scores = [&](f32x4 (&s)[2][NRB], int tile) {
       const int ts = k_begin + tile * RG::kTile;
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) {
-        const int lim = pos[rb] - ts - g4 * 8;   // key g4*8 + kb*4 + e is visible iff kb*4 + e <= lim
+        if constexpr (TREE) {
+          const int nb = ts + g4 * 8 - (N - 1 - D);   // block node of key g4*8 (before the block: < 0, seen)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+          for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (kb * 4 + e > lim) s[kb][rb][e] = -INFINITY;
+            for (int e = 0; e < 4; ++e) {
+              const int node = nb + kb * 4 + e;
+              if (!(node < 0 || (node < 64 && ((tm[rb] >> node) & 1ull)))) s[kb][rb][e] = -INFINITY;
+            }
+        } else {
+          const int lim = pos[rb] - ts - g4 * 8;   // key g4*8 + kb*4 + e is visible iff kb*4 + e <= lim
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (kb * 4 + e > lim) s[kb][rb][e] = -INFINITY;
+        }
       }
     };
     // Sets mt; true if some row's max exceeds its running max by more than `slack`.
@@ -884,7 +921,7 @@ __device__ __forceinline__ int wide_swz(int k) {
   else return (((k >> 1) & 1) << 2) | ((k >> 2) & 3);
 }
 
-template <int HD, int OUT_F32, bool RS>
+template <int HD, int OUT_F32, bool RS, bool TREE>
 __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
   constexpr int NW = 8;
   using RG = Ring<HD, NW, 1>;
@@ -997,6 +1034,8 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
     const int qi = valid ? i0 : 0;
     const int qg = valid ? row - qi * p.G : 0;
     const int pos = valid ? N - 1 - D + qi : -1;
+    unsigned long long tm = 0ull;   // draft tree: nodes this row sees
+    if constexpr (TREE) tm = valid ? p.tmask[t0 + qi] : 0ull;
     bf16x8 qf[NKS];
     {
       const uint16_t* qp = p.q + ((size_t)(t0 + qi) * Hq + (size_t)h * p.G + qg) * HD + hh * 8;
@@ -1033,10 +1072,19 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
     f32x16 sc;
     float mt = -INFINITY;
     auto mask_scores = [&](int tile) {
-      const int lim = pos - (k_begin + tile * RG::kTile) - 8 * hh;   // key (e/8)*16 + 8hh + e%8 is visible iff (e/8)*16 + e%8 <= lim
+      if constexpr (TREE) {
+        const int nb = k_begin + tile * RG::kTile + 8 * hh - (N - 1 - D);   // block node of entry 0
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if ((e >> 3) * 16 + (e & 7) > lim) sc[e] = -INFINITY;
+        for (int e = 0; e < 16; ++e) {
+          const int node = nb + (e >> 3) * 16 + (e & 7);
+          if (!(node < 0 || (node < 64 && ((tm >> node) & 1ull)))) sc[e] = -INFINITY;
+        }
+      } else {
+        const int lim = pos - (k_begin + tile * RG::kTile) - 8 * hh;   // key (e/8)*16 + 8hh + e%8 is visible iff (e/8)*16 + e%8 <= lim
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if ((e >> 3) * 16 + (e & 7) > lim) sc[e] = -INFINITY;
+      }
     };
     auto row_max = [&](float slack) {
       float m = sc[0];
@@ -1349,7 +1397,7 @@ __global__ __launch_bounds__(256) void verify_attn_combine(AttnParams p) {
 // ---------------------------------------------------------------------------
 // Host side: variant choice, workspace layout, launches.
 struct AttnLayout {
-  size_t plan_off, items_off, ml_off, o_off, total;
+  size_t plan_off, items_off, ml_off, o_off, mask_off, total;
   int rpad, item_cap, variant;
   // variant 0: verify_attn_main, 4 waves x 16 rows (64 rows), two workgroups per CU;
   // variant 1: verify_attn_wide, 8 waves, up to 128 rows (the sets split the tiles);
@@ -1393,6 +1441,7 @@ static AttnLayout attn_layout(int B, int Hkv, int G, int HD, int max_pages, int 
   L.items_off = take((size_t)cap * sizeof(ItemDesc));
   L.ml_off = take((size_t)cap * L.rpad * 2 * 4);
   L.o_off = take((size_t)cap * L.rpad * HD * 4);
+  L.mask_off = take((size_t)B * (1 + max_draft) * 8);   // draft-tree masks (tree calls only)
   L.total = off;
   return L;
 }
@@ -1406,11 +1455,19 @@ size_t sdv_attn_workspace_bytes(int B, int Hkv, int G, int head_dim, int max_pag
   return attn_layout(B, Hkv, G, head_dim, max_pages, max_draft, kv_chunk).total;
 }
 
+// The draft-tree mask is a template parameter, so that causal calls run code
+// with no trace of it.
+template <int HD, int OUTF, bool TREE>
+static void launch_variant(int variant, const AttnParams& p, int grid, hipStream_t st) {
+  if (variant == 0) verify_attn_main<HD, 1, 4, 2, OUTF, TREE><<<grid, 256, 0, st>>>(p);
+  else if (variant == 1) verify_attn_wide<HD, OUTF, false, TREE><<<grid, 512, 0, st>>>(p);
+  else verify_attn_wide<HD, OUTF, true, TREE><<<grid, 512, 0, st>>>(p);
+}
+
 template <int HD, int OUTF>
 static void launch_main(int variant, const AttnParams& p, int grid, hipStream_t st) {
-  if (variant == 0) verify_attn_main<HD, 1, 4, 2, OUTF><<<grid, 256, 0, st>>>(p);
-  else if (variant == 1) verify_attn_wide<HD, OUTF, false><<<grid, 512, 0, st>>>(p);
-  else verify_attn_wide<HD, OUTF, true><<<grid, 512, 0, st>>>(p);
+  if (p.tmask) launch_variant<HD, OUTF, true>(variant, p, grid, st);
+  else launch_variant<HD, OUTF, false>(variant, p, grid, st);
 }
 
 hipError_t sdv_attn_launch(const SdAttnLaunch& a) {
@@ -1449,6 +1506,12 @@ hipError_t sdv_attn_launch(const SdAttnLaunch& a) {
   const float scale = a.softmax_scale > 0.f ? a.softmax_scale : 1.f / sqrtf((float)a.head_dim);
   p.scale_log2 = scale * 1.4426950408889634f;
 
+  p.tmask = nullptr;
+  if (a.parents) {
+    unsigned long long* masks = (unsigned long long*)(ws + L.mask_off);
+    verify_tree_masks<<<(a.B + 255) / 256, 256, 0, a.stream>>>(p, a.parents, masks);
+    p.tmask = masks;
+  }
   verify_attn_plan<<<1, kPlanThreads, 0, a.stream>>>(p, a.kv_chunk, slots, kItemOverheadBytes / (4 * a.head_dim));
   if (a.head_dim == 128) {
     if (a.out_f32) launch_main<128, 1>(L.variant, p, grid, a.stream);

@@ -75,6 +75,7 @@ struct SdAttnLaunch {
   const int32_t* block_table;
   const int32_t* kv_len;
   const int32_t* q_start;
+  const int32_t* parents;   // NULL: causal verify block; else draft-tree parents (see sd_verify_tree_attention)
   void* out;
   void* workspace;
   int B, Hkv, G, head_dim, max_pages, num_pages, max_draft, out_f32, kv_chunk, total_q;
@@ -100,6 +101,7 @@ size_t sdv_attn_workspace_bytes(int B, int Hkv, int G, int head_dim, int max_pag
 hipError_t sdv_attn_launch(const SdAttnLaunch& a);
 size_t sdv_accept_workspace_bytes(int B, int T, int V, int stochastic);
 hipError_t sdv_accept_launch(const SdAccLaunch& a);
+hipError_t sdv_tree_accept_launch(const SdAccLaunch& a, const int32_t* parents, int32_t* out_nodes);
 
 struct SdGemmLaunch {
   const void* x;

@@ -105,6 +105,36 @@ def test_deterministic():
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
+@pytest.mark.parametrize("mode", ["stochastic", "greedy"])
+def test_workspace_contents_never_matter(mode):
+    """Every workspace byte the call reads is written by the call first: with
+    the workspace filled with different byte patterns before each call, the
+    results are those of the oracle every time."""
+    import speculative_decoding_verification_sd_amd as sdv
+    inp = generate(spec(seed=9, mode=mode, batch=40), device="cuda")
+    al_o, tok_o = oracle_accept(inp, mode)
+    B = inp.q_start.shape[0] - 1
+    T, V = inp.target_logits.shape
+    nbytes = sdv.sd_accept_reject_workspace_size(sdv.accept_desc(B, V, inp.max_draft, mode), T)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    gen = torch.Generator(device="cuda").manual_seed(3)
+    stoch = mode == "stochastic"
+    for fill in (0xFF, 0x00, 0x7F, None, 0x80, None):
+        if fill is None:
+            ws.copy_(torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda", generator=gen))
+        else:
+            ws.fill_(fill)
+        al = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+        out = torch.full((T,), -7, dtype=torch.int32, device="cuda")
+        sdv.sd_accept_reject(inp.target_logits, inp.draft_logits if stoch else None, inp.draft_tokens, inp.q_start,
+                             inp.uniforms if stoch else None, al, out, mode=mode, max_draft=inp.max_draft,
+                             workspace=ws)
+        torch.cuda.synchronize()
+        say(f"case: accept {mode} workspace fill {fill}")
+        assert np.array_equal(al.cpu().numpy(), al_o)
+        assert np.array_equal(out.cpu().numpy(), tok_o)
+
+
 @pytest.mark.parametrize("name", ["g8_kv32k_D15", "g32_kv128k_D3_greedy", "ragged_b64"])
 def test_full_size_workloads(name):
     sp = preset(name)

@@ -1,0 +1,135 @@
+"""GPU parity of draft-tree verification against the fp64 tree oracle, through
+the C ABI: attention under the ancestor mask (|err| <= 2e-2 on bf16 outputs;
+a chain tree must give the causal call's output bit for bit) and greedy
+acceptance of the longest accepted path (bit-exact lengths, tokens and nodes)."""
+
+import numpy as np
+import pytest
+import torch
+
+import speculative_decoding_verification_sd_amd as sdv
+from oracle import accept_tree_greedy, verify_tree_attention
+from tests.gpu_util import ATTN_TOL, gpu_attention, say
+from tests.oracle_io import attention_args
+from workloads import WorkloadSpec, generate
+
+pytestmark = pytest.mark.gpu
+
+
+def _spec(**kw):
+    base = dict(name="tree_case", batch=3, kv_heads=2, group=8, head_dim=128, kv_len=[1000, 77, 2500],
+                draft_len=[15, 3, 7], vocab=64, mode="greedy")
+    base.update(kw)
+    return WorkloadSpec(**base)
+
+
+def _parents(q_start, kind, rng):
+    par = []
+    for b in range(len(q_start) - 1):
+        T = int(q_start[b + 1] - q_start[b]) - 1
+        for i in range(1, T + 1):
+            par.append(i - 1 if kind == "chain" else 0 if kind == "star" else int(rng.integers(0, i)))
+    return np.asarray(par, np.int32)
+
+
+def _tree_attention(inp, parents, kv_chunk=0):
+    x = inp if inp.q.is_cuda else inp.to("cuda")
+    out = torch.full(x.q.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    sdv.sd_verify_tree_attention(x.q, x.k_cache, x.v_cache, x.block_table, x.kv_len, x.q_start,
+                                 torch.from_numpy(parents).cuda(), out, group_size=inp.group,
+                                 max_draft=inp.max_draft, kv_chunk=kv_chunk)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("G,drafts,d", [(8, [3, 1, 7], 128), (8, [15, 9, 4], 128), (8, [31, 20, 5], 128),
+                                        (4, [63, 30, 0], 64)])
+def test_chain_tree_is_bitwise_the_causal_call(G, drafts, d):
+    inp = generate(_spec(group=G, head_dim=d, draft_len=drafts, seed=G + d))
+    par = _parents(inp.q_start.cpu().numpy(), "chain", None)
+    say(f"case: chain G={G} drafts={drafts} d={d}")
+    a = _tree_attention(inp, par)
+    c = gpu_attention(inp)
+    assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+
+
+@pytest.mark.parametrize("kind", ["random", "star"])
+@pytest.mark.parametrize("G,drafts,d,kv_chunk", [(8, [15, 3, 7], 128, 0), (8, [31, 12, 6], 128, 0),
+                                                 (4, [7, 2, 5], 64, 0), (8, [15, 3, 7], 128, 256),
+                                                 (2, [40, 63, 1], 64, 0)])
+def test_tree_attention_matches_oracle(kind, G, drafts, d, kv_chunk):
+    inp = generate(_spec(group=G, head_dim=d, draft_len=drafts, seed=3 * G + d + len(kind)))
+    rng = np.random.default_rng(G + d)
+    a = attention_args(inp)
+    par = _parents(a["q_start"], kind, rng)
+    say(f"case: {kind} tree G={G} drafts={drafts} d={d} kv_chunk={kv_chunk}")
+    out = _tree_attention(inp, par, kv_chunk).float().cpu().numpy().astype(np.float64)
+    ref = verify_tree_attention(parents=par, **a)
+    err = float(np.max(np.abs(out - ref)))
+    say(f"max|err| = {err:.3e}")
+    assert err <= ATTN_TOL
+
+
+@pytest.mark.parametrize("G,drafts", [(8, [3, 1, 7]), (8, [15, 9, 4]), (8, [31, 20, 5])])
+def test_tree_workspace_contents_never_matter(G, drafts):
+    """The tree masks and the plan are written by the call before they are
+    read: different workspace fills give the same bits every call."""
+    inp = generate(_spec(group=G, draft_len=drafts, seed=G + 1))
+    par = _parents(attention_args(inp)["q_start"], "random", np.random.default_rng(7))
+    x = inp.to("cuda")
+    desc = sdv.attn_desc(x.q, x.k_cache, x.block_table, inp.group, inp.max_draft)
+    nbytes = sdv.sd_verify_attention_workspace_size(desc, x.q.shape[0])
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    parents = torch.from_numpy(par).cuda()
+    say(f"case: tree workspace garbage G={G} drafts={drafts}")
+    outs = []
+    for fill in (0xFF, 0x00, 0x7F, 0x80, 0x55):
+        ws.fill_(fill)
+        out = torch.full(x.q.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+        sdv.sd_verify_tree_attention(x.q, x.k_cache, x.v_cache, x.block_table, x.kv_len, x.q_start, parents, out,
+                                     group_size=inp.group, max_draft=inp.max_draft, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append(out)
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+    ref = verify_tree_attention(parents=par, **attention_args(inp))
+    err = float(np.max(np.abs(outs[0].float().cpu().numpy() - ref)))
+    say(f"max|err| = {err:.3e}")
+    assert err <= ATTN_TOL
+
+
+def _run_accept(target, tokens, q_start, parents, max_draft):
+    T = target.shape[0]
+    B = q_start.shape[0] - 1
+    al = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    out = torch.full((T,), -7, dtype=torch.int32, device="cuda")
+    nodes = torch.full((T,), -7, dtype=torch.int32, device="cuda")
+    sdv.sd_tree_accept(target, tokens, q_start, parents, al, out, nodes, max_draft=max_draft)
+    torch.cuda.synchronize()
+    return al.cpu().numpy(), out.cpu().numpy(), nodes.cpu().numpy()
+
+
+@pytest.mark.parametrize("seed,V", [(0, 5), (1, 7), (2, 1001), (3, 32000), (4, 151936)])
+def test_tree_accept_matches_oracle(seed, V):
+    rng = np.random.default_rng(seed)
+    B = 6
+    sizes = rng.integers(1, 30, size=B)
+    sizes[0] = 1                              # a sequence with no drafts
+    q_start = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    T = int(q_start[-1])
+    target = rng.standard_normal((T, V)).astype(np.float32) * 3
+    parents = _parents(q_start, "random", rng)
+    tokens = rng.integers(0, V, size=T - B).astype(np.int32)
+    for b in range(B):                        # plant matches so that paths get long
+        t0, d0 = int(q_start[b]), int(q_start[b]) - b
+        for i in range(1, int(sizes[b])):
+            if rng.random() < 0.7:
+                tokens[d0 + i - 1] = int(np.argmax(target[t0 + parents[d0 + i - 1]]))
+    tokens[rng.random(T - B) < 0.05] = -3     # out-of-range drafts fail
+    say(f"case: tree accept seed={seed} V={V}")
+    got = _run_accept(torch.from_numpy(target).cuda(), torch.from_numpy(tokens).cuda(),
+                      torch.from_numpy(q_start).cuda(), torch.from_numpy(parents).cuda(), int(sizes.max()) - 1)
+    ref = accept_tree_greedy(target, tokens, q_start, parents)
+    for g, r, name in zip(got, ref, ("accept_len", "out_tokens", "out_nodes")):
+        np.testing.assert_array_equal(g, r, err_msg=name)
+    say(f"AL = {got[0].tolist()}")
