@@ -280,6 +280,139 @@ def write_profiles(bench_json: str, kt_dir: str, fetch_dir: str, write_dir: str,
 
 
 SWEEP_PRESET = "g8_kv32k_sweep"
+TREE_PRESET = "g8_kv32k_D15"
+TREE_BRANCHING = (2, 2, 2, 2)   # a full binary tree of depth 4: 30 drafted nodes, G*(1+30) = 248 rows
+
+
+def tree_algorithmic(inp, parents):
+    """Bytes and flops of one tree-attention call: every key read once; node i of
+    sequence b sees the N_b-1-T_b prefix keys plus the nodes on its root path."""
+    import numpy as np
+    kv = inp.kv_len.cpu().numpy().astype(np.int64)
+    qs = inp.q_start.cpu().numpy().astype(np.int64)
+    par = parents.cpu().numpy().astype(np.int64)
+    sp = inp.spec
+    d, Hkv, G = sp.head_dim, sp.kv_heads, sp.group
+    T_q = int(qs[-1])
+    nbytes = int((kv * Hkv * d * 2 * 2).sum()) + 2 * T_q * Hkv * G * d * 2 \
+        + int(((kv + sp.page_size - 1) // sp.page_size).sum()) * 4 + par.size * 4 + T_q * 8
+    visible = 0
+    for b in range(len(kv)):
+        T = int(qs[b + 1] - qs[b]) - 1
+        depth = [0] * (T + 1)
+        for i in range(1, T + 1):
+            depth[i] = depth[int(par[qs[b] - b + i - 1])] + 1
+        visible += sum(max(int(kv[b]) - 1 - T, 0) + depth[i] + 1 for i in range(T + 1))
+    return nbytes, 4 * d * Hkv * G * visible
+
+
+def run_tree(args):
+    """Tree verification (ancestor-mask attention + greedy longest-path
+    acceptance) on the default shapes with a full binary draft tree of depth 4;
+    one JSON line."""
+    import numpy as np
+    import torch
+
+    import speculative_decoding_verification_sd_amd as sdv
+    from workloads import preset
+    from workloads.tree import tree_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sp = preset(TREE_PRESET, seed=args.seed)
+    print(f"[bench] tree {TREE_BRANCHING}: generating", file=sys.stderr, flush=True)
+    inp, parents, tokens = tree_inputs(sp, TREE_BRANCHING, device=dev)
+    B, T_q = sp.batch, inp.q.shape[0]
+    out = torch.empty_like(inp.q)
+    al = torch.empty(B, dtype=torch.int32, device=dev)
+    tok = torch.empty(T_q, dtype=torch.int32, device=dev)
+    nodes = torch.empty(T_q, dtype=torch.int32, device=dev)
+    adesc = sdv.attn_desc(inp.q, inp.k_cache, inp.block_table, sp.group, inp.max_draft)
+    cdesc = sdv.accept_desc(B, sp.vocab, inp.max_draft, "greedy")
+    ws_a = torch.empty(max(1, sdv.sd_verify_attention_workspace_size(adesc, T_q)), dtype=torch.uint8, device=dev)
+    ws_c = torch.empty(max(1, sdv.sd_tree_accept_workspace_size(cdesc, T_q)), dtype=torch.uint8, device=dev)
+
+    def attention():
+        sdv.sd_verify_tree_attention(inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.kv_len, inp.q_start,
+                                     parents, out, group_size=sp.group, max_draft=inp.max_draft, workspace=ws_a)
+
+    def accept():
+        sdv.sd_tree_accept(inp.target_logits, tokens, inp.q_start, parents, al, tok, nodes,
+                           max_draft=inp.max_draft, workspace=ws_c)
+
+    t_end = time.perf_counter() + max(0.0, args.settle_s)
+    while time.perf_counter() < t_end:
+        for _ in range(5):
+            attention()
+            accept()
+        torch.cuda.synchronize()
+    for _ in range(max(1, args.warmup)):
+        attention()
+        accept()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        attention()
+        ev[k][1].record(stream)
+        accept()
+        ev[k][2].record(stream)
+    torch.cuda.synchronize()
+    a_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    c_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    a_bytes, a_flops = tree_algorithmic(inp, parents)
+    c_bytes = T_q * sp.vocab * 4
+    step_s = (a_ms + c_ms) * 1e-3
+    achieved = a_bytes / (a_ms * 1e-3) / 1e9
+    ntree = len(parents) // B
+    print(json.dumps({
+        "metric": "draft-tree nodes verified/s per tree-verify step (+ % HBM roofline of the tree attention)",
+        "value": T_q / step_s, "unit": "tree nodes/s", "higher_is_better": True, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": a_ms + c_ms, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{sp.name.replace('_D15', '')}_tree{''.join(map(str, TREE_BRANCHING))}_greedy",
+                   "batch": B, "kv_heads": sp.kv_heads, "group": sp.group, "head_dim": sp.head_dim,
+                   "kv_len": sp.kv_len, "vocab": sp.vocab, "tree_branching": list(TREE_BRANCHING),
+                   "tree_nodes": ntree + 1, "rows_per_kv_head": sp.group * (ntree + 1), "seed": args.seed},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "tree verify attention (masks + plan + main + combine launches)",
+                     "algorithmic_bytes_per_launch": a_bytes,
+                     "mfma_tflops": a_flops / (a_ms * 1e-3) / 1e12,
+                     "mfma_frac": a_flops / (a_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+        "attention_ms": a_ms, "accept_ms": c_ms, "accept_gbs": c_bytes / (c_ms * 1e-3) / 1e9,
+        "mean_accept_len": float(al.float().mean().item()),
+        "accepted_tokens_per_s": float(al.sum().item()) / step_s,
+        "clock_settle_s": args.settle_s}), flush=True)
+
+
+def write_tree_profile(bench_json: str, kt_dir: str):
+    """Kernel-time summary under profiles/ of a rocprofv3 --kernel-trace --stats
+    run of `bench.py --tree`, with the bench line of the same call."""
+    with open(bench_json) as f:
+        line = json.loads(f.read().strip().splitlines()[-1])
+    wl = line["config"]["workload"]
+    stats = [r for r in _rocprof_csv(kt_dir, "kernel_stats") if "sdv::" in r["Name"]]
+    calls = int(stats[0]["Calls"]) if stats else 0
+    path = os.path.join(ROOT, "profiles", f"verify_tree_{wl}_kernel_stats.txt")
+    with open(path, "w") as f:
+        f.write(f"# rocprofv3 kernel-trace summary of the library's kernels, workload {wl}:\n"
+                "# one tree-verify step = tree attention (ancestor masks, plan, main, split-KV combine)\n"
+                f"# + greedy tree acceptance (row statistics, path walk).  {calls} calls per kernel =\n"
+                "# clock-settle + warmup + timed steps.  Durations in ns.\n"
+                "$ cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d REPO/gpurun_out/kt_tree "
+                "-o run --output-format csv -- python3 REPO/bench.py --tree\n")
+        f.write("Name,Calls,TotalDurationNs,AverageNs,Percentage,MinNs,MaxNs,StdDev\n")
+        for r in stats:
+            f.write(",".join([r["Name"], r["Calls"], r["TotalDurationNs"], r["AverageNs"], r["Percentage"],
+                              r["MinNs"], r["MaxNs"], r["StdDev"]]) + "\n")
+        attn = sum(float(r["AverageNs"]) for r in stats if "verify_attn" in r["Name"] or "tree_masks" in r["Name"])
+        f.write(f"tree attention call (masks + plan + main + combine averages): {attn / 1e3:.1f} us\n")
+        f.write(f"bench.py in the same call: attention {line['attention_ms'] * 1e3:.1f} us/step (HIP events), "
+                f"accept {line['accept_ms'] * 1e3:.1f} us/step, {line['value']:.0f} tree nodes/s, "
+                f"HBM {line['roofline']['frac']:.3f} of peak, mean AL {line['mean_accept_len']:.3f}\n")
+    print(f"wrote {path}")
 
 
 def run_sweep(args):
@@ -499,7 +632,14 @@ def main():
                     help="write the profiles/ table of a --linear-sweep line")
     ap.add_argument("--write-profiles", nargs=4, metavar=("BENCH_JSON", "KT_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write the profiles/ summaries from a bench line and three rocprofv3 runs (no GPU)")
+    ap.add_argument("--tree", action="store_true",
+                    help="tree verification (ancestor-mask attention + greedy path acceptance), binary tree of depth 4")
+    ap.add_argument("--write-tree-profile", nargs=2, metavar=("BENCH_JSON", "KT_DIR"),
+                    help="write the profiles/ summary of a --tree line and its rocprofv3 kernel trace (no GPU)")
     args = ap.parse_args()
+    if args.write_tree_profile:
+        write_tree_profile(*args.write_tree_profile)
+        return
     if args.write_profiles:
         write_profiles(*args.write_profiles, copy_bytes=args.calibrate_copy or (1 << 30))
         return
@@ -518,6 +658,9 @@ def main():
     if args.linear_sweep:
         args.settle_s = min(args.settle_s, 0.5)
         run_linear_sweep(args)
+        return
+    if args.tree:
+        run_tree(args)
         return
     if args.sweep is not None:
         args.sweep = args.sweep or list(range(32))

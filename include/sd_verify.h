@@ -208,7 +208,7 @@ sd_status sd_verify_tree_attention(const sd_attn_desc* desc, int32_t total_q,
                                    const int32_t* q_start, const int32_t* parents, void* out,
                                    void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes sd_tree_accept needs (desc->mode must be SD_ACCEPT_GREEDY); 0 if invalid. */
+/* Workspace bytes sd_tree_accept needs (desc->mode must be SD_ACCEPT_GREEDY, desc->max_draft <= 63); 0 if invalid. */
 size_t sd_tree_accept_workspace_size(const sd_accept_desc* desc, int32_t total_q);
 
 /*
@@ -220,7 +220,9 @@ size_t sd_tree_accept_workspace_size(const sd_accept_desc* desc, int32_t total_q
  *   out_tokens[t0+k] = the token of the path's node at depth k+1 (k < L),
  *   out_tokens[t0+L] = the target's top token at the path's last node,
  *   out_nodes[t0+k] = the index of the path's node at depth k+1 (k < L);
- * other entries up to t0+T_b are -1.  desc->mode must be SD_ACCEPT_GREEDY.
+ * other entries up to t0+T_b are -1.  A parent outside [0, i) is taken as the
+ * root.  desc->mode must be SD_ACCEPT_GREEDY, and a tree has at most 64 nodes
+ * (desc->max_draft <= 63); SD_ERR_UNSUPPORTED otherwise.
  *
  *   target_logits fp32 [total_q, V];  tree_tokens, parents int32 [total_q - B]
  *   accept_len int32 [B]; out_tokens, out_nodes int32 [total_q] (written)

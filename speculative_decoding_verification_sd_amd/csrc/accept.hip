@@ -265,7 +265,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_decide(AccParams p) {
 // the target's top token at that node after it (the LLM inference handbook,
 // section "Medusa": the longest accepted candidate prefix moves on).
 __global__ __launch_bounds__(kAccThreads) void accept_tree(AccParams p, const int* parents, int* out_nodes) {
-  extern __shared__ int tdyn[];                  // amax[T+1], depth[T+1], par[T+1]
+  extern __shared__ int amax[];                  // [T+1]: each node's top token
   __shared__ RowPart stage[kDecideSlots];
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
@@ -276,9 +276,6 @@ __global__ __launch_bounds__(kAccThreads) void accept_tree(AccParams p, const in
     if (tid == 0) p.accept_len[b] = 0;
     return;
   }
-  int* amax = tdyn;
-  int* depth = tdyn + (p.max_draft + 1);
-  int* par = tdyn + 2 * (p.max_draft + 1);
 
   const int nrows = T + 1;
   const int rows_per_pass = max(1, kDecideSlots / p.nchunk);
@@ -297,35 +294,50 @@ __global__ __launch_bounds__(kAccThreads) void accept_tree(AccParams p, const in
       amax[r0 + rr] = ai;
     }
   }
-  // parents out of order are taken as the root (so that every walk below ends)
-  for (int i = 1 + tid; i <= T; i += kAccThreads) {
-    const int q = parents[d0 + i - 1];
-    par[i] = (q >= 0 && q < i) ? q : 0;
-  }
   __syncthreads();
-  if (tid == 0) {
-    // depth[i] >= 0: accepted at that depth; -1: not accepted
-    depth[0] = 0;
-    int best = 0;
-    for (int i = 1; i <= T; ++i) {
-      const int q = par[i];
-      const int x = p.tokens[d0 + i - 1];
-      depth[i] = (depth[q] >= 0 && x >= 0 && x < p.V && x == amax[q]) ? depth[q] + 1 : -1;
-      if (depth[i] > depth[best]) best = i;
-    }
-    const int L = depth[best];
-    for (int i = best, k = L - 1; i != 0; i = par[i], --k) {
-      p.out_tokens[t0 + k] = p.tokens[d0 + i - 1];
-      out_nodes[t0 + k] = i;
-    }
+  if (tid >= 64) return;
+  // One wave decides: lane i holds node i.  A node matches when its token is the
+  // top token of its parent's row; it is accepted when every node on its root
+  // path matches, i.e. when its ancestor mask (built by pointer jumping, as for
+  // tree attention) has no non-matching node.  A parent out of [0, i) is the root.
+  const int lane = tid;
+  int up = 0, x = -1;
+  bool match = lane == 0;
+  if (lane >= 1 && lane <= T) {
+    const int q = parents[d0 + lane - 1];
+    up = (q >= 0 && q < lane) ? q : 0;
+    x = p.tokens[d0 + lane - 1];
+    match = x >= 0 && x < p.V && x == amax[up];
+  }
+  const unsigned long long ok = __ballot(match);
+  unsigned long long m = 1ull << lane;
+#pragma unroll
+  for (int k = 0; k < 6; ++k) {
+    const unsigned long long mu = __shfl(m, up);
+    const int uu = __shfl(up, up);
+    m |= mu;
+    up = uu;
+  }
+  const int depth = __popcll(m) - 1;
+  // the deepest accepted node, the lowest index among equal depths
+  int key = (lane <= T && (m & ~ok) == 0) ? depth * 64 + (63 - lane) : -1;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) key = max(key, __shfl_xor(key, off));
+  const int best = 63 - (key & 63);
+  const int L = key >> 6;
+  const unsigned long long path = __shfl(m, best);
+  if (lane >= 1 && ((path >> lane) & 1ull)) {     // (node indices grow along a path)
+    p.out_tokens[t0 + depth - 1] = x;
+    out_nodes[t0 + depth - 1] = lane;
+  }
+  if (lane == 0) {
     p.out_tokens[t0 + L] = amax[best];
     p.accept_len[b] = L + 1;
-    depth[0] = L;                                // hand L to the other threads
   }
-  __syncthreads();
-  const int L = depth[0];
-  for (int k = L + 1 + tid; k <= T; k += kAccThreads) p.out_tokens[t0 + k] = -1;
-  for (int k = L + tid; k <= T; k += kAccThreads) out_nodes[t0 + k] = -1;
+  for (int k = lane; k <= T; k += 64) {
+    if (k > L) p.out_tokens[t0 + k] = -1;
+    if (k >= L) out_nodes[t0 + k] = -1;
+  }
 }
 
 // fp64 weights of one token of the sampling row from its target logit tl and
@@ -674,6 +686,6 @@ hipError_t sdv_tree_accept_launch(const SdAccLaunch& a, const int32_t* parents, 
   const unsigned grid1 = (unsigned)((size_t)a.T * L.nchunk);
   if (vec4) accept_rowstats<0, 1><<<grid1, kAccThreads, 0, a.stream>>>(p);
   else accept_rowstats<0, 0><<<grid1, kAccThreads, 0, a.stream>>>(p);
-  accept_tree<<<a.B, kAccThreads, (size_t)3 * (a.max_draft + 1) * sizeof(int), a.stream>>>(p, parents, out_nodes);
+  accept_tree<<<a.B, kAccThreads, (size_t)(a.max_draft + 1) * sizeof(int), a.stream>>>(p, parents, out_nodes);
   return hipGetLastError();
 }

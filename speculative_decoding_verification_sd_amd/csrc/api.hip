@@ -247,7 +247,7 @@ SD_EXPORT sd_status sd_verify_tree_attention(const sd_attn_desc* desc, int32_t t
 }
 
 SD_EXPORT size_t sd_tree_accept_workspace_size(const sd_accept_desc* desc, int32_t total_q) {
-  if (check_accept(desc, total_q) != SD_OK || desc->mode != SD_ACCEPT_GREEDY) return 0;
+  if (check_accept(desc, total_q) != SD_OK || desc->mode != SD_ACCEPT_GREEDY || desc->max_draft > 63) return 0;
   return acc_ws(desc, total_q);
 }
 
@@ -258,6 +258,7 @@ SD_EXPORT sd_status sd_tree_accept(const sd_accept_desc* d, int32_t total_q, con
   sd_status s = check_accept(d, total_q);
   if (s != SD_OK) return s;
   if (d->mode != SD_ACCEPT_GREEDY) return fail(SD_ERR_UNSUPPORTED, "draft trees are accepted greedily only");
+  if (d->max_draft > 63) return fail(SD_ERR_UNSUPPORTED, "max_draft=%d: a draft tree has at most 64 nodes", d->max_draft);
   if (d->num_seqs == 0) return SD_OK;
   const bool any = total_q > d->num_seqs;
   if (!target_logits || !q_start || !accept_len || !out_tokens || !out_nodes || (any && (!tree_tokens || !parents)))

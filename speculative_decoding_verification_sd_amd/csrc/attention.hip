@@ -89,25 +89,39 @@ __device__ __forceinline__ int seq_drafts(const AttnParams& p, int b) {
 }
 
 // ---------------------------------------------------------------------------
-// Draft-tree masks (one thread per sequence): node i of sequence b sees its
-// root path, mask(i) = mask(parent(i)) | bit i with mask(root) = bit 0, where
+// Draft-tree masks, one wave per sequence: node i of sequence b sees its root
+// path, mask(i) = mask(parent(i)) | bit i with mask(root) = bit 0, where
 // parents[(q_start[b]-b) + i-1] < i (the LLM inference handbook, section
 // "Medusa": tree attention keeps the causal order inside each branch).  A
-// parent out of that range is taken as the root.  At most 64 nodes per tree.
-__global__ __launch_bounds__(256) void verify_tree_masks(AttnParams p, const int* parents,
-                                                         unsigned long long* masks) {
-  const int b = blockIdx.x * 256 + threadIdx.x;
-  if (b >= p.B) return;
+// parent out of that range is taken as the root.  Lane i holds node i and
+// doubles its reach six times (pointer jumping: after round k its mask holds
+// the nodes up to 2^(k+1)-1 steps above it and `up` the node 2^(k+1) steps
+// above, the root's parent being the root), which covers every path of a tree
+// of at most 64 nodes.
+constexpr int kMaskSeqsPerBlock = 4;
+__global__ __launch_bounds__(64 * kMaskSeqsPerBlock) void verify_tree_masks(AttnParams p, const int* parents,
+                                                                             unsigned long long* masks) {
+  const int lane = threadIdx.x & 63;
+  const int b = blockIdx.x * kMaskSeqsPerBlock + (threadIdx.x >> 6);
+  if (b >= p.B) return;                         // (whole waves)
   const int t0 = p.q_start[b];
   const int T = min(seq_drafts(p, b), 63);
   const int d0 = t0 - b;
   if (t0 < 0 || t0 + T >= p.total_q || d0 < 0 || d0 + T > p.total_q - p.B) return;
-  masks[t0] = 1ull;
-  for (int i = 1; i <= T; ++i) {
-    int q = parents[d0 + i - 1];
-    q = (q >= 0 && q < i) ? q : 0;
-    masks[t0 + i] = masks[t0 + q] | (1ull << i);   // (the parent's mask was written above by this thread)
+  int up = 0;
+  if (lane >= 1 && lane <= T) {
+    const int q = parents[d0 + lane - 1];
+    up = (q >= 0 && q < lane) ? q : 0;
   }
+  unsigned long long m = 1ull << lane;
+#pragma unroll
+  for (int k = 0; k < 6; ++k) {
+    const unsigned long long mu = __shfl(m, up);
+    const int uu = __shfl(up, up);
+    m |= mu;
+    up = uu;
+  }
+  if (lane <= T) masks[t0 + lane] = m;
 }
 
 // ---------------------------------------------------------------------------
@@ -1509,7 +1523,8 @@ hipError_t sdv_attn_launch(const SdAttnLaunch& a) {
   p.tmask = nullptr;
   if (a.parents) {
     unsigned long long* masks = (unsigned long long*)(ws + L.mask_off);
-    verify_tree_masks<<<(a.B + 255) / 256, 256, 0, a.stream>>>(p, a.parents, masks);
+    verify_tree_masks<<<(a.B + kMaskSeqsPerBlock - 1) / kMaskSeqsPerBlock, 64 * kMaskSeqsPerBlock, 0, a.stream>>>(
+        p, a.parents, masks);
     p.tmask = masks;
   }
   verify_attn_plan<<<1, kPlanThreads, 0, a.stream>>>(p, a.kv_chunk, slots, kItemOverheadBytes / (4 * a.head_dim));

@@ -162,3 +162,29 @@ def test_linear_workspace_and_rejections():
     # m = 0 is a no-op
     d = sdv.linear_desc(0, 128, 64)
     assert lib.sd_verify_linear(ctypes.byref(d), None, None, None, None, 0, None) == B.SD_OK
+
+
+def test_tree_calls_reject_bad_arguments():
+    lib = sdv.lib()
+    dummy = ctypes.c_void_p(4096)
+    # trees are greedy only and hold at most 64 nodes
+    a = _acc(mode=1)
+    assert sdv.sd_tree_accept_workspace_size(a, 8) == 0
+    st = lib.sd_tree_accept(ctypes.byref(a), 8, *([dummy] * 7), dummy, 1 << 30, None)
+    assert st == B.SD_ERR_UNSUPPORTED and "greedily" in sdv.sd_last_error()
+    a = _acc(mode=0, max_draft=64)
+    assert sdv.sd_tree_accept_workspace_size(a, 8) == 0
+    st = lib.sd_tree_accept(ctypes.byref(a), 8, *([dummy] * 7), dummy, 1 << 30, None)
+    assert st == B.SD_ERR_UNSUPPORTED and "64 nodes" in sdv.sd_last_error()
+    a = _acc(mode=0)
+    assert sdv.sd_tree_accept_workspace_size(a, 8) > 0
+    st = lib.sd_tree_accept(ctypes.byref(a), 8, dummy, dummy, dummy, None, dummy, dummy, dummy, dummy, 1 << 30, None)
+    assert st == B.SD_ERR_INVALID_ARG and "NULL" in sdv.sd_last_error()
+    st = lib.sd_tree_accept(ctypes.byref(a), 8, *([dummy] * 7), dummy, 8, None)
+    assert st == B.SD_ERR_WORKSPACE
+    d = _attn(max_draft=64, group_size=1)
+    st = lib.sd_verify_tree_attention(ctypes.byref(d), 8, *([dummy] * 8), dummy, 1 << 30, None)
+    assert st == B.SD_ERR_UNSUPPORTED and "64 nodes" in sdv.sd_last_error()
+    d = _attn()
+    st = lib.sd_verify_tree_attention(ctypes.byref(d), 8, *([dummy] * 6), None, dummy, dummy, 1 << 30, None)
+    assert st == B.SD_ERR_INVALID_ARG and "parents" in sdv.sd_last_error()

@@ -133,3 +133,40 @@ def test_tree_accept_matches_oracle(seed, V):
     for g, r, name in zip(got, ref, ("accept_len", "out_tokens", "out_nodes")):
         np.testing.assert_array_equal(g, r, err_msg=name)
     say(f"AL = {got[0].tolist()}")
+
+
+def test_full_size_tree_workload():
+    """The benchmarked tree-verify step (16 sequences, G = 8, 32768-token caches,
+    a full binary tree of depth 4, 131072-token vocabulary) in the launch
+    configuration bench.py times: sampled (sequence, KV head) attention units
+    against the tree oracle one by one, and the whole greedy tree acceptance
+    bit-exact."""
+    from oracle import verify_tree_attention_unit
+    from tests.gpu_util import unit_subproblem
+    from workloads import preset
+    from workloads.tree import tree_inputs
+    sp = preset("g8_kv32k_D15")
+    inp, parents, tokens = tree_inputs(sp, (2, 2, 2, 2), device="cuda")
+    say("case: full-size tree verify step")
+    out = torch.empty_like(inp.q)
+    sdv.sd_verify_tree_attention(inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.kv_len, inp.q_start,
+                                 parents, out, group_size=sp.group, max_draft=inp.max_draft)
+    torch.cuda.synchronize()
+    par = parents.cpu().numpy()
+    T = len(par) // sp.batch
+    rng = np.random.default_rng(0)
+    picks = {(0, 0), (sp.batch - 1, sp.kv_heads - 1)} | {(int(rng.integers(sp.batch)), int(rng.integers(sp.kv_heads)))
+                                                        for _ in range(2)}
+    worst = 0.0
+    for b, h in sorted(picks):
+        sub, (t0, t1) = unit_subproblem(inp, b)
+        ref = verify_tree_attention_unit(**sub, parents=par[b * T:(b + 1) * T], b=0, h=h)
+        got = out[t0:t1, h * sp.group:(h + 1) * sp.group].float().cpu().numpy()
+        worst = max(worst, float(np.abs(got - ref).max()))
+    say(f"tree attention max|err| over {len(picks)} units = {worst:.3e}")
+    assert worst <= ATTN_TOL
+    got = _run_accept(inp.target_logits, tokens, inp.q_start, parents, inp.max_draft)
+    ref = accept_tree_greedy(inp.target_logits.cpu().numpy(), tokens.cpu().numpy(), inp.q_start.cpu().numpy(), par)
+    for g, r, name in zip(got, ref, ("accept_len", "out_tokens", "out_nodes")):
+        np.testing.assert_array_equal(g, r, err_msg=name)
+    say(f"mean AL = {got[0].mean():.3f}")

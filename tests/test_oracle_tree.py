@@ -145,3 +145,21 @@ def test_parents_must_precede_children():
     with pytest.raises(ValueError):
         tree_ancestors([0, 2])
     assert tree_ancestors([0, 0, 1]) == [{0}, {0, 1}, {0, 2}, {0, 1, 3}]
+
+
+def test_tree_workload_shape():
+    """The tree drafter of workloads/: a full tree in level order (parents
+    precede children), distinct sibling tokens, the same shape per sequence."""
+    from workloads import WorkloadSpec, tree_inputs, tree_parents
+    par = tree_parents([2, 2, 2, 2])
+    assert len(par) == 30 and all(0 <= p < i for i, p in enumerate(par, start=1))
+    assert [par.count(p) for p in range(15)] == [2] * 15
+    sp = WorkloadSpec(name="t", batch=2, kv_heads=1, group=2, head_dim=64, kv_len=100, draft_len=1, vocab=50,
+                      mode="greedy", target_std=3.0, draft_noise_std=1.0)
+    inp, parents, tokens = tree_inputs(sp, [3, 2])
+    assert inp.q.shape[0] == 2 * 10 and parents.tolist() == tree_parents([3, 2]) * 2
+    for b in range(2):
+        tk = tokens[b * 9:(b + 1) * 9].tolist()
+        for p in range(10):
+            sib = [tk[i - 1] for i, q in enumerate(tree_parents([3, 2]), start=1) if q == p]
+            assert len(set(sib)) == len(sib)
