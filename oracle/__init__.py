@@ -16,6 +16,9 @@ the pages' definitions:
 * tree.py — tree verification: attention under the ancestor mask of a draft
   tree, and greedy acceptance of its longest accepted path (the LLM inference
   handbook, section "Medusa").
+* lossy.py — acceptance relaxed by the Jensen-Shannon distance between the
+  draft and target distributions, with the draft entropy reported per row
+  (the LLM inference handbook, section "AdaSD").
 * gemm.py — the verify-shaped linear layer y = x W^T whose GEMM-M grows to
   M*(1+D) under speculation (the co-design page, section "Draft length and
   performance of linear layers").
@@ -29,11 +32,12 @@ only the seeded input generators in ``workloads/``.
 from .attention import bf16_bits_to_f64, verify_attention, verify_attention_unit
 from .accept import accept_greedy, accept_stochastic, accept_reject, row_log_normalizer
 from .gemm import linear_abs_sum, verify_linear
+from .lossy import accept_lossy, js_distance, row_entropy
 from .tree import accept_tree_greedy, tree_ancestors, verify_tree_attention, verify_tree_attention_unit
 
 __all__ = [
     "bf16_bits_to_f64", "verify_attention", "verify_attention_unit",
     "accept_greedy", "accept_stochastic", "accept_reject", "row_log_normalizer",
-    "verify_linear", "linear_abs_sum",
+    "verify_linear", "linear_abs_sum", "accept_lossy", "js_distance", "row_entropy",
     "verify_tree_attention", "verify_tree_attention_unit", "accept_tree_greedy", "tree_ancestors",
 ]
