@@ -387,6 +387,127 @@ def run_tree(args):
         "clock_settle_s": args.settle_s}), flush=True)
 
 
+def run_lossy(args):
+    """Relaxed acceptance (a draft also passes when the JS distance of its rows
+    is at most tau) on the default workload, timed beside the lossless call and
+    the attention; one JSON line."""
+    import numpy as np
+    import torch
+
+    import speculative_decoding_verification_sd_amd as sdv
+    from workloads import generate, preset
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sp = preset("g8_kv32k_D15", seed=args.seed)
+    tau = args.js_threshold
+    print(f"[bench] lossy tau={tau}: generating {sp.name}", file=sys.stderr, flush=True)
+    inp = generate(sp, device=dev)
+    B, T, V = sp.batch, inp.q.shape[0], sp.vocab
+    out = torch.empty_like(inp.q)
+    al = torch.empty(B, dtype=torch.int32, device=dev)
+    al0 = torch.empty(B, dtype=torch.int32, device=dev)
+    tok = torch.empty(T, dtype=torch.int32, device=dev)
+    ent = torch.empty(T - B, dtype=torch.float32, device=dev)
+    js = torch.empty(T - B, dtype=torch.float32, device=dev)
+    adesc = sdv.attn_desc(inp.q, inp.k_cache, inp.block_table, sp.group, inp.max_draft)
+    cdesc = sdv.accept_desc(B, V, inp.max_draft, sp.mode)
+    ws_a = torch.empty(max(1, sdv.sd_verify_attention_workspace_size(adesc, T)), dtype=torch.uint8, device=dev)
+    ws_c = torch.empty(max(1, sdv.sd_accept_lossy_workspace_size(cdesc, T)), dtype=torch.uint8, device=dev)
+
+    def attention():
+        sdv.sd_verify_attention(inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.kv_len, inp.q_start, out,
+                                group_size=sp.group, max_draft=inp.max_draft, workspace=ws_a)
+
+    def lossless():
+        sdv.sd_accept_reject(inp.target_logits, inp.draft_logits, inp.draft_tokens, inp.q_start, inp.uniforms,
+                             al0, tok, mode=sp.mode, max_draft=inp.max_draft, workspace=ws_c)
+
+    def lossy():
+        sdv.sd_accept_lossy(inp.target_logits, inp.draft_logits, inp.draft_tokens, inp.q_start, inp.uniforms,
+                            al, tok, mode=sp.mode, max_draft=inp.max_draft, js_threshold=tau,
+                            draft_entropy=ent, js_distance=js, workspace=ws_c)
+
+    t_end = time.perf_counter() + max(0.0, args.settle_s)
+    while time.perf_counter() < t_end:
+        for _ in range(5):
+            attention()
+            lossless()
+            lossy()
+        torch.cuda.synchronize()
+    for _ in range(max(1, args.warmup)):
+        attention()
+        lossless()
+        lossy()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        attention()
+        ev[k][1].record(stream)
+        lossless()
+        ev[k][2].record(stream)
+        lossy()
+        ev[k][3].record(stream)
+    torch.cuda.synchronize()
+    a_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    l0_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    l_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    c0 = algorithmic_accept(inp)
+    c_bytes = c0 + 2 * (T - B) * V * 4          # + the second read of every drafted row pair
+    achieved = c_bytes / (l_ms * 1e-3) / 1e9
+    step_s = (a_ms + l_ms) * 1e-3
+    print(json.dumps({
+        "metric": "verified tokens/s per verify step with JS-relaxed acceptance (+ % HBM roofline of the "
+                  "relaxed accept call)",
+        "value": T / step_s, "unit": "verified tokens/s", "higher_is_better": True, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": a_ms + l_ms, "dtype": "fp32", "data": "synthetic",
+        "config": {"workload": f"{sp.name}_lossy", "batch": B, "kv_heads": sp.kv_heads, "group": sp.group,
+                   "head_dim": sp.head_dim, "kv_len": sp.kv_len, "draft_len": sp.draft_len, "vocab": V,
+                   "accept": sp.mode, "js_threshold": tau, "seed": sp.seed},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "relaxed accept/reject (row statistics, JS terms, decision and sampling launches)",
+                     "algorithmic_bytes_per_launch": c_bytes},
+        "attention_ms": a_ms, "lossless_accept_ms": l0_ms, "lossy_accept_ms": l_ms,
+        "mean_accept_len": float(al.float().mean().item()),
+        "mean_accept_len_lossless": float(al0.float().mean().item()),
+        "emitted_tokens_per_s": float(al.sum().item()) / step_s,
+        "emitted_tokens_per_s_lossless": float(al0.sum().item()) / ((a_ms + l0_ms) * 1e-3),
+        "mean_js_distance": float(js.mean().item()), "mean_draft_entropy": float(ent.mean().item()),
+        "clock_settle_s": args.settle_s}), flush=True)
+
+
+def write_lossy_profile(bench_json: str, kt_dir: str):
+    """Kernel-time summary under profiles/ of a rocprofv3 --kernel-trace --stats
+    run of `bench.py --lossy`, with the bench line of the same call."""
+    with open(bench_json) as f:
+        line = json.loads(f.read().strip().splitlines()[-1])
+    wl = line["config"]["workload"]
+    stats = [r for r in _rocprof_csv(kt_dir, "kernel_stats") if "sdv::" in r["Name"] and "attn" not in r["Name"]]
+    path = os.path.join(ROOT, "profiles", f"accept_lossy_{wl}_kernel_stats.txt")
+    with open(path, "w") as f:
+        f.write(f"# rocprofv3 kernel-trace summary of the accept kernels, workload {wl} (tau = "
+                f"{line['config']['js_threshold']}):\n"
+                "# each step runs the lossless call (accept_rowstats<1,...>, accept_finish<false>) and the relaxed\n"
+                "# call (accept_rowstats<2,...>, accept_jsd, accept_finish<true>).  Calls = clock-settle + warmup +\n"
+                "# timed steps.  Durations in ns.\n"
+                "$ cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d REPO/gpurun_out/kt_lossy "
+                "-o run --output-format csv -- python3 REPO/bench.py --lossy\n")
+        f.write("Name,Calls,TotalDurationNs,AverageNs,Percentage,MinNs,MaxNs,StdDev\n")
+        for r in stats:
+            f.write(",".join([r["Name"], r["Calls"], r["TotalDurationNs"], r["AverageNs"], r["Percentage"],
+                              r["MinNs"], r["MaxNs"], r["StdDev"]]) + "\n")
+        lossy = sum(float(r["AverageNs"]) for r in stats if "<2" in r["Name"] or "jsd" in r["Name"]
+                    or "finish<true>" in r["Name"])
+        f.write(f"relaxed accept call (rowstats<2> + jsd + finish<true> averages): {lossy / 1e3:.1f} us\n")
+        f.write(f"bench.py in the same call: relaxed accept {line['lossy_accept_ms'] * 1e3:.1f} us/step, lossless "
+                f"{line['lossless_accept_ms'] * 1e3:.1f} us/step (HIP events), HBM {line['roofline']['frac']:.3f} "
+                f"of peak, mean AL {line['mean_accept_len']:.3f} (lossless {line['mean_accept_len_lossless']:.3f})\n")
+    print(f"wrote {path}")
+
+
 def write_tree_profile(bench_json: str, kt_dir: str):
     """Kernel-time summary under profiles/ of a rocprofv3 --kernel-trace --stats
     run of `bench.py --tree`, with the bench line of the same call."""
@@ -636,9 +757,17 @@ def main():
                     help="tree verification (ancestor-mask attention + greedy path acceptance), binary tree of depth 4")
     ap.add_argument("--write-tree-profile", nargs=2, metavar=("BENCH_JSON", "KT_DIR"),
                     help="write the profiles/ summary of a --tree line and its rocprofv3 kernel trace (no GPU)")
+    ap.add_argument("--lossy", action="store_true",
+                    help="acceptance relaxed by the Jensen-Shannon distance, beside the lossless call")
+    ap.add_argument("--js-threshold", type=float, default=0.3, help="JS-distance threshold of --lossy")
+    ap.add_argument("--write-lossy-profile", nargs=2, metavar=("BENCH_JSON", "KT_DIR"),
+                    help="write the profiles/ summary of a --lossy line and its rocprofv3 kernel trace (no GPU)")
     args = ap.parse_args()
     if args.write_tree_profile:
         write_tree_profile(*args.write_tree_profile)
+        return
+    if args.write_lossy_profile:
+        write_lossy_profile(*args.write_lossy_profile)
         return
     if args.write_profiles:
         write_profiles(*args.write_profiles, copy_bytes=args.calibrate_copy or (1 << 30))
@@ -661,6 +790,9 @@ def main():
         return
     if args.tree:
         run_tree(args)
+        return
+    if args.lossy:
+        run_lossy(args)
         return
     if args.sweep is not None:
         args.sweep = args.sweep or list(range(32))

@@ -162,6 +162,44 @@ sd_status sd_accept_reject(const sd_accept_desc* desc, int32_t total_q,
                            const float* uniforms, int32_t* accept_len, int32_t* out_tokens,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* Workspace bytes sd_accept_lossy needs.  Returns 0 for an invalid description. */
+size_t sd_accept_lossy_workspace_size(const sd_accept_desc* desc, int32_t total_q);
+
+/*
+ * Relaxed (lossy) accept / reject.  Adaptive speculative decoding may loosen
+ * how strictly each draft token is checked, so that tokens close enough to the
+ * target pass and the output leaves the target's exact distribution; AdaSD
+ * decides "close enough" by the Jensen-Shannon distance between the draft and
+ * target distributions and reports the draft entropy, which tells the drafter
+ * when to stop (the LLM inference handbook, sections on adaptive speculative
+ * decoding and "AdaSD").
+ *
+ * As sd_accept_reject (same layouts, modes and sampling after the first
+ * failure), except that draft x_{i+1} of a sequence also passes when
+ *   JS(p_i, q_i) <= js_threshold,
+ * with p_i = softmax(target row t0+i), q_i = softmax(draft row d0+i) and
+ * JS = sqrt(KL(p||m)/2 + KL(q||m)/2), m = (p+q)/2, natural logarithms
+ * (0 <= JS <= sqrt(ln 2)).  A token outside [0, V) never passes.  A negative
+ * js_threshold gives the lossless result; NaN is rejected.  draft_logits are
+ * required in both modes (uniforms only for SD_ACCEPT_STOCHASTIC).
+ *
+ *   draft_entropy fp32 [total_q - B] or NULL: -sum_j q_i(j) ln q_i(j) of every
+ *                 drafted row, written also past the first failure;
+ *   js_distance   fp32 [total_q - B] or NULL: JS(p_i, q_i) of every drafted row.
+ *
+ * The divergence terms are evaluated in fp32 per token and summed in fp64;
+ * the statistics and the threshold test are taken in fp64 from those sums.
+ * Extra cost over sd_accept_reject: one more read of every drafted target and
+ * draft row.
+ */
+sd_status sd_accept_lossy(const sd_accept_desc* desc, int32_t total_q,
+                          const float* target_logits, const float* draft_logits,
+                          const int32_t* draft_tokens, const int32_t* q_start,
+                          const float* uniforms, float js_threshold,
+                          int32_t* accept_len, int32_t* out_tokens,
+                          float* draft_entropy, float* js_distance,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace for sd_verify_step: one buffer holding both parts' scratch. */
 size_t sd_verify_step_workspace_size(const sd_attn_desc* attn, const sd_accept_desc* acc,
                                      int32_t total_q);

@@ -1,7 +1,9 @@
 """The speculative-decoding verify step on AMD Instinct MI355X (gfx950).
 
 Verify attention over a paged bf16 KV cache and vocab-parallel accept/reject
-(plus draft-tree verification and the verify-shaped linear layer y = x W^T), as hand-written HIP kernels behind a C ABI (``include/sd_verify.h``,
+(plus draft-tree verification, acceptance relaxed by the Jensen-Shannon
+distance, and the verify-shaped linear layer y = x W^T), as hand-written HIP
+kernels behind a C ABI (``include/sd_verify.h``,
 ``libsdverify.so``).  This package is the Python binding of that ABI: it
 marshals PyTorch device tensors and the current stream into the C calls.
 """
@@ -14,6 +16,8 @@ from .binding import (  # noqa: F401
     attn_desc,
     lib,
     linear_desc,
+    sd_accept_lossy,
+    sd_accept_lossy_workspace_size,
     sd_accept_reject,
     sd_accept_reject_workspace_size,
     sd_last_error,
@@ -34,4 +38,5 @@ __all__ = [
     "sd_last_error", "sd_verify_attention", "sd_verify_attention_workspace_size", "sd_verify_step",
     "sd_verify_step_workspace_size", "sd_version", "linear_desc", "sd_verify_linear",
     "sd_verify_linear_workspace_size", "sd_verify_tree_attention", "sd_tree_accept", "sd_tree_accept_workspace_size",
+    "sd_accept_lossy", "sd_accept_lossy_workspace_size",
 ]

@@ -74,6 +74,9 @@ SIGNATURES = {
     "sd_accept_reject_workspace_size": (_SZ, [ctypes.POINTER(sd_accept_desc), _I]),
     "sd_accept_reject": (ctypes.c_int, [ctypes.POINTER(sd_accept_desc), _I, _P, _P, _P, _P, _P, _P, _P, _P,
                                         _SZ, _P]),
+    "sd_accept_lossy_workspace_size": (_SZ, [ctypes.POINTER(sd_accept_desc), _I]),
+    "sd_accept_lossy": (ctypes.c_int, [ctypes.POINTER(sd_accept_desc), _I, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P,
+                                       _P, _P, _P, _SZ, _P]),
     "sd_verify_step_workspace_size": (_SZ, [ctypes.POINTER(sd_attn_desc), ctypes.POINTER(sd_accept_desc), _I]),
     "sd_verify_step": (ctypes.c_int, [ctypes.POINTER(sd_attn_desc), ctypes.POINTER(sd_accept_desc), _I,
                                       _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -153,6 +156,10 @@ def sd_accept_reject_workspace_size(desc: sd_accept_desc, total_q: int) -> int:
     return int(lib().sd_accept_reject_workspace_size(ctypes.byref(desc), total_q))
 
 
+def sd_accept_lossy_workspace_size(desc: sd_accept_desc, total_q: int) -> int:
+    return int(lib().sd_accept_lossy_workspace_size(ctypes.byref(desc), total_q))
+
+
 def sd_verify_step_workspace_size(attn: sd_attn_desc, acc: sd_accept_desc, total_q: int) -> int:
     return int(lib().sd_verify_step_workspace_size(ctypes.byref(attn), ctypes.byref(acc), total_q))
 
@@ -230,6 +237,33 @@ def sd_accept_reject(target_logits, draft_logits, draft_tokens, q_start, uniform
                                   _ptr(draft_tokens), _ptr(q_start), _ptr(uniforms if stoch else None),
                                   _ptr(accept_len), _ptr(out_tokens), _ptr(ws), ws.numel() * ws.element_size(),
                                   _stream(target_logits.device, stream)))
+
+
+def sd_accept_lossy(target_logits, draft_logits, draft_tokens, q_start, uniforms, accept_len, out_tokens, *,
+                    mode: str, max_draft: int, js_threshold: float, draft_entropy: Optional[torch.Tensor] = None,
+                    js_distance: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                    stream=None) -> None:
+    """Accept/reject where a draft also passes when the Jensen-Shannon distance
+    of its target and draft rows is at most js_threshold (negative: lossless);
+    optionally writes every drafted row's draft entropy and JS distance."""
+    stoch = mode == "stochastic"
+    _check_accept_args(target_logits, draft_logits, draft_tokens, q_start, uniforms, accept_len, out_tokens, mode)
+    B = q_start.shape[0] - 1
+    T, V = target_logits.shape
+    _need(draft_logits, "draft_logits", torch.float32, target_logits.device)
+    if draft_logits.shape != (T - B, V):
+        raise ValueError("draft_logits [T_q - B, V] expected")
+    for t, name in ((draft_entropy, "draft_entropy"), (js_distance, "js_distance")):
+        if t is not None:
+            _need(t, name, torch.float32, target_logits.device)
+            if t.shape != (T - B,):
+                raise ValueError(f"{name} [T_q - B] expected")
+    desc = accept_desc(B, V, max_draft, mode)
+    ws = _workspace(sd_accept_lossy_workspace_size(desc, T), target_logits.device, workspace)
+    _check(lib().sd_accept_lossy(ctypes.byref(desc), T, _ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens),
+                                 _ptr(q_start), _ptr(uniforms if stoch else None), float(js_threshold),
+                                 _ptr(accept_len), _ptr(out_tokens), _ptr(draft_entropy), _ptr(js_distance),
+                                 _ptr(ws), ws.numel() * ws.element_size(), _stream(target_logits.device, stream)))
 
 
 def sd_verify_step(q, k_cache, v_cache, block_table, kv_len, q_start, attn_out, target_logits, draft_logits,

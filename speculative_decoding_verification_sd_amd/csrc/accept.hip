@@ -74,6 +74,12 @@ struct AccParams {
   unsigned* arrived;  // [B] sampling workgroups done (cleared by accept_rowstats)
   double* rsum;       // [B, nschunk, 2]  (residual, p) chunk sums
   double* rsub;       // [B, nschunk, 256, 2]  (residual, p) sums of each thread's 16 tokens
+  // relaxed acceptance only
+  double* ent;        // [T-B, nchunk]  chunk sums of exp(x - m) (x - m) of the draft rows
+  double* jsp;        // [T-B, nchunk]  chunk sums of the Jensen-Shannon terms
+  float* out_ent;     // [T-B] draft entropy per drafted row (or NULL)
+  float* out_js;      // [T-B] JS distance per drafted row (or NULL)
+  float tau;          // JS threshold (< 0: off)
   int B, T, V, nchunk, nschunk, max_draft, vec4;
 };
 
@@ -128,33 +134,28 @@ __device__ __forceinline__ bool seq_ok(const AccParams& p, int t0, int D, int d0
   return t0 >= 0 && t0 + D < p.T && d0 >= 0 && d0 + D <= p.T - p.B;
 }
 
-// ---------------------------------------------------------------------------
-template <int STOCH, int VEC4>
-__global__ __launch_bounds__(kAccThreads) void accept_rowstats(AccParams p) {
-  __shared__ float sm[4];
-  __shared__ int si[4];
-  __shared__ double sd[4];
-  const int row = blockIdx.x / p.nchunk;
-  const int c = blockIdx.x - row * p.nchunk;
-  if (STOCH && blockIdx.x == 0)
-    for (int i = threadIdx.x; i < p.B; i += kAccThreads) p.arrived[i] = 0u;
-  const float* src = row < p.T ? p.target + (size_t)row * p.V : p.draft + (size_t)(row - p.T) * p.V;
+// Element k of this thread in a chunk of kChunk logits starting at j0: index
+// j0 + (k/4)*1024 + tid*4 + k%4 (VEC4) or j0 + k*256 + tid (scalar),
+// increasing in k either way; past the vocabulary it reads -inf.
+template <int VEC4>
+__device__ __forceinline__ int chunk_index(int j0, int k) {
   const int tid = threadIdx.x;
-  const int j0 = c * kChunk;
+  return VEC4 ? j0 + ((k >> 2) * kAccThreads + tid) * 4 + (k & 3) : j0 + k * kAccThreads + tid;
+}
 
-  // element k of this thread has index j0 + (k/4)*1024 + tid*4 + k%4 (VEC4) or
-  // j0 + k*256 + tid (scalar): increasing in k either way
-  float x[kPerThread];
+template <int VEC4>
+__device__ __forceinline__ void load_chunk(const float* src, int j0, int V, float (&x)[kPerThread]) {
+  const int tid = threadIdx.x;
   if (VEC4) {
 #pragma unroll
     for (int k = 0; k < kPerThread / 4; ++k) {
       const int j = j0 + (k * kAccThreads + tid) * 4;
       f32x4 v;
-      if (j + 3 < p.V) {
+      if (j + 3 < V) {
         v = *(const f32x4*)(src + j);
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = j + e < p.V ? src[j + e] : -INFINITY;
+        for (int e = 0; e < 4; ++e) v[e] = j + e < V ? src[j + e] : -INFINITY;
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[k * 4 + e] = v[e];
@@ -163,55 +164,195 @@ __global__ __launch_bounds__(kAccThreads) void accept_rowstats(AccParams p) {
 #pragma unroll
     for (int k = 0; k < kPerThread; ++k) {
       const int j = j0 + k * kAccThreads + tid;
-      x[k] = j < p.V ? src[j] : -INFINITY;
-    }
-  }
-  auto index_of = [&](int k) {
-    return VEC4 ? j0 + ((k >> 2) * kAccThreads + tid) * 4 + (k & 3) : j0 + k * kAccThreads + tid;
-  };
-
-  if (!STOCH) {
-    // lowest-index maximum: strict '>' over increasing indices; a row of -inf
-    // still reports a real index (first element inside the vocabulary)
-    float m = -INFINITY;
-    int idx = INT_MAX;
-#pragma unroll
-    for (int k = 0; k < kPerThread; ++k) {
-      const int j = index_of(k);
-      if (x[k] > m || (idx == INT_MAX && j < p.V)) { m = x[k]; idx = j; }
-    }
-    block_argmax(m, idx, sm, si);
-    if (tid == 0) {
-      RowPart r;
-      r.m = m;
-      r.idx = idx;
-      r.s = 0.0;
-      p.part[(size_t)row * p.nchunk + c] = r;
-    }
-  } else {
-    float m = x[0];
-#pragma unroll
-    for (int k = 1; k < kPerThread; ++k) m = fmaxf(m, x[k]);
-    m = block_max(m, sm);
-    double s = 0.0;
-    if (m != -INFINITY) {
-      // exp(x - m) as 2^((x - m) log2 e); fp32 terms, fp64 running sum
-      const float ml = m * 1.4426950408889634f;
-#pragma unroll
-      for (int k = 0; k < kPerThread; ++k) s += (double)fast_exp2(fmaf(x[k], 1.4426950408889634f, -ml));
-      s = block_sum(s, sd);
-    }
-    if (tid == 0) {
-      RowPart r;
-      r.m = m;
-      r.idx = 0;
-      r.s = s;
-      p.part[(size_t)row * p.nchunk + c] = r;
+      x[k] = j < V ? src[j] : -INFINITY;
     }
   }
 }
 
 // ---------------------------------------------------------------------------
+// MODE 0: greedy (lowest-index maximum); 1: stochastic (maximum and sum of
+// exp(x - max)); 2: relaxed acceptance (all of those, and for draft rows the
+// sum of exp(x - max) (x - max), from which the row's entropy follows).
+template <int MODE, int VEC4>
+__global__ __launch_bounds__(kAccThreads) void accept_rowstats(AccParams p) {
+  __shared__ float sm[4];
+  __shared__ int si[4];
+  __shared__ double sd[4];
+  const int row = blockIdx.x / p.nchunk;
+  const int c = blockIdx.x - row * p.nchunk;
+  if (MODE != 0 && p.arrived && blockIdx.x == 0)
+    for (int i = threadIdx.x; i < p.B; i += kAccThreads) p.arrived[i] = 0u;
+  const float* src = row < p.T ? p.target + (size_t)row * p.V : p.draft + (size_t)(row - p.T) * p.V;
+  const int tid = threadIdx.x;
+  const int j0 = c * kChunk;
+  float x[kPerThread];
+  load_chunk<VEC4>(src, j0, p.V, x);
+
+  RowPart r;
+  r.idx = 0;
+  r.s = 0.0;
+  float m;
+  if (MODE != 1) {
+    // lowest-index maximum: strict '>' over increasing indices; a row of -inf
+    // still reports a real index (first element inside the vocabulary)
+    m = -INFINITY;
+    int idx = INT_MAX;
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) {
+      const int j = chunk_index<VEC4>(j0, k);
+      if (x[k] > m || (idx == INT_MAX && j < p.V)) { m = x[k]; idx = j; }
+    }
+    block_argmax(m, idx, sm, si);
+    r.idx = idx;
+  } else {
+    m = x[0];
+#pragma unroll
+    for (int k = 1; k < kPerThread; ++k) m = fmaxf(m, x[k]);
+    m = block_max(m, sm);
+  }
+  r.m = m;
+  if (MODE != 0) {
+    const bool ent = MODE == 2 && row >= p.T;   // (uniform over the workgroup)
+    double s = 0.0, s1 = 0.0;
+    if (m != -INFINITY) {
+      // exp(x - m) as 2^((x - m) log2 e); fp32 terms, fp64 running sums
+      const float ml = m * 1.4426950408889634f;
+#pragma unroll
+      for (int k = 0; k < kPerThread; ++k) {
+        const float e = fast_exp2(fmaf(x[k], 1.4426950408889634f, -ml));
+        s += (double)e;
+        if (ent && e > 0.f) s1 += (double)(e * (x[k] - m));
+      }
+      s = block_sum(s, sd);
+      if (ent) s1 = block_sum(s1, sd);
+    }
+    r.s = s;
+    if (ent && tid == 0) p.ent[(size_t)(row - p.T) * p.nchunk + c] = s1;
+  }
+  if (tid == 0) p.part[(size_t)row * p.nchunk + c] = r;
+}
+
+// log-normaliser of row `prow` from its chunk statistics, by one wave (lane k
+// takes chunks k, k+64, ...); every lane gets it.
+__device__ __forceinline__ double row_lse64(const AccParams& p, int prow) {
+  const int lane = threadIdx.x & 63;
+  const RowPart* pr = p.part + (size_t)prow * p.nchunk;
+  float M = -INFINITY;
+  for (int k = lane; k < p.nchunk; k += 64) M = fmaxf(M, pr[k].m);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  double Z = 0.0;
+  for (int k = lane; k < p.nchunk; k += 64) {
+    const RowPart q = pr[k];
+    if (q.m != -INFINITY) Z += exp((double)q.m - (double)M) * q.s;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) Z += __shfl_xor(Z, off);
+  return (double)M + log(Z);
+}
+
+// ---------------------------------------------------------------------------
+// Relaxed acceptance: chunk sums of the Jensen-Shannon divergence terms of one
+// drafted row pair (grid = drafted rows x vocab chunks), the JS distance
+// between the draft and target distributions being what decides whether a
+// draft token is close enough (the LLM inference handbook, section "AdaSD").
+// With l = ln((p_j + q_j)/2) the divergence is half the sum over j of
+// t_j = p_j (ln p_j - l) + q_j (ln q_j - l).  With x = |ln p_j - ln q_j|,
+// u = x/2 and P the larger of p_j, q_j, t_j = 2 sqrt(p_j q_j) (u sinh u -
+// cosh u ln cosh u), whose series is sqrt(p_j q_j) (u^2 + u^6/72 - u^8/360 +
+// 443 u^10/604800 - 559 u^12/2721600 + ...) (relative error below 2e-8 for
+// x < 1); for x >= 1, t_j = P ((1 + e^-x) h - x e^-x) with h = ln 2 -
+// ln(1 + e^-x), which has no cancellation there and gives P ln 2 when one side
+// is zero.  Terms in fp32 with the hardware exp2/log2, sums in fp64.
+template <int VEC4>
+__global__ __launch_bounds__(kAccThreads) void accept_jsd(AccParams p) {
+  __shared__ double sd[4];
+  __shared__ double s_lse[2];
+  const int r = blockIdx.x / p.nchunk;          // drafted row
+  const int c = blockIdx.x - r * p.nchunk;
+  const int tid = threadIdx.x;
+  // its sequence: the last b with q_start[b] - b <= r
+  int lo = 0, hi = p.B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.q_start[mid] - mid <= r) lo = mid;
+    else hi = mid - 1;
+  }
+  const int b = lo;
+  const int t0 = p.q_start[b], D = seq_d(p, b), d0 = t0 - b;
+  const int i = r - d0;
+  if (!seq_ok(p, t0, D, d0) || i < 0 || i >= D) {
+    if (tid == 0) p.jsp[(size_t)r * p.nchunk + c] = 0.0;
+    return;
+  }
+  if (tid < 64) {
+    const double lp = row_lse64(p, t0 + i);
+    const double lq = row_lse64(p, p.T + r);
+    if (tid == 0) { s_lse[0] = lp; s_lse[1] = lq; }
+  }
+  __syncthreads();
+  const float lse_p = (float)s_lse[0], lse_q = (float)s_lse[1];
+  const float dlse = (float)(s_lse[0] - s_lse[1]);
+  const int j0 = c * kChunk;
+  float tl[kPerThread], dl[kPerThread];
+  load_chunk<VEC4>(p.target + (size_t)(t0 + i) * p.V, j0, p.V, tl);
+  load_chunk<VEC4>(p.draft + (size_t)r * p.V, j0, p.V, dl);
+  double acc = 0.0;
+#pragma unroll
+  for (int k0 = 0; k0 < kPerThread; k0 += 8) {
+    float part = 0.f;                            // eight terms in fp32, then into the fp64 sum
+#pragma unroll
+    for (int k = k0; k < k0 + 8; ++k) {
+      const float a = tl[k] - lse_p, bq = dl[k] - lse_q;     // ln p_j, ln q_j
+      const float hi = fmaxf(a, bq);
+      const float x = fabsf((tl[k] - dl[k]) - dlse);          // |ln p_j - ln q_j| (inf: one side 0)
+      float t;
+      if (x < 1.f) {
+        const float u = 0.5f * x, u2 = u * u;
+        const float poly = u2 * (1.f + u2 * u2 * (1.f / 72.f + u2 * (-1.f / 360.f + u2 * (443.f / 604800.f +
+                                                                       u2 * (-559.f / 2721600.f)))));
+        t = __expf(0.5f * (a + bq)) * poly;
+      } else {
+        const float y = __expf(-x);
+        const float h = 0.69314718f * (1.f - __log2f(1.f + y));
+        t = __expf(hi) * ((1.f + y) * h - (y > 0.f ? y * x : 0.f));
+      }
+      if (hi != -INFINITY) part += t;                         // (p_j = q_j = 0: no term)
+    }
+    acc += (double)part;
+  }
+  acc = block_sum(acc, sd);
+  if (tid == 0) p.jsp[(size_t)r * p.nchunk + c] = acc;
+}
+
+// Entropy (nats) and JS distance of drafted row r, from the chunk sums, by one
+// thread: H = log S0 - S1/S0 with S0 = sum_c exp(m_c - M) s_c and S1 = sum_c
+// exp(m_c - M) (e_c + (m_c - M) s_c); JS = sqrt(JSD) with JSD half the sum of
+// the chunk sums of the divergence terms.
+__device__ __forceinline__ void row_relaxed_stats(const AccParams& p, int r, double& H, double& js) {
+  const RowPart* pr = p.part + (size_t)(p.T + r) * p.nchunk;
+  const double* e = p.ent + (size_t)r * p.nchunk;
+  const double* jp = p.jsp + (size_t)r * p.nchunk;
+  float M = -INFINITY;
+  for (int k = 0; k < p.nchunk; ++k) M = fmaxf(M, pr[k].m);
+  double S0 = 0.0, S1 = 0.0, J = 0.0;
+  for (int k = 0; k < p.nchunk; ++k) {
+    const RowPart q = pr[k];
+    if (q.m != -INFINITY) {
+      const double w = exp((double)q.m - (double)M);
+      S0 += w * q.s;
+      S1 += w * (e[k] + ((double)q.m - (double)M) * q.s);
+    }
+    J += jp[k];
+  }
+  H = log(S0) - S1 / S0;
+  js = sqrt(fmax(0.0, 0.5 * J));
+}
+
+// ---------------------------------------------------------------------------
+// LOSSY: a draft also passes when the JS distance of its rows is at most tau,
+// and the rows' entropy and JS distance are written out.
+template <bool LOSSY>
 __global__ __launch_bounds__(kAccThreads) void accept_decide(AccParams p) {
   extern __shared__ int amax[];                 // [D+1] row argmaxes
   __shared__ RowPart stage[kDecideSlots];
@@ -248,7 +389,15 @@ __global__ __launch_bounds__(kAccThreads) void accept_decide(AccParams p) {
 
   for (int i = tid; i < D; i += kAccThreads) {
     const int x = p.tokens[d0 + i];
-    if (!(x >= 0 && x < p.V && x == amax[i])) atomicMin(&first_fail, i);
+    bool pass = x >= 0 && x < p.V && x == amax[i];
+    if constexpr (LOSSY) {
+      double H, js;
+      row_relaxed_stats(p, d0 + i, H, js);
+      if (p.out_ent) p.out_ent[d0 + i] = (float)H;
+      if (p.out_js) p.out_js[d0 + i] = (float)js;
+      pass = x >= 0 && x < p.V && (x == amax[i] || js <= (double)p.tau);
+    }
+    if (!pass) atomicMin(&first_fail, i);
   }
   __syncthreads();
   const int n = first_fail;
@@ -387,6 +536,7 @@ __device__ __forceinline__ double row_lse16(const AccParams& p, int prow, int la
 }
 
 // ---------------------------------------------------------------------------
+template <bool LOSSY>
 __global__ __launch_bounds__(kAccThreads) void accept_finish(AccParams p) {
   __shared__ double sd[4], s_wtot[4];
   __shared__ int s_fail, s_have, s_last, s_chunk, s_usep, s_slice, s_slice_last;
@@ -427,7 +577,18 @@ __global__ __launch_bounds__(kAccThreads) void accept_finish(AccParams p) {
     if (live) { my_lp = lp; my_lq = lq; my_i = i; }
     if (test) {
       const double r = exp(((double)tl - lp) - ((double)dl - lq));
-      if (!(inv && (double)ut < r)) atomicMin(&s_fail, i);
+      bool pass = inv && (double)ut < r;
+      if constexpr (LOSSY) {
+        // relaxed: the draft also passes when the JS distance of its rows is at most tau
+        double H, js;
+        row_relaxed_stats(p, d0 + i, H, js);
+        if (blockIdx.x == 0) {
+          if (p.out_ent) p.out_ent[d0 + i] = (float)H;
+          if (p.out_js) p.out_js[d0 + i] = (float)js;
+        }
+        pass = inv && ((double)ut < r || js <= (double)p.tau);
+      }
+      if (!pass) atomicMin(&s_fail, i);
     }
   }
   __syncthreads();
@@ -591,21 +752,27 @@ __global__ __launch_bounds__(kAccThreads) void accept_finish(AccParams p) {
 }
 
 struct AccLayout {
-  size_t part_off, arrived_off, rsum_off, rsub_off, total;
+  size_t part_off, arrived_off, rsum_off, rsub_off, ent_off, jsp_off, total;
   int nchunk, nschunk;
 };
 
-static AccLayout acc_layout(int B, int T, int V, int stochastic) {
+// Row statistics cover the target rows, and the draft rows too when the
+// acceptance is stochastic or relaxed; the relaxed rule adds two chunk-sum
+// arrays over the draft rows.
+static AccLayout acc_layout(int B, int T, int V, int stochastic, int lossy) {
   AccLayout L;
   L.nchunk = (V + kChunk - 1) / kChunk;
   L.nschunk = (V + kSChunk - 1) / kSChunk;
-  const size_t rows = stochastic ? (size_t)T + (size_t)(T - B) : (size_t)T;
+  const size_t drows = (size_t)(T - B);
+  const size_t rows = (stochastic || lossy) ? (size_t)T + drows : (size_t)T;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += (bytes + 255) / 256 * 256; return o; };
   L.part_off = take(rows * L.nchunk * sizeof(RowPart));
   L.arrived_off = take((size_t)B * sizeof(unsigned));
   L.rsum_off = take((size_t)B * L.nschunk * 2 * sizeof(double));
   L.rsub_off = take(stochastic ? (size_t)B * L.nschunk * kAccThreads * 2 * sizeof(double) : 0);
+  L.ent_off = take(lossy ? drows * L.nchunk * sizeof(double) : 0);
+  L.jsp_off = take(lossy ? drows * L.nchunk * sizeof(double) : 0);
   L.total = off;
   return L;
 }
@@ -614,12 +781,12 @@ static AccLayout acc_layout(int B, int T, int V, int stochastic) {
 
 using namespace sdv;
 
-size_t sdv_accept_workspace_bytes(int B, int T, int V, int stochastic) {
-  return acc_layout(B, T, V, stochastic).total;
+size_t sdv_accept_workspace_bytes(int B, int T, int V, int stochastic, int lossy) {
+  return acc_layout(B, T, V, stochastic, lossy).total;
 }
 
 hipError_t sdv_accept_launch(const SdAccLaunch& a) {
-  const AccLayout L = acc_layout(a.B, a.T, a.V, a.stochastic);
+  const AccLayout L = acc_layout(a.B, a.T, a.V, a.stochastic, a.lossy);
   unsigned char* ws = (unsigned char*)a.workspace;
   AccParams p;
   p.target = a.target;
@@ -633,6 +800,11 @@ hipError_t sdv_accept_launch(const SdAccLaunch& a) {
   p.arrived = (unsigned*)(ws + L.arrived_off);
   p.rsum = (double*)(ws + L.rsum_off);
   p.rsub = (double*)(ws + L.rsub_off);
+  p.ent = a.lossy ? (double*)(ws + L.ent_off) : nullptr;
+  p.jsp = a.lossy ? (double*)(ws + L.jsp_off) : nullptr;
+  p.out_ent = a.lossy ? a.out_entropy : nullptr;
+  p.out_js = a.lossy ? a.out_js : nullptr;
+  p.tau = a.lossy ? a.js_threshold : -1.f;
   p.B = a.B;
   p.T = a.T;
   p.V = a.V;
@@ -640,28 +812,44 @@ hipError_t sdv_accept_launch(const SdAccLaunch& a) {
   p.nschunk = L.nschunk;
   p.max_draft = a.max_draft;
 
+  const bool need_draft = a.stochastic || a.lossy;
   const bool vec4 = (a.V % 4 == 0) && ((uintptr_t)a.target % 16 == 0) &&
-                    (!a.stochastic || (uintptr_t)a.draft % 16 == 0);
+                    (!need_draft || (uintptr_t)a.draft % 16 == 0);
   p.vec4 = vec4;
-  const size_t rows = a.stochastic ? (size_t)a.T + (size_t)(a.T - a.B) : (size_t)a.T;
+  const size_t drows = (size_t)(a.T - a.B);
+  const size_t rows = need_draft ? (size_t)a.T + drows : (size_t)a.T;
   const unsigned grid1 = (unsigned)(rows * L.nchunk);
-  if (a.stochastic) {
+  if (a.lossy) {
+    if (vec4) accept_rowstats<2, 1><<<grid1, kAccThreads, 0, a.stream>>>(p);
+    else accept_rowstats<2, 0><<<grid1, kAccThreads, 0, a.stream>>>(p);
+    if (drows > 0) {
+      const unsigned grid2 = (unsigned)(drows * L.nchunk);
+      if (vec4) accept_jsd<1><<<grid2, kAccThreads, 0, a.stream>>>(p);
+      else accept_jsd<0><<<grid2, kAccThreads, 0, a.stream>>>(p);
+    }
+  } else if (a.stochastic) {
     if (vec4) accept_rowstats<1, 1><<<grid1, kAccThreads, 0, a.stream>>>(p);
     else accept_rowstats<1, 0><<<grid1, kAccThreads, 0, a.stream>>>(p);
-    // workgroups per sequence: all chunks, or about kFinishWGs / B in all when
-    // that is fewer (each then takes several chunks)
-    const int per_seq = std::max(1, std::min(L.nschunk, (kFinishWGs + a.B - 1) / std::max(a.B, 1)));
-    accept_finish<<<dim3(per_seq, a.B), kAccThreads, 0, a.stream>>>(p);
   } else {
     if (vec4) accept_rowstats<0, 1><<<grid1, kAccThreads, 0, a.stream>>>(p);
     else accept_rowstats<0, 0><<<grid1, kAccThreads, 0, a.stream>>>(p);
-    accept_decide<<<a.B, kAccThreads, (size_t)(a.max_draft + 1) * sizeof(int), a.stream>>>(p);
+  }
+  if (a.stochastic) {
+    // workgroups per sequence: all chunks, or about kFinishWGs / B in all when
+    // that is fewer (each then takes several chunks)
+    const int per_seq = std::max(1, std::min(L.nschunk, (kFinishWGs + a.B - 1) / std::max(a.B, 1)));
+    if (a.lossy) accept_finish<true><<<dim3(per_seq, a.B), kAccThreads, 0, a.stream>>>(p);
+    else accept_finish<false><<<dim3(per_seq, a.B), kAccThreads, 0, a.stream>>>(p);
+  } else {
+    const size_t lds = (size_t)(a.max_draft + 1) * sizeof(int);
+    if (a.lossy) accept_decide<true><<<a.B, kAccThreads, lds, a.stream>>>(p);
+    else accept_decide<false><<<a.B, kAccThreads, lds, a.stream>>>(p);
   }
   return hipGetLastError();
 }
 
 hipError_t sdv_tree_accept_launch(const SdAccLaunch& a, const int32_t* parents, int32_t* out_nodes) {
-  const AccLayout L = acc_layout(a.B, a.T, a.V, 0);
+  const AccLayout L = acc_layout(a.B, a.T, a.V, 0, 0);
   unsigned char* ws = (unsigned char*)a.workspace;
   AccParams p;
   p.target = a.target;
@@ -675,6 +863,9 @@ hipError_t sdv_tree_accept_launch(const SdAccLaunch& a, const int32_t* parents, 
   p.arrived = (unsigned*)(ws + L.arrived_off);
   p.rsum = nullptr;
   p.rsub = nullptr;
+  p.ent = p.jsp = nullptr;
+  p.out_ent = p.out_js = nullptr;
+  p.tau = -1.f;
   p.B = a.B;
   p.T = a.T;
   p.V = a.V;

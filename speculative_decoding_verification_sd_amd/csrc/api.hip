@@ -55,7 +55,7 @@ sd_status check_attn(const sd_attn_desc* d, int32_t total_q) {
   return SD_OK;
 }
 
-sd_status check_accept(const sd_accept_desc* d, int32_t total_q) {
+sd_status check_accept(const sd_accept_desc* d, int32_t total_q, bool lossy = false) {
   if (!d) return fail(SD_ERR_INVALID_ARG, "accept descriptor is NULL");
   if (d->num_seqs < 0) return fail(SD_ERR_INVALID_ARG, "num_seqs=%d must be >= 0", d->num_seqs);
   if (d->vocab < 1) return fail(SD_ERR_INVALID_ARG, "vocab=%d must be >= 1", d->vocab);
@@ -65,7 +65,7 @@ sd_status check_accept(const sd_accept_desc* d, int32_t total_q) {
     return fail(SD_ERR_INVALID_ARG, "mode=%d is not an sd_accept_mode", d->mode);
   if (total_q < d->num_seqs || (long long)total_q > (long long)d->num_seqs * (1LL + d->max_draft))
     return fail(SD_ERR_INVALID_ARG, "total_q=%d must lie in [num_seqs, num_seqs*(1+max_draft)]", total_q);
-  const long long rows = d->mode == SD_ACCEPT_STOCHASTIC ? 2LL * total_q - d->num_seqs : total_q;
+  const long long rows = (d->mode == SD_ACCEPT_STOCHASTIC || lossy) ? 2LL * total_q - d->num_seqs : total_q;
   if (rows * ((d->vocab + 4095) / 4096) > 0x7fffffffLL)
     return fail(SD_ERR_UNSUPPORTED, "rows x vocab chunks exceeds the launch grid");
   return SD_OK;
@@ -76,8 +76,8 @@ size_t attn_ws(const sd_attn_desc* d) {
                                   d->max_pages_per_seq, d->max_draft, d->kv_chunk);
 }
 
-size_t acc_ws(const sd_accept_desc* d, int32_t total_q) {
-  return sdv_accept_workspace_bytes(d->num_seqs, total_q, d->vocab, d->mode == SD_ACCEPT_STOCHASTIC);
+size_t acc_ws(const sd_accept_desc* d, int32_t total_q, bool lossy = false) {
+  return sdv_accept_workspace_bytes(d->num_seqs, total_q, d->vocab, d->mode == SD_ACCEPT_STOCHASTIC, lossy);
 }
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -122,11 +122,20 @@ sd_status run_attention(const sd_attn_desc* d, int32_t total_q, const void* q, c
   return SD_OK;
 }
 
+// The relaxed rule (lossy) adds the JS threshold and the two optional per-row outputs.
+struct Relaxed {
+  bool on = false;
+  float tau = -1.f;
+  float* entropy = nullptr;
+  float* js = nullptr;
+};
+
 sd_status run_accept(const sd_accept_desc* d, int32_t total_q, const float* target, const float* draft,
                      const int32_t* tokens, const int32_t* q_start, const float* uniforms, int32_t* al,
-                     int32_t* out_tokens, void* ws, size_t ws_bytes, void* stream) {
-  sd_status s = check_accept(d, total_q);
+                     int32_t* out_tokens, void* ws, size_t ws_bytes, void* stream, Relaxed rx = Relaxed()) {
+  sd_status s = check_accept(d, total_q, rx.on);
   if (s != SD_OK) return s;
+  if (rx.on && isnan(rx.tau)) return fail(SD_ERR_INVALID_ARG, "js_threshold is NaN");
   if (d->num_seqs == 0) return SD_OK;
   const bool stoch = d->mode == SD_ACCEPT_STOCHASTIC;
   const bool any_drafts = total_q > d->num_seqs;
@@ -134,11 +143,13 @@ sd_status run_accept(const sd_accept_desc* d, int32_t total_q, const float* targ
     return fail(SD_ERR_INVALID_ARG, "a required accept pointer is NULL");
   if (stoch && (!uniforms || (any_drafts && !draft)))
     return fail(SD_ERR_INVALID_ARG, "stochastic acceptance needs draft_logits and uniforms");
-  const size_t need = acc_ws(d, total_q);
+  if (rx.on && any_drafts && !draft)
+    return fail(SD_ERR_INVALID_ARG, "relaxed acceptance needs draft_logits");
+  const size_t need = acc_ws(d, total_q, rx.on);
   if (!ws || ws_bytes < need)
     return fail(SD_ERR_WORKSPACE, "accept workspace %zu bytes < required %zu", ws_bytes, need);
   if ((uintptr_t)ws % 16) return fail(SD_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-  SdAccLaunch a;
+  SdAccLaunch a{};
   a.target = target;
   a.draft = draft;
   a.tokens = tokens;
@@ -152,6 +163,10 @@ sd_status run_accept(const sd_accept_desc* d, int32_t total_q, const float* targ
   a.V = d->vocab;
   a.max_draft = d->max_draft;
   a.stochastic = stoch;
+  a.lossy = rx.on;
+  a.js_threshold = rx.tau;
+  a.out_entropy = rx.entropy;
+  a.out_js = rx.js;
   a.stream = (hipStream_t)stream;
   hipError_t e = sdv_accept_launch(a);
   if (e != hipSuccess) return fail(SD_ERR_HIP, "accept/reject launch: %s", hipGetErrorString(e));
@@ -200,6 +215,25 @@ SD_EXPORT sd_status sd_accept_reject(const sd_accept_desc* desc, int32_t total_q
                            size_t workspace_bytes, void* stream) {
   return run_accept(desc, total_q, target_logits, draft_logits, draft_tokens, q_start, uniforms, accept_len,
                     out_tokens, workspace, workspace_bytes, stream);
+}
+
+SD_EXPORT size_t sd_accept_lossy_workspace_size(const sd_accept_desc* desc, int32_t total_q) {
+  if (check_accept(desc, total_q, true) != SD_OK) return 0;
+  return acc_ws(desc, total_q, true);
+}
+
+SD_EXPORT sd_status sd_accept_lossy(const sd_accept_desc* desc, int32_t total_q, const float* target_logits,
+                                    const float* draft_logits, const int32_t* draft_tokens, const int32_t* q_start,
+                                    const float* uniforms, float js_threshold, int32_t* accept_len,
+                                    int32_t* out_tokens, float* draft_entropy, float* js_distance, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  Relaxed rx;
+  rx.on = true;
+  rx.tau = js_threshold;
+  rx.entropy = draft_entropy;
+  rx.js = js_distance;
+  return run_accept(desc, total_q, target_logits, draft_logits, draft_tokens, q_start, uniforms, accept_len,
+                    out_tokens, workspace, workspace_bytes, stream, rx);
 }
 
 SD_EXPORT size_t sd_verify_step_workspace_size(const sd_attn_desc* attn, const sd_accept_desc* acc, int32_t total_q) {
@@ -267,7 +301,7 @@ SD_EXPORT sd_status sd_tree_accept(const sd_accept_desc* d, int32_t total_q, con
   if (!workspace || workspace_bytes < need)
     return fail(SD_ERR_WORKSPACE, "tree-accept workspace %zu bytes < required %zu", workspace_bytes, need);
   if ((uintptr_t)workspace % 16) return fail(SD_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-  SdAccLaunch a;
+  SdAccLaunch a{};
   a.target = target_logits;
   a.draft = nullptr;
   a.tokens = tree_tokens;

@@ -93,13 +93,17 @@ struct SdAccLaunch {
   int32_t* out_tokens;
   void* workspace;
   int B, T, V, max_draft, stochastic;
+  int lossy;              // relaxed acceptance: a draft also passes when its rows' JS distance <= js_threshold
+  float js_threshold;
+  float* out_entropy;     // [T-B] or NULL (relaxed only)
+  float* out_js;          // [T-B] or NULL (relaxed only)
   hipStream_t stream;
 };
 
 size_t sdv_attn_workspace_bytes(int B, int Hkv, int G, int head_dim, int max_pages, int max_draft,
                                 int kv_chunk);
 hipError_t sdv_attn_launch(const SdAttnLaunch& a);
-size_t sdv_accept_workspace_bytes(int B, int T, int V, int stochastic);
+size_t sdv_accept_workspace_bytes(int B, int T, int V, int stochastic, int lossy);
 hipError_t sdv_accept_launch(const SdAccLaunch& a);
 hipError_t sdv_tree_accept_launch(const SdAccLaunch& a, const int32_t* parents, int32_t* out_nodes);
 

@@ -188,3 +188,24 @@ def test_tree_calls_reject_bad_arguments():
     d = _attn()
     st = lib.sd_verify_tree_attention(ctypes.byref(d), 8, *([dummy] * 6), None, dummy, dummy, 1 << 30, None)
     assert st == B.SD_ERR_INVALID_ARG and "parents" in sdv.sd_last_error()
+
+
+def test_lossy_call_rejects_bad_arguments():
+    lib = sdv.lib()
+    dummy = ctypes.c_void_p(4096)
+    a = _acc(mode=0)
+    assert sdv.sd_accept_lossy_workspace_size(a, 8) > sdv.sd_accept_reject_workspace_size(a, 8)
+    # greedy still needs the draft logits (the JS distance compares both distributions)
+    st = lib.sd_accept_lossy(ctypes.byref(a), 8, dummy, None, dummy, dummy, None, ctypes.c_float(0.1), dummy,
+                             dummy, None, None, dummy, 1 << 30, None)
+    assert st == B.SD_ERR_INVALID_ARG and "draft_logits" in sdv.sd_last_error()
+    st = lib.sd_accept_lossy(ctypes.byref(a), 8, dummy, dummy, dummy, dummy, None, ctypes.c_float(float("nan")),
+                             dummy, dummy, None, None, dummy, 1 << 30, None)
+    assert st == B.SD_ERR_INVALID_ARG and "NaN" in sdv.sd_last_error()
+    st = lib.sd_accept_lossy(ctypes.byref(a), 8, dummy, dummy, dummy, dummy, None, ctypes.c_float(0.1),
+                             dummy, dummy, None, None, dummy, 8, None)
+    assert st == B.SD_ERR_WORKSPACE
+    a = _acc(mode=1)
+    st = lib.sd_accept_lossy(ctypes.byref(a), 8, dummy, dummy, dummy, dummy, None, ctypes.c_float(0.1),
+                             dummy, dummy, None, None, dummy, 1 << 30, None)
+    assert st == B.SD_ERR_INVALID_ARG and "uniforms" in sdv.sd_last_error()
