@@ -19,6 +19,10 @@ the pages' definitions:
 * lossy.py — acceptance relaxed by the Jensen-Shannon distance between the
   draft and target distributions, with the draft entropy reported per row
   (the LLM inference handbook, section "AdaSD").
+* loop.py — a closed speculative-decoding loop on a bigram toy LM: an n-gram
+  drafter, greedy verification and an EMA-of-AL controller over draft-length
+  tiers (the LLM inference handbook, section on SGLang's adaptive speculative
+  decoding).
 * gemm.py — the verify-shaped linear layer y = x W^T whose GEMM-M grows to
   M*(1+D) under speculation (the co-design page, section "Draft length and
   performance of linear layers").
