@@ -479,6 +479,103 @@ def run_lossy(args):
         "clock_settle_s": args.settle_s}), flush=True)
 
 
+LOOP_B, LOOP_V, LOOP_PROMPT, LOOP_MAX_LEN, LOOP_STEPS = 64, 4096, 256, 4096, 400
+
+
+def run_loop(args):
+    """The closed speculative-decoding loop on a bigram toy LM (64 sequences,
+    V = 4096, 256-token random prompts, trigram drafter), adaptive over tiers
+    1/3/7 with one graph per tier, beside the same loop with direct launches,
+    a fixed top tier and no speculation (D = 0); one JSON line."""
+    import numpy as np
+    import torch
+
+    import speculative_decoding_verification_sd_amd as sdv
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    g = torch.Generator().manual_seed(args.seed)
+    W = (torch.randn((LOOP_V, LOOP_V), generator=g) * 3.0).to(dev)
+    rng = np.random.default_rng(args.seed)
+    prompts = torch.from_numpy(rng.integers(0, LOOP_V, size=(LOOP_B, LOOP_PROMPT)).astype(np.int32))
+    ws = torch.empty(sdv.sd_closed_loop_workspace_size(sdv.loop_desc(LOOP_B, LOOP_V, LOOP_MAX_LEN, (0, 1, 3, 7))),
+                     dtype=torch.uint8, device=dev)
+
+    def once(tiers, graphs, steps=LOOP_STEPS):
+        h = torch.zeros((LOOP_B, LOOP_MAX_LEN), dtype=torch.int32, device=dev)
+        h[:, :LOOP_PROMPT] = prompts.to(dev)
+        ln = torch.full((LOOP_B,), LOOP_PROMPT, dtype=torch.int32, device=dev)
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        al, tr = sdv.sd_closed_loop(W, h, ln, steps=steps, tiers=tiers, ngram=3, ema_weight=0.5,
+                                    use_graphs=graphs, workspace=ws)
+        torch.cuda.synchronize()
+        t = time.perf_counter() - t
+        return t, al.numpy(), tr.numpy(), (h.cpu().numpy(), ln.cpu().numpy())
+
+    once((1, 3, 7), True, steps=20)                          # warm the clock and the code paths
+    runs, outs = {}, []
+    for name, tiers, graphs in (("adaptive_graphs", (1, 3, 7), True), ("adaptive_direct", (1, 3, 7), False),
+                                ("fixed_D7_graphs", (7,), True), ("no_speculation_graphs", (0,), True)):
+        t, al, tr, h = once(tiers, graphs)
+        runs[name] = {"seconds": t, "tokens": int(al.sum()), "tokens_per_s": float(al.sum()) / t,
+                      "us_per_round": t / LOOP_STEPS * 1e6, "mean_al": float(al[al > 0].mean()),
+                      "rounds_per_tier": {str(d): int((tr == d).sum()) for d in sorted(set(tr.tolist()))}}
+        print(f"[bench] loop {name}: {runs[name]['tokens_per_s']:.0f} tok/s, {runs[name]['us_per_round']:.1f} "
+              f"us/round, AL {runs[name]['mean_al']:.2f}", file=sys.stderr, flush=True)
+        outs.append(h)
+    # every run is the same greedy decoding, so the histories agree on their common prefix
+    agree = all(np.array_equal(a[0][b, :min(a[1][b], c[1][b])], c[0][b, :min(a[1][b], c[1][b])])
+                for a in outs for c in outs for b in range(LOOP_B))
+    main = runs["adaptive_graphs"]
+    # per-round algorithmic bytes: W rows gathered into the logits (read + write) and read once by the accept
+    # pass, at the adaptive run's mean 1+D
+    rows = LOOP_B * (1 + np.mean([int(d) for d, n in main["rounds_per_tier"].items() for _ in range(n)]))
+    nbytes = rows * LOOP_V * 4 * 3
+    achieved = nbytes / (main["us_per_round"] * 1e-6) / 1e9
+    print(json.dumps({
+        "metric": "emitted tokens/s of the closed adaptive speculative-decoding loop (bigram toy LM)",
+        "value": main["tokens_per_s"], "unit": "emitted tokens/s", "higher_is_better": True, "n_gpus": 1,
+        "steps": LOOP_STEPS, "warmup": 20, "ms_per_step": main["us_per_round"] / 1e3, "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": f"loop_b{LOOP_B}_v{LOOP_V}_prompt{LOOP_PROMPT}_tiers137_ngram3", "batch": LOOP_B,
+                   "vocab": LOOP_V, "prompt": LOOP_PROMPT, "max_len": LOOP_MAX_LEN, "rounds": LOOP_STEPS,
+                   "tiers": [1, 3, 7], "ngram": 3, "ema_weight": 0.5, "seed": args.seed},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "one round (draft, toy-LM logits, accept, append) incl. launch and host sync",
+                     "algorithmic_bytes_per_launch": nbytes,
+                     "note": "latency-bound: a round moves a few MB and waits for the host each time"},
+        "outputs_agree": bool(agree), "runs": runs}), flush=True)
+
+
+def write_loop_profile(bench_json: str, kt_dir: str):
+    """Kernel-time summary under profiles/ of a rocprofv3 --kernel-trace --stats
+    run of `bench.py --loop`, with the bench line of the same call."""
+    with open(bench_json) as f:
+        line = json.loads(f.read().strip().splitlines()[-1])
+    wl = line["config"]["workload"]
+    stats = [r for r in _rocprof_csv(kt_dir, "kernel_stats") if "sdv::" in r["Name"]]
+    path = os.path.join(ROOT, "profiles", f"closed_loop_{wl}_kernel_stats.txt")
+    with open(path, "w") as f:
+        f.write(f"# rocprofv3 kernel-trace summary of the closed loop, workload {wl}: every round runs\n"
+                "# loop_draft, loop_logits, accept_rowstats<0,...>, accept_decide<false>, loop_append; the calls\n"
+                "# cover all four runs of bench.py --loop (adaptive with graphs, adaptive with direct launches,\n"
+                "# fixed D = 7, no speculation) and the warm-up.  Durations in ns.\n"
+                "$ cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d REPO/gpurun_out/kt_loop "
+                "-o run --output-format csv -- python3 REPO/bench.py --loop\n")
+        f.write("Name,Calls,TotalDurationNs,AverageNs,Percentage,MinNs,MaxNs,StdDev\n")
+        for r in stats:
+            f.write(",".join([r["Name"], r["Calls"], r["TotalDurationNs"], r["AverageNs"], r["Percentage"],
+                              r["MinNs"], r["MaxNs"], r["StdDev"]]) + "\n")
+        per_round = sum(float(r["AverageNs"]) for r in stats if "qstart" not in r["Name"])
+        f.write(f"kernel time per round (sum of the five averages): {per_round / 1e3:.1f} us\n")
+        for name, r in line["runs"].items():
+            f.write(f"bench.py {name}: {r['us_per_round']:.1f} us/round wall (incl. launch and host sync), "
+                    f"{r['tokens_per_s']:.0f} emitted tokens/s, mean AL {r['mean_al']:.2f}\n")
+    print(f"wrote {path}")
+
+
 def write_lossy_profile(bench_json: str, kt_dir: str):
     """Kernel-time summary under profiles/ of a rocprofv3 --kernel-trace --stats
     run of `bench.py --lossy`, with the bench line of the same call."""
@@ -760,6 +857,10 @@ def main():
     ap.add_argument("--lossy", action="store_true",
                     help="acceptance relaxed by the Jensen-Shannon distance, beside the lossless call")
     ap.add_argument("--js-threshold", type=float, default=0.3, help="JS-distance threshold of --lossy")
+    ap.add_argument("--loop", action="store_true",
+                    help="the closed adaptive speculative-decoding loop on a bigram toy LM (graphs vs direct)")
+    ap.add_argument("--write-loop-profile", nargs=2, metavar=("BENCH_JSON", "KT_DIR"),
+                    help="write the profiles/ summary of a --loop line and its rocprofv3 kernel trace (no GPU)")
     ap.add_argument("--write-lossy-profile", nargs=2, metavar=("BENCH_JSON", "KT_DIR"),
                     help="write the profiles/ summary of a --lossy line and its rocprofv3 kernel trace (no GPU)")
     args = ap.parse_args()
@@ -768,6 +869,9 @@ def main():
         return
     if args.write_lossy_profile:
         write_lossy_profile(*args.write_lossy_profile)
+        return
+    if args.write_loop_profile:
+        write_loop_profile(*args.write_loop_profile)
         return
     if args.write_profiles:
         write_profiles(*args.write_profiles, copy_bytes=args.calibrate_copy or (1 << 30))
@@ -793,6 +897,9 @@ def main():
         return
     if args.lossy:
         run_lossy(args)
+        return
+    if args.loop:
+        run_loop(args)
         return
     if args.sweep is not None:
         args.sweep = args.sweep or list(range(32))

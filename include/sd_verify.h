@@ -271,6 +271,59 @@ sd_status sd_tree_accept(const sd_accept_desc* desc, int32_t total_q, const floa
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Closed speculative-decoding loop on a toy LM (an extension next to the
+ * verify step proper).  Each round drafts D tokens per sequence, verifies them
+ * in one pass and keeps the accepted prefix; after each round the mean
+ * acceptance length feeds an exponential moving average (EMA) that picks the
+ * next round's D among a few tiers, each tier with its own captured HIP graph,
+ * so that switching tiers costs no recapture (the LLM inference handbook,
+ * section on SGLang's adaptive speculative decoding, default tiers [1, 3, 7]).
+ * Only the speculation length adapts, so the output is the target's greedy
+ * decoding.
+ *
+ *   target    a bigram toy LM: the logits after token a are row a of
+ *             bigram_logits (fp32 [V, V]); verification is sd_accept_reject's
+ *             greedy rule;
+ *   drafter   model-free n-gram lookup: the latest earlier occurrence of the
+ *             history's last k tokens (k = ngram, ngram-1, ..., 1) proposes the
+ *             D tokens that followed it (-1, never accepted, where the history
+ *             ends or nothing matches);
+ *   controller ema starts at 1; after round s, ema = (1-w) ema + w mean(AL)
+ *             over the sequences that appended; the next D is the smallest
+ *             tier >= ema, else the largest tier.
+ *
+ * history int32 [B, max_len] and length int32 [B] (device; length >= 1) are
+ * updated in place: a round appends the AL emitted tokens of each sequence,
+ * or nothing once they would pass max_len.  accept_trace int32 [steps, B] and
+ * tier_trace int32 [steps] are host buffers (pinned memory is fastest) that
+ * receive the tokens appended per sequence and the D of each round.
+ *
+ * Unlike the other calls this one waits for the stream once per round (to
+ * read the acceptance lengths), and with use_graphs != 0 it creates, captures
+ * and destroys one graph per tier on a stream of its own (graph objects are
+ * the only resources it creates).  tiers: 1..8 strictly ascending values in
+ * [0, 63]; ngram in [1, 8]; vocab <= 65536; ema_weight in (0, 1].
+ */
+#define SD_LOOP_MAX_TIERS 8
+typedef struct {
+  int32_t num_seqs;                    /* B >= 1 */
+  int32_t vocab;                       /* V */
+  int32_t max_len;                     /* history capacity per sequence */
+  int32_t ngram;                       /* drafter order */
+  int32_t num_tiers;
+  int32_t tiers[SD_LOOP_MAX_TIERS];    /* draft lengths, ascending */
+  float ema_weight;                    /* w */
+  int32_t use_graphs;                  /* 1: one captured graph per tier; 0: direct launches */
+} sd_loop_desc;
+
+size_t sd_closed_loop_workspace_size(const sd_loop_desc* desc);
+
+sd_status sd_closed_loop(const sd_loop_desc* desc, const float* bigram_logits,
+                         int32_t* history, int32_t* length, int32_t steps,
+                         int32_t* accept_trace, int32_t* tier_trace,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Verify-shaped linear layer (an extension next to the verify step proper).
  * With speculation every linear layer of the target sees M*(1+D) rows in the
  * verify pass instead of M, against the same weight: the GEMM-M grows by the

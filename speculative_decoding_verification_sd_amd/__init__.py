@@ -2,7 +2,8 @@
 
 Verify attention over a paged bf16 KV cache and vocab-parallel accept/reject
 (plus draft-tree verification, acceptance relaxed by the Jensen-Shannon
-distance, and the verify-shaped linear layer y = x W^T), as hand-written HIP
+distance, a closed adaptive-speculation loop on a toy LM, and the
+verify-shaped linear layer y = x W^T), as hand-written HIP
 kernels behind a C ABI (``include/sd_verify.h``,
 ``libsdverify.so``).  This package is the Python binding of that ABI: it
 marshals PyTorch device tensors and the current stream into the C calls.
@@ -16,10 +17,13 @@ from .binding import (  # noqa: F401
     attn_desc,
     lib,
     linear_desc,
+    loop_desc,
     sd_accept_lossy,
     sd_accept_lossy_workspace_size,
     sd_accept_reject,
     sd_accept_reject_workspace_size,
+    sd_closed_loop,
+    sd_closed_loop_workspace_size,
     sd_last_error,
     sd_verify_attention,
     sd_verify_attention_workspace_size,
@@ -38,5 +42,5 @@ __all__ = [
     "sd_last_error", "sd_verify_attention", "sd_verify_attention_workspace_size", "sd_verify_step",
     "sd_verify_step_workspace_size", "sd_version", "linear_desc", "sd_verify_linear",
     "sd_verify_linear_workspace_size", "sd_verify_tree_attention", "sd_tree_accept", "sd_tree_accept_workspace_size",
-    "sd_accept_lossy", "sd_accept_lossy_workspace_size",
+    "sd_accept_lossy", "sd_accept_lossy_workspace_size", "loop_desc", "sd_closed_loop", "sd_closed_loop_workspace_size",
 ]

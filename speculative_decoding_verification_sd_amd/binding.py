@@ -62,6 +62,22 @@ class sd_linear_desc(ctypes.Structure):
     ]
 
 
+SD_LOOP_MAX_TIERS = 8
+
+
+class sd_loop_desc(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("vocab", ctypes.c_int32),
+        ("max_len", ctypes.c_int32),
+        ("ngram", ctypes.c_int32),
+        ("num_tiers", ctypes.c_int32),
+        ("tiers", ctypes.c_int32 * SD_LOOP_MAX_TIERS),
+        ("ema_weight", ctypes.c_float),
+        ("use_graphs", ctypes.c_int32),
+    ]
+
+
 _lib: Optional[ctypes.CDLL] = None
 _P = ctypes.c_void_p
 _SZ = ctypes.c_size_t
@@ -84,6 +100,8 @@ SIGNATURES = {
                                                 _P, _SZ, _P]),
     "sd_tree_accept_workspace_size": (_SZ, [ctypes.POINTER(sd_accept_desc), _I]),
     "sd_tree_accept": (ctypes.c_int, [ctypes.POINTER(sd_accept_desc), _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "sd_closed_loop_workspace_size": (_SZ, [ctypes.POINTER(sd_loop_desc)]),
+    "sd_closed_loop": (ctypes.c_int, [ctypes.POINTER(sd_loop_desc), _P, _P, _P, _I, _P, _P, _P, _SZ, _P]),
     "sd_verify_linear_workspace_size": (_SZ, [ctypes.POINTER(sd_linear_desc)]),
     "sd_verify_linear": (ctypes.c_int, [ctypes.POINTER(sd_linear_desc), _P, _P, _P, _P, _SZ, _P]),
     "sd_last_error": (ctypes.c_char_p, []),
@@ -264,6 +282,46 @@ def sd_accept_lossy(target_logits, draft_logits, draft_tokens, q_start, uniforms
                                  _ptr(q_start), _ptr(uniforms if stoch else None), float(js_threshold),
                                  _ptr(accept_len), _ptr(out_tokens), _ptr(draft_entropy), _ptr(js_distance),
                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(target_logits.device, stream)))
+
+
+def loop_desc(num_seqs: int, vocab: int, max_len: int, tiers=(1, 3, 7), ngram: int = 3, ema_weight: float = 0.5,
+              use_graphs: bool = True) -> sd_loop_desc:
+    tiers = list(tiers)
+    if not 1 <= len(tiers) <= SD_LOOP_MAX_TIERS:
+        raise ValueError(f"1..{SD_LOOP_MAX_TIERS} tiers expected")
+    arr = (ctypes.c_int32 * SD_LOOP_MAX_TIERS)(*(tiers + [0] * (SD_LOOP_MAX_TIERS - len(tiers))))
+    return sd_loop_desc(num_seqs=num_seqs, vocab=vocab, max_len=max_len, ngram=ngram, num_tiers=len(tiers),
+                        tiers=arr, ema_weight=ema_weight, use_graphs=int(bool(use_graphs)))
+
+
+def sd_closed_loop_workspace_size(desc: sd_loop_desc) -> int:
+    return int(lib().sd_closed_loop_workspace_size(ctypes.byref(desc)))
+
+
+def sd_closed_loop(bigram_logits, history, length, *, steps: int, tiers=(1, 3, 7), ngram: int = 3,
+                   ema_weight: float = 0.5, use_graphs: bool = True, workspace: Optional[torch.Tensor] = None,
+                   stream=None):
+    """Run `steps` rounds of the closed speculative-decoding loop on the bigram
+    toy LM (bigram_logits fp32 [V, V]); history int32 [B, max_len] and length
+    int32 [B] are updated in place.  Returns (accept_trace int32 [steps, B],
+    tier_trace int32 [steps]) as host tensors."""
+    dev = bigram_logits.device
+    _need(bigram_logits, "bigram_logits", torch.float32)
+    _need(history, "history", torch.int32, dev)
+    _need(length, "length", torch.int32, dev)
+    V = bigram_logits.shape[0]
+    if bigram_logits.shape != (V, V) or history.dim() != 2 or length.shape != (history.shape[0],):
+        raise ValueError("bigram_logits [V, V], history [B, max_len] and length [B] expected")
+    B, max_len = history.shape
+    desc = loop_desc(B, V, max_len, tiers, ngram, ema_weight, use_graphs)
+    ws = _workspace(sd_closed_loop_workspace_size(desc), dev, workspace)
+    pin = torch.cuda.is_available()
+    al = torch.zeros((max(steps, 0), B), dtype=torch.int32, pin_memory=pin)
+    tr = torch.zeros(max(steps, 0), dtype=torch.int32, pin_memory=pin)
+    _check(lib().sd_closed_loop(ctypes.byref(desc), _ptr(bigram_logits), _ptr(history), _ptr(length), steps,
+                                ctypes.c_void_p(al.data_ptr()), ctypes.c_void_p(tr.data_ptr()), _ptr(ws),
+                                ws.numel() * ws.element_size(), _stream(dev, stream)))
+    return al, tr
 
 
 def sd_verify_step(q, k_cache, v_cache, block_table, kv_len, q_start, attn_out, target_logits, draft_logits,

@@ -173,6 +173,29 @@ sd_status run_accept(const sd_accept_desc* d, int32_t total_q, const float* targ
   return SD_OK;
 }
 
+sd_status check_loop(const sd_loop_desc* d) {
+  if (!d) return fail(SD_ERR_INVALID_ARG, "loop descriptor is NULL");
+  if (d->num_seqs < 1) return fail(SD_ERR_INVALID_ARG, "num_seqs=%d must be >= 1", d->num_seqs);
+  if (d->vocab < 1 || d->vocab > 65536) return fail(SD_ERR_UNSUPPORTED, "vocab=%d must lie in [1, 65536]", d->vocab);
+  if (d->max_len < 2) return fail(SD_ERR_INVALID_ARG, "max_len=%d must be >= 2", d->max_len);
+  if (d->ngram < 1 || d->ngram > 8) return fail(SD_ERR_UNSUPPORTED, "ngram=%d must lie in [1, 8]", d->ngram);
+  if (d->num_tiers < 1 || d->num_tiers > SD_LOOP_MAX_TIERS)
+    return fail(SD_ERR_INVALID_ARG, "num_tiers=%d must lie in [1, %d]", d->num_tiers, SD_LOOP_MAX_TIERS);
+  for (int t = 0; t < d->num_tiers; ++t) {
+    if (d->tiers[t] < 0 || d->tiers[t] > 63) return fail(SD_ERR_UNSUPPORTED, "tier %d = %d must lie in [0, 63]", t, d->tiers[t]);
+    if (t > 0 && d->tiers[t] <= d->tiers[t - 1]) return fail(SD_ERR_INVALID_ARG, "tiers must be strictly ascending");
+  }
+  if (!(d->ema_weight > 0.f && d->ema_weight <= 1.f)) return fail(SD_ERR_INVALID_ARG, "ema_weight must lie in (0, 1]");
+  const long long rows = (long long)d->num_seqs * (1 + d->tiers[d->num_tiers - 1]);
+  if (rows * ((d->vocab + 1023) / 1024) > 0x7fffffffLL)
+    return fail(SD_ERR_UNSUPPORTED, "num_seqs x (1 + largest tier) rows exceed the launch grid");
+  return SD_OK;
+}
+
+size_t loop_ws(const sd_loop_desc* d) {
+  return sdv_loop_workspace_bytes(d->num_seqs, d->vocab, d->num_tiers, d->tiers[d->num_tiers - 1]);
+}
+
 sd_status check_gemm(const sd_linear_desc* d) {
   if (!d) return fail(SD_ERR_INVALID_ARG, "linear-layer descriptor is NULL");
   if (d->m < 0) return fail(SD_ERR_INVALID_ARG, "m=%d must be >= 0", d->m);
@@ -318,6 +341,47 @@ SD_EXPORT sd_status sd_tree_accept(const sd_accept_desc* d, int32_t total_q, con
   a.stream = (hipStream_t)stream;
   hipError_t e = sdv_tree_accept_launch(a, parents, out_nodes);   // (parents is read only for drafted nodes)
   if (e != hipSuccess) return fail(SD_ERR_HIP, "tree accept launch: %s", hipGetErrorString(e));
+  return SD_OK;
+}
+
+SD_EXPORT size_t sd_closed_loop_workspace_size(const sd_loop_desc* desc) {
+  if (check_loop(desc) != SD_OK) return 0;
+  return loop_ws(desc);
+}
+
+SD_EXPORT sd_status sd_closed_loop(const sd_loop_desc* desc, const float* bigram_logits, int32_t* history,
+                                   int32_t* length, int32_t steps, int32_t* accept_trace, int32_t* tier_trace,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  sd_status s = check_loop(desc);
+  if (s != SD_OK) return s;
+  if (steps < 0) return fail(SD_ERR_INVALID_ARG, "steps=%d must be >= 0", steps);
+  if (steps == 0) return SD_OK;
+  if (!bigram_logits || !history || !length || !accept_trace || !tier_trace)
+    return fail(SD_ERR_INVALID_ARG, "a required closed-loop pointer is NULL");
+  const size_t need = loop_ws(desc);
+  if (!workspace || workspace_bytes < need)
+    return fail(SD_ERR_WORKSPACE, "closed-loop workspace %zu bytes < required %zu", workspace_bytes, need);
+  if ((uintptr_t)workspace % 16 || (uintptr_t)bigram_logits % 16)
+    return fail(SD_ERR_INVALID_ARG, "bigram_logits and workspace must be 16-byte aligned");
+  SdLoopLaunch c{};
+  c.W = bigram_logits;
+  c.hist = history;
+  c.len = length;
+  c.al_trace = accept_trace;
+  c.tier_trace = tier_trace;
+  c.tiers = desc->tiers;
+  c.workspace = workspace;
+  c.B = desc->num_seqs;
+  c.V = desc->vocab;
+  c.max_len = desc->max_len;
+  c.ngram = desc->ngram;
+  c.ntiers = desc->num_tiers;
+  c.steps = steps;
+  c.use_graphs = desc->use_graphs != 0;
+  c.ema_weight = desc->ema_weight;
+  c.stream = (hipStream_t)stream;
+  hipError_t e = sdv_closed_loop(c);
+  if (e != hipSuccess) return fail(SD_ERR_HIP, "closed loop: %s", hipGetErrorString(e));
   return SD_OK;
 }
 

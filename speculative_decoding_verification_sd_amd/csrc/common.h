@@ -107,6 +107,22 @@ size_t sdv_accept_workspace_bytes(int B, int T, int V, int stochastic, int lossy
 hipError_t sdv_accept_launch(const SdAccLaunch& a);
 hipError_t sdv_tree_accept_launch(const SdAccLaunch& a, const int32_t* parents, int32_t* out_nodes);
 
+// A closed speculative-decoding loop on a bigram toy LM (loop.hip).
+struct SdLoopLaunch {
+  const float* W;         // [V, V] bigram logits (device)
+  int32_t* hist;          // [B, max_len] histories (device, updated)
+  int32_t* len;           // [B] lengths (device, updated)
+  int32_t* al_trace;      // [steps, B] appended tokens per round (host)
+  int32_t* tier_trace;    // [steps] draft length of each round (host)
+  const int32_t* tiers;   // [ntiers] ascending draft lengths (host)
+  void* workspace;
+  int B, V, max_len, ngram, ntiers, steps, use_graphs;
+  float ema_weight;
+  hipStream_t stream;
+};
+size_t sdv_loop_workspace_bytes(int B, int V, int ntiers, int dmax);
+hipError_t sdv_closed_loop(const SdLoopLaunch& c);
+
 struct SdGemmLaunch {
   const void* x;
   const void* w;

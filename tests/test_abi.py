@@ -209,3 +209,27 @@ def test_lossy_call_rejects_bad_arguments():
     st = lib.sd_accept_lossy(ctypes.byref(a), 8, dummy, dummy, dummy, dummy, None, ctypes.c_float(0.1),
                              dummy, dummy, None, None, dummy, 1 << 30, None)
     assert st == B.SD_ERR_INVALID_ARG and "uniforms" in sdv.sd_last_error()
+
+
+def test_closed_loop_rejects_bad_descriptions():
+    lib = sdv.lib()
+    dummy = ctypes.c_void_p(4096)
+    ok = sdv.loop_desc(4, 100, 64)
+    assert sdv.sd_closed_loop_workspace_size(ok) > 0
+    for kw, status, needle in [(dict(tiers=(3, 1)), B.SD_ERR_INVALID_ARG, "ascending"),
+                               (dict(tiers=(1, 64)), B.SD_ERR_UNSUPPORTED, "tier"),
+                               (dict(ngram=9), B.SD_ERR_UNSUPPORTED, "ngram"),
+                               (dict(ema_weight=0.0), B.SD_ERR_INVALID_ARG, "ema_weight"),
+                               (dict(max_len=1), B.SD_ERR_INVALID_ARG, "max_len")]:
+        args = dict(num_seqs=4, vocab=100, max_len=64)
+        args.update(kw)
+        d = sdv.loop_desc(**args)
+        assert sdv.sd_closed_loop_workspace_size(d) == 0
+        assert lib.sd_closed_loop(ctypes.byref(d), dummy, dummy, dummy, 3, dummy, dummy, dummy, 1 << 30,
+                                  None) == status
+        assert needle in sdv.sd_last_error()
+    assert lib.sd_closed_loop(ctypes.byref(ok), dummy, dummy, dummy, 3, None, dummy, dummy, 1 << 30,
+                              None) == B.SD_ERR_INVALID_ARG
+    assert lib.sd_closed_loop(ctypes.byref(ok), dummy, dummy, dummy, 3, dummy, dummy, dummy, 8,
+                              None) == B.SD_ERR_WORKSPACE
+    assert lib.sd_closed_loop(ctypes.byref(ok), None, None, None, 0, None, None, None, 0, None) == B.SD_OK
