@@ -479,6 +479,37 @@ def run_lossy(args):
         "clock_settle_s": args.settle_s}), flush=True)
 
 
+def run_read_ceiling(args):
+    """The HBM read rate a plain library reduction reaches on this GPU (row sums
+    of a 2 GiB fp32 matrix of 4096-wide rows, cold each time), as the practical
+    read ceiling next to the datasheet peak; one JSON line."""
+    import numpy as np
+    import torch
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    nbytes = 2 << 30
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device=dev).view(-1, 4096)
+    other = torch.ones(nbytes // 4, dtype=torch.float32, device=dev).view(-1, 4096)   # evicts x between runs
+    sink = torch.empty(x.shape[0], dtype=torch.float32, device=dev)
+    times = []
+    for k in range(args.warmup + args.steps):
+        torch.sum(other, dim=1, out=sink)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.sum(x, dim=1, out=sink)
+        e1.record()
+        torch.cuda.synchronize()
+        if k >= args.warmup:
+            times.append(e0.elapsed_time(e1) * 1e-3)
+    t = float(np.median(times))
+    print(json.dumps({"metric": "HBM read rate of a plain reduction (practical read ceiling)",
+                      "value": nbytes / t / 1e9, "unit": "GB/s", "peak": HBM_PEAK_GBS,
+                      "frac": nbytes / t / 1e9 / HBM_PEAK_GBS, "bytes": nbytes, "us": t * 1e6,
+                      "kernel": "torch.sum over the rows of a 2 GiB fp32 [131072, 4096] matrix",
+                      "steps": args.steps}), flush=True)
+
+
 LOOP_B, LOOP_V, LOOP_PROMPT, LOOP_MAX_LEN, LOOP_STEPS = 64, 4096, 256, 4096, 400
 
 
@@ -857,6 +888,8 @@ def main():
     ap.add_argument("--lossy", action="store_true",
                     help="acceptance relaxed by the Jensen-Shannon distance, beside the lossless call")
     ap.add_argument("--js-threshold", type=float, default=0.3, help="JS-distance threshold of --lossy")
+    ap.add_argument("--read-ceiling", action="store_true",
+                    help="HBM read rate of a plain library reduction over 2 GiB (the practical read ceiling)")
     ap.add_argument("--loop", action="store_true",
                     help="the closed adaptive speculative-decoding loop on a bigram toy LM (graphs vs direct)")
     ap.add_argument("--write-loop-profile", nargs=2, metavar=("BENCH_JSON", "KT_DIR"),
@@ -900,6 +933,9 @@ def main():
         return
     if args.loop:
         run_loop(args)
+        return
+    if args.read_ceiling:
+        run_read_ceiling(args)
         return
     if args.sweep is not None:
         args.sweep = args.sweep or list(range(32))
