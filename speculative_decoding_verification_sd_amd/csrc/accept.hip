@@ -40,8 +40,12 @@
 namespace sdv {
 
 constexpr int kAccThreads = 256;
-constexpr int kChunk = 8192;                      // logits per row-statistics workgroup
-constexpr int kPerThread = kChunk / kAccThreads;  // 32
+// logits per row-statistics workgroup (build-time tunable)
+#ifndef SDV_ACC_CHUNK
+#define SDV_ACC_CHUNK 8192
+#endif
+constexpr int kChunk = SDV_ACC_CHUNK;
+constexpr int kPerThread = kChunk / kAccThreads;  // 32 at the default chunk
 constexpr int kSChunk = 4096;                     // logits per sampling workgroup
 constexpr int kSPerThread = kSChunk / kAccThreads;  // 16: one slice of the sampling search per thread
 static_assert(kSPerThread % 4 == 0 && kSPerThread <= 64, "a slice is scanned by one wave");

@@ -162,7 +162,10 @@ __global__ __launch_bounds__(kPlanThreads) void verify_attn_plan(AttnParams p, i
   __shared__ long long s_ksum, s_full;
   __shared__ int s_nmax;
   __shared__ int s_n[kPlanCacheSeqs];      // N_b
+  __shared__ int s_t0[kPlanCacheSeqs];     // q_start[b]
+  __shared__ int s_d[kPlanCacheSeqs];      // drafts of sequence b
   __shared__ int s_tail[kPlanCacheSeqs];   // tail_pos[b]
+  __shared__ int s_wsum[2][kPlanThreads / 64];
   const int tid = threadIdx.x;
   const int max_keys = p.max_pages * kPage;
   const int cap_chunk = max(kMinChunk, min(kMaxChunk, (max_keys + 63) / 64 * 64));
@@ -179,7 +182,13 @@ __global__ __launch_bounds__(kPlanThreads) void verify_attn_plan(AttnParams p, i
     __syncthreads();
     const int nb = base + tid < p.B ? seq_keys(p, base + tid) : 0;
     s_keys[tid] = nb;
-    if (base + tid < kPlanCacheSeqs) s_n[base + tid] = nb;
+    if (base + tid < kPlanCacheSeqs) {        // (the descriptors' fields, loaded here alongside N_b)
+      s_n[base + tid] = nb;
+      if (base + tid < p.B) {
+        s_t0[base + tid] = p.q_start[base + tid];
+        s_d[base + tid] = seq_drafts(p, base + tid);
+      }
+    }
     ksum += nb;
     nmax = max(nmax, nb);
     __syncthreads();
@@ -268,18 +277,21 @@ __global__ __launch_bounds__(kPlanThreads) void verify_attn_plan(AttnParams p, i
       v = ns * p.Hkv;
       split_of(N, full, tl);
     }
-    scan[tid] = v;
-    fscan[tid] = b < p.B ? full * p.Hkv : 0;
+    // inclusive scans of v and of the full-chunk items: within each wave by
+    // shuffles, then the totals of the waves before it
+    int sv = v, sf = b < p.B ? full * p.Hkv : 0;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int a = __shfl_up(sv, off), f = __shfl_up(sf, off);
+      if (lane >= off) { sv += a; sf += f; }
+    }
+    if (lane == 63) { s_wsum[0][tid >> 6] = sv; s_wsum[1][tid >> 6] = sf; }
     s_keys[tid] = N;
     __syncthreads();
-    for (int off = 1; off < kPlanThreads; off <<= 1) {
-      const int add = tid >= off ? scan[tid - off] : 0;
-      const int fadd = tid >= off ? fscan[tid - off] : 0;
-      __syncthreads();
-      scan[tid] += add;
-      fscan[tid] += fadd;
-      __syncthreads();
-    }
+    for (int w = 0; w < (tid >> 6); ++w) { sv += s_wsum[0][w]; sf += s_wsum[1][w]; }
+    scan[tid] = sv;
+    fscan[tid] = sf;
+    __syncthreads();
     if (b < p.B) p.plan[kPlanHeader + b] = carry + scan[tid] - v;
     const int n = min(kPlanThreads, p.B - base);
     const int group_items = scan[n - 1];
@@ -304,8 +316,8 @@ __global__ __launch_bounds__(kPlanThreads) void verify_attn_plan(AttnParams p, i
       d.h = hj;
       d.k_begin = sj * chunk;
       d.k_end = min(Nj, (sj + 1) * chunk);
-      d.t0 = p.q_start[bj];
-      d.D = seq_drafts(p, bj);
+      d.t0 = bj < kPlanCacheSeqs ? s_t0[bj] : p.q_start[bj];
+      d.D = bj < kPlanCacheSeqs ? s_d[bj] : seq_drafts(p, bj);
       d.N = Nj;
       d.nsplit = nsj;
       p.items[pos] = d;
