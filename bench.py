@@ -234,7 +234,7 @@ def write_profiles(bench_json: str, kt_dir: str, fetch_dir: str, write_dir: str,
         f.write(f"# rocprofv3 kernel-trace summary of the library's kernels, workload {wl}:\n"
                 "# one verify step = verify attention (plan, main, split-KV combine) + accept/reject.\n"
                 f"# {calls} calls per kernel = clock-settle + warmup + timed steps.  Durations in ns.\n"
-                f"$ cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d REPO/gpurun_out/kt "
+                f"$ cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d OUT/kt "
                 f"-o run --output-format csv -- python3 REPO/bench.py {args}\n")
         f.write("Name,Calls,TotalDurationNs,AverageNs,Percentage,MinNs,MaxNs,StdDev\n")
         for r in stats:
@@ -266,7 +266,7 @@ def write_profiles(bench_json: str, kt_dir: str, fetch_dir: str, write_dir: str,
                 "# (__amd_rocclr_copyBuffer) whose counter readings give the scale from counter KiB to bytes.\n")
         for c in ("FETCH_SIZE", "WRITE_SIZE"):
             f.write(f"$ cd /tmp && export TMPDIR=/tmp && timeout -s KILL 90 rocprofv3 --pmc {c} --kernel-trace "
-                    f"-d REPO/gpurun_out/pmc_{c.split('_')[0].lower()} -o run --output-format csv -- python3 "
+                    f"-d OUT/pmc_{c.split('_')[0].lower()} -o run --output-format csv -- python3 "
                     f"REPO/bench.py {args} --steps 5 --warmup 2 --calibrate-copy {copy_bytes}\n")
         f.write(f"kernel: {short}\n"
                 f"attention_source_sha256: {attention_source_digest()}\n"
@@ -593,7 +593,7 @@ def write_loop_profile(bench_json: str, kt_dir: str):
                 "# loop_draft, loop_logits, accept_rowstats<0,...>, accept_decide<false>, loop_append; the calls\n"
                 "# cover all four runs of bench.py --loop (adaptive with graphs, adaptive with direct launches,\n"
                 "# fixed D = 7, no speculation) and the warm-up.  Durations in ns.\n"
-                "$ cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d REPO/gpurun_out/kt_loop "
+                "$ cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d OUT/kt_loop "
                 "-o run --output-format csv -- python3 REPO/bench.py --loop\n")
         f.write("Name,Calls,TotalDurationNs,AverageNs,Percentage,MinNs,MaxNs,StdDev\n")
         for r in stats:
@@ -621,7 +621,7 @@ def write_lossy_profile(bench_json: str, kt_dir: str):
                 "# each step runs the lossless call (accept_rowstats<1,...>, accept_finish<false>) and the relaxed\n"
                 "# call (accept_rowstats<2,...>, accept_jsd, accept_finish<true>).  Calls = clock-settle + warmup +\n"
                 "# timed steps.  Durations in ns.\n"
-                "$ cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d REPO/gpurun_out/kt_lossy "
+                "$ cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d OUT/kt_lossy "
                 "-o run --output-format csv -- python3 REPO/bench.py --lossy\n")
         f.write("Name,Calls,TotalDurationNs,AverageNs,Percentage,MinNs,MaxNs,StdDev\n")
         for r in stats:
@@ -650,7 +650,7 @@ def write_tree_profile(bench_json: str, kt_dir: str):
                 "# one tree-verify step = tree attention (ancestor masks, plan, main, split-KV combine)\n"
                 f"# + greedy tree acceptance (row statistics, path walk).  {calls} calls per kernel =\n"
                 "# clock-settle + warmup + timed steps.  Durations in ns.\n"
-                "$ cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d REPO/gpurun_out/kt_tree "
+                "$ cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d OUT/kt_tree "
                 "-o run --output-format csv -- python3 REPO/bench.py --tree\n")
         f.write("Name,Calls,TotalDurationNs,AverageNs,Percentage,MinNs,MaxNs,StdDev\n")
         for r in stats:
@@ -919,7 +919,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the verify step is built and timed on a single MI355X "
-              "(--gpus 1); multi-GPU runs are not part of this build.", file=sys.stderr)
+              "(--gpus 1); the path is not sharded across GPUs.", file=sys.stderr)
         sys.exit(2)
     if args.linear_sweep:
         args.settle_s = min(args.settle_s, 0.5)
