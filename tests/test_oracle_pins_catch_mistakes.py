@@ -32,6 +32,30 @@ MUTATIONS = [
     ("oracle/attention.py", "return bf16_bits_to_f64(cache_bits[pages, h, j % ps, :])",
      "return bf16_bits_to_f64(cache_bits[pages, h, (j // ps) % ps, :])",
      "test_oracle_attention.py::test_matches_sdpa_lower_right_causal"),
+    # draft trees
+    ("oracle/tree.py", "anc.append(anc[p] | {i})", "anc.append({0, i})",
+     "test_oracle_tree.py::test_chain_tree_is_the_causal_block"),
+    ("oracle/tree.py", "accepted[i] = accepted[p] and 0 <= x < V and x == top[p]",
+     "accepted[i] = accepted[p] and 0 <= x < V and x == top[i]",
+     "test_oracle_tree.py::test_chain_acceptance_is_linear_greedy"),
+    ("oracle/tree.py", "if accepted[i] and depth[i] > depth[best]:", "if accepted[i] and depth[i] >= depth[best]:",
+     "test_oracle_tree.py::test_acceptance_matches_path_enumeration"),
+    # relaxed acceptance
+    ("oracle/lossy.py", "return math.sqrt(max(0.0, 0.5 * (kp + kq)))", "return max(0.0, 0.5 * (kp + kq))",
+     "test_oracle_lossy.py::test_statistics_match_scipy"),
+    ("oracle/lossy.py", "                if not strict:", "                if strict:",
+     "test_oracle_lossy.py::test_negative_threshold_is_the_lossless_rule"),
+    ("oracle/lossy.py", "ent[d0 + i] = row_entropy(draft[d0 + i])", "ent[d0 + i] = row_entropy(target[t0 + i])",
+     "test_oracle_lossy.py::test_negative_threshold_is_the_lossless_rule"),
+    # closed loop
+    ("oracle/loop.py", "for j in range(L - k - 1, -1, -1):", "for j in range(0, L - k):",
+     "test_oracle_loop.py::test_ngram_drafter_by_hand"),
+    ("oracle/loop.py", "        if d >= ema:", "        if d > ema:", "test_oracle_loop.py::test_tier_rule_by_hand"),
+    ("oracle/loop.py", "            rows.append(h[-1])", "            rows.append(h[-2] if len(h) > 1 else h[-1])",
+     "test_oracle_loop.py::test_loop_output_is_plain_greedy_decoding"),
+    # verify-shaped linear layer
+    ("oracle/gemm.py", "if a.dtype in (np.uint16, np.int16):", "if a.dtype in (np.int16,):",
+     "test_oracle_gemm.py::test_identity_weight_returns_x"),
 ]
 
 
