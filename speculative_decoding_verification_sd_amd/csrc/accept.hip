@@ -156,7 +156,7 @@ __device__ __forceinline__ void load_chunk(const float* src, int j0, int V, floa
       const int j = j0 + (k * kAccThreads + tid) * 4;
       f32x4 v;
       if (j + 3 < V) {
-        v = *(const f32x4*)(src + j);
+        v = __builtin_nontemporal_load((const f32x4*)(src + j));   // streamed once: no cache residency
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = j + e < V ? src[j + e] : -INFINITY;

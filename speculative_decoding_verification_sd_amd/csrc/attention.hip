@@ -565,7 +565,7 @@ __global__ __launch_bounds__(64 * NW, WPC) void verify_attn_main(AttnParams p) {
       const unsigned sb = lds_base + (unsigned)(st * RG::kHalf);
 #pragma unroll
       for (int i = 0; i < LPW; ++i)
-        dma16((dma[i].kv ? vbase : kbase) + (dma[i].page ? off1 : off0), dma[i].src,
+        dma16<true>((dma[i].kv ? vbase : kbase) + (dma[i].page ? off1 : off0), dma[i].src,
               sb + (unsigned)(dma[i].kv * S * RG::kHalf + dma[i].dst));
     };
     // zero what this wave loaded into stage st for keys at or past k_end (last tile only)
@@ -1045,7 +1045,7 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
       const unsigned sb = lds_base + (unsigned)(st * RG::kHalf);
 #pragma unroll
       for (int i = 0; i < LPW; ++i)
-        dma16((dma[i].kv ? vbase : kbase) + (dma[i].page ? off1 : off0), dma[i].src,
+        dma16<true>((dma[i].kv ? vbase : kbase) + (dma[i].page ? off1 : off0), dma[i].src,
               sb + (unsigned)(dma[i].kv * S * RG::kHalf + dma[i].dst));
     };
     auto zero_tail = [&](int tile) {

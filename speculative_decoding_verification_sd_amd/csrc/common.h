@@ -52,18 +52,26 @@ __device__ __forceinline__ void block_sync() {
 // would wait for all of them); the ring waits for them explicitly with
 // s_waitcnt vmcnt before its barrier.  M0 is written only here in the
 // kernels that use it, which a build test checks on the generated ISA.
+// STREAM: data read once per call (the KV cache) goes with the non-temporal
+// hint, so that it does not displace what the caches hold for reuse.
+template <bool STREAM = false>
 __device__ __forceinline__ void dma16(const unsigned char* base, unsigned voff, unsigned lds_addr) {
   // readfirstlane returns int: go through unsigned so the low word is zero-extended
   const uint64_t b = (uint64_t)base;
   const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(b >> 32));
   const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)b);
   const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :
-               : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(sb)
-               : "memory", "m0");
+  if constexpr (STREAM)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(sb)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(sb)
+                 : "memory", "m0");
 }
-
 
 }  // namespace sdv
 
