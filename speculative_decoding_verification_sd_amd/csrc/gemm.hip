@@ -75,7 +75,10 @@ struct GemmShape {
   static_assert(WM >= 1 && WN >= 1 && (A_LOADS + B_LOADS) % 4 == 0, "tile shape");
 };
 
-template <int BM, int BN, int S>
+// STREAM_W: W tiles go with the non-temporal hint, for shapes with a single
+// m-tile (each W byte is then read once; with several m-tiles the tiles of W
+// are shared through L2 and stay cached).
+template <int BM, int BN, int S, bool STREAM_W>
 __global__ __launch_bounds__(256) void verify_gemm(GemmParams p) {
   using SH = GemmShape<BM, BN>;
   static_assert(S >= 2 && S <= 4 && (S - 2) * SH::LPW < 64, "ring depth");
@@ -119,7 +122,8 @@ __global__ __launch_bounds__(256) void verify_gemm(GemmParams p) {
     const size_t kofs = (size_t)(kb0 + st * kGemmBK) * 2;
 #pragma unroll
     for (int i = 0; i < SH::LPW; ++i)
-      dma16((isb[i] ? wt : xt) + kofs, src[i], lds_base + (unsigned)(slot * SH::STAGE) + dst[i]);
+      if (isb[i]) dma16<STREAM_W>(wt + kofs, src[i], lds_base + (unsigned)(slot * SH::STAGE) + dst[i]);
+      else dma16<false>(xt + kofs, src[i], lds_base + (unsigned)(slot * SH::STAGE) + dst[i]);
   };
 
   // operand offsets: lane reads row r32 of a 32-row block at logical chunk 2ks + hh
@@ -257,10 +261,13 @@ hipError_t sdv_gemm_launch(const SdGemmLaunch& a) {
   const long long tiles = (long long)p.mt * p.nt * g.ksplit;
   p.per_xcd = (int)((tiles + 7) / 8);
   const dim3 grid((unsigned)(8LL * p.per_xcd));
-  if (g.bm == 32) verify_gemm<32, 128, 4><<<grid, 256, 0, a.stream>>>(p);
-  else if (g.bm == 64) verify_gemm<64, 128, 3><<<grid, 256, 0, a.stream>>>(p);
-  else if (g.bn == 128) verify_gemm<128, 128, 4><<<grid, 256, 0, a.stream>>>(p);
-  else verify_gemm<128, 256, 3><<<grid, 256, 0, a.stream>>>(p);
+  const bool stream_w = p.mt == 1;
+  if (g.bm == 32 && stream_w) verify_gemm<32, 128, 4, true><<<grid, 256, 0, a.stream>>>(p);
+  else if (g.bm == 32) verify_gemm<32, 128, 4, false><<<grid, 256, 0, a.stream>>>(p);
+  else if (g.bm == 64 && stream_w) verify_gemm<64, 128, 3, true><<<grid, 256, 0, a.stream>>>(p);
+  else if (g.bm == 64) verify_gemm<64, 128, 3, false><<<grid, 256, 0, a.stream>>>(p);
+  else if (g.bn == 128) verify_gemm<128, 128, 4, false><<<grid, 256, 0, a.stream>>>(p);
+  else verify_gemm<128, 256, 3, false><<<grid, 256, 0, a.stream>>>(p);
   if (g.ksplit > 1) {
     const size_t groups = (size_t)a.m * a.n / 4;
     verify_gemm_reduce<<<(unsigned)((groups + 255) / 256), 256, 0, a.stream>>>(p);
