@@ -1068,11 +1068,15 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
 #pragma unroll
       for (int c = 0; c < NKS; ++c) {
         u32x4 raw = valid ? *(const u32x4*)(qp + c * 16) : u32x4{0, 0, 0, 0};
-        qf[c] = __builtin_bit_cast(bf16x8, raw);
+        bf16x8 t = __builtin_bit_cast(bf16x8, raw);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t[e] = (__bf16)((float)t[e] * p.scale_log2);
+        qf[c] = t;
       }
     }
     float m_run = -INFINITY;
     float m_off = 0.f;
+    f32x16 mneg;                   // fast pass: -(reference max) in every entry, the score chains' initial value
     float l_run;                   // this lane's share of its row sum (its 16 of each tile's 32 keys);
                                    // the row's sum adds the partner lane l ^ 32
     f32x16 o[NMB];
@@ -1117,11 +1121,25 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
 #pragma unroll
       for (int e = 1; e < 16; ++e) m = fmaxf(m, sc[e]);
       auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-      mt = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1])) * p.scale_log2;
+      mt = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
       return mt > m_run + slack;
     };
-    // S^T of the set's tile at stage offset `off` (two accumulation chains)
-    auto scores = [&](int off) {
+    // S^T of the set's tile at stage offset `off`, in log2 units (Q carries the
+    // scale).  PRE (fast pass after the first step): one chain that starts from
+    // mneg, so the MFMAs leave the scores less the reference max and P needs no
+    // VALU operation before the exp.  Otherwise two chains from zero, whose sum
+    // takes one add per score.  (With two waves per SIMD the other wave's MFMAs
+    // fill the single chain's dependency stalls: measured, one chain with no
+    // adds beats two chains by 1-3%.)
+    auto scores = [&](int off, auto prec) {
+      if constexpr (decltype(prec)::value) {
+        f32x16 s0 = mneg;
+#pragma unroll
+        for (int c = 0; c < NKS; ++c)
+          s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(smem + off + koff[c]), qf[c], s0, 0, 0, 0);
+        sc = s0;
+        return;
+      }
       f32x16 s0, s1;
 #pragma unroll
       for (int e = 0; e < 16; ++e) { s0[e] = 0.f; s1[e] = 0.f; }
@@ -1134,14 +1152,19 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
       }
       sc = s0 + s1;
     };
+    // P = 2^(score - reference max) in bf16 (PRE: the scores already hold the difference)
+    auto p_of = [&](float x, auto prec) {
+      if constexpr (decltype(prec)::value) return (__bf16)fast_exp2(x);
+      else return (__bf16)fast_exp2(x + m_off);
+    };
     // P from the scores, then O^T += V^T P^T at stage offset `off`, and the
     // lane's share of l from the same bf16 P (dot products with (1, 1))
-    auto accumulate = [&](int off) {
+    auto accumulate = [&](int off, auto prec) {
       bf16x8 pf[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pf[ks][e] = (__bf16)fast_exp2(fmaf(sc[ks * 8 + e], p.scale_log2, m_off));
+        for (int e = 0; e < 8; ++e) pf[ks][e] = p_of(sc[ks * 8 + e], prec);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -1158,11 +1181,11 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
       asm volatile("" ::"v"(l_run));   // keep the sums here: sunk past later tiles they hold P live
     };
     // The two halves of accumulate(), for the row-split step's pipeline.
-    auto make_p = [&](bf16x8* pf) {
+    auto make_p = [&](bf16x8* pf, auto prec) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pf[ks][e] = (__bf16)fast_exp2(fmaf(sc[ks * 8 + e], p.scale_log2, m_off));
+        for (int e = 0; e < 8; ++e) pf[ks][e] = p_of(sc[ks * 8 + e], prec);
       const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
@@ -1184,18 +1207,16 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
     // tile is formed (VALU) while the scores of the second accumulate (MFMA,
     // one chain), then P V of the first, then the second tile.
     auto rs_pair = [&](int off0, int off1) {
-      scores(off0);
+      scores(off0, std::true_type{});
       bf16x8 pf[2];
-      make_p(pf);
-      f32x16 s1;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s1[e] = 0.f;
+      make_p(pf, std::true_type{});
+      f32x16 s1 = mneg;
 #pragma unroll
       for (int c = 0; c < NKS; ++c)
         s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(smem + off1 + koff[c]), qf[c], s1, 0, 0, 0);
       pv(off0, pf);
       sc = s1;
-      make_p(pf);
+      make_p(pf, std::true_type{});
       pv(off1, pf);
     };
     auto row_sum = [&]() {
@@ -1231,7 +1252,7 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
     auto tile_generic = [&](int k, int tt, int off, auto safec) {
       constexpr bool SAFE = decltype(safec)::value;
       if (wave_active && tt < ntiles) {
-        scores(off);
+        scores(off, std::false_type{});
         if (k_begin + (tt + 1) * RG::kTile > N - D) mask_scores(tt);
         if constexpr (SAFE) {
           if (__any(row_max(kLazy))) rescale();
@@ -1240,7 +1261,7 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
           m_run = mt;
           m_off = mt == -INFINITY ? 0.f : -mt;
         }
-        accumulate(off);
+        accumulate(off, std::false_type{});
       }
     };
     auto step_generic = [&](int k, auto safec) {
@@ -1261,6 +1282,8 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
     const int plain = max(1, min(ntiles / 2, (N - D - k_begin) / (2 * RG::kTile)));
     const int ngroups = (plain - 1) / (S / 2);
     if (nsteps > 0) step_generic(0, std::false_type{});
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mneg[e] = m_off;
     auto fast_steady = [&](auto activec) {
       constexpr bool ACTIVE = decltype(activec)::value;
       for (int g = 0; g < ngroups; ++g) {
@@ -1273,8 +1296,8 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
             if constexpr (RS) {
               rs_pair(st * RG::kHalf, (st + 1) * RG::kHalf);
             } else {
-              scores(st * RG::kHalf);
-              accumulate(st * RG::kHalf);
+              scores(st * RG::kHalf, std::true_type{});
+              accumulate(st * RG::kHalf, std::true_type{});
             }
           }
         };
