@@ -73,7 +73,8 @@ struct AttnParams {
   void* out;
   float* part_o;    // [item_cap, rpad, d]   unnormalised partial outputs
   float* part_ml;   // [item_cap, rpad, 2]   (running max in log2 units, sum)
-  int* plan;        // [16 + 2B + 1]: chunk, total items, full items, work counters, item_start, tail_pos
+  int* plan;        // [16 + 3B + 1]: chunk, total items, full items, split sequences, work counters,
+                    // item_start, tail_pos, split sequence list
   const unsigned long long* tmask;   // NULL: causal block; else per verify row, the nodes of its draft tree it sees
   ItemDesc* items;  // [item_cap]
   int B, Hkv, G, max_pages, num_pages, max_draft, rpad, total_q, item_cap;
@@ -145,15 +146,21 @@ __global__ __launch_bounds__(64 * kMaskSeqsPerBlock) void verify_tree_masks(Attn
 // kLenBuckets buckets, longest bucket first.  Split-KV partials stay addressed
 // by the natural index item_start[b] + h * nsplit_b + split.
 //
-// plan[]: [0] chunk, [1] items, [2] full-chunk items, [8..15] work counters
-// (cleared here), then item_start[0..B] and tail_pos[0..B-1] (scheduled index
+// plan[]: [0] chunk, [1] items, [2] full-chunk items, [3] sequences split in
+// more than one item (when list_splits), [8..15] work counters (cleared here),
+// then from kPlanHeader on item_start[0..B], tail_pos[0..B-1] (scheduled index
 // of head 0's shorter item of sequence b; kept in LDS for the first
-// kPlanCacheSeqs sequences) from kPlanHeader on.
+// kPlanCacheSeqs sequences) and, when list_splits, the list of the split
+// sequences (plan[3] entries, any order) for the combine of large batches.
 constexpr int kLenBuckets = 64;
 constexpr int kPlanCacheSeqs = 2048;     // sequences whose key count and tail index the plan keeps in LDS
+constexpr int kHistBins = kMaxChunk / 64 + 2;   // ceil(N/64) = 0 .. 256, and "longer"
+constexpr int kLongSeqs = 256;           // sequences longer than kMaxChunk the chunk search lists in LDS
+constexpr int kDirectSeqs = 32;          // chunk search: batches this small skip the histogram
+constexpr int kSearchCost = 8;           // descriptors: an item found by binary search costs about 8 written directly
 
 __global__ __launch_bounds__(kPlanThreads) void verify_attn_plan(AttnParams p, int fixed_chunk, int slots,
-                                                                 int ovh_keys) {
+                                                                 int ovh_keys, int list_splits) {
   __shared__ int s_keys[kPlanThreads];
   __shared__ int scan[kPlanThreads];
   __shared__ int fscan[kPlanThreads];
@@ -166,34 +173,98 @@ __global__ __launch_bounds__(kPlanThreads) void verify_attn_plan(AttnParams p, i
   __shared__ int s_d[kPlanCacheSeqs];      // drafts of sequence b
   __shared__ int s_tail[kPlanCacheSeqs];   // tail_pos[b]
   __shared__ int s_wsum[2][kPlanThreads / 64];
+  __shared__ int s_hist[kHistBins];        // sequences by ceil(N/64), the last bin N > kMaxChunk
+  __shared__ int s_above[kHistBins];       // s_above[x] = sequences with ceil(N/64) > x
+  __shared__ int s_long[kLongSeqs];        // ceil(N/64) of the sequences longer than kMaxChunk
+  __shared__ int s_nlong, s_nsplit;
   const int tid = threadIdx.x;
   const int max_keys = p.max_pages * kPage;
   const int cap_chunk = max(kMinChunk, min(kMaxChunk, (max_keys + 63) / 64 * 64));
   const int my_chunk = min(kMinChunk + 64 * tid, cap_chunk);
   int* tail_pos = p.plan + kPlanHeader + p.B + 1;
+  int* split_list = p.plan + kPlanHeader + 2 * p.B + 1;   // the sequences with more than one split
   auto keys_of = [&](int b) { return b < kPlanCacheSeqs ? s_n[b] : seq_keys(p, b); };
 
-  // (1) the chunk
-  if (tid == 0) { s_best = ~0ull; s_ksum = 0; s_full = 0; s_nmax = 0; }
+  // (1) the chunk.  Candidates are c = 64 d keys (d >= 4), and ceil(N/c) =
+  // ceil(ceil(N/64) / d), so with n_b = ceil(N_b/64) the item count is
+  // sum_b max(1, ceil(n_b/d)) = B + sum_{k>=1} #{b : n_b > k d}.  For the
+  // sequences of at most kMaxChunk keys (n_b <= 256) the terms come from the
+  // suffix counts of their histogram (s_above, non-increasing, so the sum stops
+  // at the first zero); each longer sequence adds ceil(n_b/d) - 1.  The search
+  // costs O(B + 256 * long sequences) instead of 256 divisions per sequence.
+  // Up to kDirectSeqs sequences every candidate simply divides each length.
+  const bool direct = p.B <= kDirectSeqs;
+  if (tid == 0) { s_best = ~0ull; s_ksum = 0; s_full = 0; s_nmax = 0; s_nlong = 0; s_nsplit = 0; }
   if (tid < kLenBuckets) s_bucket[tid] = 0;
+  if (!direct) {
+    for (int i = tid; i < kHistBins; i += kPlanThreads) s_hist[i] = 0;
+    __syncthreads();
+  }
   long long my_items = 0, ksum = 0;
   int nmax = 0;
   for (int base = 0; base < p.B; base += kPlanThreads) {
-    __syncthreads();
-    const int nb = base + tid < p.B ? seq_keys(p, base + tid) : 0;
-    s_keys[tid] = nb;
+    const bool in = base + tid < p.B;
+    const int nb = in ? seq_keys(p, base + tid) : 0;
     if (base + tid < kPlanCacheSeqs) {        // (the descriptors' fields, loaded here alongside N_b)
       s_n[base + tid] = nb;
-      if (base + tid < p.B) {
+      if (in) {
         s_t0[base + tid] = p.q_start[base + tid];
         s_d[base + tid] = seq_drafts(p, base + tid);
       }
     }
     ksum += nb;
     nmax = max(nmax, nb);
+    if (in && !direct) {
+      const int n64 = (nb + 63) >> 6;
+      atomicAdd(&s_hist[min(n64, kHistBins - 1)], 1);
+      if (n64 > kHistBins - 2) {
+        const int sl = atomicAdd(&s_nlong, 1);
+        if (sl < kLongSeqs) s_long[sl] = n64;
+      }
+    }
+  }
+  __syncthreads();
+  static_assert(kHistBins <= 5 * 64, "one wave, five bins per lane");
+  static_assert(kDirectSeqs <= kPlanCacheSeqs, "the direct count reads the lengths from LDS");
+  if (direct) {
+    for (int b = 0; b < p.B; ++b) my_items += max(1, (s_n[b] + my_chunk - 1) / my_chunk);
+  } else {
+    if (tid < 64) {                                  // suffix counts: s_above[x] = short sequences past bin x
+      int loc[5], tot = 0;
+  #pragma unroll
+      for (int q = 0; q < 5; ++q) {
+        loc[q] = 5 * tid + q < kHistBins - 1 ? s_hist[5 * tid + q] : 0;   // (the last bin: the long ones)
+        tot += loc[q];
+      }
+      int suf = tot;                                 // inclusive suffix scan over the lanes
+  #pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_down(suf, off);
+        if (tid + off < 64) suf += t;
+      }
+      int after = suf - tot;
+  #pragma unroll
+      for (int q = 4; q >= 0; --q) {
+        if (5 * tid + q < kHistBins) s_above[5 * tid + q] = after;
+        after += loc[q];
+      }
+    }
     __syncthreads();
-    const int n = min(kPlanThreads, p.B - base);
-    for (int j = 0; j < n; ++j) my_items += max(1, (s_keys[j] + my_chunk - 1) / my_chunk);
+    if (s_nlong <= kLongSeqs) {
+      const int d = my_chunk >> 6;
+      long long acc = p.B;
+      for (int x = d; x <= kHistBins - 2; x += d) {
+        const int a = s_above[x];
+        if (a == 0) break;
+        acc += a;
+      }
+      for (int i = 0; i < s_nlong; ++i) acc += (s_long[i] + d - 1) / d - 1;
+      my_items = acc;
+    } else {
+      // more long sequences than listed: count each one (the attention over that
+      // many sequences of more than kMaxChunk keys takes far longer than this)
+      for (int b = 0; b < p.B; ++b) my_items += max(1, (keys_of(b) + my_chunk - 1) / my_chunk);
+    }
   }
   // (block reductions: a wave reduction, then one LDS atomic per wave)
   const int lane = tid & 63;
@@ -229,8 +300,8 @@ __global__ __launch_bounds__(kPlanThreads) void verify_attn_plan(AttnParams p, i
     full = N / chunk;
     tail_len = (N % chunk != 0 || N == 0) ? N - full * chunk : -1;
   };
-  auto bucket_of = [&](int len) {
-    return kLenBuckets - 1 - (int)(((long long)len * kLenBuckets) / ((long long)chunk + 1));
+  auto bucket_of = [&](int len) {   // (len <= chunk <= kMaxChunk: the product fits 32 bits)
+    return kLenBuckets - 1 - (len * kLenBuckets) / (chunk + 1);
   };
   long long nfull = 0;
   for (int b = tid; b < p.B; b += kPlanThreads) {
@@ -276,6 +347,7 @@ __global__ __launch_bounds__(kPlanThreads) void verify_attn_plan(AttnParams p, i
       ns = max(1, (N + chunk - 1) / chunk);
       v = ns * p.Hkv;
       split_of(N, full, tl);
+      if (list_splits && ns > 1) split_list[atomicAdd(&s_nsplit, 1)] = b;   // (any order: each head merges alone)
     }
     // inclusive scans of v and of the full-chunk items: within each wave by
     // shuffles, then the totals of the waves before it
@@ -295,32 +367,65 @@ __global__ __launch_bounds__(kPlanThreads) void verify_attn_plan(AttnParams p, i
     if (b < p.B) p.plan[kPlanHeader + b] = carry + scan[tid] - v;
     const int n = min(kPlanThreads, p.B - base);
     const int group_items = scan[n - 1];
-    for (int e = tid; e < group_items; e += kPlanThreads) {
-      int lo = 0, hi = n - 1;                 // first j with scan[j] > e
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (scan[mid] > e) hi = mid;
-        else lo = mid + 1;
+    // one thread per sequence (no search, no division) unless the group's
+    // longest sequence would keep its thread past kSearchCost times the
+    // per-thread share of a search over the group's items
+    if (!direct && __syncthreads_or(v > kSearchCost * ((group_items + kPlanThreads - 1) / kPlanThreads)) == 0) {
+      if (b < p.B) {
+        const int t0b = b < kPlanCacheSeqs ? s_t0[b] : p.q_start[b];
+        const int Db = b < kPlanCacheSeqs ? s_d[b] : seq_drafts(p, b);
+        const int tpos = b < kPlanCacheSeqs ? s_tail[b] : tail_pos[b];
+        const int fbase = fcarry + fscan[tid] - full * p.Hkv;
+        for (int hj = 0; hj < p.Hkv; ++hj)
+          for (int sj = 0; sj < ns; ++sj) {
+            const int pos = sj < full ? fbase + hj * full + sj : tpos + hj;
+            if (pos < 0 || pos >= p.item_cap) continue;
+            ItemDesc d;
+            d.b = b;
+            d.h = hj;
+            d.k_begin = sj * chunk;
+            d.k_end = min(N, (sj + 1) * chunk);
+            d.t0 = t0b;
+            d.D = Db;
+            d.N = N;
+            d.nsplit = ns;
+            p.items[pos] = d;
+          }
       }
-      const int bj = base + lo;
-      const int Nj = s_keys[lo];
-      const int nsj = max(1, (Nj + chunk - 1) / chunk);
-      const int fj = Nj / chunk;
-      const int r = e - (lo > 0 ? scan[lo - 1] : 0);
-      const int hj = r / nsj, sj = r % nsj;
-      const int pos = sj < fj ? fcarry + (lo > 0 ? fscan[lo - 1] : 0) + hj * fj + sj
-                              : (bj < kPlanCacheSeqs ? s_tail[bj] : tail_pos[bj]) + hj;
-      if (pos < 0 || pos >= p.item_cap) continue;
-      ItemDesc d;
-      d.b = bj;
-      d.h = hj;
-      d.k_begin = sj * chunk;
-      d.k_end = min(Nj, (sj + 1) * chunk);
-      d.t0 = bj < kPlanCacheSeqs ? s_t0[bj] : p.q_start[bj];
-      d.D = bj < kPlanCacheSeqs ? s_d[bj] : seq_drafts(p, bj);
-      d.N = Nj;
-      d.nsplit = nsj;
-      p.items[pos] = d;
+    } else {
+      for (int e = tid; e < group_items; e += kPlanThreads) {
+        int lo = 0, hi = n - 1;                 // first j with scan[j] > e
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (scan[mid] > e) hi = mid;
+          else lo = mid + 1;
+        }
+        const int bj = base + lo;
+        const int Nj = s_keys[lo];
+        const int r = e - (lo > 0 ? scan[lo - 1] : 0);
+        int nsj = 1, fj = 0, hj = r, sj = 0;    // (one item per head: no division)
+        if (Nj > chunk) {
+          nsj = (Nj + chunk - 1) / chunk;
+          fj = Nj / chunk;
+          hj = r / nsj;
+          sj = r - hj * nsj;
+        } else if (Nj == chunk) {
+          fj = 1;
+        }
+        const int pos = sj < fj ? fcarry + (lo > 0 ? fscan[lo - 1] : 0) + hj * fj + sj
+                                : (bj < kPlanCacheSeqs ? s_tail[bj] : tail_pos[bj]) + hj;
+        if (pos < 0 || pos >= p.item_cap) continue;
+        ItemDesc d;
+        d.b = bj;
+        d.h = hj;
+        d.k_begin = sj * chunk;
+        d.k_end = min(Nj, (sj + 1) * chunk);
+        d.t0 = bj < kPlanCacheSeqs ? s_t0[bj] : p.q_start[bj];
+        d.D = bj < kPlanCacheSeqs ? s_d[bj] : seq_drafts(p, bj);
+        d.N = Nj;
+        d.nsplit = nsj;
+        p.items[pos] = d;
+      }
     }
     carry += scan[kPlanThreads - 1];
     fcarry += fscan[kPlanThreads - 1];
@@ -331,6 +436,7 @@ __global__ __launch_bounds__(kPlanThreads) void verify_attn_plan(AttnParams p, i
     p.plan[0] = chunk;
     p.plan[1] = carry;
     p.plan[2] = (int)s_full;
+    p.plan[3] = s_nsplit;
     p.plan[kPlanHeader + p.B] = carry;
   }
 }
@@ -1388,17 +1494,13 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Merge the split-KV partials of one (sequence, KV head): 8 rows per
-// workgroup, 32 threads per row, each thread one 4-wide slice of d.
+// Merge the split-KV partials of one (sequence, KV head), 8 rows at a time:
+// 32 threads per row, each thread one 4-wide slice of d.
 template <int HD, int OUT_F32>
-__global__ __launch_bounds__(256) void verify_attn_combine(AttnParams p) {
+__device__ __forceinline__ void combine_rows(const AttnParams& p, int b, int h, int rblk) {
   constexpr int kRowsPerBlock = 256 / 32;
-  const int row_blocks = p.rpad / kRowsPerBlock;
-  const int unit = blockIdx.x / row_blocks;
-  const int rblk = blockIdx.x - unit * row_blocks;
-  const int b = unit / p.Hkv;
-  const int h = unit - b * p.Hkv;
   const int chunk = p.plan[0];
+  if (b < 0 || b >= p.B || chunk < 64) return;
   const int N = seq_keys(p, b);
   const int nsplit = max(1, (N + chunk - 1) / chunk);
   if (nsplit == 1) return;
@@ -1406,6 +1508,7 @@ __global__ __launch_bounds__(256) void verify_attn_combine(AttnParams p) {
   const int R = p.G * (1 + D);
   const int row = rblk * kRowsPerBlock + (threadIdx.x >> 5);
   const int t0 = p.q_start[b];
+  // (whole 32-lane groups leave together: the shuffles below stay within one group)
   if (row >= R || t0 < 0 || t0 + row / p.G >= p.total_q) return;
   const int sub = threadIdx.x & 31;
   const int item0 = p.plan[kPlanHeader + b] + h * nsplit;
@@ -1443,6 +1546,32 @@ __global__ __launch_bounds__(256) void verify_attn_combine(AttnParams p) {
   }
 }
 
+// A workgroup per (sequence, KV head, block of 8 rows); unsplit sequences leave at once.
+template <int HD, int OUT_F32>
+__global__ __launch_bounds__(256) void verify_attn_combine(AttnParams p) {
+  const int row_blocks = p.rpad / 8;
+  const int unit = blockIdx.x / row_blocks;
+  const int rblk = blockIdx.x - unit * row_blocks;
+  const int b = unit / p.Hkv;
+  combine_rows<HD, OUT_F32>(p, b, unit - b * p.Hkv, rblk);
+}
+
+// Large batches: a bounded grid walks only the sequences the plan listed as
+// split (the others were written by the main kernels).
+template <int HD, int OUT_F32>
+__global__ __launch_bounds__(256) void verify_attn_combine_list(AttnParams p) {
+  const int row_blocks = p.rpad / 8;
+  const int per_seq = p.Hkv * row_blocks;
+  const int* split_list = p.plan + kPlanHeader + 2 * p.B + 1;
+  const int total = min(max(p.plan[3], 0), p.B) * per_seq;
+  for (int w = blockIdx.x; w < total; w += gridDim.x) {
+    const int si = w / per_seq;
+    const int unit = w - si * per_seq;
+    const int h = unit / row_blocks;
+    combine_rows<HD, OUT_F32>(p, split_list[si], h, unit - h * row_blocks);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Host side: variant choice, workspace layout, launches.
 struct AttnLayout {
@@ -1463,6 +1592,7 @@ static int attn_slots(int cus, int variant) { return cus * (variant == 0 ? 2 : 1
 // computed for the largest CU count of a gfx950 part so that the size query
 // needs no device.
 constexpr int kMaxCus = 256;
+constexpr int kCombineGrid = 16 * kMaxCus;   // combine workgroups: 8 rows of one (sequence, KV head) each
 
 static AttnLayout attn_layout(int B, int Hkv, int G, int HD, int max_pages, int max_draft, int kv_chunk) {
   AttnLayout L;
@@ -1486,7 +1616,7 @@ static AttnLayout attn_layout(int B, int Hkv, int G, int HD, int max_pages, int 
   L.item_cap = (int)cap;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += (bytes + 255) / 256 * 256; return o; };
-  L.plan_off = take((size_t)(kPlanHeader + 2 * B + 1) * 4);
+  L.plan_off = take((size_t)(kPlanHeader + 3 * B + 1) * 4);
   L.items_off = take((size_t)cap * sizeof(ItemDesc));
   L.ml_off = take((size_t)cap * L.rpad * 2 * 4);
   L.o_off = take((size_t)cap * L.rpad * HD * 4);
@@ -1562,7 +1692,9 @@ hipError_t sdv_attn_launch(const SdAttnLaunch& a) {
         p, a.parents, masks);
     p.tmask = masks;
   }
-  verify_attn_plan<<<1, kPlanThreads, 0, a.stream>>>(p, a.kv_chunk, slots, kItemOverheadBytes / (4 * a.head_dim));
+  const long long cunits = (long long)a.B * a.Hkv * (L.rpad / 8);   // combine workgroups, one per 8 rows of a head
+  verify_attn_plan<<<1, kPlanThreads, 0, a.stream>>>(p, a.kv_chunk, slots, kItemOverheadBytes / (4 * a.head_dim),
+                                                     cunits > kCombineGrid);
   if (a.head_dim == 128) {
     if (a.out_f32) launch_main<128, 1>(L.variant, p, grid, a.stream);
     else launch_main<128, 0>(L.variant, p, grid, a.stream);
@@ -1570,13 +1702,25 @@ hipError_t sdv_attn_launch(const SdAttnLaunch& a) {
     if (a.out_f32) launch_main<64, 1>(L.variant, p, grid, a.stream);
     else launch_main<64, 0>(L.variant, p, grid, a.stream);
   }
-  const int cgrid = a.B * a.Hkv * (L.rpad / 8);
-  if (a.head_dim == 128) {
-    if (a.out_f32) verify_attn_combine<128, 1><<<cgrid, 256, 0, a.stream>>>(p);
-    else verify_attn_combine<128, 0><<<cgrid, 256, 0, a.stream>>>(p);
+  // one workgroup per (sequence, KV head, 8 rows), or for large batches a
+  // bounded grid over the split sequences only (their number is known on the device)
+  if (cunits <= kCombineGrid) {
+    const int cgrid = (int)cunits;
+    if (a.head_dim == 128) {
+      if (a.out_f32) verify_attn_combine<128, 1><<<cgrid, 256, 0, a.stream>>>(p);
+      else verify_attn_combine<128, 0><<<cgrid, 256, 0, a.stream>>>(p);
+    } else {
+      if (a.out_f32) verify_attn_combine<64, 1><<<cgrid, 256, 0, a.stream>>>(p);
+      else verify_attn_combine<64, 0><<<cgrid, 256, 0, a.stream>>>(p);
+    }
   } else {
-    if (a.out_f32) verify_attn_combine<64, 1><<<cgrid, 256, 0, a.stream>>>(p);
-    else verify_attn_combine<64, 0><<<cgrid, 256, 0, a.stream>>>(p);
+    if (a.head_dim == 128) {
+      if (a.out_f32) verify_attn_combine_list<128, 1><<<kCombineGrid, 256, 0, a.stream>>>(p);
+      else verify_attn_combine_list<128, 0><<<kCombineGrid, 256, 0, a.stream>>>(p);
+    } else {
+      if (a.out_f32) verify_attn_combine_list<64, 1><<<kCombineGrid, 256, 0, a.stream>>>(p);
+      else verify_attn_combine_list<64, 0><<<kCombineGrid, 256, 0, a.stream>>>(p);
+    }
   }
   return hipGetLastError();
 }
