@@ -664,6 +664,91 @@ def write_tree_profile(bench_json: str, kt_dir: str):
     print(f"wrote {path}")
 
 
+BATCH_SWEEP = [(16, 32768), (256, 2048), (2048, 512), (4096, 256)]   # (sequences, keys each)
+BATCH_SWEEP_SETTLE = 1000   # untimed calls per point before the timed ones (about a second)
+
+
+def run_batch_sweep(args):
+    """Verify attention time against the batch size at a fixed shape per
+    sequence (H_kv=8, G=8, d=128, D=3): B sequences of N keys for the pairs of
+    BATCH_SWEEP, from 16 long sequences to 4096 short ones, where the
+    device-side plan and the combine cost most.  One JSON line."""
+    import numpy as np
+    import torch
+
+    import speculative_decoding_verification_sd_amd as sdv
+    from workloads import WorkloadSpec, generate
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    points = []
+    for B, N in BATCH_SWEEP:
+        sp = WorkloadSpec(name=f"b{B}_hkv8_g8_d128_kv{N}_D3", batch=B, kv_heads=8, group=8, head_dim=128,
+                          kv_len=N, draft_len=3, vocab=64, mode="greedy", seed=args.seed)
+        print(f"[bench] batch sweep: generating {sp.name}", file=sys.stderr, flush=True)
+        inp = generate(sp, device=dev)
+        out = torch.empty_like(inp.q)
+        desc = sdv.attn_desc(inp.q, inp.k_cache, inp.block_table, sp.group, inp.max_draft)
+        ws = torch.empty(max(1, sdv.sd_verify_attention_workspace_size(desc, inp.q.shape[0])), dtype=torch.uint8,
+                         device=dev)
+
+        def attention():
+            sdv.sd_verify_attention(inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.kv_len, inp.q_start,
+                                    out, group_size=sp.group, max_draft=inp.max_draft, workspace=ws)
+
+        # a fixed number of calls per point (clock settle, then the timed ones), so that
+        # a kernel trace of this run splits evenly into the points
+        for _ in range(BATCH_SWEEP_SETTLE):
+            attention()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for k in range(args.steps):
+            ev[k][0].record()
+            attention()
+            ev[k][1].record()
+        torch.cuda.synchronize()
+        ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+        kv_bytes = B * N * sp.kv_heads * sp.head_dim * 4
+        points.append({"batch": B, "kv_len": N, "attention_ms": ms, "hbm_frac": kv_bytes / (ms * 1e-3) / 8e12})
+        del inp, out, ws
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "verify attention time against the batch size", "unit": "ms",
+                      "higher_is_better": False, "n_gpus": 1, "steps": args.steps, "dtype": "bf16",
+                      "data": "synthetic", "config": {"workload": "hkv8_g8_d128_D3_batch_sweep", "seed": args.seed},
+                      "points": points}))
+
+
+def write_batch_profile(bench_json: str, kt_dir: str):
+    """Per-kernel medians per batch point under profiles/, from a rocprofv3
+    --kernel-trace run of `bench.py --batch-sweep` (the points run in order)."""
+    import statistics
+    with open(bench_json) as f:
+        line = json.loads(f.read().strip().splitlines()[-1])
+    rows = [r for r in _rocprof_csv(kt_dir, "kernel_trace") if "sdv::" in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    plans = [i for i, r in enumerate(rows) if "verify_attn_plan" in r["Kernel_Name"]]
+    per_point = len(plans) // len(line["points"])
+    path = os.path.join(ROOT, "profiles", "verify_attn_batch_sweep_hkv8_g8_d128_D3.txt")
+    with open(path, "w") as f:
+        f.write("# Verify attention against the batch size (H_kv=8, G=8, d=128, D=3; B sequences of N keys):\n"
+                "# median kernel durations per point from a rocprofv3 kernel trace, and the call time with HIP\n"
+                "# events in the same run.  The plan and the combine are the launches whose cost grows with B.\n"
+                "$ cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace -d OUT/kt_batch -o run "
+                "--output-format csv -- python3 REPO/bench.py --batch-sweep\n")
+        f.write("batch,kv_len,plan_us,main_us,combine_us,call_us_events,hbm_frac\n")
+        for k, pt in enumerate(line["points"]):
+            lo = plans[k * per_point]
+            hi = plans[(k + 1) * per_point] if (k + 1) * per_point < len(plans) else len(rows)
+            med = {}
+            for part, key in (("plan", "verify_attn_plan"), ("main", "verify_attn_main"), ("wide", "verify_attn_wide"),
+                              ("combine", "verify_attn_combine")):
+                d = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows[lo:hi] if key in r["Kernel_Name"]]
+                med[part] = statistics.median(d) / 1e3 if d else 0.0
+            f.write(f"{pt['batch']},{pt['kv_len']},{med['plan']:.1f},{med['main'] + med['wide']:.1f},"
+                    f"{med['combine']:.1f},{pt['attention_ms'] * 1e3:.1f},{pt['hbm_frac']:.3f}\n")
+    print(f"wrote {path}")
+
+
 def run_sweep(args):
     """Verify attention (and accept) time per draft length D on the tile-boundary
     sweep workload (B=32, H_kv=8, G=8, d=128, 32768-token cache, V=32000,
@@ -881,6 +966,10 @@ def main():
                     help="write the profiles/ table of a --linear-sweep line")
     ap.add_argument("--write-profiles", nargs=4, metavar=("BENCH_JSON", "KT_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write the profiles/ summaries from a bench line and three rocprofv3 runs (no GPU)")
+    ap.add_argument("--batch-sweep", action="store_true",
+                    help="verify attention time against the batch size (16 x 32K keys .. 4096 x 256 keys)")
+    ap.add_argument("--write-batch-profile", nargs=2, metavar=("BENCH_JSON", "KT_DIR"),
+                    help="write the profiles/ table of a --batch-sweep line and its kernel trace")
     ap.add_argument("--tree", action="store_true",
                     help="tree verification (ancestor-mask attention + greedy path acceptance), binary tree of depth 4")
     ap.add_argument("--write-tree-profile", nargs=2, metavar=("BENCH_JSON", "KT_DIR"),
@@ -912,6 +1001,9 @@ def main():
     if args.write_sweep_profile:
         write_sweep_profile(args.write_sweep_profile)
         return
+    if args.write_batch_profile:
+        write_batch_profile(*args.write_batch_profile)
+        return
     if args.write_linear_profile:
         write_linear_profile(args.write_linear_profile)
         return
@@ -927,6 +1019,9 @@ def main():
         return
     if args.tree:
         run_tree(args)
+        return
+    if args.batch_sweep:
+        run_batch_sweep(args)
         return
     if args.lossy:
         run_lossy(args)
