@@ -39,6 +39,7 @@
  *    logits (no row entirely -inf), uniforms in [0, 1).  Kernels clamp
  *    indices so that a violation cannot read or write out of bounds; the
  *    values computed for an offending sequence are then unspecified.
+ *    sd_validate_inputs checks this contract on request.
  *  - Results are deterministic: the same inputs give bit-identical outputs.
  *  - Concurrent calls are safe when they use distinct workspaces and outputs.
  *
@@ -355,6 +356,39 @@ size_t sd_verify_linear_workspace_size(const sd_linear_desc* desc);
  */
 sd_status sd_verify_linear(const sd_linear_desc* desc, const void* x, const void* w, void* y,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Opt-in check of the device-side contract above (the verify calls do not
+ * check it: they clamp what they index, and a violating sequence gets
+ * unspecified values).  One pass over the given inputs; *status_word (one
+ * device uint32, overwritten) becomes the OR of the SD_BAD_* bits of every
+ * violation found, 0 when there is none.  Either descriptor may be NULL to
+ * check one half only (both given: num_seqs and max_draft must agree):
+ *  - always: q_start [B+1] (SD_BAD_Q_START);
+ *  - with attn: kv_len [B] against each sequence's 1+D_b rows and
+ *    max_pages_per_seq*page_size keys (SD_BAD_KV_LEN), and the first
+ *    ceil(kv_len[b]/page_size) entries of block_table row b (SD_BAD_PAGE);
+ *  - with acc: draft_tokens [total_q - B] (SD_BAD_TOKEN), uniforms [total_q]
+ *    when not NULL (SD_BAD_UNIFORM), and target_logits [total_q, V] and
+ *    draft_logits [total_q - B, V] when not NULL (SD_BAD_LOGITS; a full pass
+ *    over the logits).
+ * Every index the pass reads is range-checked first, so it stays in bounds
+ * on any input.  Stream-ordered like the other calls; read the word after
+ * the stream has reached it.
+ */
+typedef enum {
+  SD_BAD_Q_START = 1,   /* q_start[0] != 0, a sequence with no row or more than 1+max_draft, q_start[B] != total_q */
+  SD_BAD_KV_LEN = 2,    /* kv_len[b] < 1+D_b, or > max_pages_per_seq*page_size */
+  SD_BAD_PAGE = 4,      /* a page id a sequence uses outside [0, num_pages) */
+  SD_BAD_TOKEN = 8,     /* a drafted token outside [0, vocab) */
+  SD_BAD_UNIFORM = 16,  /* a uniform outside [0, 1), NaN included */
+  SD_BAD_LOGITS = 32    /* a NaN or +inf logit, or a row with every logit -inf */
+} sd_bad_input;
+
+sd_status sd_validate_inputs(const sd_attn_desc* attn, const sd_accept_desc* acc, int32_t total_q,
+                             const int32_t* block_table, const int32_t* kv_len, const int32_t* q_start,
+                             const int32_t* draft_tokens, const float* uniforms, const float* target_logits,
+                             const float* draft_logits, uint32_t* status_word, void* stream);
 
 /* Message describing the last non-OK status returned on the calling thread. */
 const char* sd_last_error(void);

@@ -35,6 +35,8 @@ from .binding import (  # noqa: F401
     sd_tree_accept,
     sd_tree_accept_workspace_size,
     sd_version,
+    sd_validate_inputs,
+    SD_BAD,
 )
 
 __all__ = [
@@ -43,4 +45,5 @@ __all__ = [
     "sd_verify_step_workspace_size", "sd_version", "linear_desc", "sd_verify_linear",
     "sd_verify_linear_workspace_size", "sd_verify_tree_attention", "sd_tree_accept", "sd_tree_accept_workspace_size",
     "sd_accept_lossy", "sd_accept_lossy_workspace_size", "loop_desc", "sd_closed_loop", "sd_closed_loop_workspace_size",
+    "sd_validate_inputs", "SD_BAD",
 ]

@@ -104,6 +104,8 @@ SIGNATURES = {
     "sd_closed_loop": (ctypes.c_int, [ctypes.POINTER(sd_loop_desc), _P, _P, _P, _I, _P, _P, _P, _SZ, _P]),
     "sd_verify_linear_workspace_size": (_SZ, [ctypes.POINTER(sd_linear_desc)]),
     "sd_verify_linear": (ctypes.c_int, [ctypes.POINTER(sd_linear_desc), _P, _P, _P, _P, _SZ, _P]),
+    "sd_validate_inputs": (ctypes.c_int, [ctypes.POINTER(sd_attn_desc), ctypes.POINTER(sd_accept_desc), _I,
+                                          _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "sd_last_error": (ctypes.c_char_p, []),
     "sd_version": (ctypes.c_char_p, []),
 }
@@ -417,3 +419,51 @@ def sd_version() -> str:
 
 def sd_last_error() -> str:
     return lib().sd_last_error().decode()
+
+
+# Bits of the word sd_validate_inputs writes (0: no violation found).
+SD_BAD = {"q_start": 1, "kv_len": 2, "page": 4, "token": 8, "uniform": 16, "logits": 32}
+
+
+def sd_validate_inputs(q_start, *, max_draft: int, q=None, k_cache=None, block_table=None, kv_len=None,
+                       group_size: int = 1, draft_tokens=None, uniforms=None, target_logits=None, draft_logits=None,
+                       vocab: Optional[int] = None, status_word: Optional[torch.Tensor] = None,
+                       stream=None) -> torch.Tensor:
+    """Opt-in device-side check of the inputs' contract (the verify calls only
+    clamp what they index).  The attention half is checked when block_table is
+    given (with q, k_cache and kv_len), the accept half when draft_tokens or
+    target_logits is given; logits are scanned only when passed.  Returns the
+    status word (int32 [1] on the device, stream-ordered): the OR of the
+    SD_BAD bits found, 0 when the inputs keep the contract."""
+    B = q_start.shape[0] - 1
+    dev = q_start.device
+    _need(q_start, "q_start", torch.int32, dev)
+    T = next((t.shape[0] for t in (q, target_logits, uniforms) if t is not None), None)
+    if T is None:
+        raise ValueError("total_q comes from q, target_logits or uniforms: pass one of them")
+    ad = cd = None
+    if block_table is not None:
+        if q is None or k_cache is None or kv_len is None:
+            raise ValueError("the attention half needs q, k_cache, block_table and kv_len")
+        _need(block_table, "block_table", torch.int32, dev)
+        _need(kv_len, "kv_len", torch.int32, dev)
+        ad = attn_desc(q, k_cache, block_table, group_size, max_draft)
+    if draft_tokens is not None or target_logits is not None:
+        V = target_logits.shape[1] if target_logits is not None else vocab
+        if V is None:
+            raise ValueError("the accept half needs target_logits or vocab")
+        for t, name, dt in ((draft_tokens, "draft_tokens", torch.int32), (uniforms, "uniforms", torch.float32),
+                            (target_logits, "target_logits", torch.float32),
+                            (draft_logits, "draft_logits", torch.float32)):
+            if t is not None:
+                _need(t, name, dt, dev)
+        cd = accept_desc(B, V, max_draft, "stochastic" if uniforms is not None else "greedy")
+    if status_word is None:
+        status_word = torch.empty(1, dtype=torch.int32, device=dev)
+    _need(status_word, "status_word", torch.int32, dev)
+    _check(lib().sd_validate_inputs(ctypes.byref(ad) if ad is not None else None,
+                                    ctypes.byref(cd) if cd is not None else None, T,
+                                    _ptr(block_table), _ptr(kv_len), _ptr(q_start), _ptr(draft_tokens),
+                                    _ptr(uniforms), _ptr(target_logits), _ptr(draft_logits), _ptr(status_word),
+                                    _stream(dev, stream)))
+    return status_word

@@ -416,6 +416,41 @@ SD_EXPORT sd_status sd_verify_linear(const sd_linear_desc* desc, const void* x, 
   return SD_OK;
 }
 
+SD_EXPORT sd_status sd_validate_inputs(const sd_attn_desc* attn, const sd_accept_desc* acc, int32_t total_q,
+                                       const int32_t* block_table, const int32_t* kv_len, const int32_t* q_start,
+                                       const int32_t* draft_tokens, const float* uniforms, const float* target_logits,
+                                       const float* draft_logits, uint32_t* status_word, void* stream) {
+  if (!attn && !acc) return fail(SD_ERR_INVALID_ARG, "sd_validate_inputs needs an attention or an accept descriptor");
+  sd_status s = SD_OK;
+  if (attn && (s = check_attn(attn, total_q)) != SD_OK) return s;
+  if (acc && (s = check_accept(acc, total_q)) != SD_OK) return s;
+  if (attn && acc && (attn->num_seqs != acc->num_seqs || attn->max_draft != acc->max_draft))
+    return fail(SD_ERR_INVALID_ARG, "the two descriptors disagree on num_seqs or max_draft");
+  const int B = attn ? attn->num_seqs : acc->num_seqs;
+  if (!status_word || !q_start) return fail(SD_ERR_INVALID_ARG, "status_word and q_start are required");
+  if (attn && (!block_table || !kv_len)) return fail(SD_ERR_INVALID_ARG, "block_table and kv_len are required with attn");
+  if (acc && total_q > B && !draft_tokens) return fail(SD_ERR_INVALID_ARG, "draft_tokens is required with acc");
+  SdValidateLaunch v{};
+  v.block_table = attn ? block_table : nullptr;
+  v.kv_len = attn ? kv_len : nullptr;
+  v.q_start = q_start;
+  v.tokens = acc ? draft_tokens : nullptr;
+  v.uniforms = acc ? uniforms : nullptr;
+  v.target = acc ? target_logits : nullptr;
+  v.draft = acc && total_q > B ? draft_logits : nullptr;
+  v.status = status_word;
+  v.B = B;
+  v.T = total_q;
+  v.V = acc ? acc->vocab : 1;
+  v.max_draft = attn ? attn->max_draft : acc->max_draft;
+  v.max_pages = attn ? attn->max_pages_per_seq : 0;
+  v.num_pages = attn ? attn->num_pages : 0;
+  v.stream = (hipStream_t)stream;
+  hipError_t e = sdv_validate_launch(v);
+  if (e != hipSuccess) return fail(SD_ERR_HIP, "validation launch: %s", hipGetErrorString(e));
+  return SD_OK;
+}
+
 SD_EXPORT const char* sd_last_error(void) { return g_error.c_str(); }
 
 SD_EXPORT const char* sd_version(void) { return "sdverify 0.1.0 (gfx950)"; }

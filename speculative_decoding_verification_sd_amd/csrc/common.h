@@ -131,6 +131,22 @@ struct SdLoopLaunch {
 size_t sdv_loop_workspace_bytes(int B, int V, int ntiers, int dmax);
 hipError_t sdv_closed_loop(const SdLoopLaunch& c);
 
+// Opt-in check of the inputs' device-side contract (validate.hip).  NULL
+// pointers switch the matching checks off; status gets SD_BAD_* bits.
+struct SdValidateLaunch {
+  const int32_t* block_table;   // [B, max_pages] (NULL: no cache checks)
+  const int32_t* kv_len;        // [B]
+  const int32_t* q_start;       // [B+1]
+  const int32_t* tokens;        // [T - B] drafted tokens (NULL: not checked)
+  const float* uniforms;        // [T] (NULL: not checked)
+  const float* target;          // [T, V] (NULL: not checked)
+  const float* draft;           // [T - B, V] (NULL: not checked)
+  uint32_t* status;             // one word, cleared then OR-ed
+  int B, T, V, max_draft, max_pages, num_pages;
+  hipStream_t stream;
+};
+hipError_t sdv_validate_launch(const SdValidateLaunch& v);
+
 struct SdGemmLaunch {
   const void* x;
   const void* w;

@@ -233,3 +233,38 @@ def test_closed_loop_rejects_bad_descriptions():
     assert lib.sd_closed_loop(ctypes.byref(ok), dummy, dummy, dummy, 3, dummy, dummy, dummy, 8,
                               None) == B.SD_ERR_WORKSPACE
     assert lib.sd_closed_loop(ctypes.byref(ok), None, None, None, 0, None, None, None, 0, None) == B.SD_OK
+
+
+_FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every case below fails before anything is enqueued
+
+
+@pytest.mark.parametrize("case,needle", [
+    ("no_desc", "needs an attention or an accept descriptor"),
+    ("disagree", "disagree on num_seqs or max_draft"),
+    ("no_status", "status_word and q_start are required"),
+    ("no_table", "block_table and kv_len are required"),
+    ("no_tokens", "draft_tokens is required"),
+    ("bad_attn", "head_dim"),
+])
+def test_validate_inputs_rejects_bad_arguments(case, needle):
+    lib = sdv.lib()
+    a, c = _attn(), _acc()
+    args = dict(attn=ctypes.byref(a), acc=ctypes.byref(c), table=_FAKE, kv=_FAKE, qs=_FAKE, tok=_FAKE, status=_FAKE)
+    if case == "no_desc":
+        args.update(attn=None, acc=None)
+    elif case == "disagree":
+        c2 = _acc(max_draft=5)
+        args.update(acc=ctypes.byref(c2))
+    elif case == "no_status":
+        args.update(status=None)
+    elif case == "no_table":
+        args.update(table=None)
+    elif case == "no_tokens":
+        args.update(tok=None)
+    elif case == "bad_attn":
+        a2 = _attn(head_dim=96)
+        args.update(attn=ctypes.byref(a2))
+    st = lib.sd_validate_inputs(args["attn"], args["acc"], 8, args["table"], args["kv"], args["qs"], args["tok"],
+                                None, None, None, args["status"], None)
+    assert st != B.SD_OK
+    assert needle in sdv.sd_last_error()

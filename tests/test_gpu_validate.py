@@ -1,0 +1,134 @@
+"""GPU check of sd_validate_inputs, the opt-in pass over the verify step's
+device-side contract, through the C ABI: valid inputs give 0; each planted
+violation gives exactly its bit (several give the OR); entries outside what the
+contract covers (block-table columns past a sequence's pages, a single -inf
+logit) give nothing.  The planted inputs go to the validator only."""
+
+import pytest
+import torch
+
+import speculative_decoding_verification_sd_amd as sdv
+from tests.gpu_util import on_gpu, say
+from workloads import WorkloadSpec, generate
+
+pytestmark = pytest.mark.gpu
+
+BAD = sdv.SD_BAD
+
+
+@pytest.fixture(scope="module")
+def inputs():
+    sp = WorkloadSpec(name="validate_case", batch=4, kv_heads=2, group=4, head_dim=64, kv_len=[300, 40, 1000, 77],
+                      draft_len=[3, 0, 7, 2], vocab=500, mode="stochastic", seed=41)
+    return on_gpu(generate(sp))
+
+
+def run(x, attn=True, acc=True, logits=True, **over):
+    a = dict(q=x.q, k_cache=x.k_cache, block_table=x.block_table, kv_len=x.kv_len, group_size=x.group,
+             draft_tokens=x.draft_tokens, uniforms=x.uniforms, target_logits=x.target_logits,
+             draft_logits=x.draft_logits)
+    a.update(over)
+    if not attn:
+        a.update(block_table=None, kv_len=None, k_cache=None)
+    if not acc:
+        a.update(draft_tokens=None, uniforms=None, target_logits=None, draft_logits=None)
+    elif not logits:
+        a.update(target_logits=None, draft_logits=None, vocab=x.target_logits.shape[1])
+    w = sdv.sd_validate_inputs(a.pop("q_start", x.q_start), max_draft=x.max_draft, **a)
+    torch.cuda.synchronize()
+    return int(w.item())
+
+
+def test_valid_inputs_report_nothing(inputs):
+    say("case: validate valid inputs")
+    assert run(inputs) == 0
+    assert run(inputs, attn=False) == 0
+    assert run(inputs, acc=False) == 0
+    assert run(inputs, logits=False) == 0
+
+
+def test_q_start(inputs):
+    x = inputs
+    qs = x.q_start.clone()
+    qs[2] = qs[1]                      # sequence 1 gets no row
+    assert run(x, q_start=qs) & BAD["q_start"]
+    qs = x.q_start.clone()
+    qs[-1] -= 1                        # does not end at total_q
+    assert run(x, q_start=qs) == BAD["q_start"]
+    qs = x.q_start.clone()
+    qs[1] = qs[0] + x.max_draft + 2    # sequence 0 takes more than 1+max_draft rows
+    assert run(x, q_start=qs) & BAD["q_start"]
+
+
+def test_kv_len(inputs):
+    x = inputs
+    kv = x.kv_len.clone()
+    kv[2] = 7                          # sequence 2 has 1+7 rows: needs at least 8 keys
+    assert run(x, kv_len=kv) == BAD["kv_len"]
+    kv = x.kv_len.clone()
+    kv[0] = x.block_table.shape[1] * 16 + 1
+    # (every column of row 0 is then in use, and the generator leaves -1 past a sequence's pages)
+    assert run(x, kv_len=kv) == BAD["kv_len"] | BAD["page"]
+
+
+def test_page_ids(inputs):
+    x = inputs
+    bt = x.block_table.clone()
+    n_pages = x.k_cache.shape[0]
+    bt[0, 0] = n_pages
+    assert run(x, block_table=bt) == BAD["page"]
+    bt = x.block_table.clone()
+    bt[3, 4] = -3                      # sequence 3 (77 keys) uses pages 0..4
+    assert run(x, block_table=bt) == BAD["page"]
+    bt = x.block_table.clone()
+    bt[1, 3:] = -5                     # sequence 1 (40 keys) uses pages 0..2 only
+    assert run(x, block_table=bt) == 0
+
+
+def test_tokens_and_uniforms(inputs):
+    x = inputs
+    tok = x.draft_tokens.clone()
+    tok[0] = x.target_logits.shape[1]
+    assert run(x, draft_tokens=tok) == BAD["token"]
+    tok = x.draft_tokens.clone()
+    tok[-1] = -1
+    assert run(x, draft_tokens=tok) == BAD["token"]
+    for v in (1.0, -0.25, float("nan")):
+        u = x.uniforms.clone()
+        u[3] = v
+        assert run(x, uniforms=u) == BAD["uniform"], v
+
+
+def test_logits(inputs):
+    x = inputs
+    t = x.target_logits.clone()
+    t[2, 5] = float("nan")
+    assert run(x, target_logits=t) == BAD["logits"]
+    t = x.target_logits.clone()
+    t[0, 0] = float("inf")
+    assert run(x, target_logits=t) == BAD["logits"]
+    d = x.draft_logits.clone()
+    d[4, :] = float("-inf")            # a draft row with no finite logit
+    assert run(x, draft_logits=d) == BAD["logits"]
+    d = x.draft_logits.clone()
+    d[4, 7] = float("-inf")            # a single -inf is allowed
+    assert run(x, draft_logits=d) == 0
+    t = x.target_logits.clone()
+    t[0, 0] = float("nan")
+    assert run(x, target_logits=t, logits=False) == 0   # logits not passed: not scanned
+
+
+def test_several_violations_or_together(inputs):
+    x = inputs
+    kv = x.kv_len.clone()
+    kv[1] = 0
+    tok = x.draft_tokens.clone()
+    tok[1] = 10**6
+    u = x.uniforms.clone()
+    u[0] = 2.0
+    got = run(x, kv_len=kv, draft_tokens=tok, uniforms=u)
+    say(f"  status word {got:#x}")
+    assert got == BAD["kv_len"] | BAD["token"] | BAD["uniform"]
+    # the halves check only their own inputs
+    assert run(x, kv_len=kv, draft_tokens=tok, uniforms=u, acc=False) == BAD["kv_len"]
+    assert run(x, kv_len=kv, draft_tokens=tok, uniforms=u, attn=False) == BAD["token"] | BAD["uniform"]
