@@ -153,7 +153,7 @@ __global__ __launch_bounds__(64 * kMaskSeqsPerBlock) void verify_tree_masks(Attn
 // kPlanCacheSeqs sequences) and, when list_splits, the list of the split
 // sequences (plan[3] entries, any order) for the combine of large batches.
 constexpr int kLenBuckets = 64;
-constexpr int kPlanCacheSeqs = 2048;     // sequences whose key count and tail index the plan keeps in LDS
+constexpr int kPlanCacheSeqs = 8192;     // sequences whose fields the plan keeps in LDS (4 x 32 KiB; gfx950 allows 160 KiB per workgroup)
 constexpr int kHistBins = kMaxChunk / 64 + 2;   // ceil(N/64) = 0 .. 256, and "longer"
 constexpr int kLongSeqs = 256;           // sequences longer than kMaxChunk the chunk search lists in LDS
 constexpr int kDirectSeqs = 32;          // chunk search: batches this small skip the histogram

@@ -62,17 +62,21 @@ def test_row_block_variants(G, drafts, d):
 
 @pytest.mark.parametrize("kv_chunk", [0, 256])
 def test_many_sequences_mixed_lengths(kv_chunk):
-    """More sequences than the plan keeps in LDS (2048), lengths 1..900 plus one
+    """More sequences than the plan keeps in LDS (8192), lengths 1..300 plus one
     long sequence: the plan's global path, items shorter than the chunk in
-    longest-first order, and workgroups taking items from the counters."""
+    longest-first order, and workgroups taking items from the counters.
+    Checked on sampled units, the long one, and sequences on both sides of
+    the LDS boundary."""
     rng = np.random.default_rng(21)
-    B = 2100
-    kv = [int(x) for x in rng.integers(1, 900, size=B)]
+    B = 8300
+    kv = [int(x) for x in rng.integers(1, 300, size=B)]
     kv[0] = 20000
     dr = [int(x) for x in rng.integers(0, 4, size=B)]
     inp = generate(spec(batch=B, kv_heads=1, group=2, head_dim=64, kv_len=kv, draft_len=dr, seed=21))
     say(f"case: B={B} mixed lengths kv_chunk={kv_chunk}")
-    err = compare_attention(inp, gpu_attention(inp, kv_chunk=kv_chunk))
+    units = [(0, 0)] + [(int(b), 0) for b in rng.choice(B, size=60, replace=False)] + \
+        [(b, 0) for b in (8190, 8191, 8192, 8193, B - 1)]
+    err = compare_attention(inp, gpu_attention(inp, kv_chunk=kv_chunk), units=units)
     say(f"max|err| = {err:.3e}")
     assert err <= ATTN_TOL
 
