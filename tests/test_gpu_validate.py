@@ -132,3 +132,22 @@ def test_several_violations_or_together(inputs):
     # the halves check only their own inputs
     assert run(x, kv_len=kv, draft_tokens=tok, uniforms=u, acc=False) == BAD["kv_len"]
     assert run(x, kv_len=kv, draft_tokens=tok, uniforms=u, attn=False) == BAD["token"] | BAD["uniform"]
+
+
+def test_full_size_workload_validates_clean():
+    """The benchmarked verify step (16 sequences, 32768-token caches, 8 KV heads,
+    D=15, V=131072) keeps the contract; the pass over its logits is timed."""
+    from workloads import preset
+    x = on_gpu(generate(preset("g8_kv32k_D15")))
+    say("case: validate the full-size default workload")
+    assert run(x) == 0
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ev[0].record()
+    run(x, logits=False)
+    ev[1].record()
+    ev[2].record()
+    run(x)
+    ev[3].record()
+    torch.cuda.synchronize()
+    say(f"  validation without logits {ev[0].elapsed_time(ev[1]) * 1e3:.0f} us, "
+        f"with logits {ev[2].elapsed_time(ev[3]) * 1e3:.0f} us (host sync included)")
