@@ -156,7 +156,7 @@ constexpr int kLenBuckets = 64;
 constexpr int kPlanCacheSeqs = 8192;     // sequences whose fields the plan keeps in LDS (4 x 32 KiB; gfx950 allows 160 KiB per workgroup)
 constexpr int kHistBins = kMaxChunk / 64 + 2;   // ceil(N/64) = 0 .. 256, and "longer"
 constexpr int kLongSeqs = 256;           // sequences longer than kMaxChunk the chunk search lists in LDS
-constexpr int kDirectSeqs = 32;          // chunk search: batches this small skip the histogram
+constexpr int kDirectSeqs = 64;          // chunk search: batches this small skip the histogram
 constexpr int kSearchCost = 8;           // descriptors: an item found by binary search costs about 8 written directly
 
 __global__ __launch_bounds__(kPlanThreads) void verify_attn_plan(AttnParams p, int fixed_chunk, int slots,
@@ -1592,7 +1592,7 @@ static int attn_slots(int cus, int variant) { return cus * (variant == 0 ? 2 : 1
 // computed for the largest CU count of a gfx950 part so that the size query
 // needs no device.
 constexpr int kMaxCus = 256;
-constexpr int kCombineGrid = 16 * kMaxCus;   // combine workgroups: 8 rows of one (sequence, KV head) each
+constexpr int kCombineGrid = 32 * kMaxCus;   // combine workgroups: 8 rows of one (sequence, KV head) each
 
 static AttnLayout attn_layout(int B, int Hkv, int G, int HD, int max_pages, int max_draft, int kv_chunk) {
   AttnLayout L;

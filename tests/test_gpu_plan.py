@@ -29,7 +29,7 @@ PAGE = 16
 def expected_plan(kv, hkv, group, max_draft, head_dim, max_pages, cus, kv_chunk=0):
     """(chunk, items, sequences split in more than one item) by the rule above;
     the plan lists the split sequences only for batches whose combine would
-    need more than 4096 workgroups of 8 rows (it writes 0 otherwise)."""
+    need more than 8192 workgroups of 8 rows (it writes 0 otherwise)."""
     n = np.minimum(np.maximum(np.asarray(kv, np.int64), 0), max_pages * PAGE)
     B = len(n)
     rmax = group * (1 + max_draft)
@@ -61,7 +61,7 @@ def expected_plan(kv, hkv, group, max_draft, head_dim, max_pages, cus, kv_chunk=
         chunk = cap_chunk if best is None else min(256 + 64 * best[1], cap_chunk)
     per_seq = np.maximum(1, -(-n // chunk))
     rpad = -(-rmax // 16) * 16
-    listed = B * hkv * (rpad // 8) > 4096
+    listed = B * hkv * (rpad // 8) > 8192
     return chunk, hkv * int(per_seq.sum()), int((per_seq > 1).sum()) if listed else 0
 
 
@@ -133,13 +133,14 @@ def test_more_long_sequences_than_the_plan_lists():
 
 
 def test_large_batch_every_sequence_split():
-    """600 sequences over 8 row blocks each, all split by a 512-key chunk: the
-    combine walks the plan's list of split sequences."""
+    """1100 sequences over 8 row blocks each (8800 combine workgroups), all
+    split by a 512-key chunk: the combine walks the plan's list of split
+    sequences."""
     rng = np.random.default_rng(36)
-    kv = [int(x) for x in rng.integers(600, 2000, size=600)]
-    inp = generate(spec(batch=600, kv_heads=1, group=8, kv_len=kv, draft_len=7, seed=36))
-    say("case: plan B=600 kv_chunk=512, listed splits")
-    check(inp, kv_chunk=512, units=[(0, 0), (299, 0), (599, 0)])
+    kv = [int(x) for x in rng.integers(600, 2000, size=1100)]
+    inp = generate(spec(batch=1100, kv_heads=1, group=8, kv_len=kv, draft_len=7, seed=36))
+    say("case: plan B=1100 kv_chunk=512, listed splits")
+    check(inp, kv_chunk=512, units=[(0, 0), (549, 0), (1099, 0)])
 
 
 def test_explicit_chunk_counts_split_sequences():
