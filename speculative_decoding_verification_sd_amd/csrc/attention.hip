@@ -632,6 +632,7 @@ __global__ __launch_bounds__(64 * NW, WPC) void verify_attn_main(AttnParams p) {
     if (!dyn) return vi + (int)gridDim.x;
     block_sync();
     if (threadIdx.x == 0) s_next = first_dyn + 8 * atomicAdd(p.plan + 8 + cls, 1);
+    wait_lds();   // s_barrier does not wait for LDS stores: without this a wave can read the old index
     block_sync();
     return s_next;
   };
@@ -1116,6 +1117,7 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
     if (!dyn) return vi + (int)gridDim.x;
     block_sync();
     if (threadIdx.x == 0) s_next = first_dyn + 8 * atomicAdd(p.plan + 8 + cls, 1);
+    wait_lds();   // s_barrier does not wait for LDS stores: without this a wave can read the old index
     block_sync();
     return s_next;
   };
@@ -1443,6 +1445,7 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
         xch[(16 * NMB) * 64] = lt;
         xch[(16 * NMB + 1) * 64] = m_run;
       }
+      wait_lds();   // (the stores have landed before the barrier)
       block_sync();
       if (set == 0 && wave_active && valid) {
         const float lb = xch[(16 * NMB) * 64];

@@ -10,7 +10,7 @@ import torch
 import speculative_decoding_verification_sd_amd as sdv
 
 from oracle import verify_attention_unit
-from tests.gpu_util import ATTN_TOL, compare_attention, gpu_attention, say, unit_subproblem
+from tests.gpu_util import ATTN_TOL, compare_attention, gpu_attention, on_gpu, say, unit_subproblem
 from workloads import WorkloadSpec, generate, preset
 
 pytestmark = pytest.mark.gpu
@@ -205,5 +205,47 @@ def test_score_far_above_the_first_tile_max(key, prefix, kv_chunk):
     _plant_dominant_key(inp, 0, 1, key, negative_prefix=prefix)
     say(f"case: dominant key {key} prefix {prefix} kv_chunk={kv_chunk}")
     err = compare_attention(inp, gpu_attention(inp, kv_chunk=kv_chunk))
+    say(f"max|err| = {err:.3e}")
+    assert err <= ATTN_TOL
+
+
+@pytest.mark.parametrize("group,kv_chunk", [(8, 0), (8, 512), (16, 512)])
+def test_dynamic_schedule_many_items_per_workgroup(group, kv_chunk):
+    """1100 sequences of 600..2000 keys with D=7 (64 rows per KV head: every wave
+    of the R <= 64 kernel has rows; group 16: the wide kernel), several items
+    per workgroup handed out by the work counters.  Each wave must take the
+    item index the counter gave its workgroup: the index passes through LDS,
+    and a barrier does not wait for LDS stores by itself (a wave that read the
+    old index redid the previous item and left its rows of the new one
+    unwritten).  Three workspace fills give bit-identical outputs with every
+    row written, and sampled units (late, dynamically scheduled items
+    included) match the oracle."""
+    rng = np.random.default_rng(37)
+    B = 1100
+    kv = [int(x) for x in rng.integers(600, 2000, size=B)]
+    inp = generate(spec(batch=B, kv_heads=1, group=group, head_dim=64, kv_len=kv, draft_len=7, seed=37))
+    x = on_gpu(inp)
+    desc = sdv.attn_desc(x.q, x.k_cache, x.block_table, group, inp.max_draft, kv_chunk=kv_chunk)
+    n = sdv.sd_verify_attention_workspace_size(desc, x.q.shape[0])
+    say(f"case: dynamic schedule B={B} G={group} kv_chunk={kv_chunk}")
+    outs = []
+    for fill in ("zeros", "ones", "random"):
+        ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+        if fill == "zeros":
+            ws.zero_()
+        elif fill == "ones":
+            ws.fill_(255)
+        else:
+            ws.copy_(torch.randint(0, 256, (n,), dtype=torch.uint8))
+        out = torch.full(x.q.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+        sdv.sd_verify_attention(x.q, x.k_cache, x.v_cache, x.block_table, x.kv_len, x.q_start, out,
+                                group_size=group, max_draft=inp.max_draft, kv_chunk=kv_chunk, workspace=ws)
+        torch.cuda.synchronize()
+        assert not torch.isnan(out.float()).any(), f"unwritten rows with a {fill} workspace"
+        outs.append(out.cpu())
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+    units = [(int(b), 0) for b in rng.choice(B, size=24, replace=False)] + [(B - 1, 0), (B - 2, 0)]
+    err = compare_attention(inp, outs[0], units=units)
     say(f"max|err| = {err:.3e}")
     assert err <= ATTN_TOL
