@@ -170,3 +170,42 @@ def test_full_size_tree_workload():
     for g, r, name in zip(got, ref, ("accept_len", "out_tokens", "out_nodes")):
         np.testing.assert_array_equal(g, r, err_msg=name)
     say(f"mean AL = {got[0].mean():.3f}")
+
+
+@pytest.mark.parametrize("group", [8, 16])
+def test_tree_dynamic_schedule_many_items_per_workgroup(group):
+    """900 sequences of 600..2000 keys with random trees of 7 nodes (64 or 128
+    rows per KV head: the R <= 64 kernel and the wide kernel, tree variants)
+    and a 512-key chunk, so that workgroups take several items each from the
+    work counters (whose index reaches the waves through LDS).  Three
+    workspace fills give bit-identical outputs with every row written;
+    sampled units match the tree oracle."""
+    rng = np.random.default_rng(38)
+    B = 900
+    kv = [int(x) for x in rng.integers(600, 2000, size=B)]
+    inp = generate(_spec(batch=B, kv_heads=1, group=group, head_dim=64, kv_len=kv, draft_len=7, seed=38))
+    args = attention_args(inp)
+    par = _parents(args["q_start"], "random", rng)
+    x = inp.to("cuda")
+    parents = torch.from_numpy(par).cuda()
+    desc = sdv.attn_desc(x.q, x.k_cache, x.block_table, inp.group, inp.max_draft, kv_chunk=512)
+    nbytes = sdv.sd_verify_attention_workspace_size(desc, x.q.shape[0])
+    say(f"case: tree dynamic schedule B={B} G={group}")
+    outs = []
+    for fill in (0x00, 0xFF, 0x5A):
+        ws = torch.full((nbytes,), fill, dtype=torch.uint8, device="cuda")
+        out = torch.full(x.q.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+        sdv.sd_verify_tree_attention(x.q, x.k_cache, x.v_cache, x.block_table, x.kv_len, x.q_start, parents, out,
+                                     group_size=inp.group, max_draft=inp.max_draft, kv_chunk=512, workspace=ws)
+        torch.cuda.synchronize()
+        assert not torch.isnan(out.float()).any(), f"unwritten rows with workspace fill {fill:#x}"
+        outs.append(out.cpu())
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+    units = [(int(b), 0) for b in rng.choice(B, size=16, replace=False)] + [(B - 1, 0)]
+    ref = verify_tree_attention(parents=par, units=units, **args)
+    got = outs[0].float().numpy().astype(np.float64)
+    mask = ~np.isnan(ref)
+    err = float(np.max(np.abs(got[mask] - ref[mask])))
+    say(f"max|err| over {len(units)} units = {err:.3e}")
+    assert err <= ATTN_TOL
