@@ -468,6 +468,17 @@ __device__ __forceinline__ float row_max4(float v) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// The max a split-KV partial is stored with: the offset its P values were
+// actually computed against.  In the fast pass a row whose first tile of the
+// item shows no visible key keeps a reference of -inf and takes its P against
+// 0, which happens under a draft-tree mask when a split begins inside the tree
+// and the row's own nodes lie in a later tile of the item; such a partial then
+// holds l > 0 and must carry 0, not -inf, or the combine weights it by zero.
+// A partial with l = 0 keeps -inf so that it cannot raise the merged max.
+__device__ __forceinline__ float partial_max(float m, float l) {
+  return l > 0.f ? (m == -INFINITY ? 0.f : m) : -INFINITY;
+}
+
 template <int HD, int NW, int WPC>
 struct Ring {
   static constexpr int kTile = 32;                        // keys per tile (two pages)
@@ -632,8 +643,7 @@ __global__ __launch_bounds__(64 * NW, WPC) void verify_attn_main(AttnParams p) {
     if (!dyn) return vi + (int)gridDim.x;
     block_sync();
     if (threadIdx.x == 0) s_next = first_dyn + 8 * atomicAdd(p.plan + 8 + cls, 1);
-    wait_lds();   // s_barrier does not wait for LDS stores: without this a wave can read the old index
-    block_sync();
+    block_sync_lds();   // (a bare barrier would let a wave read the old index)
     return s_next;
   };
   constexpr int row0 = 0;
@@ -675,7 +685,9 @@ __global__ __launch_bounds__(64 * NW, WPC) void verify_attn_main(AttnParams p) {
         dma16<true>((dma[i].kv ? vbase : kbase) + (dma[i].page ? off1 : off0), dma[i].src,
               sb + (unsigned)(dma[i].kv * S * RG::kHalf + dma[i].dst));
     };
-    // zero what this wave loaded into stage st for keys at or past k_end (last tile only)
+    // zero what this wave loaded into stage st for keys at or past k_end (last
+    // tile only); the stores complete here, since the ring barrier that
+    // follows is the bare one
     auto zero_tail = [&](int tile, int st) {
       zero_keys_past<LPW, RG, S>(smem + st * RG::kHalf, dma, lane, k_end - (k_begin + tile * RG::kTile));
       wait_lds();
@@ -725,8 +737,7 @@ __global__ __launch_bounds__(64 * NW, WPC) void verify_attn_main(AttnParams p) {
     for (int j = tid; j < ntiles * (RG::kTile / kPage); j += 64 * NW)
       s_pages[j] = min(max(bt[min(page0 + j, last_page)], 0), p.num_pages - 1);
     wait_vmem<0>();
-    wait_lds();
-    block_sync();
+    block_sync_lds();
 
     // Scores of tile `tile`: causal (or draft-tree) mask, only for tiles that
     // reach the draft block, and row max.
@@ -1016,7 +1027,7 @@ __global__ __launch_bounds__(64 * NW, WPC) void verify_attn_main(AttnParams p) {
           for (int db = 0; db < NDB; ++db) *(f32x4*)(slab + db * 16) = o[rb][db];
           if (g4 == 0) {
             float* ml = p.part_ml + ((size_t)pslot * p.rpad + row) * 2;
-            ml[0] = m_run[rb];
+            ml[0] = partial_max(m_run[rb], lt);
             ml[1] = lt;
           }
         }
@@ -1117,8 +1128,7 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
     if (!dyn) return vi + (int)gridDim.x;
     block_sync();
     if (threadIdx.x == 0) s_next = first_dyn + 8 * atomicAdd(p.plan + 8 + cls, 1);
-    wait_lds();   // s_barrier does not wait for LDS stores: without this a wave can read the old index
-    block_sync();
+    block_sync_lds();   // (a bare barrier would let a wave read the old index)
     return s_next;
   };
   for (int item = blockIdx.x; item < total; item = next_item(item)) {
@@ -1156,6 +1166,7 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
         dma16<true>((dma[i].kv ? vbase : kbase) + (dma[i].page ? off1 : off0), dma[i].src,
               sb + (unsigned)(dma[i].kv * S * RG::kHalf + dma[i].dst));
     };
+    // (as in verify_attn_main: the zeroing stores complete before the bare ring barrier)
     auto zero_tail = [&](int tile) {
       zero_keys_past<LPW, RG, S>(smem + (tile % S) * RG::kHalf, dma, lane, k_end - (k_begin + tile * RG::kTile));
       wait_lds();
@@ -1204,8 +1215,7 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
     for (int j = tid; j < ntiles * (RG::kTile / kPage); j += 64 * NW)
       s_pages[j] = min(max(bt[min(page0 + j, last_page)], 0), p.num_pages - 1);
     wait_vmem<0>();
-    wait_lds();
-    block_sync();
+    block_sync_lds();
 
     f32x16 sc;
     float mt = -INFINITY;
@@ -1433,8 +1443,8 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
 
     // ---- Merge the two sets' partials (RS false: set 1 hands (O, l, m) to set 0
     // through LDS; RS true: each set owns its rows).
-    float M = m_run;
     float lt = row_sum();
+    float M = partial_max(m_run, lt);
     if constexpr (!RS) {
       float* xch = (float*)smem + (size_t)w4 * kMergeF * 64 + lane;
       if (set == 1 && wave_active) {
@@ -1443,15 +1453,15 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
 #pragma unroll
           for (int e = 0; e < 16; ++e) xch[(mb * 16 + e) * 64] = o[mb][e];
         xch[(16 * NMB) * 64] = lt;
-        xch[(16 * NMB + 1) * 64] = m_run;
+        xch[(16 * NMB + 1) * 64] = M;
       }
-      wait_lds();   // (the stores have landed before the barrier)
-      block_sync();
+      block_sync_lds();
       if (set == 0 && wave_active && valid) {
         const float lb = xch[(16 * NMB) * 64];
         const float mb_ = xch[(16 * NMB + 1) * 64];
-        M = fmaxf(m_run, mb_);
-        const float wa = M == -INFINITY ? 0.f : fast_exp2(m_run - M);
+        const float ma = M;
+        M = fmaxf(ma, mb_);
+        const float wa = M == -INFINITY ? 0.f : fast_exp2(ma - M);
         const float wb = M == -INFINITY ? 0.f : fast_exp2(mb_ - M);
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb)

@@ -38,10 +38,22 @@ __device__ __forceinline__ void wait_lds() {
   __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
 }
 
+// A bare workgroup barrier.  s_barrier does not wait for this wave's own LDS
+// stores (nor for its vector loads): the LDS-DMA ring uses it as is, because
+// each wave waits for its DMA loads with s_waitcnt vmcnt before the barrier
+// and writes no LDS with ordinary stores there.
 __device__ __forceinline__ void block_sync() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+}
+
+// A barrier that publishes this wave's LDS stores to the workgroup: wait until
+// they have completed, then s_barrier.  Every hand-off of values through LDS
+// by ordinary stores (a work index, partial results) goes through this.
+__device__ __forceinline__ void block_sync_lds() {
+  wait_lds();
+  block_sync();
 }
 
 // One 16-byte-per-lane global->LDS DMA (global_load_lds_dwordx4, scalar-base
@@ -50,8 +62,10 @@ __device__ __forceinline__ void block_sync() {
 // Issued as inline asm so that the compiler's waitcount logic does not pace
 // every later LDS read on these loads (it cannot tell ring stages apart and
 // would wait for all of them); the ring waits for them explicitly with
-// s_waitcnt vmcnt before its barrier.  M0 is written only here in the
-// kernels that use it, which a build test checks on the generated ISA.
+// s_waitcnt vmcnt before its barrier.  The asm saves M0 in a scratch SGPR,
+// sets it, issues the load (one wait state after the M0 write) and puts the
+// saved value back, so M0 is unchanged across the statement and the compiler
+// may keep anything of its own there.
 // STREAM: data read once per call (the KV cache) goes with the non-temporal
 // hint, so that it does not displace what the caches hold for reuse.
 template <bool STREAM = false>
@@ -61,16 +75,19 @@ __device__ __forceinline__ void dma16(const unsigned char* base, unsigned voff, 
   const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(b >> 32));
   const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)b);
   const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
+  unsigned saved;
   if constexpr (STREAM)
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
-                 :
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3 nt\n\t"
+                 "s_mov_b32 m0, %0"
+                 : "=&s"(saved)
                  : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(sb)
-                 : "memory", "m0");
+                 : "memory");
   else
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                 :
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3\n\t"
+                 "s_mov_b32 m0, %0"
+                 : "=&s"(saved)
                  : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(sb)
-                 : "memory", "m0");
+                 : "memory");
 }
 
 }  // namespace sdv

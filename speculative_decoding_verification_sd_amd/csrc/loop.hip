@@ -215,10 +215,10 @@ hipError_t sdv_closed_loop(const SdLoopLaunch& c) {
   std::vector<hipGraph_t> graphs;
   std::vector<hipGraphExec_t> execs;
   hipStream_t cs = nullptr;
-  auto cleanup = [&]() {
-    for (auto x : execs) hipGraphExecDestroy(x);
-    for (auto g : graphs) hipGraphDestroy(g);
-    if (cs) hipStreamDestroy(cs);
+  auto cleanup = [&]() {   // (teardown errors cannot change the call's result)
+    for (auto x : execs) (void)hipGraphExecDestroy(x);
+    for (auto g : graphs) (void)hipGraphDestroy(g);
+    if (cs) (void)hipStreamDestroy(cs);
   };
   if (c.use_graphs) {
     e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);

@@ -2,8 +2,8 @@
 kernels, the ones that use the LDS-DMA ring (CPU only: hipcc cross-compiles the
 device code to assembly).
 
-* M0 is written only by the LDS-DMA sequence (s_mov_b32 m0 / s_nop / global_load_lds),
-  so the inline-asm DMA's M0 clobber cannot disturb anything the compiler keeps in M0.
+* Every LDS-DMA load is issued by the inline-asm sequence that saves M0, sets it, loads
+  and restores it, so the asm never changes M0 behind the compiler's back.
 * No transposed V read (ds_read_b64_tr_b16) or K read (ds_read_b128) waits for every
   vector load in flight: between a barrier and the LDS reads of a tile there is no
   s_waitcnt vmcnt(0), which would drain the DMA ring on every tile.
@@ -35,12 +35,12 @@ def _compile(tmp_path_factory, unit):
     fname, pattern, least = UNITS[unit]
     out = tmp_path_factory.mktemp("isa") / (unit + ".s")
     cmd = [cc, *B.COMMON_FLAGS, *B.DEVICE_FLAGS, *B.FILE_FLAGS.get(fname, []), "--cuda-device-only",
-           "-S", "-Wno-inline-asm", os.path.join(CSRC, fname), "-o", str(out)]
+           "-S", os.path.join(CSRC, fname), "-o", str(out)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-3000:]
     text = out.read_text()
     found = {}
-    for m in re.finditer(r"^(_Z\w*" + pattern + r"\w*):[^\n]*\n(.*?)^\s*s_endpgm", text, re.M | re.S):
+    for m in re.finditer(r"^(_Z\w*" + pattern + r"\w*):[^\n]*\n(.*?)^\.Lfunc_end\d+:", text, re.M | re.S):
         found[m.group(1)] = [l.strip() for l in m.group(2).split("\n")]
     assert len(found) >= least, f"expected every instantiation of the {unit} kernels"
     return found
@@ -65,13 +65,22 @@ def _instrs(lines):
     return [l for l in lines if l and not l.startswith((";", ".")) and not l.endswith(":")]
 
 
-def test_m0_written_only_by_the_dma_sequence(kernels):
+def test_dma_sequence_saves_and_restores_m0(kernels):
+    """Every LDS-DMA load sits in the inline-asm sequence that saves M0, sets it,
+    waits one state, loads, and restores M0 from the saved SGPR: the asm leaves
+    M0 as it found it, whatever the compiler keeps there."""
     for name, lines in kernels.items():
         ins = _instrs(lines)
+        n = 0
         for i, l in enumerate(ins):
-            if re.search(r"\bm0\b", l):
-                assert l.startswith("s_mov_b32 m0, s"), (name, l)
-                assert ins[i + 1] == "s_nop 0" and ins[i + 2].startswith("global_load_lds_dwordx4"), (name, ins[i:i + 3])
+            if not l.startswith("global_load_lds_dwordx4"):
+                continue
+            n += 1
+            save = re.match(r"s_mov_b32 (s\d+|vcc_lo|vcc_hi), m0$", ins[i - 3])
+            assert save and re.match(r"s_mov_b32 m0, s\d+$", ins[i - 2]) and ins[i - 1] == "s_nop 0", \
+                (name, ins[i - 3:i + 1])
+            assert ins[i + 1] == f"s_mov_b32 m0, {save.group(1)}", (name, ins[i - 3:i + 2])
+        assert n > 0, name
 
 
 def test_no_full_vmem_drain_before_tile_reads(kernels):
