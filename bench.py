@@ -60,13 +60,40 @@ def algorithmic_accept(inp):
     return (2 * T - B) * V * 4 + 2 * B * V * 4   # one pass over all rows + the residual/bonus rows
 
 
-def cpu_baseline(inp, budget_s: float = 20.0):
-    """Time the oracle on the host cores over the same workload.
+def cpu_info():
+    """Host CPUs the oracle may use here, the host's total and its model name."""
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):        # pragma: no cover
+        usable = os.cpu_count() or 1
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:                           # pragma: no cover
+        pass
+    return usable, os.cpu_count() or usable, model
+
+
+# The GPU box gives one GPU a share of 16 host cores, whatever the host's total:
+# the oracle's pool is sized to that share (or fewer, where fewer are usable).
+ORACLE_THREADS = 16
+
+
+def cpu_baseline(inp, budget_s: float = 20.0, gpu_out=None, gpu_al=None, gpu_tok=None, tol: float = 2e-2):
+    """Time the oracle on the host cores over the same workload, and compare its
+    results with the GPU's outputs of the same inputs.
 
     Attention units (sequence, KV head) are taken in a seeded random order and
     run in batches on a thread pool until every unit is done or `budget_s` has
     passed; then the same for the sequences' accept/reject.  The measured time
     is scaled by units done / units in the step (1.0 when the whole step ran).
+    With the GPU's outputs given, every unit the oracle ran is compared with
+    them: attention element by element (max |err| and the count above `tol`),
+    accept lengths and emitted tokens bit for bit.  Returns (baseline, parity).
     """
     import numpy as np
     from concurrent.futures import ThreadPoolExecutor
@@ -77,8 +104,9 @@ def cpu_baseline(inp, budget_s: float = 20.0):
     except ImportError:        # pragma: no cover
         threadpool_limits = None
     sp = inp.spec
-    B, Hkv = sp.batch, sp.kv_heads
-    workers = max(1, min(16, os.cpu_count() or 1))
+    B, Hkv, G = sp.batch, sp.kv_heads, sp.group
+    usable, host_cpus, model = cpu_info()
+    workers = max(1, min(ORACLE_THREADS, usable))
     rng = np.random.default_rng(1)
 
     def bits(t):
@@ -88,6 +116,8 @@ def cpu_baseline(inp, budget_s: float = 20.0):
     qs = inp.q_start.cpu().numpy()
     kvl = inp.kv_len.cpu().numpy()
     seq_cache = {}
+    got = gpu_out.float().cpu().numpy() if gpu_out is not None else None
+    att_err, att_over, att_units, att_nonfinite = 0.0, 0, 0, 0
 
     def seq_args(b):
         # host copy of one sequence's pages, shared by its KV heads
@@ -99,7 +129,7 @@ def cpu_baseline(inp, budget_s: float = 20.0):
             seq_cache[b] = dict(q_bits=bits(inp.q[t0:t1]), k_bits=bits(inp.k_cache[pages]),
                                 v_bits=bits(inp.v_cache[pages]), block_table=np.arange(npg, dtype=np.int32)[None],
                                 kv_len=np.asarray([n], np.int32), q_start=np.asarray([0, t1 - t0], np.int32),
-                                group=sp.group, b=0)
+                                group=G, b=0)
         return seq_cache[b]
 
     order = [(int(b), h) for b in rng.permutation(B) for h in range(Hkv)]
@@ -113,9 +143,18 @@ def cpu_baseline(inp, budget_s: float = 20.0):
                 batch = order[i:i + workers]
                 args = [dict(seq_args(b), h=h) for b, h in batch]
                 t_start = time.perf_counter()
-                list(ex.map(lambda a: verify_attention_unit(**a), args))
+                refs = list(ex.map(lambda a: verify_attention_unit(**a), args))
                 t_attn += time.perf_counter() - t_start
                 done += len(batch)
+                if got is not None:
+                    for (b, h), ref in zip(batch, refs):
+                        g = got[int(qs[b]):int(qs[b + 1]), h * G:(h + 1) * G]
+                        fin = np.isfinite(g)
+                        att_nonfinite += int((~fin).sum())
+                        e = np.abs(np.where(fin, g, 0.0) - ref)
+                        att_err = max(att_err, float(e.max()) if e.size else 0.0)
+                        att_over += int((e > tol).sum()) + int((~fin).sum())
+                        att_units += 1
                 for b, _ in batch:
                     if all(o[0] != b for o in order[i + workers:]):
                         seq_cache.pop(b, None)
@@ -126,12 +165,15 @@ def cpu_baseline(inp, budget_s: float = 20.0):
         dl = inp.draft_logits
         toks = inp.draft_tokens.cpu().numpy()
         uni = inp.uniforms.cpu().numpy()
+        al_gpu = gpu_al.cpu().numpy() if gpu_al is not None else None
+        tok_gpu = gpu_tok.cpu().numpy() if gpu_tok is not None else None
+        acc_seqs, al_bad, tok_bad = 0, 0, 0
         t_acc, done_acc = 0.0, 0
         seqs = [int(b) for b in rng.permutation(B)]
         with ThreadPoolExecutor(workers) as ex:
             for i in range(0, B, workers):
-                jobs = []
-                for b in seqs[i:i + workers]:
+                jobs, bs = [], seqs[i:i + workers]
+                for b in bs:
                     t0, t1 = int(qs[b]), int(qs[b + 1])
                     d0 = t0 - b
                     job = dict(target_logits=tl[t0:t1].cpu().numpy(), draft_tokens=toks[d0:d0 + t1 - t0 - 1],
@@ -141,11 +183,18 @@ def cpu_baseline(inp, budget_s: float = 20.0):
                     jobs.append(job)
                 t_start = time.perf_counter()
                 if sp.mode == "stochastic":
-                    list(ex.map(lambda j: accept_stochastic(**j), jobs))
+                    res = list(ex.map(lambda j: accept_stochastic(**j), jobs))
                 else:
-                    list(ex.map(lambda j: accept_greedy(j["target_logits"], j["draft_tokens"], j["q_start"]), jobs))
+                    res = list(ex.map(lambda j: accept_greedy(j["target_logits"], j["draft_tokens"], j["q_start"]),
+                                      jobs))
                 t_acc += time.perf_counter() - t_start
                 done_acc += len(jobs)
+                if al_gpu is not None:
+                    for b, (al_o, tok_o) in zip(bs, res):
+                        t0, t1 = int(qs[b]), int(qs[b + 1])
+                        acc_seqs += 1
+                        al_bad += int(al_o[0] != al_gpu[b])
+                        tok_bad += int(not np.array_equal(tok_o, tok_gpu[t0:t1]))
                 if t_acc > budget_s / 2:
                     break
     finally:
@@ -155,11 +204,20 @@ def cpu_baseline(inp, budget_s: float = 20.0):
     T = int(qs[-1])
     whole = done == B * Hkv and done_acc == B
     used = max(min(workers, B * Hkv), min(workers, B))   # threads the pools actually ran
-    return {"value": T / step_s, "unit": "verified tokens/s", "cores": used, "kind": "oracle",
+    base = {"value": T / step_s, "unit": "verified tokens/s", "cores": used, "kind": "oracle",
             "sample": (f"{done} of {B * Hkv} (sequence, KV head) attention units and {done_acc} of {B} sequences' "
                        f"accept/reject, fp64 oracle on {used} threads"
                        + ("" if whole else ", scaled to the whole step")),
-            "step_seconds_estimate": step_s, "sample_seconds": t_attn + t_acc}
+            "step_seconds_estimate": step_s, "sample_seconds": t_attn + t_acc,
+            "host_cpus": host_cpus, "usable_cpus": usable, "cpu_model": model}
+    parity = None
+    if got is not None:
+        parity = {"attention": {"units_compared": att_units, "units_total": B * Hkv, "max_abs_err": att_err,
+                                "elements_over_tol": att_over, "non_finite": att_nonfinite, "tol": tol},
+                  "accept": {"sequences_compared": acc_seqs, "sequences_total": B,
+                             "accept_len_mismatches": al_bad, "token_mismatches": tok_bad},
+                  "ok": att_over == 0 and al_bad == 0 and tok_bad == 0 and att_units > 0 and acc_seqs > 0}
+    return base, parity
 
 
 def attention_source_digest() -> str:
@@ -1101,18 +1159,17 @@ def main():
     K = args.steps
     a_bytes, a_flops = algorithmic_attention(inp)
     c_bytes = algorithmic_accept(inp)
-    # A step whose working set fits the 256 MB Infinity Cache would be served from it on the next
-    # step: then a 1 GiB scratch read between steps (outside the timed events) evicts it.  A read,
-    # not a write, so that no dirty lines are left to be written back inside the timed step.
-    flush = (a_bytes + c_bytes) < (1 << 30)
-    scratch = torch.ones(1 << 28, dtype=torch.float32, device=dev) if flush else None
+    # Between steps, outside the timed events, a 1 GiB scratch read evicts the 256 MB Infinity
+    # Cache, so that no step finds the previous step's logits or pages there (the K/V stream
+    # carries the non-temporal hint and need not evict them itself).  A read, not a write, so
+    # that no dirty lines are left to be written back inside the timed step.
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     sink = torch.empty(1, dtype=torch.float32, device=dev)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     for k in range(K):
-        if flush:
-            torch.amax(scratch, dim=0, keepdim=True, out=sink)
+        torch.amax(scratch, dim=0, keepdim=True, out=sink)
         ev[k][0].record()
         attention()
         ev[k][1].record()
@@ -1122,14 +1179,13 @@ def main():
     t_wall = time.perf_counter() - t_wall
     attn_ms = np.asarray([ev[k][0].elapsed_time(ev[k][1]) for k in range(K)])
     acc_ms = np.asarray([ev[k][1].elapsed_time(ev[k][2]) for k in range(K)])
-    if flush:
-        ms_per_step = float((attn_ms + acc_ms).mean())
-    else:
-        ms_per_step = ev[0][0].elapsed_time(ev[K - 1][2]) / K
-    print(f"[bench] {K} steps: {ms_per_step:.3f} ms/step (attention {attn_ms.mean():.3f} ms, "
-          f"accept {acc_ms.mean():.3f} ms)", file=sys.stderr, flush=True)
+    step_ms = attn_ms + acc_ms
+    ms_per_step = float(np.median(step_ms))
+    p1090 = lambda a: [float(np.percentile(a, 10)), float(np.percentile(a, 90))]
+    print(f"[bench] {K} steps: median {ms_per_step:.3f} ms/step (attention {np.median(attn_ms):.3f} ms, "
+          f"accept {np.median(acc_ms):.3f} ms)", file=sys.stderr, flush=True)
 
-    t_attn = float(attn_ms.mean()) * 1e-3
+    t_attn = float(np.median(attn_ms)) * 1e-3
     achieved = a_bytes / t_attn / 1e9
     mean_al = float(al.float().mean().item())
 
@@ -1160,19 +1216,27 @@ def main():
             "algorithmic_bytes_per_launch": a_bytes,
             "mfma_tflops": a_flops / t_attn / 1e12, "mfma_frac": a_flops / t_attn / 1e12 / BF16_PEAK_TFLOPS,
         },
-        "attention_ms": float(attn_ms.mean()),
-        "attention_ms_p10_p90": [float(np.percentile(attn_ms, 10)), float(np.percentile(attn_ms, 90))],
-        "accept_ms": float(acc_ms.mean()),
-        "accept_gbs": c_bytes / (float(acc_ms.mean()) * 1e-3) / 1e9,
+        "timing": "median of the timed steps (HIP events on the stream the calls run on); p10-p90 beside it",
+        "step_ms_p10_p90": p1090(step_ms),
+        "step_ms_mean": float(step_ms.mean()),
+        "attention_ms": float(np.median(attn_ms)),
+        "attention_ms_p10_p90": p1090(attn_ms),
+        "accept_ms": float(np.median(acc_ms)),
+        "accept_ms_p10_p90": p1090(acc_ms),
+        "accept_gbs": c_bytes / (float(np.median(acc_ms)) * 1e-3) / 1e9,
+        "accept_hbm_frac": c_bytes / (float(np.median(acc_ms)) * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "algorithmic_accept_bytes": c_bytes,
+        "step_us": ms_per_step * 1e3,
         "emitted_tokens_per_s": float(al.sum().item()) / (ms_per_step * 1e-3),
         "mean_accept_len": mean_al,
         "host_wall_s": t_wall,
         "clock_settle": {"seconds": args.settle_s, "steps": settle_steps},
-        "cache_flush": "1 GiB scratch read between steps, outside the timed events" if flush else None,
+        "cache_flush": "1 GiB scratch read before every timed step, outside the timed events",
     }
     if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(inp)
+        print("[bench] timing the CPU oracle on a bounded sample and comparing it with the GPU outputs",
+              file=sys.stderr, flush=True)
+        line["cpu_baseline"], line["parity"] = cpu_baseline(inp, gpu_out=out, gpu_al=al, gpu_tok=tok)
     if args.calibrate_copy > 0:
         copy_calibration(args.calibrate_copy)
     print(json.dumps(line), flush=True)

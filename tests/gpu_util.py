@@ -1,6 +1,8 @@
 """Helpers for the GPU parity tests: run the HIP path through the binding and
 compare with the oracle on the same generated inputs."""
 
+import contextlib
+import os
 import sys
 
 import numpy as np
@@ -8,7 +10,7 @@ import torch
 
 import speculative_decoding_verification_sd_amd as sdv
 from oracle import accept_greedy, accept_stochastic, verify_attention
-from tests.oracle_io import accept_args, attention_args, bits, host
+from tests.oracle_io import accept_args, attention_args
 
 ATTN_TOL = 2e-2   # absolute, bf16 attention outputs against the fp64 oracle
 
@@ -52,28 +54,28 @@ def oracle_accept(inp, mode=None, margins=None):
     return accept_stochastic(**a, margins=margins)
 
 
-def compare_attention(inp, out, units=None, workers=4, tol=ATTN_TOL):
+def oracle_workers():
+    """Threads for the oracle's independent units: the CPUs this process may
+    use, at most 16 (one GPU's share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def compare_attention(inp, out, units=None, workers=None, tol=ATTN_TOL):
     """Max |gpu - oracle| over all rows (or over the listed (b, h) units)."""
-    ref = verify_attention(**attention_args(inp), units=units, workers=workers)
+    workers = workers or oracle_workers()
+    try:
+        from threadpoolctl import threadpool_limits
+        ctx = threadpool_limits(1)     # one BLAS thread per oracle thread
+    except ImportError:
+        ctx = contextlib.nullcontext()
+    with ctx:
+        ref = verify_attention(**attention_args(inp), units=units, workers=workers)
     got = out.float().cpu().numpy().astype(np.float64)
     mask = ~np.isnan(ref)
     assert np.all(np.isfinite(got[mask])), "GPU output has non-finite values where the oracle has numbers"
     err = np.abs(got[mask] - ref[mask])
     return float(err.max()) if err.size else 0.0
-
-
-def unit_subproblem(inp, b):
-    """Inputs restricted to sequence b with only its pages (for full-size sampled parity)."""
-    qs = host(inp.q_start)
-    bt = inp.block_table[b].cpu()
-    n = int(host(inp.kv_len)[b])
-    npages = (n + inp.spec.page_size - 1) // inp.spec.page_size
-    pages = bt[:npages].long()
-    dev = inp.k_cache.device
-    k_sub = inp.k_cache[pages.to(dev)]
-    v_sub = inp.v_cache[pages.to(dev)]
-    t0, t1 = int(qs[b]), int(qs[b + 1])
-    return dict(q_bits=bits(inp.q[t0:t1]), k_bits=bits(k_sub), v_bits=bits(v_sub),
-                block_table=np.arange(npages, dtype=np.int32)[None, :],
-                kv_len=np.asarray([n], np.int32), q_start=np.asarray([0, t1 - t0], np.int32),
-                group=inp.group), (t0, t1)

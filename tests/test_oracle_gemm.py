@@ -78,6 +78,32 @@ def test_brute_force_tiny():
     assert np.all(linear_abs_sum(x, w) >= np.abs(y) - 1e-12)
 
 
+def test_abs_sum_brute_force():
+    """linear_abs_sum pinned from both sides: Python-float sums of |x w| term by
+    term on a tiny case with mixed signs (where |x W^T| is strictly smaller),
+    and closed forms (non-negative operands: equal to x W^T; a row of -1
+    against ones: K)."""
+    rng = np.random.default_rng(5)
+    x = _bf16_bits(rng.standard_normal((3, 8)))
+    w = _bf16_bits(rng.standard_normal((5, 8)))
+    xf, wf = _from_bits(x), _from_bits(w)
+    got = linear_abs_sum(x, w)
+    assert got.shape == (3, 5)
+    for m in range(3):
+        for n in range(5):
+            s = 0.0
+            for k in range(8):
+                s += abs(float(xf[m, k]) * float(wf[n, k]))
+            assert abs(got[m, n] - s) <= 1e-12 * max(1.0, s)
+    assert np.any(got > np.abs(verify_linear(x, w)) + 1e-6)     # cancellation is not counted
+    xp = _bf16_bits(np.abs(rng.standard_normal((4, 64))))
+    wp = _bf16_bits(np.abs(rng.standard_normal((6, 64))))
+    np.testing.assert_allclose(linear_abs_sum(xp, wp), verify_linear(xp, wp), rtol=1e-14)
+    ones = _bf16_bits(np.ones((2, 64)))
+    neg = _bf16_bits(-np.ones((1, 64)))
+    np.testing.assert_array_equal(linear_abs_sum(neg, ones), np.full((1, 2), 64.0))
+
+
 def test_shapes():
     x = np.zeros((7, 64), np.uint16)
     w = np.zeros((128, 64), np.uint16)

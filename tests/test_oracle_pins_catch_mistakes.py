@@ -56,6 +56,10 @@ MUTATIONS = [
     # verify-shaped linear layer
     ("oracle/gemm.py", "if a.dtype in (np.uint16, np.int16):", "if a.dtype in (np.int16,):",
      "test_oracle_gemm.py::test_identity_weight_returns_x"),
+    ("oracle/gemm.py", "return np.abs(_widen(x)) @ np.abs(_widen(w)).T", "return np.abs(_widen(x) @ _widen(w).T)",
+     "test_oracle_gemm.py::test_abs_sum_brute_force"),
+    ("oracle/gemm.py", "return np.abs(_widen(x)) @ np.abs(_widen(w)).T", "return 2.0 * np.abs(_widen(x)) @ np.abs(_widen(w)).T",
+     "test_oracle_gemm.py::test_abs_sum_brute_force"),
 ]
 
 
