@@ -337,6 +337,71 @@ def write_profiles(bench_json: str, kt_dir: str, fetch_dir: str, write_dir: str,
     print(f"wrote profiles for {wl}: {short} {float(main['AverageNs']) / 1e3:.1f} us, traffic {hbm / alg:.4f}x")
 
 
+# Counter passes of the attention's dominant kernel (one rocprofv3 --pmc run each; at most 8 SQ counters).
+COUNTER_PASSES = [
+    "GRBM_GUI_ACTIVE SQ_WAVES SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS "
+    "SQ_INSTS_VALU_TRANS_F32",
+    "GRBM_GUI_ACTIVE SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_WAIT_INST_LDS "
+    "SQ_WAVE_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES",
+    "GRBM_GUI_ACTIVE SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INST_CYCLES_SALU SQ_INSTS_SALU "
+    "SQ_ACTIVE_INST_ANY SQ_LDS_DATA_FIFO_FULL",
+]
+XCDS, CUS, SIMDS = 8, 256, 1024       # MI355X: GRBM_GUI_ACTIVE sums the XCDs' busy cycles
+
+
+def write_counter_profile(label: str, args_str: str, *pass_dirs):
+    """Per-launch counter summary of the dominant attention kernel under
+    profiles/, from the rocprofv3 --pmc runs of COUNTER_PASSES (medians over the
+    launches), with the derived clock, MFMA busy fraction, LDS activity and
+    MFMA/VALU co-execution."""
+    import statistics
+    from collections import defaultdict
+    vals, durs, kname = {}, [], None
+    for d in pass_dirs:
+        per, ts = defaultdict(dict), {}
+        for r in _rocprof_csv(d, "counter_collection"):
+            if "verify_attn" not in r["Kernel_Name"]:
+                continue
+            kname = r["Kernel_Name"]
+            per[r["Dispatch_Id"]][r["Counter_Name"]] = float(r["Counter_Value"])
+            ts[r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        for k in {k for v in per.values() for k in v}:
+            vals.setdefault(k, []).append(statistics.median(v[k] for v in per.values() if k in v))
+        durs += list(ts.values())
+    c = {k: statistics.mean(v) for k, v in vals.items()}
+    dur = statistics.median(durs) * 1e-9
+    cyc = c["GRBM_GUI_ACTIVE"] / XCDS
+    short = kname.replace("void ", "").split("(")[0].replace("sdv::", "")
+    path = os.path.join(ROOT, "profiles", f"verify_attn_counters_{label}.txt")
+    with open(path, "w") as f:
+        f.write(f"# rocprofv3 counters of {short} on workload {label}: medians per launch over the launches of\n"
+                f"# each pass ({len(pass_dirs)} passes, one rocprofv3 run each).  Launches run one at a time under\n"
+                "# counter collection, so the clock here can differ from back-to-back runs.\n")
+        for i, d in enumerate(pass_dirs):
+            f.write(f"$ cd /tmp && export TMPDIR=/tmp && timeout -s KILL 120 rocprofv3 --pmc {COUNTER_PASSES[i]} "
+                    f"--kernel-include-regex verify_attn_wide -d OUT/pmc_p{i + 1} -o run --output-format csv -- "
+                    f"python3 REPO/bench.py --no-cpu-baseline --settle-s 0 --steps 3 --warmup 1 {args_str}\n")
+        f.write(f"kernel: {short}\nkernel_us: {dur * 1e6:.1f}\n")
+        for k in sorted(c):
+            f.write(f"{k}: {c[k]:.6g}\n")
+        mfma = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (cyc * SIMDS)
+        f.write("# derived (per-XCD cycles = GRBM_GUI_ACTIVE / 8; 1024 SIMDs, 256 CUs)\n")
+        f.write(f"clock_ghz: {cyc / dur / 1e9:.3f}\n")
+        f.write(f"mfma_busy_frac_of_cycles: {mfma:.3f}\n")
+        f.write(f"mfma_busy_frac_of_2.4GHz_peak: {mfma * cyc / dur / 2.4e9:.3f}\n")
+        f.write(f"mfma_valu_coexec_frac: {c.get('SQ_VALU_MFMA_COEXEC_CYCLES', 0.0) / (cyc * SIMDS):.3f}\n")
+        f.write(f"lds_idx_active_frac: {c.get('SQ_LDS_IDX_ACTIVE', 0.0) / (cyc * CUS):.3f}\n")
+        f.write(f"lds_bank_conflict_cycles: {c.get('SQ_LDS_BANK_CONFLICT', 0.0):.0f}\n")
+        waves = c.get("SQ_WAVES", 1.0)
+        for k in ("SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_LDS", "SQ_INSTS_SALU"):
+            f.write(f"{k.lower()}_per_wave: {c.get(k, 0.0) / waves:.0f}\n")
+        if "SQ_WAVE_CYCLES" in c:
+            f.write(f"wait_any_per_wave_cycle: {c.get('SQ_WAIT_ANY', 0.0) / c['SQ_WAVE_CYCLES']:.3f}\n")
+            f.write(f"valu_active_per_wave_cycle: {c.get('SQ_ACTIVE_INST_VALU', 0.0) / c['SQ_WAVE_CYCLES']:.3f}\n")
+        f.write(f"bf16_mfma_flops (MOPS x 512): {c.get('SQ_INSTS_VALU_MFMA_MOPS_BF16', 0.0) * 512:.4g}\n")
+    print(f"wrote {path}")
+
+
 SWEEP_PRESET = "g8_kv32k_sweep"
 TREE_PRESET = "g8_kv32k_D15"
 TREE_BRANCHING = (2, 2, 2, 2)   # a full binary tree of depth 4: 30 drafted nodes, G*(1+30) = 248 rows
@@ -1041,9 +1106,14 @@ def main():
                     help="the closed adaptive speculative-decoding loop on a bigram toy LM (graphs vs direct)")
     ap.add_argument("--write-loop-profile", nargs=2, metavar=("BENCH_JSON", "KT_DIR"),
                     help="write the profiles/ summary of a --loop line and its rocprofv3 kernel trace (no GPU)")
+    ap.add_argument("--write-counter-profile", nargs="+", metavar="ARG",
+                    help="LABEL 'BENCH_ARGS' PASS_DIR...: write the profiles/ counter summary of the attention kernel")
     ap.add_argument("--write-lossy-profile", nargs=2, metavar=("BENCH_JSON", "KT_DIR"),
                     help="write the profiles/ summary of a --lossy line and its rocprofv3 kernel trace (no GPU)")
     args = ap.parse_args()
+    if args.write_counter_profile:
+        write_counter_profile(*args.write_counter_profile)
+        return
     if args.write_tree_profile:
         write_tree_profile(*args.write_tree_profile)
         return
