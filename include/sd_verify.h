@@ -163,6 +163,25 @@ sd_status sd_accept_reject(const sd_accept_desc* desc, int32_t total_q,
                            const float* uniforms, int32_t* accept_len, int32_t* out_tokens,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Accept / reject with no workspace argument, for callers that cannot
+ * allocate device memory themselves (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  Same arguments, results
+ * and errors as sd_accept_reject without the workspace: the call uses scratch
+ * the library holds in a static device array of SD_NOALLOC_SCRATCH_BYTES per
+ * GPU (kept until the process ends) and allocates nothing.  A problem whose
+ * sd_accept_reject_workspace_size exceeds that returns SD_ERR_UNSUPPORTED and
+ * enqueues nothing.  Every call on one GPU shares that GPU's array: calls
+ * whose kernels may overlap on one GPU (different streams, or different host
+ * threads without ordering) race on it, so the caller orders them.
+ */
+#define SD_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+sd_status sd_accept_reject_noalloc(const sd_accept_desc* desc, int32_t total_q,
+                                   const float* target_logits, const float* draft_logits,
+                                   const int32_t* draft_tokens, const int32_t* q_start,
+                                   const float* uniforms, int32_t* accept_len, int32_t* out_tokens,
+                                   void* stream);
+
 /* Workspace bytes sd_accept_lossy needs.  Returns 0 for an invalid description. */
 size_t sd_accept_lossy_workspace_size(const sd_accept_desc* desc, int32_t total_q);
 

@@ -21,6 +21,7 @@ from .binding import (  # noqa: F401
     sd_accept_lossy,
     sd_accept_lossy_workspace_size,
     sd_accept_reject,
+    sd_accept_reject_noalloc,
     sd_accept_reject_workspace_size,
     sd_closed_loop,
     sd_closed_loop_workspace_size,
@@ -45,5 +46,5 @@ __all__ = [
     "sd_verify_step_workspace_size", "sd_version", "linear_desc", "sd_verify_linear",
     "sd_verify_linear_workspace_size", "sd_verify_tree_attention", "sd_tree_accept", "sd_tree_accept_workspace_size",
     "sd_accept_lossy", "sd_accept_lossy_workspace_size", "loop_desc", "sd_closed_loop", "sd_closed_loop_workspace_size",
-    "sd_validate_inputs", "SD_BAD",
+    "sd_validate_inputs", "SD_BAD", "sd_accept_reject_noalloc",
 ]

@@ -90,6 +90,8 @@ SIGNATURES = {
     "sd_accept_reject_workspace_size": (_SZ, [ctypes.POINTER(sd_accept_desc), _I]),
     "sd_accept_reject": (ctypes.c_int, [ctypes.POINTER(sd_accept_desc), _I, _P, _P, _P, _P, _P, _P, _P, _P,
                                         _SZ, _P]),
+    "sd_accept_reject_noalloc": (ctypes.c_int, [ctypes.POINTER(sd_accept_desc), _I, _P, _P, _P, _P, _P, _P, _P,
+                                                _P]),
     "sd_accept_lossy_workspace_size": (_SZ, [ctypes.POINTER(sd_accept_desc), _I]),
     "sd_accept_lossy": (ctypes.c_int, [ctypes.POINTER(sd_accept_desc), _I, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P,
                                        _P, _P, _P, _SZ, _P]),
@@ -467,3 +469,17 @@ def sd_validate_inputs(q_start, *, max_draft: int, q=None, k_cache=None, block_t
                                     _ptr(uniforms), _ptr(target_logits), _ptr(draft_logits), _ptr(status_word),
                                     _stream(dev, stream)))
     return status_word
+
+
+def sd_accept_reject_noalloc(target_logits, draft_logits, draft_tokens, q_start, uniforms, accept_len, out_tokens,
+                             *, mode: str, max_draft: int, stream=None) -> None:
+    """sd_accept_reject on the library's own scratch: no workspace, nothing allocated."""
+    _check_accept_args(target_logits, draft_logits, draft_tokens, q_start, uniforms, accept_len, out_tokens, mode)
+    B = q_start.shape[0] - 1
+    T, V = target_logits.shape
+    desc = accept_desc(B, V, max_draft, mode)
+    stoch = mode == "stochastic"
+    _check(lib().sd_accept_reject_noalloc(ctypes.byref(desc), T, _ptr(target_logits),
+                                          _ptr(draft_logits if stoch else None), _ptr(draft_tokens), _ptr(q_start),
+                                          _ptr(uniforms if stoch else None), _ptr(accept_len), _ptr(out_tokens),
+                                          _stream(target_logits.device, stream)))

@@ -240,6 +240,26 @@ SD_EXPORT sd_status sd_accept_reject(const sd_accept_desc* desc, int32_t total_q
                     out_tokens, workspace, workspace_bytes, stream);
 }
 
+SD_EXPORT sd_status sd_accept_reject_noalloc(const sd_accept_desc* desc, int32_t total_q,
+                                            const float* target_logits, const float* draft_logits,
+                                            const int32_t* draft_tokens, const int32_t* q_start,
+                                            const float* uniforms, int32_t* accept_len, int32_t* out_tokens,
+                                            void* stream) {
+  sd_status s = check_accept(desc, total_q);
+  if (s != SD_OK) return s;
+  const size_t need = acc_ws(desc, total_q);
+  const size_t have = sdv_noalloc_scratch_bytes();
+  if (need > have)
+    return fail(SD_ERR_UNSUPPORTED, "accept/reject needs %zu bytes of scratch, above the %zu the no-allocation "
+                "call holds: use sd_accept_reject with a workspace", need, have);
+  if (desc->num_seqs == 0) return SD_OK;
+  void* ws = nullptr;
+  hipError_t e = sdv_noalloc_scratch(&ws);
+  if (e != hipSuccess) return fail(SD_ERR_HIP, "no-allocation scratch lookup: %s", hipGetErrorString(e));
+  return run_accept(desc, total_q, target_logits, draft_logits, draft_tokens, q_start, uniforms, accept_len,
+                    out_tokens, ws, have, stream);
+}
+
 SD_EXPORT size_t sd_accept_lossy_workspace_size(const sd_accept_desc* desc, int32_t total_q) {
   if (check_accept(desc, total_q, true) != SD_OK) return 0;
   return acc_ws(desc, total_q, true);

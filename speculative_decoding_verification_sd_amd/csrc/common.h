@@ -129,6 +129,9 @@ size_t sdv_attn_workspace_bytes(int B, int Hkv, int G, int head_dim, int max_pag
                                 int kv_chunk);
 hipError_t sdv_attn_launch(const SdAttnLaunch& a);
 size_t sdv_accept_workspace_bytes(int B, int T, int V, int stochastic, int lossy);
+// Library-held scratch of the no-allocation accept call (noalloc.hip).
+size_t sdv_noalloc_scratch_bytes();
+hipError_t sdv_noalloc_scratch(void** out);
 hipError_t sdv_accept_launch(const SdAccLaunch& a);
 hipError_t sdv_tree_accept_launch(const SdAccLaunch& a, const int32_t* parents, int32_t* out_nodes);
 
