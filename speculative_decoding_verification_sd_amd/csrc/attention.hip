@@ -52,6 +52,11 @@ constexpr int kItemsPerSlot = 4;         // work items per resident workgroup th
 constexpr int kItemOverheadBytes = 192 * 1024;   // an item's fixed cost (set-up, partials) in bytes of K/V
 constexpr int kPlanHeader = 16;
 
+// LDS operands the row-split step reads ahead of their MFMAs.  Build-time tunable.
+#ifndef SDV_RS_AHEAD
+#define SDV_RS_AHEAD 2
+#endif
+
 // LDS bytes of the K/V rings of one CU (at most 8 tiles per workgroup),
 // shared by its resident workgroups.  Build-time tunable.
 #ifndef SDV_RING_BYTES_PER_CU
@@ -576,6 +581,15 @@ __device__ __forceinline__ void wait_tiles(int tiles) {
 
 template <int V>
 using ic = std::integral_constant<int, V>;
+
+// f(ic<I>{}) for I = B .. E-1, in order (compile-time indices).
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(ic<B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 // ---------------------------------------------------------------------------
 // NRB row blocks of 16 per wave, NW waves, WPC resident workgroups per CU.
@@ -1298,20 +1312,7 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
           l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[ks][2 * q], pf[ks][2 * q + 1]}, one2, l_run, false);
       asm volatile("" ::"v"(l_run));   // keep the sums here: sunk past later tiles they hold P live
     };
-    // The two halves of accumulate(), for the row-split step's pipeline.
-    auto make_p = [&](bf16x8* pf, auto prec) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pf[ks][e] = p_of(sc[ks * 8 + e], prec);
-      const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[ks][2 * q], pf[ks][2 * q + 1]}, one2, l_run, false);
-      asm volatile("" ::"v"(l_run));   // keep the sums here: sunk past later tiles they hold P live
-    };
+    // P V of one tile at stage offset `off` (the second half of accumulate()).
     auto pv = [&](int off, const bf16x8* pf) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
@@ -1321,21 +1322,62 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
           o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[mb], 0, 0, 0);
         }
     };
-    // Row-split steady step over the tiles at `off0` and `off1`: P of the first
-    // tile is formed (VALU) while the scores of the second accumulate (MFMA,
-    // one chain), then P V of the first, then the second tile.
+    // Row-split steady step over the tiles A (at `off0`) and B (at `off1`) as
+    // one fixed sequence of 2 NKS + 4 NMB slots, one MFMA each: S_A; S_B with
+    // P_A; P V of A with P_B; P V of B.  In a slot of the second and third
+    // phases the wave also issues one share of the other tile's exp / convert /
+    // row-sum work, which the SIMD runs while the MFMA occupies the matrix core,
+    // and each MFMA's LDS operand is read kAhead slots before it.  Scheduling
+    // fences between slots keep that order (left to itself the compiler runs
+    // the MFMAs back to back and the vector work after them).
     auto rs_pair = [&](int off0, int off1) {
-      scores(off0, std::true_type{});
-      bf16x8 pf[2];
-      make_p(pf, std::true_type{});
-      f32x16 s1 = mneg;
+      constexpr int kSlots = 2 * NKS + 4 * NMB;
+      constexpr int kAhead = SDV_RS_AHEAD;
+      auto operand = [&](auto jc) -> bf16x8 {            // the LDS operand of slot j
+        constexpr int j = decltype(jc)::value;
+        if constexpr (j < NKS) return *(const bf16x8*)(smem + off0 + koff[j]);
+        else if constexpr (j < 2 * NKS) return *(const bf16x8*)(smem + off1 + koff[j - NKS]);
+        else if constexpr (j < 2 * NKS + 2 * NMB)
+          return *(const bf16x8*)(smem + off0 + ((j - 2 * NKS) / NMB) * HD * 32 + voffs[(j - 2 * NKS) % NMB]);
+        else
+          return *(const bf16x8*)(smem + off1 + ((j - 2 * NKS - 2 * NMB) / NMB) * HD * 32 +
+                                  voffs[(j - 2 * NKS - 2 * NMB) % NMB]);
+      };
+      // share q of nq of a tile's P work: its 16/nq scores -> exp2 -> bf16 -> row sum
+      auto p_share = [&](const f32x16& sv, bf16x8 (&pf)[2], auto qc, auto nqc) {
+        constexpr int q = decltype(qc)::value, nq = decltype(nqc)::value;
+        constexpr int w = 16 / nq;
+        const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-      for (int c = 0; c < NKS; ++c)
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(smem + off1 + koff[c]), qf[c], s1, 0, 0, 0);
-      pv(off0, pf);
-      sc = s1;
-      make_p(pf, std::true_type{});
-      pv(off1, pf);
+        for (int e = q * w; e < (q + 1) * w; e += 2) {
+          pf[e / 8][e % 8] = (__bf16)fast_exp2(sv[e]);
+          pf[e / 8][e % 8 + 1] = (__bf16)fast_exp2(sv[e + 1]);
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[e / 8][e % 8], pf[e / 8][e % 8 + 1]}, one2, l_run, false);
+        }
+        asm volatile("" ::"v"(l_run));   // the sums stay in their slot (sunk, they would hold P live)
+      };
+      f32x16 sa = mneg, sb = mneg;
+      bf16x8 pa[2], pb[2];
+      bf16x8 f[kSlots];
+      static_for<0, kAhead>([&](auto jc) { f[decltype(jc)::value] = operand(jc); });
+      static_for<0, kSlots>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        if constexpr (j + kAhead < kSlots) f[j + kAhead] = operand(ic<j + kAhead>{});
+        if constexpr (j < NKS) {
+          sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[j], qf[j], sa, 0, 0, 0);
+        } else if constexpr (j < 2 * NKS) {
+          sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[j], qf[j - NKS], sb, 0, 0, 0);
+          p_share(sa, pa, ic<j - NKS>{}, ic<NKS>{});
+        } else if constexpr (j < 2 * NKS + 2 * NMB) {
+          constexpr int t = j - 2 * NKS;
+          o[t % NMB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[j], pa[t / NMB], o[t % NMB], 0, 0, 0);
+          p_share(sb, pb, ic<t>{}, ic<2 * NMB>{});
+        } else {
+          constexpr int t = j - 2 * NKS - 2 * NMB;
+          o[t % NMB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[j], pb[t / NMB], o[t % NMB], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
     };
     auto row_sum = [&]() {
       auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
