@@ -1053,6 +1053,100 @@ def write_linear_profile(sweep_json: str):
     print(f"wrote {path}")
 
 
+def run_probes(args):
+    """On-box microbenchmarks (libsdprobe.so): the bf16 MFMA throughput of
+    independent 32x32x16 and 16x16x32 chains at one and two waves per SIMD
+    (HIP events for the rate, s_memtime for cycles per MFMA and the clock), and
+    the SIMD each wave of an 8-wave, one-per-CU workgroup runs on.  One JSON line."""
+    import ctypes
+    import numpy as np
+    import torch
+
+    from speculative_decoding_verification_sd_amd.build import HERE, PROBE_LIB
+    path = os.path.join(HERE, PROBE_LIB)
+    if not os.path.exists(path):
+        raise SystemExit(f"{path} is missing: build it with python -m speculative_decoding_verification_sd_amd.build")
+    lib = ctypes.CDLL(path)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    res = {"cus": cus}
+    # wave placement
+    lay = torch.full((cus * 8,), -1, dtype=torch.int32, device=dev)
+    assert lib.sdp_wave_layout(ctypes.c_void_p(lay.data_ptr()), cus, stream) == 0
+    torch.cuda.synchronize()
+    v = lay.cpu().numpy().reshape(cus, 8)
+    simd = v & 15
+    res["wave_simd_histogram"] = {f"wave{w}": {int(k): int(c) for k, c in zip(*np.unique(simd[:, w], return_counts=True))}
+                                  for w in range(8)}
+    res["waves_sharing_a_simd"] = sorted({tuple(int(w) for w in np.nonzero(simd[b] == s)[0])
+                                          for b in range(cus) for s in range(4)})
+    # MFMA peak
+    iters = 20000
+    for shape, chains, flops in ((32, 4, 32 * 32 * 16 * 2), (16, 8, 16 * 16 * 32 * 2)):
+        for wps in (1, 2):
+            grid = cus * wps
+            out = torch.empty(grid * 256, dtype=torch.float32, device=dev)
+            cyc = torch.empty(grid, dtype=torch.int64, device=dev)
+            args_ = (shape, grid, iters, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(cyc.data_ptr()), stream)
+            for _ in range(3):
+                lib.sdp_mfma_peak(*args_)
+            torch.cuda.synchronize()
+            times = []
+            for _ in range(max(3, args.steps)):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                assert lib.sdp_mfma_peak(*args_) == 0
+                e1.record()
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1) * 1e-3)
+            t = float(np.median(times))
+            total = grid * 4 * iters * chains * flops
+            cycles = float(np.median(cyc.cpu().numpy()))
+            res[f"mfma_{shape}x{shape}_{wps}wave_per_simd"] = {
+                "tflops": total / t / 1e12, "frac_of_2500": total / t / 1e12 / BF16_PEAK_TFLOPS,
+                "s_memtime_ticks_per_mfma_per_wave": cycles / (iters * chains),
+                "us": t * 1e6}
+    # MFMA / VALU co-execution: time of each variant at one and two waves per SIMD
+    names = ["mfma", "mfma+2exp", "2exp", "mfma+8fma", "8fma"]
+    co_iters = 20000
+    for wps in (1, 2):
+        grid = cus * wps
+        out = torch.empty(grid * 256, dtype=torch.float32, device=dev)
+        row = {}
+        for var, nm in enumerate(names):
+            for _ in range(2):
+                lib.sdp_coexec(var, grid, co_iters, ctypes.c_void_p(out.data_ptr()), stream)
+            torch.cuda.synchronize()
+            times = []
+            for _ in range(5):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                assert lib.sdp_coexec(var, grid, co_iters, ctypes.c_void_p(out.data_ptr()), stream) == 0
+                e1.record()
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1) * 1e3)
+            row[nm] = float(np.median(times))
+        res[f"coexec_us_{wps}wave_per_simd"] = row
+    print(json.dumps({"metric": "on-box MFMA peak and wave placement", "probes": res}), flush=True)
+
+
+def write_probe_profile(probe_json: str):
+    with open(probe_json) as f:
+        line = json.loads(f.read().strip().splitlines()[-1])
+    path = os.path.join(ROOT, "profiles", "probe_mfma_peak_wave_layout.txt")
+    with open(path, "w") as f:
+        f.write("# On-box microbenchmarks (one MI355X): bf16 MFMA rate of independent chains from registers\n"
+                "# (4 chains of 32x32x16 or 8 of 16x16x32 per wave, 20000 rounds; HIP events for the rate,\n"
+                "# s_memtime cycles per wave), and the SIMD (HW_ID) each wave of an 8-wave workgroup that\n"
+                "# holds a CU alone runs on.\n"
+                "$ python3 REPO/bench.py --probe\n")
+        for k, v in line["probes"].items():
+            f.write(f"{k}: {json.dumps(v)}\n")
+    print(f"wrote {path}")
+
+
 def copy_calibration(nbytes: int, reps: int = 3):
     """A plain device-to-device copy of `nbytes` (torch's elementwise copy), for
     scaling the FETCH_SIZE / WRITE_SIZE counters to bytes."""
@@ -1106,11 +1200,17 @@ def main():
                     help="the closed adaptive speculative-decoding loop on a bigram toy LM (graphs vs direct)")
     ap.add_argument("--write-loop-profile", nargs=2, metavar=("BENCH_JSON", "KT_DIR"),
                     help="write the profiles/ summary of a --loop line and its rocprofv3 kernel trace (no GPU)")
+    ap.add_argument("--probe", action="store_true",
+                    help="on-box MFMA peak and wave-to-SIMD placement microbenchmarks (libsdprobe.so)")
+    ap.add_argument("--write-probe-profile", metavar="PROBE_JSON", help="write the profiles/ summary of a --probe line")
     ap.add_argument("--write-counter-profile", nargs="+", metavar="ARG",
                     help="LABEL 'BENCH_ARGS' PASS_DIR...: write the profiles/ counter summary of the attention kernel")
     ap.add_argument("--write-lossy-profile", nargs=2, metavar=("BENCH_JSON", "KT_DIR"),
                     help="write the profiles/ summary of a --lossy line and its rocprofv3 kernel trace (no GPU)")
     args = ap.parse_args()
+    if args.write_probe_profile:
+        write_probe_profile(args.write_probe_profile)
+        return
     if args.write_counter_profile:
         write_counter_profile(*args.write_counter_profile)
         return
@@ -1159,6 +1259,9 @@ def main():
         return
     if args.read_ceiling:
         run_read_ceiling(args)
+        return
+    if args.probe:
+        run_probes(args)
         return
     if args.sweep is not None:
         args.sweep = args.sweep or list(range(32))

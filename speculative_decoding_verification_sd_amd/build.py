@@ -42,6 +42,27 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
+PROBES = os.path.join(HERE, "probes")
+PROBE_LIB = "libsdprobe.so"
+
+
+def build_probes(verbose: bool = False) -> str:
+    """libsdprobe.so: bench.py's measurement kernels (MFMA throughput, wave
+    placement), kept out of the verify-step library."""
+    cc = hipcc()
+    out = os.path.join(HERE, PROBE_LIB)
+    srcs = sorted(os.path.join(PROBES, f) for f in os.listdir(PROBES) if f.endswith(".hip"))
+    cmd = [cc, *COMMON_FLAGS, *DEVICE_FLAGS, "-shared", "-o", out + ".tmp", *srcs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on the probes:\n{msgs}")
+    if verbose and msgs.strip():
+        print(msgs)
+    os.replace(out + ".tmp", out)
+    return out
+
+
 def build(verbose: bool = False, extra_flags=(), out: str = None) -> str:
     cc = hipcc()
     out = out or os.path.join(HERE, LIB_NAME)
@@ -73,3 +94,4 @@ def build(verbose: bool = False, extra_flags=(), out: str = None) -> str:
 if __name__ == "__main__":
     path = build(verbose="-v" in sys.argv)
     print(path)
+    print(build_probes(verbose="-v" in sys.argv))

@@ -552,12 +552,14 @@ __device__ __forceinline__ void zero_keys_past(unsigned char* sp, const DmaSlot 
     if (dma[i].kv == 0) {
       if (dma[i].key0 >= lim) *(u32x4*)(sp + dma[i].dst + lane * 16) = u32x4{0, 0, 0, 0};
     } else if (dma[i].key0 + 7 >= lim) {
+      // (compared as q >= lim - key0, so that no key0 + q stays live across the item loop)
+      const int nvalid = lim - dma[i].key0;
       unsigned short* e = (unsigned short*)(sp + S * RG::kHalf + dma[i].dst + lane * 16);
       u32x4 x = *(u32x4*)e;
       unsigned short* xs = (unsigned short*)&x;
 #pragma unroll
       for (int q = 0; q < 8; ++q)
-        if (dma[i].key0 + q >= lim) xs[q] = 0;
+        if (q >= nvalid) xs[q] = 0;
       *(u32x4*)e = x;
     }
   }
@@ -1053,12 +1055,14 @@ __global__ __launch_bounds__(64 * NW, WPC) void verify_attn_main(AttnParams p) {
 // ---------------------------------------------------------------------------
 // Verify attention with 32x32x16 MFMAs for blocks of more than 64 query rows:
 // a workgroup of 8 waves, two per SIMD, in two sets of four (32 rows per
-// wave), both fed from one LDS-DMA ring.  Up to 128 rows (RS false), set 0
+// wave), both fed from one LDS-DMA ring.  Up to 128 rows (MODE 0), set 0
 // takes the even tiles of the item and set 1 the odd ones over the same 128
 // rows, and the two partial results are merged through LDS at the end of the
-// item.  Up to 256 rows (RS true), set s takes rows 128s .. 128s+127 over every
-// tile, so the item's pages are streamed once for all its rows.  Two waves per
-// SIMD hide each other's LDS, barrier and MFMA-dependency latencies.  Operands:
+// item.  Up to 256 rows (MODE 1), set s takes rows 128s .. 128s+127 over every
+// tile, so the item's pages are streamed once for all its rows.  From 129 to
+// 192 rows (MODE 2) set 0 takes rows 0..127 over every tile and set 1 splits
+// the tiles of the remaining one or two row blocks.  Two waves per SIMD hide
+// each other's LDS, barrier and MFMA-dependency latencies.  Operands:
 //   * S^T = K Q^T per 32-key tile: A = K (lane: key row l%32, dims
 //     c*16 + (l/32)*8..+7), B = Q^T (lane: query row l%32, same dims), so each
 //     lane holds one query row and keys (e/4)*8 + (l/32)*4 + e%4, e < 16.
@@ -1079,7 +1083,14 @@ __device__ __forceinline__ int wide_swz(int k) {
   else return (((k >> 1) & 1) << 2) | ((k >> 2) & 3);
 }
 
-template <int HD, int OUT_F32, bool RS, bool TREE>
+// MODE 0 (up to 128 rows): the two wave sets split the tiles of every step
+// over the same four 32-row blocks.  MODE 1 (up to 256 rows): each wave takes
+// one of eight row blocks over both tiles of every step.  MODE 2 (129 to 192
+// rows): waves 0-3 take row blocks 0-3 over both tiles, and waves 4-7 share
+// blocks 4 and 5 two to a block, one tile of every step each, so that no SIMD
+// (it hosts waves s and s+4) carries more than three of the step's 32-row
+// tile products where the row split would give one SIMD four.
+template <int HD, int OUT_F32, int MODE, bool TREE>
 __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
   constexpr int NW = 8;
   using RG = Ring<HD, NW, 1>;
@@ -1104,12 +1115,20 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int set = wave >> 2, w4 = wave & 3;
   const int r32 = lane & 31, hh = lane >> 5;
+  // This wave's role: PAIR waves take both tiles of a step, the others the
+  // tile of parity `par`; its 32-row block; whether it hands its partial to
+  // a partner (same block, other parity) through LDS, and where.
+  const bool pair = MODE == 1 || (MODE == 2 && set == 0);
+  const int par = MODE == 0 ? set : (MODE == 2 && set == 1) ? (w4 & 1) : 0;
+  const int rblock = MODE == 0 ? w4 : MODE == 1 ? wave : set == 0 ? w4 : 4 + (w4 >> 1);
+  const bool giver = !pair && par == 1;          // hands (O, l, m) to the block's parity-0 wave
+  const int xslot = MODE == 0 ? w4 : (w4 >> 1);  // LDS hand-off slot of the block
   const int total = min(p.plan[1], p.item_cap);
   const int Hq = p.Hkv * p.G;
 
-  // Lane-constant LDS offsets, including (RS false) the set's stage parity: in
-  // step k the set reads tile 2k + set, whose stage is (2k + set) % S.  With RS
-  // both sets read both tiles of the step.
+  // Lane-constant LDS offsets, including (single-tile waves) the stage parity:
+  // in step k such a wave reads tile 2k + par, whose stage is (2k + par) % S.
+  // PAIR waves read both tiles of the step.
   // S^T takes key pi(r) = (r/16)*16 + ((r/4)%2)*8 + ((r/8)%2)*4 + r%4 as its MFMA
   // row r, so that score entry e of a lane holds key (e/8)*16 + 8hh + e%8 and
   // each 16-key step of P V reads eight consecutive keys per lane.
@@ -1117,18 +1136,17 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
   int koff[NKS];                 // K operand: key row kkey, logical chunk 2c + hh
 #pragma unroll
   for (int c = 0; c < NKS; ++c)
-    koff[c] = (RS ? 0 : set * RG::kHalf) + kkey * RG::kRowB + (((c * 2 + hh) ^ wide_swz<HD>(kkey)) * 16);
+    koff[c] = par * RG::kHalf + kkey * RG::kRowB + (((c * 2 + hh) ^ wide_swz<HD>(kkey)) * 16);
   int voffs[NMB];                // V^T operand: d-row mb*32 + r32, keys ks*16 + 8hh..+7 (page ks)
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) {
     const int dd = mb * 32 + r32;
-    voffs[mb] = (RS ? 0 : set * RG::kHalf) + S * RG::kHalf + dd * 32 + ((hh ^ ((dd >> 3) & 1)) * 16);
+    voffs[mb] = par * RG::kHalf + S * RG::kHalf + dd * 32 + ((hh ^ ((dd >> 3) & 1)) * 16);
   }
   DmaSlot dma[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) dma[i] = dma_slot<HD, RG>(wave + NW * i, lane, [](int k) { return wide_swz<HD>(k & 15); });
 
-  const int row0 = RS ? set * 128 : 0;   // first row of the set
   // Items after the first round.  When the plan's list (longest first) holds
   // items shorter than the chunk and more items than workgroups, the next item
   // of this workgroup's class (index = blockIdx % 8 modulo 8) as workgroups
@@ -1159,7 +1177,7 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
     if (pslot < 0 || pslot >= p.item_cap) continue;
     const int R = p.G * (1 + D);
     const int* bt = p.block_table + (size_t)b * p.max_pages;
-    const bool wave_active = row0 + w4 * 32 < R;
+    const bool wave_active = rblock * 32 < R;
     const int ntiles = k_end > k_begin ? (k_end - k_begin + RG::kTile - 1) / RG::kTile : 0;
     const int nsteps = (ntiles + 1) / 2;
     const bool ragged_tail = k_begin + ntiles * RG::kTile > k_end;
@@ -1187,7 +1205,7 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
     };
 
     // Query fragments (B operand of S^T): lane holds row r32, dims c*16 + hh*8..+7.
-    const int row = row0 + w4 * 32 + r32;
+    const int row = rblock * 32 + r32;
     const int i0 = row / p.G;
     const bool valid = row < R && t0 >= 0 && t0 + i0 < p.total_q;
     const int qi = valid ? i0 : 0;
@@ -1312,16 +1330,6 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
           l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[ks][2 * q], pf[ks][2 * q + 1]}, one2, l_run, false);
       asm volatile("" ::"v"(l_run));   // keep the sums here: sunk past later tiles they hold P live
     };
-    // P V of one tile at stage offset `off` (the second half of accumulate()).
-    auto pv = [&](int off, const bf16x8* pf) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) {
-          const bf16x8 vf = *(const bf16x8*)(smem + off + ks * HD * 32 + voffs[mb]);
-          o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[mb], 0, 0, 0);
-        }
-    };
     // Row-split steady step over the tiles A (at `off0`) and B (at `off1`) as
     // one fixed sequence of 2 NKS + 4 NMB slots, one MFMA each: S_A; S_B with
     // P_A; P V of A with P_B; P V of B.  In a slot of the second and third
@@ -1379,6 +1387,47 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
         __builtin_amdgcn_sched_barrier(0);
       });
     };
+    // One tile of the step as the same fenced slot sequence (S, then P, then
+    // P V): in MODE 2 a single-tile wave shares its SIMD with a PAIR wave, and
+    // the fences keep its registers within the row-split step's budget.
+    auto single_tile = [&](int off) {
+      constexpr int kSlots = NKS + 2 * NMB;
+      constexpr int kAhead = SDV_RS_AHEAD;
+      auto operand = [&](auto jc) -> bf16x8 {
+        constexpr int j = decltype(jc)::value;
+        if constexpr (j < NKS) return *(const bf16x8*)(smem + off + koff[j]);
+        else return *(const bf16x8*)(smem + off + ((j - NKS) / NMB) * HD * 32 + voffs[(j - NKS) % NMB]);
+      };
+      f32x16 sv = mneg;
+      bf16x8 pv2[2];
+      bf16x8 f[kSlots];
+      static_for<0, kAhead>([&](auto jc) { f[decltype(jc)::value] = operand(jc); });
+      static_for<0, kSlots>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        if constexpr (j + kAhead < kSlots) f[j + kAhead] = operand(ic<j + kAhead>{});
+        if constexpr (j < NKS) {
+          sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[j], qf[j], sv, 0, 0, 0);
+          if constexpr (j == NKS - 1) {
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+              for (int e = 0; e < 8; ++e) pv2[ks][e] = (__bf16)fast_exp2(sv[ks * 8 + e]);
+            const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pv2[ks][2 * q], pv2[ks][2 * q + 1]}, one2, l_run,
+                                                        false);
+            asm volatile("" ::"v"(l_run));
+          }
+        } else {
+          constexpr int t = j - NKS;
+          o[t % NMB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[j], pv2[t / NMB], o[t % NMB], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    };
     auto row_sum = [&]() {
       auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
       return __uint_as_float(a[0]) + __uint_as_float(a[1]);
@@ -1394,7 +1443,7 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
       }
     };
 
-    // Step k: tiles 2k (set 0; RS: both sets) and 2k+1 (set 1; RS: both sets).
+    // Step k: tiles 2k and 2k+1 (PAIR waves: both; the others: tile 2k + par).
     // Wait for both, barrier, refill the stages of tiles 2k-2 and 2k-1 with
     // tiles 2k+S-2 and 2k+S-1.
     auto advance = [&](int k, int st0) {
@@ -1416,7 +1465,7 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
         if (k_begin + (tt + 1) * RG::kTile > N - D) mask_scores(tt);
         if constexpr (SAFE) {
           if (__any(row_max(kLazy))) rescale();
-        } else if (k == 0 && (!RS || tt == 0)) {
+        } else if (k == 0 && (!pair || tt == 0)) {
           row_max(0.f);
           m_run = mt;
           m_off = mt == -INFINITY ? 0.f : -mt;
@@ -1426,11 +1475,17 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
     };
     auto step_generic = [&](int k, auto safec) {
       advance(k, (2 * k + S - 2) % S);
-      if constexpr (RS) {
+      if constexpr (MODE == 1) {
         tile_generic(k, 2 * k, (2 * k % S) * RG::kHalf, safec);
         tile_generic(k, 2 * k + 1, ((2 * k + 1) % S) * RG::kHalf, safec);
+      } else if constexpr (MODE == 0) {
+        tile_generic(k, 2 * k + par, (2 * k % S) * RG::kHalf, safec);   // the parity is in koff / voffs
       } else {
-        tile_generic(k, 2 * k + set, (2 * k % S) * RG::kHalf, safec);   // the set's parity is in koff / voffs
+        // one copy of the tile code for both roles (two inlined paths cost registers);
+        // a single-tile wave's parity offset is already in koff / voffs
+#pragma unroll 1
+        for (int q = 0; q < 2; ++q)
+          if (pair || q == par) tile_generic(k, 2 * k + q, (((2 * k + q) % S) - par) * RG::kHalf, safec);
       }
     };
 
@@ -1444,21 +1499,25 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
     if (nsteps > 0) step_generic(0, std::false_type{});
 #pragma unroll
     for (int e = 0; e < 16; ++e) mneg[e] = m_off;
-    auto fast_steady = [&](auto activec) {
-      constexpr bool ACTIVE = decltype(activec)::value;
+    // (ROLE: 0 idle, 1 one tile per step, 2 both tiles)
+    auto fast_steady = [&](auto rolec) {
+      constexpr int ROLE = decltype(rolec)::value;
       for (int g = 0; g < ngroups; ++g) {
         const int kb = 1 + g * (S / 2);
         auto step = [&](auto uc) {
           constexpr int u = decltype(uc)::value;
           constexpr int st = (2 * (1 + u)) % S;         // stage of tile 2k (k = kb + u; kb - 1 is a multiple of S/2)
           advance(kb + u, (st + S - 2) % S);
-          if constexpr (ACTIVE) {
-            if constexpr (RS) {
-              rs_pair(st * RG::kHalf, (st + 1) * RG::kHalf);
+          if constexpr (ROLE == 2) {
+            if constexpr (MODE == 2) {   // (one loop for both roles of MODE 2: the wave's role is uniform)
+              if (pair) rs_pair(st * RG::kHalf, (st + 1) * RG::kHalf);
+              else single_tile(st * RG::kHalf);
             } else {
-              scores(st * RG::kHalf, std::true_type{});
-              accumulate(st * RG::kHalf, std::true_type{});
+              rs_pair(st * RG::kHalf, (st + 1) * RG::kHalf);
             }
+          } else if constexpr (ROLE == 1) {
+            scores(st * RG::kHalf, std::true_type{});
+            accumulate(st * RG::kHalf, std::true_type{});
           }
         };
         step(ic<0>{});
@@ -1467,8 +1526,15 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
         if constexpr (S > 6) step(ic<3>{});
       }
     };
-    if (wave_active) fast_steady(std::true_type{});
-    else fast_steady(std::false_type{});
+    if (!wave_active) {
+      fast_steady(ic<0>{});
+    } else if constexpr (MODE == 0) {
+      fast_steady(ic<1>{});
+    } else if constexpr (MODE == 1) {
+      fast_steady(ic<2>{});
+    } else {
+      fast_steady(ic<2>{});
+    }
     for (int k = 1 + ngroups * (S / 2); k < nsteps; ++k) step_generic(k, std::false_type{});
     const bool over = wave_active && !(row_sum() <= kOverflow);
 
@@ -1483,13 +1549,14 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
     }
     block_sync();   // every wave is done with the ring (all loads landed: the last step waited for vmcnt 0)
 
-    // ---- Merge the two sets' partials (RS false: set 1 hands (O, l, m) to set 0
-    // through LDS; RS true: each set owns its rows).
+    // ---- Merge the partials of the two waves of a split block: the parity-1
+    // wave hands (O, l, m) to the parity-0 wave through LDS (MODE 1: every
+    // wave owns its rows).
     float lt = row_sum();
     float M = partial_max(m_run, lt);
-    if constexpr (!RS) {
-      float* xch = (float*)smem + (size_t)w4 * kMergeF * 64 + lane;
-      if (set == 1 && wave_active) {
+    if constexpr (MODE != 1) {
+      float* xch = (float*)smem + (size_t)xslot * kMergeF * 64 + lane;
+      if (giver && wave_active) {
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
@@ -1498,7 +1565,7 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
         xch[(16 * NMB + 1) * 64] = M;
       }
       block_sync_lds();
-      if (set == 0 && wave_active && valid) {
+      if (!pair && !giver && wave_active && valid) {
         const float lb = xch[(16 * NMB) * 64];
         const float mb_ = xch[(16 * NMB + 1) * 64];
         const float ma = M;
@@ -1512,7 +1579,7 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
         lt = lt * wa + lb * wb;
       }
     }
-    if ((RS || set == 0) && wave_active && valid) {
+    if (!giver && wave_active && valid) {
       // O^T accumulator: lane holds query row r32 and dims mb*32 + q*8 + 4hh + 0..3 in entries 4q..4q+3.
       if (nsplit == 1) {
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
@@ -1635,10 +1702,11 @@ struct AttnLayout {
   // variant 0: verify_attn_main, 4 waves x 16 rows (64 rows), two workgroups per CU;
   // variant 1: verify_attn_wide, 8 waves, up to 128 rows (the sets split the tiles);
   // variant 2: verify_attn_wide, 8 waves, up to 256 rows (the sets split the rows);
+  // variant 3: verify_attn_wide, 8 waves, 129..192 rows (blocks 4-5 split by tile parity);
   // one workgroup per CU for variants 1 and 2
 };
 
-static int attn_variant(int rmax) { return rmax <= 64 ? 0 : rmax <= 128 ? 1 : 2; }
+static int attn_variant(int rmax) { return rmax <= 64 ? 0 : rmax <= 128 ? 1 : rmax <= 192 ? 3 : 2; }
 
 // Resident workgroups of the persistent grid per CU.
 static int attn_slots(int cus, int variant) { return cus * (variant == 0 ? 2 : 1); }
@@ -1694,8 +1762,9 @@ size_t sdv_attn_workspace_bytes(int B, int Hkv, int G, int head_dim, int max_pag
 template <int HD, int OUTF, bool TREE>
 static void launch_variant(int variant, const AttnParams& p, int grid, hipStream_t st) {
   if (variant == 0) verify_attn_main<HD, 1, 4, 2, OUTF, TREE><<<grid, 256, 0, st>>>(p);
-  else if (variant == 1) verify_attn_wide<HD, OUTF, false, TREE><<<grid, 512, 0, st>>>(p);
-  else verify_attn_wide<HD, OUTF, true, TREE><<<grid, 512, 0, st>>>(p);
+  else if (variant == 1) verify_attn_wide<HD, OUTF, 0, TREE><<<grid, 512, 0, st>>>(p);
+  else if (variant == 3) verify_attn_wide<HD, OUTF, 2, TREE><<<grid, 512, 0, st>>>(p);
+  else verify_attn_wide<HD, OUTF, 1, TREE><<<grid, 512, 0, st>>>(p);
 }
 
 template <int HD, int OUTF>

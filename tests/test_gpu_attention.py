@@ -45,6 +45,10 @@ def test_ragged_lengths_and_split_kv(kv_chunk):
     (8, [3, 1], 128),          # R <= 64
     (8, [15, 9], 128),         # R <= 128
     (8, [31, 20], 128),        # R <= 256
+    (8, [16, 9], 128),         # R = 136: rows 128.. split by tile parity
+    (8, [23, 19], 128),        # R = 192
+    (12, [15, 10], 64),        # R = 192, d = 64
+    (3, [50, 47], 128),        # R = 153
     (32, [3, 1], 128),         # G = 32, R = 128
     (16, [15, 4], 64),         # R = 256, d = 64
     (1, [0, 7], 128),          # G = 1
@@ -56,6 +60,18 @@ def test_row_block_variants(G, drafts, d):
     say(f"max|err| = {err:.3e}")
     assert err <= ATTN_TOL
     err = compare_attention(inp, gpu_attention(inp))
+    assert err <= ATTN_TOL
+
+
+@pytest.mark.parametrize("drafts", [[16, 12, 2], [23, 19, 17], [31, 25, 0]])
+def test_long_items_every_row_block(drafts):
+    """Items of thousands of keys (the unrolled steady loop runs many groups) at
+    136, 192 and 256 rows per KV head: every 32-row block, whichever wave and
+    tile parity serves it, matches the oracle."""
+    inp = generate(spec(batch=3, group=8, kv_len=[9000, 5000, 7001], draft_len=drafts, seed=sum(drafts)))
+    say(f"case: long items drafts={drafts}")
+    err = compare_attention(inp, gpu_attention(inp))
+    say(f"max|err| = {err:.3e}")
     assert err <= ATTN_TOL
 
 
@@ -120,6 +136,7 @@ def test_deterministic():
     (8, [0, 0], [700, 1333], 0),                  # plain decode, split-KV with the combine
     (8, [15, 9], [700, 1333], 0),                 # R <= 128
     (8, [31, 20], [700, 1333], 0),                # R <= 256 (row split)
+    (8, [19, 12], [700, 1333], 0),                # R = 160 (blocks 4-5 split by tile parity)
     (2, [3, 0, 1, 2] * 40, [37, 900, 5000, 260] * 40, 0),   # short items: counter-driven fetch
 ])
 def test_workspace_contents_never_matter(G, drafts, kv, kv_chunk):
@@ -156,7 +173,8 @@ def test_workspace_contents_never_matter(G, drafts, kv, kv_chunk):
     ("g32_kv128k_D3_greedy", {}),                  # B4 G32 128K keys, D=3 (128 rows)
     ("g8_kv32k_sweep", dict(draft_len=0)),         # B32 G8 32K keys: 8 rows (plain decode)
     ("g8_kv32k_sweep", dict(draft_len=15)),        # 128 rows
-    ("g8_kv32k_sweep", dict(draft_len=16)),        # 136 rows (the row split)
+    ("g8_kv32k_sweep", dict(draft_len=16)),        # 136 rows
+    ("g8_kv32k_sweep", dict(draft_len=23)),        # 192 rows
     ("g8_kv32k_sweep", dict(draft_len=31)),        # 256 rows
     ("ragged_b64", {}),                            # B64 lognormal 1K..128K keys, D in {3, 7, 15}
 ])

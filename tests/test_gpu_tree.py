@@ -56,7 +56,8 @@ def test_chain_tree_is_bitwise_the_causal_call(G, drafts, d):
 @pytest.mark.parametrize("kind", ["random", "star"])
 @pytest.mark.parametrize("G,drafts,d,kv_chunk", [(8, [15, 3, 7], 128, 0), (8, [31, 12, 6], 128, 0),
                                                  (4, [7, 2, 5], 64, 0), (8, [15, 3, 7], 128, 256),
-                                                 (2, [40, 63, 1], 64, 0)])
+                                                 (2, [40, 63, 1], 64, 0), (3, [50, 20, 7], 128, 0),
+                                                 (3, [50, 20, 7], 128, 256)])
 def test_tree_attention_matches_oracle(kind, G, drafts, d, kv_chunk):
     inp = generate(_spec(group=G, head_dim=d, draft_len=drafts, seed=3 * G + d + len(kind)))
     rng = np.random.default_rng(G + d)
@@ -71,12 +72,12 @@ def test_tree_attention_matches_oracle(kind, G, drafts, d, kv_chunk):
 
 
 @pytest.mark.parametrize("kind", ["random", "star"])
-@pytest.mark.parametrize("G,kv_chunk", [(1, 64), (1, 128), (2, 64), (4, 64), (4, 128)])
+@pytest.mark.parametrize("G,kv_chunk", [(1, 64), (1, 128), (2, 64), (3, 64), (4, 64), (4, 128)])
 def test_split_boundary_inside_the_tree(kind, G, kv_chunk):
     """64-node trees whose last split begins inside the tree (1, 10 and 30 nodes
     in), with G = 1 (64 rows: the R <= 64 kernel), G = 2 (128 rows: the wide
-    kernel whose wave sets split the tiles) and G = 4 (256 rows: the row-split
-    wide kernel).  A node whose root path has no node in the first
+    kernel whose wave sets split the tiles), G = 3 (192 rows: rows past 128
+    split by tile parity) and G = 4 (256 rows: the row-split wide kernel).  A node whose root path has no node in the first
     tile of that split sees no key there, yet sees its own nodes in a later
     tile of the split: its partial must still enter the combine with the
     offset its values were computed against."""
