@@ -46,7 +46,7 @@ namespace sdv {
 
 constexpr int kPage = 16;
 constexpr int kMinChunk = 256;
-constexpr int kMaxChunk = 16384;         // keys per work item; bounds the per-item page list in LDS
+constexpr int kMaxChunk = 32768;         // keys per work item; bounds the per-item page list in LDS
 constexpr int kPlanThreads = 256;
 constexpr int kItemsPerSlot = 4;         // work items per resident workgroup the workspace admits
 constexpr int kItemOverheadBytes = 192 * 1024;   // an item's fixed cost (set-up, partials) in bytes of K/V
@@ -133,8 +133,8 @@ __global__ __launch_bounds__(64 * kMaskSeqsPerBlock) void verify_tree_masks(Attn
 // ---------------------------------------------------------------------------
 // Plan (one workgroup).
 //
-// Chunk: `fixed_chunk` if non-zero.  Otherwise thread t evaluates chunk
-// kMinChunk + 64 t (at most the longest sequence, rounded up to 64, and at
+// Chunk: `fixed_chunk` if non-zero.  Otherwise thread t evaluates candidate
+// plan_candidate(t) (at most the longest sequence, rounded up to 64, and at
 // most kMaxChunk): with items(c) = Hkv * sum_b max(1, ceil(N_b / c)), the
 // schedule of the persistent grid takes at least the average load per slot,
 // (Hkv * sum_b N_b + ovh * items(c)) / slots keys (ovh: fixed cost of an item
@@ -159,7 +159,15 @@ __global__ __launch_bounds__(64 * kMaskSeqsPerBlock) void verify_tree_masks(Attn
 // sequences (plan[3] entries, any order) for the combine of large batches.
 constexpr int kLenBuckets = 64;
 constexpr int kPlanCacheSeqs = 8192;     // sequences whose fields the plan keeps in LDS (4 x 32 KiB; gfx950 allows 160 KiB per workgroup)
-constexpr int kHistBins = kMaxChunk / 64 + 2;   // ceil(N/64) = 0 .. 256, and "longer"
+constexpr int kHistBins = kMaxChunk / 64 + 2;   // ceil(N/64) = 0 .. 512, and "longer"
+constexpr int kBinsPerLane = (kHistBins + 63) / 64;   // the suffix scan: one wave over the bins
+
+// Chunk candidate t of the plan's search (t < kPlanThreads, increasing in t):
+// every multiple of 64 keys from 256 to 15552, then 16384 .. 30720 in steps of
+// 1024 and kMaxChunk itself.
+__device__ __forceinline__ int plan_candidate(int t) {
+  return t < 240 ? kMinChunk + 64 * t : t < kPlanThreads - 1 ? 16384 + 1024 * (t - 240) : kMaxChunk;
+}
 constexpr int kLongSeqs = 256;           // sequences longer than kMaxChunk the chunk search lists in LDS
 constexpr int kDirectSeqs = 64;          // chunk search: batches this small skip the histogram
 constexpr int kSearchCost = 8;           // descriptors: an item found by binary search costs about 8 written directly
@@ -185,7 +193,7 @@ __global__ __launch_bounds__(kPlanThreads) void verify_attn_plan(AttnParams p, i
   const int tid = threadIdx.x;
   const int max_keys = p.max_pages * kPage;
   const int cap_chunk = max(kMinChunk, min(kMaxChunk, (max_keys + 63) / 64 * 64));
-  const int my_chunk = min(kMinChunk + 64 * tid, cap_chunk);
+  const int my_chunk = min(plan_candidate(tid), cap_chunk);
   int* tail_pos = p.plan + kPlanHeader + p.B + 1;
   int* split_list = p.plan + kPlanHeader + 2 * p.B + 1;   // the sequences with more than one split
   auto keys_of = [&](int b) { return b < kPlanCacheSeqs ? s_n[b] : seq_keys(p, b); };
@@ -193,7 +201,7 @@ __global__ __launch_bounds__(kPlanThreads) void verify_attn_plan(AttnParams p, i
   // (1) the chunk.  Candidates are c = 64 d keys (d >= 4), and ceil(N/c) =
   // ceil(ceil(N/64) / d), so with n_b = ceil(N_b/64) the item count is
   // sum_b max(1, ceil(n_b/d)) = B + sum_{k>=1} #{b : n_b > k d}.  For the
-  // sequences of at most kMaxChunk keys (n_b <= 256) the terms come from the
+  // sequences of at most kMaxChunk keys (n_b <= 512) the terms come from the
   // suffix counts of their histogram (s_above, non-increasing, so the sum stops
   // at the first zero); each longer sequence adds ceil(n_b/d) - 1.  The search
   // costs O(B + 256 * long sequences) instead of 256 divisions per sequence.
@@ -229,16 +237,17 @@ __global__ __launch_bounds__(kPlanThreads) void verify_attn_plan(AttnParams p, i
     }
   }
   __syncthreads();
-  static_assert(kHistBins <= 5 * 64, "one wave, five bins per lane");
+  static_assert(kBinsPerLane * 64 >= kHistBins, "one wave over the bins");
   static_assert(kDirectSeqs <= kPlanCacheSeqs, "the direct count reads the lengths from LDS");
   if (direct) {
     for (int b = 0; b < p.B; ++b) my_items += max(1, (s_n[b] + my_chunk - 1) / my_chunk);
   } else {
     if (tid < 64) {                                  // suffix counts: s_above[x] = short sequences past bin x
-      int loc[5], tot = 0;
+      int loc[kBinsPerLane], tot = 0;
   #pragma unroll
-      for (int q = 0; q < 5; ++q) {
-        loc[q] = 5 * tid + q < kHistBins - 1 ? s_hist[5 * tid + q] : 0;   // (the last bin: the long ones)
+      for (int q = 0; q < kBinsPerLane; ++q) {
+        const int x = kBinsPerLane * tid + q;
+        loc[q] = x < kHistBins - 1 ? s_hist[x] : 0;   // (the last bin: the long ones)
         tot += loc[q];
       }
       int suf = tot;                                 // inclusive suffix scan over the lanes
@@ -249,8 +258,8 @@ __global__ __launch_bounds__(kPlanThreads) void verify_attn_plan(AttnParams p, i
       }
       int after = suf - tot;
   #pragma unroll
-      for (int q = 4; q >= 0; --q) {
-        if (5 * tid + q < kHistBins) s_above[5 * tid + q] = after;
+      for (int q = kBinsPerLane - 1; q >= 0; --q) {
+        if (kBinsPerLane * tid + q < kHistBins) s_above[kBinsPerLane * tid + q] = after;
         after += loc[q];
       }
     }
@@ -297,7 +306,7 @@ __global__ __launch_bounds__(kPlanThreads) void verify_attn_plan(AttnParams p, i
   __syncthreads();
   int chunk = cap_chunk;
   if (fixed_chunk > 0) chunk = fixed_chunk;
-  else if (s_best != ~0ull) chunk = min(kMinChunk + 64 * (int)(s_best & 511), cap_chunk);
+  else if (s_best != ~0ull) chunk = min(plan_candidate((int)(s_best & 511)), cap_chunk);
 
   // (2) the shorter items: count per length bucket (bucket 0 = longest), and
   // the number of full-chunk items

@@ -6,8 +6,9 @@ short, all long, mixed, or longer than the plan's LDS list of long sequences
 holds; and the attention output of the same calls against the oracle on
 sampled (sequence, head) units.
 
-The plan's chunk rule: candidates c = 256 + 64 t keys (capped at the longest
-sequence rounded up to 64, and at 16384); items(c) = H_kv * sum_b max(1,
+The plan's chunk rule: candidates c(t), t < 256: 256 + 64 t keys for t < 240,
+then 16384 + 1024 (t - 240) and 32768 for t = 255 (capped at the longest
+sequence rounded up to 64, and at 32768); items(c) = H_kv * sum_b max(1,
 ceil(N_b / c)); among the candidates whose items fit the workspace, the one
 with the smallest max(ceil((H_kv * sum_b N_b + ovh * items(c)) / slots),
 min(c, max_b N_b)) wins, the smaller c on ties; ovh = 192 KiB of K/V in keys,
@@ -24,6 +25,11 @@ from workloads import WorkloadSpec, generate
 pytestmark = pytest.mark.gpu
 
 PAGE = 16
+MAX_CHUNK = 32768
+
+
+def candidate(t):
+    return 256 + 64 * t if t < 240 else 16384 + 1024 * (t - 240) if t < 255 else MAX_CHUNK
 
 
 def expected_plan(kv, hkv, group, max_draft, head_dim, max_pages, cus, kv_chunk=0):
@@ -40,25 +46,25 @@ def expected_plan(kv, hkv, group, max_draft, head_dim, max_pages, cus, kv_chunk=
     if kv_chunk > 0:
         cap = units * -(-max_keys // kv_chunk)
     else:
-        at_max = units * -(-max_keys // 16384)
+        at_max = units * -(-max_keys // MAX_CHUNK)
         at_min = units * -(-max_keys // 256)
         cap = min(at_min, max(256 * per_cu * 4, at_max))
     cap = max(cap, 1)
     if kv_chunk > 0:
         chunk = kv_chunk
     else:
-        cap_chunk = max(256, min(16384, (max_keys + 63) // 64 * 64))
+        cap_chunk = max(256, min(MAX_CHUNK, (max_keys + 63) // 64 * 64))
         ovh = 192 * 1024 // (4 * head_dim)
         best = None
         for t in range(256):
-            c = min(256 + 64 * t, cap_chunk)
+            c = min(candidate(t), cap_chunk)
             items = hkv * int(np.maximum(1, -(-n // c)).sum())
             if items > cap:
                 continue
             load = (int(n.sum()) * hkv + ovh * items + slots - 1) // slots
             key = (max(load, min(c, int(n.max()))), t)
             best = key if best is None else min(best, key)
-        chunk = cap_chunk if best is None else min(256 + 64 * best[1], cap_chunk)
+        chunk = cap_chunk if best is None else min(candidate(best[1]), cap_chunk)
     per_seq = np.maximum(1, -(-n // chunk))
     rpad = -(-rmax // 16) * 16
     listed = B * hkv * (rpad // 8) > 8192
@@ -106,8 +112,8 @@ def test_all_short_sequences_large_batch():
 
 
 def test_all_long_sequences():
-    """16 sequences of 32768 keys over 2 heads: every sequence past the plan's
-    histogram (longer than 16384 keys), split in several items."""
+    """16 sequences of 32768 keys over 2 heads (the plan's longest histogram
+    bin), split in several items to fill the GPU."""
     inp = generate(spec(batch=16, kv_heads=2, group=8, kv_len=32768, draft_len=7, seed=32))
     say("case: plan B=16 N=32768")
     check(inp, units=[(0, 0), (7, 1), (15, 1)])
@@ -117,7 +123,7 @@ def test_mixed_lengths_with_some_long():
     rng = np.random.default_rng(33)
     kv = [int(x) for x in rng.integers(1, 1500, size=2500)]
     for b in (3, 700, 2100):
-        kv[b] = int(rng.integers(17000, 40000))
+        kv[b] = int(rng.integers(33000, 60000))
     inp = generate(spec(batch=2500, kv_heads=1, group=2, kv_len=kv, draft_len=[int(x) for x in rng.integers(0, 4, size=2500)],
                         seed=33))
     say("case: plan B=2500 mixed, 3 long")
@@ -125,10 +131,10 @@ def test_mixed_lengths_with_some_long():
 
 
 def test_more_long_sequences_than_the_plan_lists():
-    """260 sequences just over 16384 keys: more than the 256 the chunk search
+    """260 sequences just over 32768 keys: more than the 256 the chunk search
     lists in LDS, so it counts every sequence directly."""
-    inp = generate(spec(batch=260, kv_heads=1, group=1, kv_len=16400, draft_len=0, seed=34))
-    say("case: plan B=260 N=16400")
+    inp = generate(spec(batch=260, kv_heads=1, group=1, kv_len=32800, draft_len=0, seed=34))
+    say("case: plan B=260 N=32800")
     check(inp, units=[(0, 0), (259, 0)])
 
 
