@@ -52,10 +52,10 @@ def test_noalloc_matches_the_workspace_call_twice_in_a_row(mode):
 
 
 def test_noalloc_rejects_problems_beyond_its_scratch():
-    # 256 sequences x 16 rows over a 262144-token vocabulary need more scratch than the library holds;
+    # 4096 sequences x 16 rows over a 262144-token vocabulary need more scratch than the library holds;
     # the size check comes before any pointer is used, so nothing is enqueued
-    desc = B.sd_accept_desc(num_seqs=256, vocab=262144, max_draft=15, mode=B.SD_ACCEPT_STOCHASTIC)
-    T = 256 * 16
+    desc = B.sd_accept_desc(num_seqs=4096, vocab=262144, max_draft=15, mode=B.SD_ACCEPT_STOCHASTIC)
+    T = 4096 * 16
     assert sdv.sd_accept_reject_workspace_size(desc, T) > (32 << 20)
     st = B.lib().sd_accept_reject_noalloc(ctypes.byref(desc), T, None, None, None, None, None, None, None, None)
     assert st == B.SD_ERR_UNSUPPORTED
