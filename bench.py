@@ -115,6 +115,7 @@ def cpu_baseline(inp, budget_s: float = 20.0, gpu_out=None, gpu_al=None, gpu_tok
 
     qs = inp.q_start.cpu().numpy()
     kvl = inp.kv_len.cpu().numpy()
+    v_layout = "key" if tuple(inp.v_cache.shape) == tuple(inp.k_cache.shape) else "dim"
     seq_cache = {}
     got = gpu_out.float().cpu().numpy() if gpu_out is not None else None
     att_err, att_over, att_units, att_nonfinite = 0.0, 0, 0, 0
@@ -129,7 +130,7 @@ def cpu_baseline(inp, budget_s: float = 20.0, gpu_out=None, gpu_al=None, gpu_tok
             seq_cache[b] = dict(q_bits=bits(inp.q[t0:t1]), k_bits=bits(inp.k_cache[pages]),
                                 v_bits=bits(inp.v_cache[pages]), block_table=np.arange(npg, dtype=np.int32)[None],
                                 kv_len=np.asarray([n], np.int32), q_start=np.asarray([0, t1 - t0], np.int32),
-                                group=G, b=0)
+                                group=G, b=0, v_layout=v_layout)
         return seq_cache[b]
 
     order = [(int(b), h) for b in rng.permutation(B) for h in range(Hkv)]
@@ -442,7 +443,7 @@ def run_tree(args):
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    sp = preset(TREE_PRESET, seed=args.seed)
+    sp = preset(TREE_PRESET, seed=args.seed, v_layout=args.v_layout)
     print(f"[bench] tree {TREE_BRANCHING}: generating", file=sys.stderr, flush=True)
     inp, parents, tokens = tree_inputs(sp, TREE_BRANCHING, device=dev)
     B, T_q = sp.batch, inp.q.shape[0]
@@ -522,7 +523,7 @@ def run_lossy(args):
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    sp = preset("g8_kv32k_D15", seed=args.seed)
+    sp = preset("g8_kv32k_D15", seed=args.seed, v_layout=args.v_layout)
     tau = args.js_threshold
     print(f"[bench] lossy tau={tau}: generating {sp.name}", file=sys.stderr, flush=True)
     inp = generate(sp, device=dev)
@@ -807,7 +808,7 @@ def run_batch_sweep(args):
     points = []
     for B, N in BATCH_SWEEP:
         sp = WorkloadSpec(name=f"b{B}_hkv8_g8_d128_kv{N}_D3", batch=B, kv_heads=8, group=8, head_dim=128,
-                          kv_len=N, draft_len=3, vocab=64, mode="greedy", seed=args.seed)
+                          kv_len=N, draft_len=3, vocab=64, mode="greedy", seed=args.seed, v_layout=args.v_layout)
         print(f"[bench] batch sweep: generating {sp.name}", file=sys.stderr, flush=True)
         inp = generate(sp, device=dev)
         out = torch.empty_like(inp.q)
@@ -887,7 +888,7 @@ def run_sweep(args):
     points = []
     alpha = args.alpha if args.alpha is not None else 0.6
     for D in args.sweep:
-        sp = preset(SWEEP_PRESET, draft_len=D, alpha=alpha, seed=args.seed)
+        sp = preset(SWEEP_PRESET, draft_len=D, alpha=alpha, seed=args.seed, v_layout=args.v_layout)
         print(f"[bench] sweep D={D}: generating {sp.name}", file=sys.stderr, flush=True)
         inp = generate(sp, device=dev)
         B, T = sp.batch, inp.q.shape[0]
@@ -1168,6 +1169,8 @@ def main():
     ap.add_argument("--draft", type=int, default=None, help="override D (every sequence)")
     ap.add_argument("--alpha", type=float, default=None, help="fixed acceptance rate for the synthetic drafter")
     ap.add_argument("--kv-chunk", type=int, default=0)
+    ap.add_argument("--v-layout", choices=("dim", "key"), default="key",
+                    help="V cache pages stored key-major [P,H,16,d] like K (default) or d-major [P,H,d,16]")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--settle-s", type=float, default=1.0,
@@ -1282,6 +1285,7 @@ def main():
         over["draft_len"] = args.draft
     if args.alpha is not None:
         over["alpha"] = args.alpha
+    over["v_layout"] = args.v_layout
     sp = preset(args.workload, **over)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -1380,7 +1384,7 @@ def main():
             "kv_len": sp.kv_len if not isinstance(sp.kv_len, tuple) else list(sp.kv_len),
             "draft_len": sp.draft_len if not isinstance(sp.draft_len, tuple) else list(sp.draft_len),
             "vocab": sp.vocab, "accept": sp.mode, "alpha": sp.alpha, "page_size": sp.page_size,
-            "verified_tokens_per_step": T, "seed": sp.seed,
+            "verified_tokens_per_step": T, "seed": sp.seed, "v_layout": args.v_layout,
         },
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

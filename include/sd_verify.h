@@ -69,6 +69,12 @@ typedef enum {
 typedef enum { SD_ACCEPT_GREEDY = 0, SD_ACCEPT_STOCHASTIC = 1 } sd_accept_mode;
 typedef enum { SD_OUT_BF16 = 0, SD_OUT_F32 = 1 } sd_out_dtype;
 
+/* How each (page, head) block of the V cache is stored.  SD_V_KEY_MAJOR:
+ * [page_size][d] like K (the usual paged cache); SD_V_DIM_MAJOR: [d][page_size]
+ * (the transpose), which the kernels read with plain 16-byte LDS loads where
+ * key-major pages need transposing ones. */
+typedef enum { SD_V_KEY_MAJOR = 0, SD_V_DIM_MAJOR = 1 } sd_v_layout;
+
 /* Verify-attention problem description (host memory, read during the call). */
 typedef struct {
   int32_t num_seqs;           /* B >= 0 */
@@ -82,6 +88,7 @@ typedef struct {
   float softmax_scale;        /* scores are scale * q.k; 0 selects 1/sqrt(d) */
   int32_t out_dtype;          /* sd_out_dtype */
   int32_t kv_chunk;           /* keys per split-KV work item: a multiple of 64, at most 8192; 0 = chosen per call */
+  int32_t v_layout;           /* sd_v_layout of v_cache */
 } sd_attn_desc;
 
 /* Accept/reject problem description. */
@@ -108,9 +115,10 @@ size_t sd_verify_attention_workspace_size(const sd_attn_desc* desc, int32_t tota
  *
  *   q            bf16 [total_q, H_kv*G, d]                 row-major
  *   k_cache      bf16 [num_pages, H_kv, page_size, d]      row-major
- *   v_cache      bf16 [num_pages, H_kv, d, page_size]      row-major: each page of V
- *                stored d-major (the transpose of its page_size x d block), so
- *                that the keys a P.V product contracts over are contiguous
+ *   v_cache      bf16 [num_pages, H_kv, page_size, d]      row-major, desc->v_layout = SD_V_KEY_MAJOR;
+ *                bf16 [num_pages, H_kv, d, page_size]      with SD_V_DIM_MAJOR (each page's block
+ *                stored transposed, so that the keys a P.V product contracts over
+ *                are contiguous)
  *   block_table  int32 [B, max_pages_per_seq]
  *   kv_len       int32 [B]
  *   q_start      int32 [B+1]

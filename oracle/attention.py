@@ -38,12 +38,15 @@ def bf16_bits_to_f64(bits) -> np.ndarray:
     return b.view(np.float32).astype(np.float64)
 
 
-def _check(q_bits, k_bits, v_bits, block_table, kv_len, q_start, group):
+def _check(q_bits, k_bits, v_bits, block_table, kv_len, q_start, group, v_layout="dim"):
     if q_bits.ndim != 3 or k_bits.ndim != 4 or v_bits.ndim != 4:
-        raise ValueError("q [T, Hq, d], k [P, Hkv, page, d], v [P, Hkv, d, page] expected")
+        raise ValueError("q [T, Hq, d], k [P, Hkv, page, d], v [P, Hkv, d, page] or [P, Hkv, page, d] expected")
     P, Hkv, ps, d = k_bits.shape
-    if v_bits.shape != (P, Hkv, d, ps):
-        raise ValueError("v must be [P, Hkv, d, page]: each page stored d-major")
+    if v_layout not in ("dim", "key"):
+        raise ValueError("v_layout is 'dim' ([P, Hkv, d, page]) or 'key' ([P, Hkv, page, d])")
+    if v_bits.shape != ((P, Hkv, d, ps) if v_layout == "dim" else (P, Hkv, ps, d)):
+        raise ValueError("v must be [P, Hkv, d, page] (each page stored d-major, v_layout 'dim') "
+                         "or [P, Hkv, page, d] (key-major, v_layout 'key')")
     if q_bits.shape[1] != Hkv * group or q_bits.shape[2] != d:
         raise ValueError("q heads must be Hkv*G with the cache's head_dim")
     B = len(kv_len)
@@ -71,9 +74,12 @@ def _sequence_keys(cache_bits, table_row, n, h):
     return bf16_bits_to_f64(cache_bits[pages, h, j % ps, :])
 
 
-def _sequence_values(cache_bits, table_row, n, h):
-    """Values 0..n-1 of one sequence and KV head from a [P, Hkv, d, page] cache
-    (pages stored d-major), in position order: [n, d]."""
+def _sequence_values(cache_bits, table_row, n, h, v_layout="dim"):
+    """Values 0..n-1 of one sequence and KV head, in position order: [n, d],
+    from a [P, Hkv, d, page] cache (each page stored d-major, v_layout 'dim')
+    or a [P, Hkv, page, d] one (key-major like K, v_layout 'key')."""
+    if v_layout == "key":
+        return _sequence_keys(cache_bits, table_row, n, h)
     ps = cache_bits.shape[3]
     j = np.arange(n)
     pages = table_row[j // ps]
@@ -81,7 +87,7 @@ def _sequence_values(cache_bits, table_row, n, h):
 
 
 def verify_attention_unit(q_bits, k_bits, v_bits, block_table, kv_len, q_start, group,
-                          b: int, h: int, scale: Optional[float] = None) -> np.ndarray:
+                          b: int, h: int, scale: Optional[float] = None, v_layout: str = "dim") -> np.ndarray:
     """Output rows of sequence b, KV head h: float64 [1+D_b, G, d]."""
     d = k_bits.shape[3]
     if scale is None or scale == 0.0:
@@ -90,7 +96,7 @@ def verify_attention_unit(q_bits, k_bits, v_bits, block_table, kv_len, q_start, 
     t0 = int(q_start[b])
     rows = int(q_start[b + 1]) - t0            # 1 + D_b
     K = _sequence_keys(k_bits, block_table[b], n, h)
-    V = _sequence_values(v_bits, block_table[b], n, h)
+    V = _sequence_values(v_bits, block_table[b], n, h, v_layout)
     out = np.zeros((rows, group, d), dtype=np.float64)
     for i in range(rows):
         P = n - rows + i
@@ -107,7 +113,7 @@ def verify_attention_unit(q_bits, k_bits, v_bits, block_table, kv_len, q_start, 
 def verify_attention(q_bits, k_bits, v_bits, block_table, kv_len, q_start, group: int,
                      scale: Optional[float] = None,
                      units: Optional[Iterable[Tuple[int, int]]] = None,
-                     workers: int = 1) -> np.ndarray:
+                     workers: int = 1, v_layout: str = "dim") -> np.ndarray:
     """All output rows, float64 [T_q, Hkv*G, d].
 
     ``units`` restricts the work to the listed (b, h) pairs (other rows are
@@ -119,7 +125,7 @@ def verify_attention(q_bits, k_bits, v_bits, block_table, kv_len, q_start, group
     block_table = np.asarray(block_table)
     kv_len = np.asarray(kv_len)
     q_start = np.asarray(q_start)
-    _check(q_bits, k_bits, v_bits, block_table, kv_len, q_start, group)
+    _check(q_bits, k_bits, v_bits, block_table, kv_len, q_start, group, v_layout)
     T, Hq, d = q_bits.shape
     Hkv = k_bits.shape[1]
     out = np.full((T, Hq, d), np.nan, dtype=np.float64)
@@ -128,7 +134,7 @@ def verify_attention(q_bits, k_bits, v_bits, block_table, kv_len, q_start, group
     def run(u):
         b, h = u
         return u, verify_attention_unit(q_bits, k_bits, v_bits, block_table, kv_len, q_start,
-                                        group, b, h, scale)
+                                        group, b, h, scale, v_layout)
 
     if workers > 1:
         with ThreadPoolExecutor(workers) as ex:

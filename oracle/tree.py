@@ -57,7 +57,7 @@ def tree_ancestors(parents_b) -> List[Set[int]]:
 
 
 def verify_tree_attention_unit(q_bits, k_bits, v_bits, block_table, kv_len, q_start, parents, group,
-                               b: int, h: int, scale: Optional[float] = None) -> np.ndarray:
+                               b: int, h: int, scale: Optional[float] = None, v_layout: str = "dim") -> np.ndarray:
     """Output rows of sequence b, KV head h under the tree mask: float64 [1+T_b, G, d]."""
     d = k_bits.shape[3]
     if scale is None or scale == 0.0:
@@ -66,7 +66,7 @@ def verify_tree_attention_unit(q_bits, k_bits, v_bits, block_table, kv_len, q_st
     t0, T, d0 = _seq(q_start, b)
     anc = tree_ancestors(np.asarray(parents)[d0:d0 + T])
     K = _sequence_keys(k_bits, block_table[b], n, h)
-    V = _sequence_values(v_bits, block_table[b], n, h)
+    V = _sequence_values(v_bits, block_table[b], n, h, v_layout)
     first = n - 1 - T                          # key position of the root
     out = np.zeros((1 + T, group, d), dtype=np.float64)
     for i in range(1 + T):
@@ -83,12 +83,12 @@ def verify_tree_attention_unit(q_bits, k_bits, v_bits, block_table, kv_len, q_st
 
 def verify_tree_attention(q_bits, k_bits, v_bits, block_table, kv_len, q_start, parents, group: int,
                           scale: Optional[float] = None, units: Optional[Iterable[Tuple[int, int]]] = None,
-                          workers: int = 1) -> np.ndarray:
+                          workers: int = 1, v_layout: str = "dim") -> np.ndarray:
     """All output rows under the tree mask, float64 [T_q, Hkv*G, d] (rows of
     units not listed in ``units`` are NaN)."""
     q_bits, k_bits, v_bits = np.asarray(q_bits), np.asarray(k_bits), np.asarray(v_bits)
     block_table, kv_len, q_start = np.asarray(block_table), np.asarray(kv_len), np.asarray(q_start)
-    _check(q_bits, k_bits, v_bits, block_table, kv_len, q_start, group)
+    _check(q_bits, k_bits, v_bits, block_table, kv_len, q_start, group, v_layout)
     T, Hq, d = q_bits.shape
     Hkv = k_bits.shape[1]
     out = np.full((T, Hq, d), np.nan, dtype=np.float64)
@@ -97,7 +97,7 @@ def verify_tree_attention(q_bits, k_bits, v_bits, block_table, kv_len, q_start, 
     def run(u):
         b, h = u
         return u, verify_tree_attention_unit(q_bits, k_bits, v_bits, block_table, kv_len, q_start, parents,
-                                             group, b, h, scale)
+                                             group, b, h, scale, v_layout)
 
     if workers > 1:
         with ThreadPoolExecutor(workers) as ex:

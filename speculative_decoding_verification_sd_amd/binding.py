@@ -20,6 +20,7 @@ LIB_PATH = os.environ.get("SDVERIFY_LIB") or os.path.join(HERE, "libsdverify.so"
 SD_OK, SD_ERR_INVALID_ARG, SD_ERR_UNSUPPORTED, SD_ERR_WORKSPACE, SD_ERR_HIP = range(5)
 SD_ACCEPT_GREEDY, SD_ACCEPT_STOCHASTIC = 0, 1
 SD_OUT_BF16, SD_OUT_F32 = 0, 1
+SD_V_KEY_MAJOR, SD_V_DIM_MAJOR = 0, 1
 MODES = {"greedy": SD_ACCEPT_GREEDY, "stochastic": SD_ACCEPT_STOCHASTIC}
 
 
@@ -42,6 +43,7 @@ class sd_attn_desc(ctypes.Structure):
         ("softmax_scale", ctypes.c_float),
         ("out_dtype", ctypes.c_int32),
         ("kv_chunk", ctypes.c_int32),
+        ("v_layout", ctypes.c_int32),
     ]
 
 
@@ -156,14 +158,24 @@ def _need(t: torch.Tensor, name: str, dtype, device=None):
         raise ValueError(f"{name} must be contiguous")
 
 
+def v_layout_of(k_cache, v_cache) -> int:
+    """The sd_v_layout of a V cache from its shape: [pages, heads, page, d] like
+    K (key-major) or [pages, heads, d, page] (d-major).  head_dim is 64 or 128
+    and the page 16 keys, so the two never coincide.  (No V cache: key-major;
+    the workspace size does not depend on it.)"""
+    if v_cache is None or tuple(v_cache.shape) == tuple(k_cache.shape):
+        return SD_V_KEY_MAJOR
+    return SD_V_DIM_MAJOR
+
+
 def attn_desc(q, k_cache, block_table, group_size: int, max_draft: int, softmax_scale: float = 0.0,
-              out_dtype=torch.bfloat16, kv_chunk: int = 0) -> sd_attn_desc:
+              out_dtype=torch.bfloat16, kv_chunk: int = 0, v_cache=None) -> sd_attn_desc:
     num_pages, hkv, page, d = k_cache.shape
     return sd_attn_desc(num_seqs=block_table.shape[0], num_kv_heads=hkv, group_size=group_size, head_dim=d,
                         page_size=page, max_pages_per_seq=block_table.shape[1], num_pages=num_pages,
                         max_draft=max_draft, softmax_scale=softmax_scale,
                         out_dtype=SD_OUT_F32 if out_dtype == torch.float32 else SD_OUT_BF16,
-                        kv_chunk=kv_chunk)
+                        kv_chunk=kv_chunk, v_layout=v_layout_of(k_cache, v_cache))
 
 
 def accept_desc(num_seqs: int, vocab: int, max_draft: int, mode: str) -> sd_accept_desc:
@@ -206,9 +218,10 @@ def _check_attention_args(q, k_cache, v_cache, block_table, kv_len, q_start, out
         raise TypeError("out must be bf16 or fp32")
     _need(out, "out", out.dtype, dev)
     if k_cache.dim() != 4 or v_cache.dim() != 4 or \
-            tuple(v_cache.shape) != (k_cache.shape[0], k_cache.shape[1], k_cache.shape[3], k_cache.shape[2]):
-        raise ValueError("k_cache must be [pages, kv_heads, page_size, head_dim] and v_cache "
-                         "[pages, kv_heads, head_dim, page_size] (pages stored d-major)")
+            tuple(v_cache.shape) not in (tuple(k_cache.shape),
+                                         (k_cache.shape[0], k_cache.shape[1], k_cache.shape[3], k_cache.shape[2])):
+        raise ValueError("k_cache must be [pages, kv_heads, page_size, head_dim] and v_cache the same "
+                         "(key-major) or [pages, kv_heads, head_dim, page_size] (pages stored d-major)")
     if q.dim() != 3 or out.shape != q.shape:
         raise ValueError("q and out must be [total_q, query_heads, head_dim]")
     B = block_table.shape[0]
@@ -220,7 +233,7 @@ def sd_verify_attention(q, k_cache, v_cache, block_table, kv_len, q_start, out, 
                         max_draft: int, softmax_scale: float = 0.0, kv_chunk: int = 0,
                         workspace: Optional[torch.Tensor] = None, stream=None) -> None:
     _check_attention_args(q, k_cache, v_cache, block_table, kv_len, q_start, out)
-    desc = attn_desc(q, k_cache, block_table, group_size, max_draft, softmax_scale, out.dtype, kv_chunk)
+    desc = attn_desc(q, k_cache, block_table, group_size, max_draft, softmax_scale, out.dtype, kv_chunk, v_cache)
     total_q = q.shape[0]
     ws = _workspace(sd_verify_attention_workspace_size(desc, total_q), q.device, workspace)
     _check(lib().sd_verify_attention(ctypes.byref(desc), total_q, _ptr(q), _ptr(k_cache), _ptr(v_cache),
@@ -334,7 +347,8 @@ def sd_verify_step(q, k_cache, v_cache, block_table, kv_len, q_start, attn_out, 
                    stream=None) -> None:
     _check_attention_args(q, k_cache, v_cache, block_table, kv_len, q_start, attn_out)
     _check_accept_args(target_logits, draft_logits, draft_tokens, q_start, uniforms, accept_len, out_tokens, mode)
-    adesc = attn_desc(q, k_cache, block_table, group_size, max_draft, softmax_scale, attn_out.dtype, kv_chunk)
+    adesc = attn_desc(q, k_cache, block_table, group_size, max_draft, softmax_scale, attn_out.dtype, kv_chunk,
+                      v_cache)
     B = q_start.shape[0] - 1
     T, V = target_logits.shape
     cdesc = accept_desc(B, V, max_draft, mode)
@@ -357,7 +371,7 @@ def sd_verify_tree_attention(q, k_cache, v_cache, block_table, kv_len, q_start, 
     _need(parents, "parents", torch.int32, q.device)
     if parents.shape != (q.shape[0] - B,):
         raise ValueError("parents must be [total_q - B]")
-    desc = attn_desc(q, k_cache, block_table, group_size, max_draft, softmax_scale, out.dtype, kv_chunk)
+    desc = attn_desc(q, k_cache, block_table, group_size, max_draft, softmax_scale, out.dtype, kv_chunk, v_cache)
     total_q = q.shape[0]
     ws = _workspace(sd_verify_attention_workspace_size(desc, total_q), q.device, workspace)
     _check(lib().sd_verify_tree_attention(ctypes.byref(desc), total_q, _ptr(q), _ptr(k_cache), _ptr(v_cache),

@@ -49,6 +49,8 @@ sd_status check_attn(const sd_attn_desc* d, int32_t total_q) {
     return fail(SD_ERR_INVALID_ARG, "kv_chunk=%d must be 0 or a positive multiple of 64", d->kv_chunk);
   if (d->kv_chunk > 8192)
     return fail(SD_ERR_UNSUPPORTED, "kv_chunk=%d exceeds 8192 keys per work item", d->kv_chunk);
+  if (d->v_layout != SD_V_KEY_MAJOR && d->v_layout != SD_V_DIM_MAJOR)
+    return fail(SD_ERR_INVALID_ARG, "v_layout=%d is not an sd_v_layout", d->v_layout);
   if (total_q < d->num_seqs || (long long)total_q > (long long)d->num_seqs * (1LL + d->max_draft))
     return fail(SD_ERR_INVALID_ARG, "total_q=%d must lie in [num_seqs, num_seqs*(1+max_draft)] = [%d, %lld]",
                 total_q, d->num_seqs, (long long)d->num_seqs * (1LL + d->max_draft));
@@ -114,6 +116,7 @@ sd_status run_attention(const sd_attn_desc* d, int32_t total_q, const void* q, c
   a.max_draft = d->max_draft;
   a.out_f32 = d->out_dtype == SD_OUT_F32;
   a.kv_chunk = d->kv_chunk;
+  a.v_key_major = d->v_layout == SD_V_KEY_MAJOR;
   a.total_q = total_q;
   a.softmax_scale = d->softmax_scale;
   a.stream = (hipStream_t)stream;

@@ -473,6 +473,24 @@ typedef __attribute__((address_space(3))) unsigned char lds_u8;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
+// The V^T operand of a P V MFMA: eight keys of one head dimension per lane.
+// d-major V pages hold them contiguously (one ds_read_b128); key-major pages
+// (VKM) need two transposing reads (ds_read_b64_tr_b16: each group of 16
+// lanes reads four key rows x 16 dimensions and each lane gets four keys of
+// its dimension), the second four key rows further.
+template <bool VKM, int ROWB>
+__device__ __forceinline__ bf16x8 vt_operand(lds_u8* lds, int off) {
+  if constexpr (VKM) {
+    const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + off));
+    const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + off + 4 * ROWB));
+    const u32x2 lo = __builtin_bit_cast(u32x2, lo4);
+    const u32x2 hi = __builtin_bit_cast(u32x2, hi4);
+    return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+  } else {
+    return *(const bf16x8*)((const __attribute__((address_space(3))) unsigned char*)lds + off);
+  }
+}
+
 
 // Reductions over the four lanes {l, l^16, l^32, l^48} that hold one query row.
 __device__ __forceinline__ float row_max4(float v) {
@@ -514,29 +532,46 @@ struct Ring {
 // bytes per lane) of one (page, head) block into a ring stage.
 //   K: kKeysPerLoad key rows in key order; the lane's 16 bytes are logical
 //      chunk (lane % kCpr) ^ swz(key) of its key row.
-//   V: 32 d-rows of one d-major V page (16 keys x 2 bytes per d); LDS half h
-//      of d-row d holds keys ((h ^ bit 3 of d) * 8)..+7, so that sixteen
-//      consecutive d-rows read at one key half land on distinct banks.
+//   V (d-major pages): 32 d-rows of one V page (16 keys x 2 bytes per d); LDS
+//      half h of d-row d holds keys ((h ^ bit 3 of d) * 8)..+7, so that
+//      sixteen consecutive d-rows read at one key half land on distinct banks.
+//   V (key-major pages, VKM): like K, key rows in key order, with the chunk
+//      swizzle vkm_swz of the transposing reads.
 struct DmaSlot {
   unsigned src;   // lane's byte offset inside the (page, head) block
   int dst;        // byte offset of the instruction's 1 KiB inside the stage's K (or V) tile
   int page;       // page of the tile (0 or 1)
   int kv;         // 0: K, 1: V
   int key0;       // tile-relative key of the lane's first element
+  int rows;       // 1: the lane's 16 bytes are one key's (K, key-major V); 0: eight keys of one dimension
 };
 
-template <int HD, class RG, class SWZ>
+// XOR swizzle of the 16-byte chunks of a key-major V row in LDS (period 16
+// keys), for the transposing reads of the V^T operand: one read covers key
+// rows 16s + {0..3, 8..11} (or + 4) times four chunks (the 32x32x16 kernel), or
+// rows 8g + 0..3 of the four 8-key groups times two chunks (16x16x32); both
+// touch every bank group exactly twice, and rows k and k + 4 (k & 4 == 0)
+// share the swizzle, so the second read of a lane sits 4 rows further.
+template <int HD>
+__device__ __forceinline__ int vkm_swz(int k) {
+  if constexpr (HD == 128) return ((k & 3) << 2) | (((k >> 3) & 1) << 1);
+  else return (((k >> 1) & 1) << 2) | (((k >> 3) & 1) << 1);
+}
+
+template <int HD, class RG, bool VKM, class SWZ>
 __device__ __forceinline__ DmaSlot dma_slot(int j, int lane, SWZ swz) {
   DmaSlot s;
-  if (j < RG::kLoadsKV / 2) {
-    const int row0 = j * RG::kKeysPerLoad;
+  if (j < RG::kLoadsKV / 2 || VKM) {
+    const bool v = j >= RG::kLoadsKV / 2;
+    const int row0 = (v ? j - RG::kLoadsKV / 2 : j) * RG::kKeysPerLoad;
     const int key = row0 + lane / RG::kCpr;
-    const int lc = (lane % RG::kCpr) ^ swz(key);
+    const int lc = (lane % RG::kCpr) ^ (v ? vkm_swz<HD>(key) : swz(key));
     s.src = (unsigned)(((key & 15) * HD + lc * 8) * 2);
     s.dst = row0 * RG::kRowB;
     s.page = row0 / kPage;
-    s.kv = 0;
+    s.kv = v ? 1 : 0;
     s.key0 = key;
+    s.rows = 1;
   } else {
     constexpr int kPerPage = HD / 32;             // instructions per V page (32 d-rows of 32 bytes)
     const int jv = j - RG::kLoadsKV / 2;
@@ -548,18 +583,21 @@ __device__ __forceinline__ DmaSlot dma_slot(int j, int lane, SWZ swz) {
     s.page = page;
     s.kv = 1;
     s.key0 = page * kPage + half * 8;
+    s.rows = 0;
   }
   return s;
 }
 
 // Zero the elements of this wave's DMA loads of stage `sp` whose keys lie at or
-// past `lim` (tile-relative): whole K rows, single entries of the V pages.
+// past `lim` (tile-relative): whole key rows (K, key-major V), single entries
+// of the d-major V pages.
 template <int LPW, class RG, int S>
 __device__ __forceinline__ void zero_keys_past(unsigned char* sp, const DmaSlot (&dma)[LPW], int lane, int lim) {
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
-    if (dma[i].kv == 0) {
-      if (dma[i].key0 >= lim) *(u32x4*)(sp + dma[i].dst + lane * 16) = u32x4{0, 0, 0, 0};
+    if (dma[i].rows) {
+      if (dma[i].key0 >= lim)
+        *(u32x4*)(sp + dma[i].kv * S * RG::kHalf + dma[i].dst + lane * 16) = u32x4{0, 0, 0, 0};
     } else if (dma[i].key0 + 7 >= lim) {
       // (compared as q >= lim - key0, so that no key0 + q stays live across the item loop)
       const int nvalid = lim - dma[i].key0;
@@ -604,7 +642,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 // ---------------------------------------------------------------------------
 // NRB row blocks of 16 per wave, NW waves, WPC resident workgroups per CU.
-template <int HD, int NRB, int NW, int WPC, int OUT_F32, bool TREE>
+template <int HD, int NRB, int NW, int WPC, int OUT_F32, bool TREE, bool VKM>
 __global__ __launch_bounds__(64 * NW, WPC) void verify_attn_main(AttnParams p) {
   using RG = Ring<HD, NW, WPC>;
   constexpr int S = RG::kStages;
@@ -644,13 +682,19 @@ __global__ __launch_bounds__(64 * NW, WPC) void verify_attn_main(AttnParams p) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
     const int dd = db * 16 + l16;
-    voffs[db] = S * RG::kHalf + (g4 >> 1) * HD * 32 + dd * 32 + (((g4 & 1) ^ ((dd >> 3) & 1)) * 16);
+    if constexpr (VKM) {   // transposing read: key row g4*8 + l16/4 (+4 for the second), dims dd0..+3
+      const int key = g4 * 8 + (l16 >> 2);
+      const int dd0 = db * 16 + 4 * (l16 & 3);
+      voffs[db] = S * RG::kHalf + key * RG::kRowB + (((dd0 >> 3) ^ vkm_swz<HD>(key)) * 16) + (dd0 & 7) * 2;
+    } else {
+      voffs[db] = S * RG::kHalf + (g4 >> 1) * HD * 32 + dd * 32 + (((g4 & 1) ^ ((dd >> 3) & 1)) * 16);
+    }
   }
 
   // DMA instruction j = wave + NW*i of a tile: K rows for j < kLoadsKV/2, V pages after
   DmaSlot dma[LPW];
 #pragma unroll
-  for (int i = 0; i < LPW; ++i) dma[i] = dma_slot<HD, RG>(wave + NW * i, lane, [](int k) { return key_swz<HD>(k); });
+  for (int i = 0; i < LPW; ++i) dma[i] = dma_slot<HD, RG, VKM>(wave + NW * i, lane, [](int k) { return key_swz<HD>(k); });
   bf16x8 ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
@@ -815,7 +859,7 @@ __global__ __launch_bounds__(64 * NW, WPC) void verify_attn_main(AttnParams p) {
     };
     auto read_v = [&](int off, bf16x8 (&vf)[NDB]) {
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) vf[db] = *(const bf16x8*)(smem + off + voffs[db]);
+      for (int db = 0; db < NDB; ++db) vf[db] = vt_operand<VKM, RG::kRowB>(lds_smem, off + voffs[db]);
     };
     // the 2*NRB accumulation chains advance together (k-step outermost), so
     // consecutive MFMAs never depend on each other
@@ -1099,7 +1143,7 @@ __device__ __forceinline__ int wide_swz(int k) {
 // blocks 4 and 5 two to a block, one tile of every step each, so that no SIMD
 // (it hosts waves s and s+4) carries more than three of the step's 32-row
 // tile products where the row split would give one SIMD four.
-template <int HD, int OUT_F32, int MODE, bool TREE>
+template <int HD, int OUT_F32, int MODE, bool TREE, bool VKM>
 __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
   constexpr int NW = 8;
   using RG = Ring<HD, NW, 1>;
@@ -1150,11 +1194,20 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) {
     const int dd = mb * 32 + r32;
-    voffs[mb] = par * RG::kHalf + S * RG::kHalf + dd * 32 + ((hh ^ ((dd >> 3) & 1)) * 16);
+    if constexpr (VKM) {   // transposing read: key row 8hh + j16/4 (+4 for the second), dims dd0..+3
+      const int j16 = lane & 15;
+      const int key = 8 * hh + (j16 >> 2);
+      const int dd0 = mb * 32 + 16 * ((lane >> 4) & 1) + 4 * (j16 & 3);
+      voffs[mb] = par * RG::kHalf + S * RG::kHalf + key * RG::kRowB + (((dd0 >> 3) ^ vkm_swz<HD>(key)) * 16) +
+                  (dd0 & 7) * 2;
+    } else {
+      voffs[mb] = par * RG::kHalf + S * RG::kHalf + dd * 32 + ((hh ^ ((dd >> 3) & 1)) * 16);
+    }
   }
   DmaSlot dma[LPW];
 #pragma unroll
-  for (int i = 0; i < LPW; ++i) dma[i] = dma_slot<HD, RG>(wave + NW * i, lane, [](int k) { return wide_swz<HD>(k & 15); });
+  for (int i = 0; i < LPW; ++i)
+    dma[i] = dma_slot<HD, RG, VKM>(wave + NW * i, lane, [](int k) { return wide_swz<HD>(k & 15); });
 
   // Items after the first round.  When the plan's list (longest first) holds
   // items shorter than the chunk and more items than workgroups, the next item
@@ -1328,7 +1381,7 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) {
-          const bf16x8 vf = *(const bf16x8*)(smem + off + ks * HD * 32 + voffs[mb]);
+          const bf16x8 vf = vt_operand<VKM, RG::kRowB>(lds_smem, off + ks * HD * 32 + voffs[mb]);
           o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[mb], 0, 0, 0);
         }
       const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
@@ -1355,10 +1408,10 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
         if constexpr (j < NKS) return *(const bf16x8*)(smem + off0 + koff[j]);
         else if constexpr (j < 2 * NKS) return *(const bf16x8*)(smem + off1 + koff[j - NKS]);
         else if constexpr (j < 2 * NKS + 2 * NMB)
-          return *(const bf16x8*)(smem + off0 + ((j - 2 * NKS) / NMB) * HD * 32 + voffs[(j - 2 * NKS) % NMB]);
+          return vt_operand<VKM, RG::kRowB>(lds_smem, off0 + ((j - 2 * NKS) / NMB) * HD * 32 + voffs[(j - 2 * NKS) % NMB]);
         else
-          return *(const bf16x8*)(smem + off1 + ((j - 2 * NKS - 2 * NMB) / NMB) * HD * 32 +
-                                  voffs[(j - 2 * NKS - 2 * NMB) % NMB]);
+          return vt_operand<VKM, RG::kRowB>(lds_smem, off1 + ((j - 2 * NKS - 2 * NMB) / NMB) * HD * 32 +
+                                                      voffs[(j - 2 * NKS - 2 * NMB) % NMB]);
       };
       // share q of nq of a tile's P work: its 16/nq scores -> exp2 -> bf16 -> row sum
       auto p_share = [&](const f32x16& sv, bf16x8 (&pf)[2], auto qc, auto nqc) {
@@ -1405,7 +1458,7 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
       auto operand = [&](auto jc) -> bf16x8 {
         constexpr int j = decltype(jc)::value;
         if constexpr (j < NKS) return *(const bf16x8*)(smem + off + koff[j]);
-        else return *(const bf16x8*)(smem + off + ((j - NKS) / NMB) * HD * 32 + voffs[(j - NKS) % NMB]);
+        else return vt_operand<VKM, RG::kRowB>(lds_smem, off + ((j - NKS) / NMB) * HD * 32 + voffs[(j - NKS) % NMB]);
       };
       f32x16 sv = mneg;
       bf16x8 pv2[2];
@@ -1768,18 +1821,23 @@ size_t sdv_attn_workspace_bytes(int B, int Hkv, int G, int head_dim, int max_pag
 
 // The draft-tree mask is a template parameter, so that causal calls run code
 // with no trace of it.
-template <int HD, int OUTF, bool TREE>
+template <int HD, int OUTF, bool TREE, bool VKM>
 static void launch_variant(int variant, const AttnParams& p, int grid, hipStream_t st) {
-  if (variant == 0) verify_attn_main<HD, 1, 4, 2, OUTF, TREE><<<grid, 256, 0, st>>>(p);
-  else if (variant == 1) verify_attn_wide<HD, OUTF, 0, TREE><<<grid, 512, 0, st>>>(p);
-  else if (variant == 3) verify_attn_wide<HD, OUTF, 2, TREE><<<grid, 512, 0, st>>>(p);
-  else verify_attn_wide<HD, OUTF, 1, TREE><<<grid, 512, 0, st>>>(p);
+  if (variant == 0) verify_attn_main<HD, 1, 4, 2, OUTF, TREE, VKM><<<grid, 256, 0, st>>>(p);
+  else if (variant == 1) verify_attn_wide<HD, OUTF, 0, TREE, VKM><<<grid, 512, 0, st>>>(p);
+  else if (variant == 3) verify_attn_wide<HD, OUTF, 2, TREE, VKM><<<grid, 512, 0, st>>>(p);
+  else verify_attn_wide<HD, OUTF, 1, TREE, VKM><<<grid, 512, 0, st>>>(p);
 }
 
 template <int HD, int OUTF>
-static void launch_main(int variant, const AttnParams& p, int grid, hipStream_t st) {
-  if (p.tmask) launch_variant<HD, OUTF, true>(variant, p, grid, st);
-  else launch_variant<HD, OUTF, false>(variant, p, grid, st);
+static void launch_main(int variant, const AttnParams& p, int grid, hipStream_t st, bool vkm) {
+  if (p.tmask) {
+    if (vkm) launch_variant<HD, OUTF, true, true>(variant, p, grid, st);
+    else launch_variant<HD, OUTF, true, false>(variant, p, grid, st);
+  } else {
+    if (vkm) launch_variant<HD, OUTF, false, true>(variant, p, grid, st);
+    else launch_variant<HD, OUTF, false, false>(variant, p, grid, st);
+  }
 }
 
 hipError_t sdv_attn_launch(const SdAttnLaunch& a) {
@@ -1829,11 +1887,11 @@ hipError_t sdv_attn_launch(const SdAttnLaunch& a) {
   verify_attn_plan<<<1, kPlanThreads, 0, a.stream>>>(p, a.kv_chunk, slots, kItemOverheadBytes / (4 * a.head_dim),
                                                      cunits > kCombineGrid);
   if (a.head_dim == 128) {
-    if (a.out_f32) launch_main<128, 1>(L.variant, p, grid, a.stream);
-    else launch_main<128, 0>(L.variant, p, grid, a.stream);
+    if (a.out_f32) launch_main<128, 1>(L.variant, p, grid, a.stream, a.v_key_major);
+    else launch_main<128, 0>(L.variant, p, grid, a.stream, a.v_key_major);
   } else {
-    if (a.out_f32) launch_main<64, 1>(L.variant, p, grid, a.stream);
-    else launch_main<64, 0>(L.variant, p, grid, a.stream);
+    if (a.out_f32) launch_main<64, 1>(L.variant, p, grid, a.stream, a.v_key_major);
+    else launch_main<64, 0>(L.variant, p, grid, a.stream, a.v_key_major);
   }
   // one workgroup per (sequence, KV head, 8 rows), or for large batches a
   // bounded grid over the split sequences only (their number is known on the device)

@@ -104,6 +104,7 @@ struct SdAttnLaunch {
   void* out;
   void* workspace;
   int B, Hkv, G, head_dim, max_pages, num_pages, max_draft, out_f32, kv_chunk, total_q;
+  int v_key_major;          // 1: v_cache [P, H_kv, page, d] (like K); 0: [P, H_kv, d, page]
   float softmax_scale;
   hipStream_t stream;
 };

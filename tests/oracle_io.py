@@ -14,10 +14,16 @@ def host(t):
     return None if t is None else t.detach().cpu().numpy()
 
 
+def v_layout(inp) -> str:
+    """'key' when the V pages are stored like K ([P, H, page, d]), else 'dim'
+    ([P, H, d, page]); head_dim is never the page size here."""
+    return "key" if tuple(inp.v_cache.shape) == tuple(inp.k_cache.shape) else "dim"
+
+
 def attention_args(inp):
     return dict(q_bits=bits(inp.q), k_bits=bits(inp.k_cache), v_bits=bits(inp.v_cache),
                 block_table=host(inp.block_table), kv_len=host(inp.kv_len),
-                q_start=host(inp.q_start), group=inp.group)
+                q_start=host(inp.q_start), group=inp.group, v_layout=v_layout(inp))
 
 
 def accept_args(inp):

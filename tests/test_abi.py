@@ -37,7 +37,7 @@ def test_library_exports_every_declared_function():
 
 def _attn(**kw):
     d = dict(num_seqs=2, num_kv_heads=2, group_size=4, head_dim=64, page_size=16, max_pages_per_seq=16,
-             num_pages=40, max_draft=3, softmax_scale=0.0, out_dtype=0, kv_chunk=0)
+             num_pages=40, max_draft=3, softmax_scale=0.0, out_dtype=0, kv_chunk=0, v_layout=0)
     d.update(kw)
     return B.sd_attn_desc(**d)
 
@@ -71,6 +71,7 @@ def test_workspace_queries():
     (dict(kv_chunk=100), B.SD_ERR_INVALID_ARG, "kv_chunk"),
     (dict(softmax_scale=float("nan")), B.SD_ERR_INVALID_ARG, "softmax_scale"),
     (dict(out_dtype=7), B.SD_ERR_INVALID_ARG, "out_dtype"),
+    (dict(v_layout=2), B.SD_ERR_INVALID_ARG, "v_layout"),
 ])
 def test_attention_rejects_bad_descriptions(kw, status, needle):
     lib = sdv.lib()
@@ -268,3 +269,12 @@ def test_validate_inputs_rejects_bad_arguments(case, needle):
                                 None, None, None, args["status"], None)
     assert st != B.SD_OK
     assert needle in sdv.sd_last_error()
+
+
+def test_v_layout_from_the_cache_shape():
+    """The binding passes the V cache's page layout from its shape: [P, H, 16, d]
+    like K is key-major, [P, H, d, 16] d-major; any other shape is refused."""
+    import torch
+    k = torch.zeros(4, 2, 16, 64, dtype=torch.bfloat16)
+    assert B.v_layout_of(k, torch.zeros(4, 2, 16, 64)) == B.SD_V_KEY_MAJOR
+    assert B.v_layout_of(k, torch.zeros(4, 2, 64, 16)) == B.SD_V_DIM_MAJOR

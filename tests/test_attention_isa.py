@@ -77,7 +77,7 @@ def test_dma_sequence_saves_and_restores_m0(kernels):
                 continue
             n += 1
             save = re.match(r"s_mov_b32 (s\d+|vcc_lo|vcc_hi), m0$", ins[i - 3])
-            assert save and re.match(r"s_mov_b32 m0, s\d+$", ins[i - 2]) and ins[i - 1] == "s_nop 0", \
+            assert save and re.match(r"s_mov_b32 m0, (s\d+|vcc_lo|vcc_hi)$", ins[i - 2]) and ins[i - 1] == "s_nop 0", \
                 (name, ins[i - 3:i + 1])
             assert ins[i + 1] == f"s_mov_b32 m0, {save.group(1)}", (name, ins[i - 3:i + 2])
         assert n > 0, name

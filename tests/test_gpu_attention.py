@@ -63,6 +63,60 @@ def test_row_block_variants(G, drafts, d):
     assert err <= ATTN_TOL
 
 
+def _dim_major(inp):
+    """The same inputs with each V page stored d-major ([P, H, d, page])."""
+    x = on_gpu(inp)
+    dm = x.v_cache.transpose(2, 3).contiguous()
+    return x, dm
+
+
+@pytest.mark.parametrize("G,drafts,d,kv_chunk", [
+    (8, [0, 0], 128, 0),         # R = 8
+    (4, [3, 2], 64, 256),        # R = 16, d = 64, split
+    (8, [7, 5], 128, 0),         # R = 64
+    (8, [15, 9], 128, 256),      # R = 128 (the wave sets split the tiles)
+    (8, [16, 9], 128, 0),        # R = 136 (rows past 128 split by tile parity)
+    (8, [31, 20], 128, 256),     # R = 256 (row split)
+    (16, [15, 4], 64, 0),        # R = 256, d = 64
+])
+def test_dim_major_v_cache(G, drafts, d, kv_chunk):
+    """V pages stored d-major ([P, H_kv, d, 16]): the kernels copy the V^T
+    operand straight from the page and must give exactly the output of the
+    key-major call (transposing LDS loads; the same bf16 operands in the same
+    order), which matches the oracle; the page tails past each sequence are NaN."""
+    inp = generate(spec(batch=2, group=G, head_dim=d, kv_len=[1700, 1333], draft_len=drafts, seed=3 * G + d),
+                   poison_tail=True)
+    x, dm = _dim_major(inp)
+    say(f"case: d-major V G={G} drafts={drafts} d={d} kv_chunk={kv_chunk}")
+    ref = gpu_attention(inp, kv_chunk=kv_chunk)
+    out = torch.full(x.q.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    sdv.sd_verify_attention(x.q, x.k_cache, dm, x.block_table, x.kv_len, x.q_start, out, group_size=inp.group,
+                            max_draft=inp.max_draft, kv_chunk=kv_chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    err = compare_attention(inp, out)
+    say(f"max|err| = {err:.3e}")
+    assert err <= ATTN_TOL
+
+
+def test_dim_major_v_cache_full_size():
+    """The benchmarked default shape with a d-major V cache: bit-identical to
+    the key-major call and equal to the oracle on every element."""
+    sp = preset("g8_kv32k_D15")
+    inp = generate(sp, device="cuda")
+    say(f"case: full size {sp.name}, d-major V")
+    ref = gpu_attention(inp)
+    dm = inp.v_cache.transpose(2, 3).contiguous()
+    out = torch.full(inp.q.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    sdv.sd_verify_attention(inp.q, inp.k_cache, dm, inp.block_table, inp.kv_len, inp.q_start, out,
+                            group_size=inp.group, max_draft=inp.max_draft)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    err = compare_attention(inp, out)
+    say(f"max|err| = {err:.3e}")
+    assert err <= ATTN_TOL
+
+
 @pytest.mark.parametrize("drafts", [[16, 12, 2], [23, 19, 17], [31, 25, 0]])
 def test_long_items_every_row_block(drafts):
     """Items of thousands of keys (the unrolled steady loop runs many groups) at

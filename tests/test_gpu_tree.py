@@ -95,6 +95,23 @@ def test_split_boundary_inside_the_tree(kind, G, kv_chunk):
     assert err <= ATTN_TOL
 
 
+@pytest.mark.parametrize("G,drafts,kv_chunk", [(1, [63, 40, 2], 64), (8, [15, 9, 4], 0), (4, [63, 31, 1], 128)])
+def test_tree_dim_major_v_cache(G, drafts, kv_chunk):
+    """Tree attention over a d-major V cache equals the key-major call bit for bit."""
+    inp = generate(_spec(group=G, draft_len=drafts, kv_len=[1087, 900, 2500], seed=50 + G))
+    par = _parents(attention_args(inp)["q_start"], "random", np.random.default_rng(51))
+    x = inp.to("cuda")
+    dm = x.v_cache.transpose(2, 3).contiguous()
+    say(f"case: tree d-major V G={G} drafts={drafts} kv_chunk={kv_chunk}")
+    ref = _tree_attention(x, par, kv_chunk)
+    out = torch.full(x.q.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    sdv.sd_verify_tree_attention(x.q, x.k_cache, dm, x.block_table, x.kv_len, x.q_start,
+                                 torch.from_numpy(par).cuda(), out, group_size=inp.group, max_draft=inp.max_draft,
+                                 kv_chunk=kv_chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
 @pytest.mark.parametrize("G,drafts", [(8, [3, 1, 7]), (8, [15, 9, 4]), (8, [31, 20, 5])])
 def test_tree_workspace_contents_never_matter(G, drafts):
     """The tree masks and the plan are written by the call before they are

@@ -166,3 +166,29 @@ def test_rejects_bad_page_ids():
     bt[0, 1] = c["kc"].shape[0]
     with pytest.raises(ValueError):
         verify_attention(c["q"], c["kc"], c["vc"], bt, c["kv_len"], c["q_start"], 1)
+
+
+def test_key_major_and_dim_major_v_pages_give_the_same_result():
+    """The oracle reads V by (page, head, slot, dimension) from either page
+    layout: a cache whose V pages are stored key-major ([P, H, page, d], like K,
+    v_layout 'key') gives exactly the output of the same cache stored d-major."""
+    rng = np.random.default_rng(11)
+    for d, G, kv, drafts in ((64, 2, [40, 17, 300], [3, 0, 7]), (128, 4, [1000, 33], [15, 2])):
+        B = len(kv)
+        q_start = np.concatenate([[0], np.cumsum(np.asarray(drafts) + 1)]).astype(np.int32)
+        T = int(q_start[-1])
+        npg = [-(-n // 16) for n in kv]
+        P = sum(npg) + 3
+        perm = rng.permutation(P).astype(np.int32)
+        bt = np.zeros((B, max(npg)), np.int32)
+        o = 0
+        for b in range(B):
+            bt[b, :npg[b]] = perm[o:o + npg[b]]
+            o += npg[b]
+        k = rng.integers(0, 1 << 16, size=(P, 2, 16, d), dtype=np.uint32).astype(np.uint16) & 0xBFFF
+        v_dm = rng.integers(0, 1 << 16, size=(P, 2, d, 16), dtype=np.uint32).astype(np.uint16) & 0xBFFF
+        q = rng.integers(0, 1 << 16, size=(T, 2 * G, d), dtype=np.uint32).astype(np.uint16) & 0xBFFF
+        args = dict(q_bits=q, k_bits=k, block_table=bt, kv_len=np.asarray(kv, np.int32), q_start=q_start, group=G)
+        a = verify_attention(v_bits=v_dm, **args)
+        b_ = verify_attention(v_bits=np.ascontiguousarray(v_dm.transpose(0, 1, 3, 2)), v_layout="key", **args)
+        np.testing.assert_array_equal(a, b_)

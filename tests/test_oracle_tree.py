@@ -63,7 +63,7 @@ def test_star_tree_matches_sdpa_on_gathered_keys():
         t0, t1 = int(qs[b]), int(qs[b + 1])
         T = t1 - t0 - 1
         K = _sequence_keys(a["k_bits"], a["block_table"][b], n, 0)
-        V = _sequence_values(a["v_bits"], a["block_table"][b], n, 0)
+        V = _sequence_values(a["v_bits"], a["block_table"][b], n, 0, a["v_layout"])
         first = n - 1 - T
         for i in range(T + 1):
             keys = list(range(first + 1)) + ([first + i] if i > 0 else [])

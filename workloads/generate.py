@@ -11,7 +11,8 @@ tensors (which is what the tests and the benchmark do).
 Layouts (the ones the C ABI takes):
   q            bf16  [T_q, H_kv*G, d]      row q_start[b]+i is position i of seq b
   k_cache      bf16  [P, H_kv, page, d]    one (page, head) block is contiguous
-  v_cache      bf16  [P, H_kv, d, page]    each page stored d-major (V^T of its 16 keys)
+  v_cache      bf16  [P, H_kv, page, d]    like K (spec.v_layout "key", the default), or
+                     [P, H_kv, d, page]    each page stored d-major (V^T of its 16 keys; "dim")
   block_table  int32 [B, max_pages]        -1 past each sequence's last page
   kv_len       int32 [B]                   keys of seq b, including its 1+D_b block
   q_start      int32 [B+1]                 seq b owns rows q_start[b] .. q_start[b+1]-1
@@ -71,6 +72,7 @@ class WorkloadSpec:
     alpha: Optional[float] = None
     draft_pick: str = "sample"         # "sample" from q, or "argmax" of the draft logits
     extra_pool_pages: int = 0          # unused pages mixed into the shared pool
+    v_layout: str = "key"              # V pages key-major like K ("key") or d-major ("dim")
     seed: int = 0
 
     def with_(self, **kw) -> "WorkloadSpec":
@@ -196,8 +198,12 @@ def generate(spec: WorkloadSpec, device="cpu", poison_tail: bool = False) -> Ver
 
     q = _randn_bf16((max(T_q, 0), Hq, d), _gen(spec.seed, "q", device), device)
     k_cache = _randn_bf16((pool, Hkv, ps, d), _gen(spec.seed, "k", device), device)
-    # values are drawn key-major and stored d-major per page: the logical V is the same draw
-    v_cache = _randn_bf16((pool, Hkv, ps, d), _gen(spec.seed, "v", device), device).transpose(2, 3).contiguous()
+    # values are drawn key-major; "dim" stores each page transposed (the logical V is the same draw)
+    if spec.v_layout not in ("key", "dim"):
+        raise ValueError(f"v_layout {spec.v_layout!r}: 'key' or 'dim'")
+    v_cache = _randn_bf16((pool, Hkv, ps, d), _gen(spec.seed, "v", device), device)
+    if spec.v_layout == "dim":
+        v_cache = v_cache.transpose(2, 3).contiguous()
     if poison_tail:
         kb = k_cache.view(torch.int16)
         vb = v_cache.view(torch.int16)
@@ -206,7 +212,10 @@ def generate(spec: WorkloadSpec, device="cpu", poison_tail: bool = False) -> Ver
             if n % ps:
                 page = int(bt[b, (n - 1) // ps])
                 kb[page, :, n % ps:, :] = BF16_NAN_BITS
-                vb[page, :, :, n % ps:] = BF16_NAN_BITS
+                if spec.v_layout == "dim":
+                    vb[page, :, :, n % ps:] = BF16_NAN_BITS
+                else:
+                    vb[page, :, n % ps:, :] = BF16_NAN_BITS
 
     target = torch.randn((T_q, V), generator=_gen(spec.seed, "target", device), device=device,
                          dtype=torch.float32) * spec.target_std
