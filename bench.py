@@ -271,6 +271,18 @@ def _per_dispatch(d: str):
     return per
 
 
+def workload_args(cfg) -> str:
+    """The bench.py options that select the workload of a bench line's config."""
+    from workloads import PRESETS
+    wl = cfg["workload"]
+    for key, v in PRESETS.items():
+        if v.name == wl:
+            return "" if key == "g8_kv32k_D15" else f" --workload {key}"
+        if v.name.endswith("_sweep") and v.name.replace("_sweep", f"_D{cfg.get('draft_len')}") == wl:
+            return f" --workload {key} --draft {cfg['draft_len']}"
+    raise SystemExit(f"workload {wl} is not a preset")
+
+
 def write_profiles(bench_json: str, kt_dir: str, fetch_dir: str, write_dir: str, copy_bytes: int):
     """Write the kernel-time and HBM-traffic summaries under profiles/ from one
     bench.py JSON line and three rocprofv3 runs of bench.py (kernel trace with
@@ -281,13 +293,11 @@ def write_profiles(bench_json: str, kt_dir: str, fetch_dir: str, write_dir: str,
         line = json.loads(f.read().strip().splitlines()[-1])
     cfg = line["config"]
     wl = cfg["workload"]
-    from workloads import PRESETS
-    key = next((k for k, v in PRESETS.items() if v.name == wl), None)
-    args = "--no-cpu-baseline" + ("" if key in (None, "g8_kv32k_D15") else f" --workload {key}")
+    args = "--no-cpu-baseline" + workload_args(cfg)
     # kernel-time summary: the library's kernels only
     stats = [r for r in _rocprof_csv(kt_dir, "kernel_stats") if "sdv::" in r["Name"]]
     calls = int(stats[0]["Calls"]) if stats else 0
-    main = max(stats, key=lambda r: float(r["TotalDurationNs"]))
+    main = max((r for r in stats if "verify_attn" in r["Name"]), key=lambda r: float(r["TotalDurationNs"]))
     prof = os.path.join(ROOT, "profiles")
     with open(os.path.join(prof, f"verify_step_{wl}_kernel_stats.txt"), "w") as f:
         f.write(f"# rocprofv3 kernel-trace summary of the library's kernels, workload {wl}:\n"
@@ -326,7 +336,7 @@ def write_profiles(bench_json: str, kt_dir: str, fetch_dir: str, write_dir: str,
         for c in ("FETCH_SIZE", "WRITE_SIZE"):
             f.write(f"$ cd /tmp && export TMPDIR=/tmp && timeout -s KILL 90 rocprofv3 --pmc {c} --kernel-trace "
                     f"-d OUT/pmc_{c.split('_')[0].lower()} -o run --output-format csv -- python3 "
-                    f"REPO/bench.py {args} --steps 5 --warmup 2 --calibrate-copy {copy_bytes}\n")
+                    f"REPO/bench.py {args} --settle-s 0 --steps 5 --warmup 2 --calibrate-copy {copy_bytes}\n")
         f.write(f"kernel: {short}\n"
                 f"attention_source_sha256: {attention_source_digest()}\n"
                 f"fetch_kib_per_launch: {fk:.1f}\nwrite_kib_per_launch: {wk:.1f}\n"
