@@ -102,6 +102,12 @@ typedef struct {
 /*
  * Workspace bytes sd_verify_attention needs for this description and
  * total_q = sum_b (1+D_b) verify rows.  Returns 0 for an invalid description.
+ * The size does not depend on the KV lengths: the split of the keys into work
+ * items is planned on the device at every call, within an item budget fixed
+ * by B, H_kv and the GPU's compute-unit count, so one workspace serves every
+ * call of the same shape however the caches grow.  total_q is an argument of
+ * the calls too, so that the host can check the row count against the
+ * workspace without reading q_start from the device.
  */
 size_t sd_verify_attention_workspace_size(const sd_attn_desc* desc, int32_t total_q);
 
@@ -233,8 +239,13 @@ size_t sd_verify_step_workspace_size(const sd_attn_desc* attn, const sd_accept_d
                                      int32_t total_q);
 
 /*
- * One verify step: sd_verify_attention followed by sd_accept_reject on the
- * same stream, sharing one workspace.  attn->num_seqs must equal
+ * One verify step: the target scores all 1+D_b positions of every sequence in
+ * one pass and the drafts are accepted or rejected against those scores in
+ * the same step ("How does speculative decoding speed up LLM inference?",
+ * section "Mechanism", Verify step).  Here: sd_verify_attention followed by
+ * sd_accept_reject on the same stream, sharing one workspace (the target
+ * logits come from the caller's LM head between the two in a full model;
+ * the call takes them as an input).  attn->num_seqs must equal
  * acc->num_seqs; arguments are as in the two calls above.
  */
 sd_status sd_verify_step(const sd_attn_desc* attn, const sd_accept_desc* acc, int32_t total_q,
@@ -327,9 +338,9 @@ sd_status sd_tree_accept(const sd_accept_desc* desc, int32_t total_q, const floa
  * receive the tokens appended per sequence and the D of each round.
  *
  * Unlike the other calls this one waits for the stream once per round (to
- * read the acceptance lengths), and with use_graphs != 0 it creates, captures
- * and destroys one graph per tier on a stream of its own (graph objects are
- * the only resources it creates).  tiers: 1..8 strictly ascending values in
+ * read the acceptance lengths), and with use_graphs != 0 it creates a
+ * non-blocking capture stream and one graph per tier, and destroys all of
+ * them before it returns (it allocates no device memory).  tiers: 1..8 strictly ascending values in
  * [0, 63]; ngram in [1, 8]; vocab <= 65536; ema_weight in (0, 1].
  */
 #define SD_LOOP_MAX_TIERS 8

@@ -15,8 +15,6 @@
 //                        max (greedy: lowest-index argmax; stochastic: sum of
 //                        exp(x - max) accumulated in fp64).  One pass over every
 //                        target (and draft) row: this is the step's HBM cost.
-//                        (Stochastic: also clears the per-sequence arrival
-//                        counters used by kernel 2b.)
 //   2a. accept_decide    greedy: one workgroup per sequence merges the chunk
 //                        argmaxes of its 1+D rows, compares the drafts, and
 //                        writes AL, the accepted tokens and the correction.
@@ -24,12 +22,15 @@
 //                        workgroup takes the sequence's decision itself (fp64
 //                        log-normalisers merged from the chunk statistics, the
 //                        D tests in fp64, the first failure n); workgroup 0
-//                        writes AL and the accepted tokens.  Each workgroup
-//                        then sums its chunk of the residual max(0, p - q) at
-//                        row n (of p at row D when every draft passed) in fp64,
-//                        per thread (16 consecutive tokens) and per chunk; the
-//                        last to finish finds the first prefix sum > u*Z by
-//                        chunk, then 16-token slice, then token.
+//                        writes AL, the accepted tokens and the decision.  Each
+//                        workgroup then sums its chunk of the residual
+//                        max(0, p - q) at row n (of p at row D when every
+//                        draft passed) in fp64, per thread (16 consecutive
+//                        tokens) and per chunk.
+//   2c. accept_draw      stochastic: one workgroup per sequence finds the first
+//                        prefix sum > u*Z by chunk, then 16-token slice, then
+//                        token.  The kernel boundary orders the sums before
+//                        their reads (no hand-off between workgroups).
 
 #include <limits.h>
 #include <algorithm>
@@ -66,6 +67,11 @@ struct SeqState {
   double lse_q;     // log-normaliser of the draft row n (residual only)
 };
 
+struct SeqRec {      // a sequence's decision, from accept_finish to accept_draw
+  double lse_p, lse_q;
+  int n, pad;
+};
+
 struct AccParams {
   const float* target;
   const float* draft;
@@ -75,7 +81,7 @@ struct AccParams {
   int* accept_len;
   int* out_tokens;
   RowPart* part;      // [rows, nchunk]
-  unsigned* arrived;  // [B] sampling workgroups done (cleared by accept_rowstats)
+  SeqRec* seqrec;     // [B] decisions of the stochastic sequences
   double* rsum;       // [B, nschunk, 2]  (residual, p) chunk sums
   double* rsub;       // [B, nschunk, 256, 2]  (residual, p) sums of each thread's 16 tokens
   // relaxed acceptance only
@@ -184,8 +190,6 @@ __global__ __launch_bounds__(kAccThreads) void accept_rowstats(AccParams p) {
   __shared__ double sd[4];
   const int row = blockIdx.x / p.nchunk;
   const int c = blockIdx.x - row * p.nchunk;
-  if (MODE != 0 && p.arrived && blockIdx.x == 0)
-    for (int i = threadIdx.x; i < p.B; i += kAccThreads) p.arrived[i] = 0u;
   const float* src = row < p.T ? p.target + (size_t)row * p.V : p.draft + (size_t)(row - p.T) * p.V;
   const int tid = threadIdx.x;
   const int j0 = c * kChunk;
@@ -542,9 +546,9 @@ __device__ __forceinline__ double row_lse16(const AccParams& p, int prow, int la
 // ---------------------------------------------------------------------------
 template <bool LOSSY>
 __global__ __launch_bounds__(kAccThreads) void accept_finish(AccParams p) {
-  __shared__ double sd[4], s_wtot[4];
-  __shared__ int s_fail, s_have, s_last, s_chunk, s_usep, s_slice, s_slice_last;
-  __shared__ double s_lp, s_lq, s_base, s_slice_base, s_T;
+  __shared__ double sd[4];
+  __shared__ int s_fail, s_have;
+  __shared__ double s_lp, s_lq;
   const int c = blockIdx.x;
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
@@ -604,12 +608,15 @@ __global__ __launch_bounds__(kAccThreads) void accept_finish(AccParams p) {
     const double lq = n < D ? row_lse16(p, p.T + d0 + n, lane16) : 0.0;
     if (lane16 == 0) { s_lp = lp; s_lq = lq; }
   }
+  __syncthreads();
   if (c == 0) {
     for (int k = tid; k <= D; k += kAccThreads)
-      if (k != n) p.out_tokens[t0 + k] = k < n ? p.tokens[d0 + k] : -1;   // k == n: the sample, below
-    if (tid == 0) p.accept_len[b] = n + 1;
+      if (k != n) p.out_tokens[t0 + k] = k < n ? p.tokens[d0 + k] : -1;   // k == n: the sample (accept_draw)
+    if (tid == 0) {
+      p.accept_len[b] = n + 1;
+      p.seqrec[b] = SeqRec{s_lp, n < D ? s_lq : 0.0, n, 0};
+    }
   }
-  __syncthreads();
   SeqState st;
   st.n = n;
   st.residual = n < D;
@@ -620,11 +627,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_finish(AccParams p) {
   // Thread t takes the 16 consecutive logits j0 .. j0+15 of a chunk (all
   // loaded before any arithmetic): the weight of token j is max(0, p_j - q_j)
   // at a rejection, p_j when every draft passed.  The thread publishes its own
-  // sums (residual, p) and the workgroup the chunk's.  Hand-off between
-  // workgroups of one sequence, possibly on different XCDs (separate L2s): the
-  // sums are agent-scope atomic stores, which are coherent across XCDs, and
-  // each is complete (vmcnt 0) before the arrival count.  A release fence would
-  // do the same by writing back the whole L2.
+  // sums (residual, p) and the workgroup the chunk's, for accept_draw.
   const float* prow = p.target + (size_t)(t0 + n) * p.V;
   const float* qrow = p.draft + (size_t)(d0 + (n < D ? n : 0)) * p.V;
   for (int c = blockIdx.x; c < p.nschunk; c += gridDim.x) {
@@ -655,31 +658,43 @@ __global__ __launch_bounds__(kAccThreads) void accept_finish(AccParams p) {
       tp += pj;
     }
     double* dst = p.rsub + (((size_t)b * p.nschunk + c) * kAccThreads + tid) * 2;
-    __hip_atomic_store(dst, tw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(dst + 1, tp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *(f64x2*)dst = f64x2{tw, tp};
     const double zw = block_sum(tw, sd);
     const double zp = block_sum(tp, sd);
     if (tid == 0) {
       double* cs = p.rsum + ((size_t)b * p.nschunk + c) * 2;
-      __hip_atomic_store(cs, zw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(cs + 1, zp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *(f64x2*)cs = f64x2{zw, zp};
     }
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned prev = __hip_atomic_fetch_add(&p.arrived[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = prev == gridDim.x - 1;
-  }
-  __syncthreads();
-  if (!s_last) return;
+}
 
-  // (2) the last workgroup of the sequence draws the token: the first token
-  // whose inclusive prefix sum of weights exceeds T = u * Z, found in three
-  // levels (chunk, 16-token slice, token).  Where rounding leaves T past every
-  // prefix of a level, the level takes its last element with weight > 0.
+// ---------------------------------------------------------------------------
+// (2) one workgroup per stochastic sequence draws the token from the sums
+// accept_finish left: the first token whose inclusive prefix sum of weights
+// exceeds T = u * Z, found in three levels (chunk, 16-token slice, token).
+// Where rounding leaves T past every prefix of a level, the level takes its
+// last element with weight > 0.
+__global__ __launch_bounds__(kAccThreads) void accept_draw(AccParams p) {
+  __shared__ double s_wtot[4];
+  __shared__ int s_chunk, s_usep, s_slice, s_slice_last;
+  __shared__ double s_base, s_slice_base, s_T;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int t0 = p.q_start[b];
+  const int D = seq_d(p, b);
+  const int d0 = t0 - b;
+  if (!seq_ok(p, t0, D, d0)) return;   // (accept_finish wrote AL = 0)
+  const SeqRec rec = p.seqrec[b];
+  const int n = min(max(rec.n, 0), D);
+  SeqState st;
+  st.n = n;
+  st.residual = n < D;
+  st.lse_p = rec.lse_p;
+  st.lse_q = rec.lse_q;
+  const float* prow = p.target + (size_t)(t0 + n) * p.V;
+  const float* qrow = p.draft + (size_t)(d0 + (n < D ? n : 0)) * p.V;
   const int lane = tid & 63, wave = tid >> 6;
-  auto ld = [](const double* a) { return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+  auto ld = [](const double* a) { return *a; };
   if (wave == 0) {
     // level 1 (one wave): totals, T, and the chunk
     const double* rs = p.rsum + (size_t)b * p.nschunk * 2;
@@ -756,7 +771,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_finish(AccParams p) {
 }
 
 struct AccLayout {
-  size_t part_off, arrived_off, rsum_off, rsub_off, ent_off, jsp_off, total;
+  size_t part_off, seqrec_off, rsum_off, rsub_off, ent_off, jsp_off, total;
   int nchunk, nschunk;
 };
 
@@ -772,7 +787,7 @@ static AccLayout acc_layout(int B, int T, int V, int stochastic, int lossy) {
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += (bytes + 255) / 256 * 256; return o; };
   L.part_off = take(rows * L.nchunk * sizeof(RowPart));
-  L.arrived_off = take((size_t)B * sizeof(unsigned));
+  L.seqrec_off = take(stochastic ? (size_t)B * sizeof(SeqRec) : 0);
   L.rsum_off = take((size_t)B * L.nschunk * 2 * sizeof(double));
   L.rsub_off = take(stochastic ? (size_t)B * L.nschunk * kAccThreads * 2 * sizeof(double) : 0);
   L.ent_off = take(lossy ? drows * L.nchunk * sizeof(double) : 0);
@@ -801,7 +816,7 @@ hipError_t sdv_accept_launch(const SdAccLaunch& a) {
   p.accept_len = a.accept_len;
   p.out_tokens = a.out_tokens;
   p.part = (RowPart*)(ws + L.part_off);
-  p.arrived = (unsigned*)(ws + L.arrived_off);
+  p.seqrec = (SeqRec*)(ws + L.seqrec_off);
   p.rsum = (double*)(ws + L.rsum_off);
   p.rsub = (double*)(ws + L.rsub_off);
   p.ent = a.lossy ? (double*)(ws + L.ent_off) : nullptr;
@@ -844,6 +859,7 @@ hipError_t sdv_accept_launch(const SdAccLaunch& a) {
     const int per_seq = std::max(1, std::min(L.nschunk, (kFinishWGs + a.B - 1) / std::max(a.B, 1)));
     if (a.lossy) accept_finish<true><<<dim3(per_seq, a.B), kAccThreads, 0, a.stream>>>(p);
     else accept_finish<false><<<dim3(per_seq, a.B), kAccThreads, 0, a.stream>>>(p);
+    accept_draw<<<a.B, kAccThreads, 0, a.stream>>>(p);
   } else {
     const size_t lds = (size_t)(a.max_draft + 1) * sizeof(int);
     if (a.lossy) accept_decide<true><<<a.B, kAccThreads, lds, a.stream>>>(p);
@@ -864,7 +880,7 @@ hipError_t sdv_tree_accept_launch(const SdAccLaunch& a, const int32_t* parents, 
   p.accept_len = a.accept_len;
   p.out_tokens = a.out_tokens;
   p.part = (RowPart*)(ws + L.part_off);
-  p.arrived = (unsigned*)(ws + L.arrived_off);
+  p.seqrec = nullptr;
   p.rsum = nullptr;
   p.rsub = nullptr;
   p.ent = p.jsp = nullptr;

@@ -1281,15 +1281,12 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
 #pragma unroll
       for (int c = 0; c < NKS; ++c) {
         u32x4 raw = valid ? *(const u32x4*)(qp + c * 16) : u32x4{0, 0, 0, 0};
-        bf16x8 t = __builtin_bit_cast(bf16x8, raw);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) t[e] = (__bf16)((float)t[e] * p.scale_log2);
-        qf[c] = t;
+        qf[c] = __builtin_bit_cast(bf16x8, raw);
       }
     }
     float m_run = -INFINITY;
     float m_off = 0.f;
-    f32x16 mneg;                   // fast pass: -(reference max) in every entry, the score chains' initial value
+    f32x16 mneg;                   // fast pass: -(reference max)/scale in every entry, the score chains' initial value
     float l_run;                   // this lane's share of its row sum (its 16 of each tile's 32 keys);
                                    // the row's sum adds the partner lane l ^ 32
     f32x16 o[NMB];
@@ -1333,16 +1330,18 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
 #pragma unroll
       for (int e = 1; e < 16; ++e) m = fmaxf(m, sc[e]);
       auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-      mt = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+      mt = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1])) * p.scale_log2;   // (scale > 0)
       return mt > m_run + slack;
     };
-    // S^T of the set's tile at stage offset `off`, in log2 units (Q carries the
-    // scale).  PRE (fast pass after the first step): one chain that starts from
-    // mneg, so the MFMAs leave the scores less the reference max and P needs no
-    // VALU operation before the exp.  Otherwise two chains from zero, whose sum
-    // takes one add per score.  (With two waves per SIMD the other wave's MFMAs
-    // fill the single chain's dependency stalls: measured, one chain with no
-    // adds beats two chains by 1-3%.)
+    // S^T = K Q^T of the set's tile at stage offset `off`, unscaled (Q stays the
+    // exact bf16 input; the fp32 scale scale*log2(e) is applied to each fp32
+    // score before the exp).  PRE (fast pass after the first step): one chain
+    // that starts from mneg = -(reference max)/scale, so the MFMAs leave the
+    // scores less the reference max and P = 2^(scale * s) takes one multiply.
+    // Otherwise two chains from zero, whose sum takes one add per score.  (With
+    // two waves per SIMD the other wave's MFMAs fill the single chain's
+    // dependency stalls: measured, one chain with no adds beats two chains by
+    // 1-3%.)
     auto scores = [&](int off, auto prec) {
       if constexpr (decltype(prec)::value) {
         f32x16 s0 = mneg;
@@ -1364,10 +1363,10 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
       }
       sc = s0 + s1;
     };
-    // P = 2^(score - reference max) in bf16 (PRE: the scores already hold the difference)
+    // P = 2^(scale * score - reference max) in bf16 (PRE: the scores already hold the difference, unscaled)
     auto p_of = [&](float x, auto prec) {
-      if constexpr (decltype(prec)::value) return (__bf16)fast_exp2(x);
-      else return (__bf16)fast_exp2(x + m_off);
+      if constexpr (decltype(prec)::value) return (__bf16)fast_exp2(x * p.scale_log2);
+      else return (__bf16)fast_exp2(fmaf(x, p.scale_log2, m_off));
     };
     // P from the scores, then O^T += V^T P^T at stage offset `off`, and the
     // lane's share of l from the same bf16 P (dot products with (1, 1))
@@ -1420,8 +1419,8 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
         const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
         for (int e = q * w; e < (q + 1) * w; e += 2) {
-          pf[e / 8][e % 8] = (__bf16)fast_exp2(sv[e]);
-          pf[e / 8][e % 8 + 1] = (__bf16)fast_exp2(sv[e + 1]);
+          pf[e / 8][e % 8] = (__bf16)fast_exp2(sv[e] * p.scale_log2);
+          pf[e / 8][e % 8 + 1] = (__bf16)fast_exp2(sv[e + 1] * p.scale_log2);
           l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[e / 8][e % 8], pf[e / 8][e % 8 + 1]}, one2, l_run, false);
         }
         asm volatile("" ::"v"(l_run));   // the sums stay in their slot (sunk, they would hold P live)
@@ -1473,7 +1472,7 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-              for (int e = 0; e < 8; ++e) pv2[ks][e] = (__bf16)fast_exp2(sv[ks * 8 + e]);
+              for (int e = 0; e < 8; ++e) pv2[ks][e] = (__bf16)fast_exp2(sv[ks * 8 + e] * p.scale_log2);
             const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
@@ -1560,7 +1559,7 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
     const int ngroups = (plain - 1) / (S / 2);
     if (nsteps > 0) step_generic(0, std::false_type{});
 #pragma unroll
-    for (int e = 0; e < 16; ++e) mneg[e] = m_off;
+    for (int e = 0; e < 16; ++e) mneg[e] = m_off / p.scale_log2;
     // (ROLE: 0 idle, 1 one tile per step, 2 both tiles)
     auto fast_steady = [&](auto rolec) {
       constexpr int ROLE = decltype(rolec)::value;
