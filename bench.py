@@ -283,6 +283,33 @@ def workload_args(cfg) -> str:
     raise SystemExit(f"workload {wl} is not a preset")
 
 
+def write_bench_lines(*bench_jsons):
+    """profiles/ table of bench lines (one per workload, each with its oracle
+    baseline and parity), followed by the lines themselves and their commands."""
+    rows, body = [], []
+    for path in bench_jsons:
+        with open(path) as f:
+            line = json.loads(f.read().strip().splitlines()[-1])
+        cfg, r, c, pa = line["config"], line["roofline"], line["cpu_baseline"], line["parity"]["attention"]
+        rows.append(f"{cfg['workload'][:52]:52s} {line['value']:10.4g} {line['step_us']:8.1f} "
+                    f"{line['attention_ms'] * 1e3:8.1f} {line['accept_ms'] * 1e3:7.1f} {r['frac']:6.3f} "
+                    f"{r['mfma_frac']:6.3f} {c['value']:10.4g} "
+                    f"{str(pa['units_compared']) + '/' + str(pa['units_total']):>12s} {pa['max_abs_err']:9.2e} "
+                    f"{str(line['parity']['ok']):>6s}")
+        body += [f"$ python3 REPO/bench.py{workload_args(cfg)}", json.dumps(line), ""]
+    path = os.path.join(ROOT, "profiles", "verify_step_bench_lines_all_workloads.txt")
+    with open(path, "w") as f:
+        f.write("# bench.py lines of every workload (one MI355X, inputs resident in HBM, median of 20 timed steps,\n"
+                "# 1 GiB cache flush before each step outside the timed events), each with its oracle baseline on\n"
+                "# the box's 16-core host share and the element-by-element parity of the oracle units it ran\n"
+                "# against the GPU outputs of the same call.  hbm / mfma: algorithmic attention bytes / flops over\n"
+                "# the whole attention call (plan + main + combine) against 8 TB/s and 2.5 PFLOP/s bf16.\n\n")
+        f.write(f"{'workload':52s} {'tok/s':>10s} {'step_us':>8s} {'attn_us':>8s} {'acc_us':>7s} {'hbm':>6s} "
+                f"{'mfma':>6s} {'cpu tok/s':>10s} {'units':>12s} {'max_err':>9s} {'parity':>6s}\n")
+        f.write("\n".join(rows) + "\n\n" + "\n".join(body))
+    print(f"wrote {path}")
+
+
 def write_profiles(bench_json: str, kt_dir: str, fetch_dir: str, write_dir: str, copy_bytes: int):
     """Write the kernel-time and HBM-traffic summaries under profiles/ from one
     bench.py JSON line and three rocprofv3 runs of bench.py (kernel trace with
@@ -752,9 +779,10 @@ def write_lossy_profile(bench_json: str, kt_dir: str):
     with open(path, "w") as f:
         f.write(f"# rocprofv3 kernel-trace summary of the accept kernels, workload {wl} (tau = "
                 f"{line['config']['js_threshold']}):\n"
-                "# each step runs the lossless call (accept_rowstats<1,...>, accept_finish<false>) and the relaxed\n"
-                "# call (accept_rowstats<2,...>, accept_jsd, accept_finish<true>).  Calls = clock-settle + warmup +\n"
-                "# timed steps.  Durations in ns.\n"
+                "# each step runs the lossless call (accept_rowstats<1,...>, accept_finish<false>, accept_draw) and\n"
+                "# the relaxed call (accept_rowstats<2,...>, accept_jsd, accept_finish<true>, accept_draw; the draw\n"
+                "# kernel is the same in both, so its line counts two launches per step).  Calls = clock-settle +\n"
+                "# warmup + timed steps.  Durations in ns.\n"
                 "$ cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d OUT/kt_lossy "
                 "-o run --output-format csv -- python3 REPO/bench.py --lossy\n")
         f.write("Name,Calls,TotalDurationNs,AverageNs,Percentage,MinNs,MaxNs,StdDev\n")
@@ -762,8 +790,8 @@ def write_lossy_profile(bench_json: str, kt_dir: str):
             f.write(",".join([r["Name"], r["Calls"], r["TotalDurationNs"], r["AverageNs"], r["Percentage"],
                               r["MinNs"], r["MaxNs"], r["StdDev"]]) + "\n")
         lossy = sum(float(r["AverageNs"]) for r in stats if "<2" in r["Name"] or "jsd" in r["Name"]
-                    or "finish<true>" in r["Name"])
-        f.write(f"relaxed accept call (rowstats<2> + jsd + finish<true> averages): {lossy / 1e3:.1f} us\n")
+                    or "finish<true>" in r["Name"] or "accept_draw" in r["Name"])
+        f.write(f"relaxed accept call (rowstats<2> + jsd + finish<true> + draw averages): {lossy / 1e3:.1f} us\n")
         f.write(f"bench.py in the same call: relaxed accept {line['lossy_accept_ms'] * 1e3:.1f} us/step, lossless "
                 f"{line['lossless_accept_ms'] * 1e3:.1f} us/step (HIP events), HBM {line['roofline']['frac']:.3f} "
                 f"of peak, mean AL {line['mean_accept_len']:.3f} (lossless {line['mean_accept_len_lossless']:.3f})\n")
@@ -1218,6 +1246,8 @@ def main():
     ap.add_argument("--write-probe-profile", metavar="PROBE_JSON", help="write the profiles/ summary of a --probe line")
     ap.add_argument("--write-counter-profile", nargs="+", metavar="ARG",
                     help="LABEL 'BENCH_ARGS' PASS_DIR...: write the profiles/ counter summary of the attention kernel")
+    ap.add_argument("--write-bench-lines", nargs="+", metavar="BENCH_JSON",
+                    help="write the profiles/ table of bench lines, one per workload (no GPU)")
     ap.add_argument("--write-lossy-profile", nargs=2, metavar=("BENCH_JSON", "KT_DIR"),
                     help="write the profiles/ summary of a --lossy line and its rocprofv3 kernel trace (no GPU)")
     args = ap.parse_args()
@@ -1232,6 +1262,9 @@ def main():
         return
     if args.write_lossy_profile:
         write_lossy_profile(*args.write_lossy_profile)
+        return
+    if args.write_bench_lines:
+        write_bench_lines(*args.write_bench_lines)
         return
     if args.write_loop_profile:
         write_loop_profile(*args.write_loop_profile)

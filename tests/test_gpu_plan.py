@@ -3,8 +3,11 @@ split-KV chunk it picks and the item and split-sequence counts it writes to the
 head of the workspace, against the selection rule evaluated here directly (one
 division per candidate chunk and sequence), on batches whose sequences are all
 short, all long, mixed, or longer than the plan's LDS list of long sequences
-holds; and the attention output of the same calls against the oracle on
-sampled (sequence, head) units.
+holds; the work-item descriptors it writes (every (sequence, KV head, split)
+exactly once, with its key range and fields, full-chunk items first, then the
+shorter items longest first by length bucket, and the natural item index of
+each sequence); and the attention output of the same calls against the oracle
+on sampled (sequence, head) units.
 
 The plan's chunk rule: candidates c(t), t < 256: 256 + 64 t keys for t < 240,
 then 16384 + 1024 (t - 240) and 32768 for t = 255 (capped at the longest
@@ -81,7 +84,34 @@ def run_and_read_plan(inp, kv_chunk=0):
     torch.cuda.synchronize()
     # the plan header sits at the start of the workspace: chunk, items, full-chunk items, split sequences
     head = ws[:16].view(torch.int32).cpu().numpy()
-    return out, int(head[0]), int(head[1]), int(head[3])
+    return out, int(head[0]), int(head[1]), int(head[3]), ws
+
+
+def check_items(ws, inp, chunk, items):
+    """The descriptors the plan wrote: 8 int32 each (b, h, k_begin, k_end, t0,
+    D, N, nsplit) in schedule order after the plan header and its 3B+1 ints,
+    rounded up to 256 bytes; item_start[b] at int 16 + b."""
+    B, hkv = inp.spec.batch, inp.spec.kv_heads
+    off = -(-(16 + 3 * B + 1) * 4 // 256) * 256 // 4
+    words = ws[:4 * (off + 8 * items)].view(torch.int32).cpu().numpy()
+    desc = words[off:off + 8 * items].reshape(items, 8)
+    kv = np.minimum(inp.kv_len.cpu().numpy().astype(np.int64), inp.block_table.shape[1] * PAGE)
+    qs = inp.q_start.cpu().numpy()
+    nsplit = np.maximum(1, -(-kv // chunk))
+    seen = set()
+    for b, h, k0, k1, t0, D, N, ns in desc.tolist():
+        assert 0 <= b < B and 0 <= h < hkv
+        assert (N, ns, t0, D) == (kv[b], nsplit[b], qs[b], qs[b + 1] - qs[b] - 1)
+        assert k0 % chunk == 0 and k1 == min(N, k0 + chunk)
+        seen.add((b, h, k0 // chunk))
+    assert len(seen) == items == hkv * int(nsplit.sum())
+    full = int(words[2])
+    lens = desc[:, 3] - desc[:, 2]
+    assert np.all(lens[:full] == chunk) and not np.any(lens[full:] == chunk)
+    bucket = 63 - (lens[full:] * 64) // (chunk + 1)
+    assert np.all(np.diff(bucket) >= 0), "shorter items longest first by bucket"
+    start = np.concatenate([[0], np.cumsum(hkv * nsplit)[:-1]])
+    assert np.array_equal(words[16:16 + B], start)
 
 
 def spec(**kw):
@@ -96,9 +126,10 @@ def check(inp, kv_chunk=0, units=None):
     sp = inp.spec
     want = expected_plan(inp.kv_len.cpu().numpy(), sp.kv_heads, sp.group, inp.max_draft, sp.head_dim,
                          inp.block_table.shape[1], cus, kv_chunk)
-    out, chunk, items, nsplit = run_and_read_plan(inp, kv_chunk)
+    out, chunk, items, nsplit, ws = run_and_read_plan(inp, kv_chunk)
     say(f"  plan: chunk {chunk}, items {items}, split sequences {nsplit} (expected {want})")
     assert (chunk, items, nsplit) == want
+    check_items(ws, inp, chunk, items)
     err = compare_attention(inp, out, units=units)
     say(f"  max|err| over {len(units) if units else 'all'} units = {err:.3e}")
     assert err <= ATTN_TOL
