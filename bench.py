@@ -299,10 +299,10 @@ def write_bench_lines(*bench_jsons):
         body += [f"$ python3 REPO/bench.py{workload_args(cfg)}", json.dumps(line), ""]
     path = os.path.join(ROOT, "profiles", "verify_step_bench_lines_all_workloads.txt")
     with open(path, "w") as f:
-        f.write("# bench.py lines of every workload (one MI355X, inputs resident in HBM, median of 20 timed steps,\n"
-                "# 1 GiB cache flush before each step outside the timed events), each with its oracle baseline on\n"
-                "# the box's 16-core host share and the element-by-element parity of the oracle units it ran\n"
-                "# against the GPU outputs of the same call.  hbm / mfma: algorithmic attention bytes / flops over\n"
+        f.write("# bench.py lines of every workload (one MI355X, inputs resident in HBM, median of the timed steps\n"
+                "# (\"steps\" in each line), 1 GiB cache flush before each step outside the timed events), each with\n"
+                "# its oracle baseline on the box's 16-core host share and the element-by-element parity of the\n"
+                "# oracle units it ran against the GPU outputs of the same call.  hbm / mfma: algorithmic attention bytes / flops over\n"
                 "# the whole attention call (plan + main + combine) against 8 TB/s and 2.5 PFLOP/s bf16.\n\n")
         f.write(f"{'workload':52s} {'tok/s':>10s} {'step_us':>8s} {'attn_us':>8s} {'acc_us':>7s} {'hbm':>6s} "
                 f"{'mfma':>6s} {'cpu tok/s':>10s} {'units':>12s} {'max_err':>9s} {'parity':>6s}\n")
@@ -1201,7 +1201,7 @@ def copy_calibration(nbytes: int, reps: int = 3):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="g8_kv32k_D15")
     ap.add_argument("--draft", type=int, default=None, help="override D (every sequence)")
@@ -1311,7 +1311,7 @@ def main():
         return
     if args.sweep is not None:
         args.sweep = args.sweep or list(range(32))
-        if args.steps == 20 and args.warmup == 5:
+        if args.steps == 50 and args.warmup == 5:
             args.steps, args.warmup = 10, 3
         args.settle_s = min(args.settle_s, 0.3)
         run_sweep(args)
