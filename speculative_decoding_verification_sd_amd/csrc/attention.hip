@@ -84,6 +84,10 @@ struct AttnParams {
   ItemDesc* items;  // [item_cap]
   int B, Hkv, G, max_pages, num_pages, max_draft, rpad, total_q, item_cap;
   float scale_log2;
+  // the plan's inputs: explicit chunk (0: chosen), resident workgroups, an
+  // item's fixed cost in keys, whether the combine walks a split list; fused:
+  // the main kernels make the plan themselves (small batches, no plan launch)
+  int fixed_chunk, slots, ovh_keys, list_splits, fused;
 };
 
 __device__ __forceinline__ int seq_keys(const AttnParams& p, int b) {
@@ -456,6 +460,166 @@ __global__ __launch_bounds__(kPlanThreads) void verify_attn_plan(AttnParams p, i
 }
 
 // ---------------------------------------------------------------------------
+// The plan inside the main kernels, for batches of up to kFusedSeqs sequences:
+// every workgroup takes the same decisions as verify_attn_plan from the same
+// inputs (the chunk by the same rule over the same candidates; full-chunk
+// items first in (sequence, head, split) order, then the shorter items longest
+// first by length bucket, sequences in index order within a bucket), in its own
+// LDS, so the call needs no plan launch.  The work is then walked with a fixed
+// stride, and each workgroup finds its item's descriptor from the LDS tables.
+// Workgroup 0 writes the plan header and the per-sequence item starts that the
+// combine reads (the launch boundary orders them before it); each item's
+// descriptor is written by the workgroup that takes it.
+constexpr int kFusedSeqs = 32;
+
+struct FusedPlan {
+  unsigned long long best;
+  int chunk, total, nfull;
+  int n[kFusedSeqs], t0[kFusedSeqs], dr[kFusedSeqs], tseq[kFusedSeqs];
+  int fpre[kFusedSeqs + 1];     // full-chunk items of the sequences before b (x H_kv)
+  int istart[kFusedSeqs + 1];   // natural index of sequence b's first item
+};
+
+// ceil(n / c) for 0 <= n < 2^24 and 64 <= c <= kMaxChunk: the float quotient
+// (relative error far below 1/n) corrected to the exact floor, then rounded up.
+__device__ __forceinline__ int ceil_div_keys(int n, int c, float rc) {
+  int q = (int)((float)n * rc);
+  if (q * c > n) --q;
+  if ((q + 1) * c <= n) ++q;
+  return q + (q * c < n ? 1 : 0);
+}
+
+// All threads of the workgroup (at least kPlanThreads) call it.
+__device__ void fused_plan(const AttnParams& p, FusedPlan& fp) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int B = p.B;
+  if (tid < B) {
+    fp.n[tid] = seq_keys(p, tid);
+    fp.t0[tid] = p.q_start[tid];
+    fp.dr[tid] = seq_drafts(p, tid);
+  }
+  if (tid == 0) fp.best = ~0ull;
+  block_sync_lds();
+  const int max_keys = p.max_pages * kPage;
+  const int cap_chunk = max(kMinChunk, min(kMaxChunk, (max_keys + 63) / 64 * 64));
+  int chunk = cap_chunk;
+  if (p.fixed_chunk > 0) {
+    chunk = p.fixed_chunk;
+  } else {
+    long long ksum = 0;
+    int nmax = 0;
+    for (int b = 0; b < B; ++b) {
+      ksum += fp.n[b];
+      nmax = max(nmax, fp.n[b]);
+    }
+    unsigned long long key = ~0ull;
+    if (tid < kPlanThreads) {
+      const int c = min(plan_candidate(tid), cap_chunk);
+      const float rc = 1.f / (float)c;
+      long long items = 0;
+      for (int b = 0; b < B; ++b) items += max(1, ceil_div_keys(fp.n[b], c, rc));
+      items *= p.Hkv;
+      if (items <= p.item_cap) {
+        const long long load = (ksum * p.Hkv + (long long)p.ovh_keys * items + p.slots - 1) / p.slots;
+        const long long est = max(load, (long long)min(c, nmax));
+        key = ((unsigned long long)est << 9) | (unsigned long long)tid;   // ties: the smaller chunk
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) key = min(key, (unsigned long long)__shfl_xor(key, off));
+    if (lane == 0 && key != ~0ull) atomicMin(&fp.best, key);
+    block_sync_lds();
+    if (fp.best != ~0ull) chunk = min(plan_candidate((int)(fp.best & 511)), cap_chunk);
+  }
+  if (tid < 64) {   // one wave: lane b takes sequence b
+    const bool in = tid < B;
+    const int N = in ? fp.n[tid] : 0;
+    const int full = in ? N / chunk : 0;
+    const bool tail = in && (N % chunk != 0 || N == 0);
+    const int bucket = tail ? kLenBuckets - 1 - ((N - full * chunk) * kLenBuckets) / (chunk + 1) : 0;
+    int sf = full * p.Hkv, si = in ? (full + (tail ? 1 : 0)) * p.Hkv : 0;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int a = __shfl_up(sf, off), c = __shfl_up(si, off);
+      if (lane >= off) { sf += a; si += c; }
+    }
+    if (in) {
+      fp.fpre[tid + 1] = sf;
+      fp.istart[tid + 1] = si;
+    }
+    int rank = 0;
+    for (int b2 = 0; b2 < B; ++b2) {
+      const int t2 = __shfl(tail ? 1 : 0, b2), k2 = __shfl(bucket, b2);
+      if (t2 && (k2 < bucket || (k2 == bucket && b2 < tid))) ++rank;
+    }
+    if (tail) fp.tseq[rank] = tid;
+    const int nf = __shfl(sf, max(B - 1, 0)), tot = __shfl(si, max(B - 1, 0));
+    if (tid == 0) {
+      fp.fpre[0] = 0;
+      fp.istart[0] = 0;
+      fp.chunk = chunk;
+      fp.nfull = B > 0 ? nf : 0;
+      fp.total = B > 0 ? tot : 0;
+    }
+  }
+  block_sync_lds();
+  if (blockIdx.x == 0) {   // what the combine reads: the header, item starts, split sequences
+    int* tail_pos = p.plan + kPlanHeader + p.B + 1;
+    int* split_list = p.plan + kPlanHeader + 2 * p.B + 1;
+    if (tid <= B) p.plan[kPlanHeader + tid] = fp.istart[tid];
+    if (tid < B) tail_pos[tid] = -1;
+    if (tid < 64) {
+      const bool split = tid < B && fp.istart[tid + 1] - fp.istart[tid] > p.Hkv;
+      const unsigned long long m = __ballot(split);
+      if (p.list_splits && split) split_list[__popcll(m & ((1ull << tid) - 1))] = tid;
+      if (tid == 0) {
+        p.plan[0] = fp.chunk;
+        p.plan[1] = fp.total;
+        p.plan[2] = fp.nfull;
+        p.plan[3] = p.list_splits ? (int)__popcll(m) : 0;
+      }
+    }
+  }
+}
+
+// Item i of the fused plan and its partial slot (natural index).
+__device__ __forceinline__ ItemDesc fused_item(const AttnParams& p, const FusedPlan& fp, int i, int& pslot) {
+  const int chunk = fp.chunk;
+  int b, h, s, k0, k1;
+  if (i < fp.nfull) {
+    b = 0;
+    while (b + 1 < p.B && fp.fpre[b + 1] <= i) ++b;
+    const int full = max((fp.fpre[b + 1] - fp.fpre[b]) / p.Hkv, 1);
+    const int r = i - fp.fpre[b];
+    h = r / full;
+    s = r - h * full;
+    k0 = s * chunk;
+    k1 = k0 + chunk;
+  } else {
+    const int j = i - fp.nfull;
+    const int rank = j / p.Hkv;
+    h = j - rank * p.Hkv;
+    b = fp.tseq[min(rank, kFusedSeqs - 1)];
+    s = fp.n[b] / chunk;
+    k0 = s * chunk;
+    k1 = fp.n[b];
+  }
+  const int ns = (fp.istart[b + 1] - fp.istart[b]) / p.Hkv;
+  pslot = fp.istart[b] + h * ns + s;
+  ItemDesc d;
+  d.b = b;
+  d.h = h;
+  d.k_begin = k0;
+  d.k_end = k1;
+  d.t0 = fp.t0[b];
+  d.D = fp.dr[b];
+  d.N = fp.n[b];
+  d.nsplit = ns;
+  return d;
+}
+
+// ---------------------------------------------------------------------------
 
 // XOR swizzle of the 16-byte chunks of a K row in LDS for verify_attn_main, a
 // function of the key's position in the 32-key tile (64 banks of 4 bytes): the
@@ -666,7 +830,9 @@ __global__ __launch_bounds__(64 * NW, WPC) void verify_attn_main(AttnParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int l16 = lane & 15;
   const int g4 = lane >> 4;
-  const int total = min(p.plan[1], p.item_cap);
+  __shared__ FusedPlan fp;
+  if (p.fused) fused_plan(p, fp);
+  const int total = __builtin_amdgcn_readfirstlane(min(p.fused ? fp.total : p.plan[1], p.item_cap));
   const int Hq = p.Hkv * p.G;
 
   // Lane-constant LDS offsets inside a stage (the stage itself is an immediate
@@ -704,8 +870,8 @@ __global__ __launch_bounds__(64 * NW, WPC) void verify_attn_main(AttnParams p) {
   // of this workgroup's class (index = blockIdx % 8 modulo 8) as workgroups
   // finish, from the class's counter; otherwise a fixed stride.
   __shared__ int s_next;
-  const int chunk = p.plan[0];
-  const bool dyn = gridDim.x >= 8 && total > (int)gridDim.x && p.plan[2] < total;
+  const int chunk = __builtin_amdgcn_readfirstlane(p.fused ? fp.chunk : p.plan[0]);
+  const bool dyn = !p.fused && gridDim.x >= 8 && total > (int)gridDim.x && p.plan[2] < total;
   const int cls = blockIdx.x & 7;
   const int first_dyn = (int)gridDim.x + ((cls - (int)(gridDim.x & 7)) & 7);
   auto next_item = [&](int vi) {
@@ -717,7 +883,9 @@ __global__ __launch_bounds__(64 * NW, WPC) void verify_attn_main(AttnParams p) {
   };
   constexpr int row0 = 0;
   for (int item = blockIdx.x; item < total; item = next_item(item)) {
-    const ItemDesc d = p.items[item];
+    int fslot = 0;
+    const ItemDesc d = p.fused ? fused_item(p, fp, item, fslot) : p.items[item];
+    if (p.fused && threadIdx.x == 0) p.items[item] = d;
     // wave-uniform copies, so that everything derived from them (page bases,
     // tile counts) stays in scalar registers
     const int b = __builtin_amdgcn_readfirstlane(d.b), h = __builtin_amdgcn_readfirstlane(d.h);
@@ -728,7 +896,8 @@ __global__ __launch_bounds__(64 * NW, WPC) void verify_attn_main(AttnParams p) {
     if (b < 0 || b >= p.B || h < 0 || h >= p.Hkv || k_begin < 0 || k_end < k_begin ||
         k_end > p.max_pages * kPage || nsplit < 1 || chunk < 64)
       continue;
-    const int pslot = p.plan[kPlanHeader + b] + h * nsplit + k_begin / chunk;   // natural index: partials
+    const int pslot = p.fused ? __builtin_amdgcn_readfirstlane(fslot)
+                              : p.plan[kPlanHeader + b] + h * nsplit + k_begin / chunk;   // natural index: partials
     if (pslot < 0 || pslot >= p.item_cap) continue;
     const int R = p.G * (1 + D);
     const int* bt = p.block_table + (size_t)b * p.max_pages;
@@ -1176,7 +1345,9 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
   const int rblock = MODE == 0 ? w4 : MODE == 1 ? wave : set == 0 ? w4 : 4 + (w4 >> 1);
   const bool giver = !pair && par == 1;          // hands (O, l, m) to the block's parity-0 wave
   const int xslot = MODE == 0 ? w4 : (w4 >> 1);  // LDS hand-off slot of the block
-  const int total = min(p.plan[1], p.item_cap);
+  __shared__ FusedPlan fp;
+  if (p.fused) fused_plan(p, fp);
+  const int total = __builtin_amdgcn_readfirstlane(min(p.fused ? fp.total : p.plan[1], p.item_cap));
   const int Hq = p.Hkv * p.G;
 
   // Lane-constant LDS offsets, including (single-tile waves) the stage parity:
@@ -1214,8 +1385,8 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
   // of this workgroup's class (index = blockIdx % 8 modulo 8) as workgroups
   // finish, from the class's counter; otherwise a fixed stride.
   __shared__ int s_next;
-  const int chunk = p.plan[0];
-  const bool dyn = gridDim.x >= 8 && total > (int)gridDim.x && p.plan[2] < total;
+  const int chunk = __builtin_amdgcn_readfirstlane(p.fused ? fp.chunk : p.plan[0]);
+  const bool dyn = !p.fused && gridDim.x >= 8 && total > (int)gridDim.x && p.plan[2] < total;
   const int cls = blockIdx.x & 7;
   const int first_dyn = (int)gridDim.x + ((cls - (int)(gridDim.x & 7)) & 7);
   auto next_item = [&](int vi) {
@@ -1226,7 +1397,9 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
     return s_next;
   };
   for (int item = blockIdx.x; item < total; item = next_item(item)) {
-    const ItemDesc d = p.items[item];
+    int fslot = 0;
+    const ItemDesc d = p.fused ? fused_item(p, fp, item, fslot) : p.items[item];
+    if (p.fused && threadIdx.x == 0) p.items[item] = d;
     const int b = __builtin_amdgcn_readfirstlane(d.b), h = __builtin_amdgcn_readfirstlane(d.h);
     const int k_begin = __builtin_amdgcn_readfirstlane(d.k_begin), k_end = __builtin_amdgcn_readfirstlane(d.k_end);
     const int t0 = __builtin_amdgcn_readfirstlane(d.t0), D = __builtin_amdgcn_readfirstlane(d.D);
@@ -1235,7 +1408,8 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
     if (b < 0 || b >= p.B || h < 0 || h >= p.Hkv || k_begin < 0 || k_end < k_begin ||
         k_end > p.max_pages * kPage || nsplit < 1 || chunk < 64)
       continue;
-    const int pslot = p.plan[kPlanHeader + b] + h * nsplit + k_begin / chunk;   // natural index: partials
+    const int pslot = p.fused ? __builtin_amdgcn_readfirstlane(fslot)
+                              : p.plan[kPlanHeader + b] + h * nsplit + k_begin / chunk;   // natural index: partials
     if (pslot < 0 || pslot >= p.item_cap) continue;
     const int R = p.G * (1 + D);
     const int* bt = p.block_table + (size_t)b * p.max_pages;
@@ -1883,8 +2057,14 @@ hipError_t sdv_attn_launch(const SdAttnLaunch& a) {
     p.tmask = masks;
   }
   const long long cunits = (long long)a.B * a.Hkv * (L.rpad / 8);   // combine workgroups, one per 8 rows of a head
-  verify_attn_plan<<<1, kPlanThreads, 0, a.stream>>>(p, a.kv_chunk, slots, kItemOverheadBytes / (4 * a.head_dim),
-                                                     cunits > kCombineGrid);
+  p.fixed_chunk = a.kv_chunk;
+  p.slots = slots;
+  p.ovh_keys = kItemOverheadBytes / (4 * a.head_dim);
+  p.list_splits = cunits > kCombineGrid;
+  p.fused = a.B <= kFusedSeqs;   // small batches: the main kernels make the plan themselves
+  if (!p.fused)
+    verify_attn_plan<<<1, kPlanThreads, 0, a.stream>>>(p, a.kv_chunk, slots, kItemOverheadBytes / (4 * a.head_dim),
+                                                       cunits > kCombineGrid);
   if (a.head_dim == 128) {
     if (a.out_f32) launch_main<128, 1>(L.variant, p, grid, a.stream, a.v_key_major);
     else launch_main<128, 0>(L.variant, p, grid, a.stream, a.v_key_major);

@@ -184,3 +184,27 @@ def test_explicit_chunk_counts_split_sequences():
     inp = generate(spec(batch=6, kv_len=[100, 256, 257, 1000, 5, 513], seed=35))
     say("case: plan kv_chunk=256")
     check(inp, kv_chunk=256)
+
+
+@pytest.mark.parametrize("batch", [32, 33])
+def test_mixed_lengths_at_the_fused_limit(batch):
+    """Uneven lengths with shorter items in several length buckets: 32
+    sequences plan inside the main kernel (fixed-stride schedule), 33 take the
+    plan kernel (dynamic schedule); both by the same selection rule."""
+    rng = np.random.default_rng(40 + batch)
+    kv = [int(x) for x in rng.integers(1, 9000, size=batch)]
+    inp = generate(spec(batch=batch, kv_heads=2, group=8, kv_len=kv,
+                        draft_len=[int(x) for x in rng.integers(0, 8, size=batch)], seed=40 + batch))
+    say(f"case: plan B={batch} mixed lengths")
+    check(inp, units=[(0, 0), (batch // 2, 1), (batch - 1, 1)])
+
+
+def test_fused_plan_with_listed_splits():
+    """32 sequences over 32 KV heads at 128 rows each (16384 combine workgroups
+    of 8 rows): the plan made inside the main kernel also writes the list of
+    split sequences the combine walks."""
+    rng = np.random.default_rng(42)
+    kv = [int(x) for x in rng.integers(300, 3000, size=32)]
+    inp = generate(spec(batch=32, kv_heads=32, group=8, kv_len=kv, draft_len=15, seed=42))
+    say("case: plan B=32 Hkv=32, listed splits")
+    check(inp, kv_chunk=512, units=[(0, 0), (13, 31), (31, 7)])
