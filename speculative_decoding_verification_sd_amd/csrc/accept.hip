@@ -51,7 +51,11 @@ constexpr int kSChunk = 4096;                     // logits per sampling workgro
 constexpr int kSPerThread = kSChunk / kAccThreads;  // 16: one slice of the sampling search per thread
 static_assert(kSPerThread % 4 == 0 && kSPerThread <= 64, "a slice is scanned by one wave");
 constexpr int kDecideSlots = 2048;
-constexpr int kFinishWGs = 1024;                  // accept_finish workgroups in flight at once (4 per CU)                // chunk statistics staged in LDS per pass
+#ifndef SDV_ROWSTATS_WGS
+#define SDV_ROWSTATS_WGS 1024
+#endif
+constexpr int kRowstatsWGs = SDV_ROWSTATS_WGS;     // accept_rowstats workgroups (persistent grid)
+constexpr int kFinishWGs = 1024;                  // accept_finish workgroups in flight at once (4 per CU)
 
 struct RowPart {
   float m;     // chunk max
@@ -69,7 +73,8 @@ struct SeqState {
 
 struct SeqRec {      // a sequence's decision, from accept_finish to accept_draw
   double lse_p, lse_q;
-  int n, pad;
+  int n;
+  float u;           // the sampling uniform u[t0 + D]
 };
 
 struct AccParams {
@@ -183,19 +188,15 @@ __device__ __forceinline__ void load_chunk(const float* src, int j0, int V, floa
 // MODE 0: greedy (lowest-index maximum); 1: stochastic (maximum and sum of
 // exp(x - max)); 2: relaxed acceptance (all of those, and for draft rows the
 // sum of exp(x - max) (x - max), from which the row's entropy follows).
+// Chunk g of the rows x chunks grid: row g / nchunk, chunk g % nchunk, whose
+// logits the caller has loaded into x.
 template <int MODE, int VEC4>
-__global__ __launch_bounds__(kAccThreads) void accept_rowstats(AccParams p) {
-  __shared__ float sm[4];
-  __shared__ int si[4];
-  __shared__ double sd[4];
-  const int row = blockIdx.x / p.nchunk;
-  const int c = blockIdx.x - row * p.nchunk;
-  const float* src = row < p.T ? p.target + (size_t)row * p.V : p.draft + (size_t)(row - p.T) * p.V;
+__device__ __forceinline__ void rowstats_chunk(const AccParams& p, int g, const float (&x)[kPerThread], float* sm,
+                                               int* si, double* sd) {
+  const int row = g / p.nchunk;
+  const int c = g - row * p.nchunk;
   const int tid = threadIdx.x;
   const int j0 = c * kChunk;
-  float x[kPerThread];
-  load_chunk<VEC4>(src, j0, p.V, x);
-
   RowPart r;
   r.idx = 0;
   r.s = 0.0;
@@ -238,6 +239,39 @@ __global__ __launch_bounds__(kAccThreads) void accept_rowstats(AccParams p) {
     if (ent && tid == 0) p.ent[(size_t)(row - p.T) * p.nchunk + c] = s1;
   }
   if (tid == 0) p.part[(size_t)row * p.nchunk + c] = r;
+}
+
+template <int VEC4>
+__device__ __forceinline__ void rowstats_load(const AccParams& p, int g, float (&x)[kPerThread]) {
+  const int row = g / p.nchunk;
+  const int c = g - row * p.nchunk;
+  const float* src = row < p.T ? p.target + (size_t)row * p.V : p.draft + (size_t)(row - p.T) * p.V;
+  load_chunk<VEC4>(src, c * kChunk, p.V, x);
+}
+
+// A persistent grid over the rows x chunks: each workgroup takes chunks
+// blockIdx.x, + gridDim.x, ..., and loads the next one before it reduces the
+// current one, so that its loads stay in flight through the reductions.
+template <int MODE, int VEC4>
+__global__ __launch_bounds__(kAccThreads) void accept_rowstats(AccParams p, int total) {
+  __shared__ float sm[4];
+  __shared__ int si[4];
+  __shared__ double sd[4];
+  float xa[kPerThread], xb[kPerThread];
+  int g = blockIdx.x;
+  if (g >= total) return;
+  rowstats_load<VEC4>(p, g, xa);
+  for (;;) {
+    const int g1 = g + (int)gridDim.x;
+    if (g1 < total) rowstats_load<VEC4>(p, g1, xb);
+    rowstats_chunk<MODE, VEC4>(p, g, xa, sm, si, sd);
+    if (g1 >= total) break;
+    const int g2 = g1 + (int)gridDim.x;
+    if (g2 < total) rowstats_load<VEC4>(p, g2, xa);
+    rowstats_chunk<MODE, VEC4>(p, g1, xb, sm, si, sd);
+    if (g2 >= total) break;
+    g = g2;
+  }
 }
 
 // log-normaliser of row `prow` from its chunk statistics, by one wave (lane k
@@ -565,6 +599,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_finish(AccParams p) {
   // 0) the test of draft i: it passes when u_i < p(x_i) / q(x_i), evaluated as
   // exp((l_p - LSE_p) - (l_q - LSE_q)) in fp64.  Row D has no draft row.
   const int lane16 = tid & 15, grp = tid >> 4;
+  const float u_sample = c == 0 && tid == 0 ? p.uniforms[t0 + D] : 0.f;   // (for the draw; loaded early)
   if (tid == 0) { s_fail = D; s_have = 0; }
   __syncthreads();
   double my_lp = 0.0, my_lq = 0.0;
@@ -614,7 +649,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_finish(AccParams p) {
       if (k != n) p.out_tokens[t0 + k] = k < n ? p.tokens[d0 + k] : -1;   // k == n: the sample (accept_draw)
     if (tid == 0) {
       p.accept_len[b] = n + 1;
-      p.seqrec[b] = SeqRec{s_lp, n < D ? s_lq : 0.0, n, 0};
+      p.seqrec[b] = SeqRec{s_lp, n < D ? s_lq : 0.0, n, u_sample};
     }
   }
   SeqState st;
@@ -678,13 +713,20 @@ __global__ __launch_bounds__(kAccThreads) void accept_draw(AccParams p) {
   __shared__ double s_wtot[4];
   __shared__ int s_chunk, s_usep, s_slice, s_slice_last;
   __shared__ double s_base, s_slice_base, s_T;
+  __shared__ float s_tl[kSPerThread], s_dl[kSPerThread];
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  // Two memory round trips.  The first: the sequence's rows, its decision and
+  // (wave 0) the chunk sums.
+  const double* rs = p.rsum + (size_t)b * p.nschunk * 2;
+  f64x2 r0 = {0.0, 0.0};
+  if (wave == 0 && lane < p.nschunk) r0 = *(const f64x2*)(rs + 2 * lane);
+  const SeqRec rec = p.seqrec[b];
   const int t0 = p.q_start[b];
   const int D = seq_d(p, b);
   const int d0 = t0 - b;
   if (!seq_ok(p, t0, D, d0)) return;   // (accept_finish wrote AL = 0)
-  const SeqRec rec = p.seqrec[b];
   const int n = min(max(rec.n, 0), D);
   SeqState st;
   st.n = n;
@@ -693,24 +735,20 @@ __global__ __launch_bounds__(kAccThreads) void accept_draw(AccParams p) {
   st.lse_q = rec.lse_q;
   const float* prow = p.target + (size_t)(t0 + n) * p.V;
   const float* qrow = p.draft + (size_t)(d0 + (n < D ? n : 0)) * p.V;
-  const int lane = tid & 63, wave = tid >> 6;
-  auto ld = [](const double* a) { return *a; };
   if (wave == 0) {
     // level 1 (one wave): totals, T, and the chunk
-    const double* rs = p.rsum + (size_t)b * p.nschunk * 2;
-    double vw0 = 0.0, vp0 = 0.0;
-    if (lane < p.nschunk) { vw0 = ld(rs + 2 * lane); vp0 = ld(rs + 2 * lane + 1); }
+    const double vw0 = r0[0], vp0 = r0[1];
     double sw = vw0, sp = vp0;
-    for (int k = lane + 64; k < p.nschunk; k += 64) { sw += ld(rs + 2 * k); sp += ld(rs + 2 * k + 1); }
+    for (int k = lane + 64; k < p.nschunk; k += 64) { sw += rs[2 * k]; sp += rs[2 * k + 1]; }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) { sw += __shfl_xor(sw, off); sp += __shfl_xor(sp, off); }
     const int usep = !(sw > 0.0);                 // the residual has no mass: sample p
-    const double T = (double)p.uniforms[t0 + D] * (usep ? sp : sw);
+    const double T = (double)rec.u * (usep ? sp : sw);
     double carry = 0.0, base = -INFINITY;
     int chunk = -1, lastpos = -1;
     for (int kb = 0; kb < p.nschunk; kb += 64) {
       const int k = kb + lane;
-      const double v = kb == 0 ? (usep ? vp0 : vw0) : (k < p.nschunk ? ld(rs + 2 * k + usep) : 0.0);
+      const double v = kb == 0 ? (usep ? vp0 : vw0) : (k < p.nschunk ? rs[2 * k + usep] : 0.0);
       const double incl = wave_incl_scan(v);
       double excl = __shfl_up(incl, 1);
       if (lane == 0) excl = 0.0;
@@ -729,11 +767,33 @@ __global__ __launch_bounds__(kAccThreads) void accept_draw(AccParams p) {
     if (lane == 0) { s_chunk = chunk; s_base = base; s_T = T; s_usep = usep; s_slice = INT_MAX; s_slice_last = -1; }
   }
   __syncthreads();
-  // level 2 (four waves): the 16-token slice inside the chunk, from the published thread sums
   const int chunk = s_chunk;
   const double T = s_T;
+  const int usep = s_usep;
+  // The second: each thread's sums in the chosen chunk, and its 16 logits there
+  // (level 3 needs only the chosen slice's, but they are then already here).
+  const f64x2 rv = *(const f64x2*)(p.rsub + (((size_t)b * p.nschunk + chunk) * kAccThreads + tid) * 2);
+  const int j0 = chunk * kSChunk + tid * kSPerThread;
+  float tl[kSPerThread], dl[kSPerThread];
+  if (p.vec4 && j0 + kSPerThread <= p.V) {
+#pragma unroll
+    for (int k = 0; k < kSPerThread / 4; ++k) {
+      const f32x4 a = *(const f32x4*)(prow + j0 + 4 * k);
+      const f32x4 q = st.residual ? *(const f32x4*)(qrow + j0 + 4 * k) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { tl[4 * k + e] = a[e]; dl[4 * k + e] = q[e]; }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kSPerThread; ++e) {
+      const bool in = j0 + e < p.V;
+      tl[e] = in ? prow[j0 + e] : -INFINITY;
+      dl[e] = in && st.residual ? qrow[j0 + e] : -INFINITY;
+    }
+  }
+  // level 2 (four waves): the 16-token slice inside the chunk, from the thread sums
   {
-    const double v = ld(p.rsub + (((size_t)b * p.nschunk + chunk) * kAccThreads + tid) * 2 + s_usep);
+    const double v = usep ? rv[1] : rv[0];
     const double incl = wave_incl_scan(v);
     if (lane == 63) s_wtot[wave] = incl;
     __syncthreads();
@@ -743,18 +803,22 @@ __global__ __launch_bounds__(kAccThreads) void accept_draw(AccParams p) {
     if (v > 0.0) atomicMax(&s_slice_last, tid);
     __syncthreads();
     if (tid == s_slice) s_slice_base = carry + (incl - v);
+    if (tid == (s_slice != INT_MAX ? s_slice : max(s_slice_last, 0))) {
+#pragma unroll
+      for (int e = 0; e < kSPerThread; ++e) { s_tl[e] = tl[e]; s_dl[e] = dl[e]; }
+    }
   }
   __syncthreads();
   if (wave == 0) {
     // level 3 (one wave): the token inside the slice, by a sequential prefix sum
     const int slice = s_slice != INT_MAX ? s_slice : max(s_slice_last, 0);
     const double base = s_slice != INT_MAX ? s_slice_base : -INFINITY;
-    if (s_usep) st.residual = 0;
+    if (usep) st.residual = 0;
     const int js = chunk * kSChunk + slice * kSPerThread;
     double w = 0.0;
-    if (lane < kSPerThread && js + lane < p.V) {
+    if (lane < kSPerThread) {   // (past the vocabulary the logits are -inf: weight 0)
       double pj;
-      sample_weight(prow[js + lane], st.residual ? qrow[js + lane] : -INFINITY, st, w, pj);
+      sample_weight(s_tl[lane], st.residual ? s_dl[lane] : -INFINITY, st, w, pj);
     }
     double C = base;
     int tok = -1, last = -1;
@@ -838,20 +902,21 @@ hipError_t sdv_accept_launch(const SdAccLaunch& a) {
   const size_t drows = (size_t)(a.T - a.B);
   const size_t rows = need_draft ? (size_t)a.T + drows : (size_t)a.T;
   const unsigned grid1 = (unsigned)(rows * L.nchunk);
+  const unsigned rs_grid = std::max(1u, std::min(grid1, (unsigned)kRowstatsWGs));
   if (a.lossy) {
-    if (vec4) accept_rowstats<2, 1><<<grid1, kAccThreads, 0, a.stream>>>(p);
-    else accept_rowstats<2, 0><<<grid1, kAccThreads, 0, a.stream>>>(p);
+    if (vec4) accept_rowstats<2, 1><<<rs_grid, kAccThreads, 0, a.stream>>>(p, (int)grid1);
+    else accept_rowstats<2, 0><<<rs_grid, kAccThreads, 0, a.stream>>>(p, (int)grid1);
     if (drows > 0) {
       const unsigned grid2 = (unsigned)(drows * L.nchunk);
       if (vec4) accept_jsd<1><<<grid2, kAccThreads, 0, a.stream>>>(p);
       else accept_jsd<0><<<grid2, kAccThreads, 0, a.stream>>>(p);
     }
   } else if (a.stochastic) {
-    if (vec4) accept_rowstats<1, 1><<<grid1, kAccThreads, 0, a.stream>>>(p);
-    else accept_rowstats<1, 0><<<grid1, kAccThreads, 0, a.stream>>>(p);
+    if (vec4) accept_rowstats<1, 1><<<rs_grid, kAccThreads, 0, a.stream>>>(p, (int)grid1);
+    else accept_rowstats<1, 0><<<rs_grid, kAccThreads, 0, a.stream>>>(p, (int)grid1);
   } else {
-    if (vec4) accept_rowstats<0, 1><<<grid1, kAccThreads, 0, a.stream>>>(p);
-    else accept_rowstats<0, 0><<<grid1, kAccThreads, 0, a.stream>>>(p);
+    if (vec4) accept_rowstats<0, 1><<<rs_grid, kAccThreads, 0, a.stream>>>(p, (int)grid1);
+    else accept_rowstats<0, 0><<<rs_grid, kAccThreads, 0, a.stream>>>(p, (int)grid1);
   }
   if (a.stochastic) {
     // workgroups per sequence: all chunks, or about kFinishWGs / B in all when
@@ -895,8 +960,9 @@ hipError_t sdv_tree_accept_launch(const SdAccLaunch& a, const int32_t* parents, 
   const bool vec4 = (a.V % 4 == 0) && ((uintptr_t)a.target % 16 == 0);
   p.vec4 = vec4;
   const unsigned grid1 = (unsigned)((size_t)a.T * L.nchunk);
-  if (vec4) accept_rowstats<0, 1><<<grid1, kAccThreads, 0, a.stream>>>(p);
-  else accept_rowstats<0, 0><<<grid1, kAccThreads, 0, a.stream>>>(p);
+  const unsigned rs_grid = std::max(1u, std::min(grid1, (unsigned)kRowstatsWGs));
+  if (vec4) accept_rowstats<0, 1><<<rs_grid, kAccThreads, 0, a.stream>>>(p, (int)grid1);
+  else accept_rowstats<0, 0><<<rs_grid, kAccThreads, 0, a.stream>>>(p, (int)grid1);
   accept_tree<<<a.B, kAccThreads, (size_t)(a.max_draft + 1) * sizeof(int), a.stream>>>(p, parents, out_nodes);
   return hipGetLastError();
 }
