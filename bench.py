@@ -888,19 +888,22 @@ def write_batch_profile(bench_json: str, kt_dir: str):
         line = json.loads(f.read().strip().splitlines()[-1])
     rows = [r for r in _rocprof_csv(kt_dir, "kernel_trace") if "sdv::" in r["Kernel_Name"]]
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
-    plans = [i for i, r in enumerate(rows) if "verify_attn_plan" in r["Kernel_Name"]]
-    per_point = len(plans) // len(line["points"])
+    # every attention call ends with one combine launch (batches of up to 32 sequences make
+    # their plan inside the main kernel, so the plan launch does not mark every call)
+    ends = [i for i, r in enumerate(rows) if "verify_attn_combine" in r["Kernel_Name"]]
+    per_point = len(ends) // len(line["points"])
     path = os.path.join(ROOT, "profiles", "verify_attn_batch_sweep_hkv8_g8_d128_D3.txt")
     with open(path, "w") as f:
         f.write("# Verify attention against the batch size (H_kv=8, G=8, d=128, D=3; B sequences of N keys):\n"
                 "# median kernel durations per point from a rocprofv3 kernel trace, and the call time with HIP\n"
-                "# events in the same run.  The plan and the combine are the launches whose cost grows with B.\n"
+                "# events in the same run.  The plan and the combine are the launches whose cost grows with B;\n"
+                "# batches of up to 32 sequences plan inside the main kernel (plan_us 0).\n"
                 "$ cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace -d OUT/kt_batch -o run "
                 "--output-format csv -- python3 REPO/bench.py --batch-sweep\n")
         f.write("batch,kv_len,plan_us,main_us,combine_us,call_us_events,hbm_frac\n")
         for k, pt in enumerate(line["points"]):
-            lo = plans[k * per_point]
-            hi = plans[(k + 1) * per_point] if (k + 1) * per_point < len(plans) else len(rows)
+            lo = ends[k * per_point - 1] + 1 if k > 0 else 0
+            hi = ends[(k + 1) * per_point - 1] + 1
             med = {}
             for part, key in (("plan", "verify_attn_plan"), ("main", "verify_attn_main"), ("wide", "verify_attn_wide"),
                               ("combine", "verify_attn_combine")):
