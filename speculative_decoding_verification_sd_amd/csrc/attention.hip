@@ -465,8 +465,10 @@ __global__ __launch_bounds__(kPlanThreads) void verify_attn_plan(AttnParams p, i
 // inputs (the chunk by the same rule over the same candidates; full-chunk
 // items first in (sequence, head, split) order, then the shorter items longest
 // first by length bucket, sequences in index order within a bucket), in its own
-// LDS, so the call needs no plan launch.  The work is then walked with a fixed
-// stride, and each workgroup finds its item's descriptor from the LDS tables.
+// LDS, so the call needs no plan launch.  Workgroup w then takes item w of
+// every round of gridDim items, walking the rounds in snake order (forward in
+// even rounds, backward in odd ones), which pairs the longest items with the
+// shortest ones, and finds each item's descriptor from the LDS tables.
 // Workgroup 0 writes the plan header and the per-sequence item starts that the
 // combine reads (the launch boundary orders them before it); each item's
 // descriptor is written by the workgroup that takes it.
@@ -875,6 +877,10 @@ __global__ __launch_bounds__(64 * NW, WPC) void verify_attn_main(AttnParams p) {
   const int cls = blockIdx.x & 7;
   const int first_dyn = (int)gridDim.x + ((cls - (int)(gridDim.x & 7)) & 7);
   auto next_item = [&](int vi) {
+    if (p.fused) {   // snake order over the longest-first list: round r runs forward when r is even
+      const int G = (int)gridDim.x, r = vi / G + 1;
+      return r * G + ((r & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x);
+    }
     if (!dyn) return vi + (int)gridDim.x;
     block_sync();
     if (threadIdx.x == 0) s_next = first_dyn + 8 * atomicAdd(p.plan + 8 + cls, 1);
@@ -1390,6 +1396,10 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
   const int cls = blockIdx.x & 7;
   const int first_dyn = (int)gridDim.x + ((cls - (int)(gridDim.x & 7)) & 7);
   auto next_item = [&](int vi) {
+    if (p.fused) {   // snake order over the longest-first list: round r runs forward when r is even
+      const int G = (int)gridDim.x, r = vi / G + 1;
+      return r * G + ((r & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x);
+    }
     if (!dyn) return vi + (int)gridDim.x;
     block_sync();
     if (threadIdx.x == 0) s_next = first_dyn + 8 * atomicAdd(p.plan + 8 + cls, 1);
