@@ -158,11 +158,14 @@ __global__ __launch_bounds__(64 * kMaskSeqsPerBlock) void verify_tree_masks(Attn
 // plan[]: [0] chunk, [1] items, [2] full-chunk items, [3] sequences split in
 // more than one item (when list_splits), [8..15] work counters (cleared here),
 // then from kPlanHeader on item_start[0..B], tail_pos[0..B-1] (scheduled index
-// of head 0's shorter item of sequence b; kept in LDS for the first
-// kPlanCacheSeqs sequences) and, when list_splits, the list of the split
-// sequences (plan[3] entries, any order) for the combine of large batches.
+// of head 0's shorter item of sequence b, -1: none), when list_splits the list
+// of the split sequences (plan[3] entries, any order) for the combine of large
+// batches, and full_base[0..B-1] (scheduled index of sequence b's first
+// full-chunk item).  The plan kernel writes the header and the per-sequence
+// tables, and the descriptors and the split list too up to kPlanWrites
+// (sequence, head) pairs; beyond, verify_attn_items writes those.
 constexpr int kLenBuckets = 64;
-constexpr int kPlanCacheSeqs = 8192;     // sequences whose fields the plan keeps in LDS (4 x 32 KiB; gfx950 allows 160 KiB per workgroup)
+constexpr int kPlanCacheSeqs = 8192;     // sequences whose key counts the plan keeps in LDS (32 KiB)
 constexpr int kHistBins = kMaxChunk / 64 + 2;   // ceil(N/64) = 0 .. 512, and "longer"
 constexpr int kBinsPerLane = (kHistBins + 63) / 64;   // the suffix scan: one wave over the bins
 
@@ -174,32 +177,96 @@ __device__ __forceinline__ int plan_candidate(int t) {
 }
 constexpr int kLongSeqs = 256;           // sequences longer than kMaxChunk the chunk search lists in LDS
 constexpr int kDirectSeqs = 64;          // chunk search: batches this small skip the histogram
-constexpr int kSearchCost = 8;           // descriptors: an item found by binary search costs about 8 written directly
+
+// floor(n / c) for 0 <= n < 2^24 and 1 <= c <= 2^24: the float quotient
+// corrected to the exact one.
+__device__ __forceinline__ int floor_div_keys(int n, int c, float rc) {
+  int q = (int)((float)n * rc);
+  if (q * c > n) --q;
+  if ((q + 1) * c <= n) ++q;
+  return q;
+}
+
+// atomicAdd(&s[key], 1) of every lane with `active`; returns the lane's old
+// value.  When all active lanes of the wave share one key (equal lengths: one
+// bucket) it is one LDS atomic for the wave, the lanes taking consecutive
+// values in lane order, instead of a 64-way conflict; otherwise one atomic per
+// lane, which the LDS runs in parallel over distinct keys.  Every lane of the
+// wave calls it.
+__device__ __forceinline__ int wave_bucket_add(int* s, int key, bool active) {
+  const int lane = threadIdx.x & 63;
+  const unsigned long long act = __ballot(active);
+  if (!act) return 0;
+  const int leader = __ffsll(act) - 1;
+  const int k0 = __shfl(key, leader);
+  if (__ballot(active && key == k0) == act) {
+    int base = 0;
+    if (lane == leader) base = atomicAdd(&s[k0], (int)__popcll(act));
+    base = __shfl(base, leader);
+    return active ? base + (int)__popcll(act & ((1ull << lane) - 1ull)) : 0;
+  }
+  return active ? atomicAdd(&s[key], 1) : 0;
+}
+
+// The descriptors of (sequence b, KV head h): its full-chunk items at
+// full_base + h * full + split, its shorter item (if any) at tail_pos + h (the
+// plan's scheduled positions for b); and, for the listed combine, the sequence
+// in the split list when it has more than one item.
+__device__ void write_item_descs(const AttnParams& p, int b, int h, int chunk, int N, int t0, int D, int full_base,
+                                 int tail_pos, int list_splits) {
+  int* split_list = p.plan + kPlanHeader + 2 * p.B + 1;
+  const int full = N / chunk;
+  const bool tail = N - full * chunk != 0 || N == 0;
+  const int ns = full + (tail ? 1 : 0);
+  ItemDesc d;
+  d.b = b;
+  d.h = h;
+  d.t0 = t0;
+  d.D = D;
+  d.N = N;
+  d.nsplit = ns;
+  const int fbase = full_base + h * full;
+  for (int s = 0; s < full; ++s) {
+    if (fbase + s < 0 || fbase + s >= p.item_cap) break;
+    d.k_begin = s * chunk;
+    d.k_end = d.k_begin + chunk;
+    p.items[fbase + s] = d;
+  }
+  if (tail) {
+    const int pos = tail_pos + h;
+    if (pos >= 0 && pos < p.item_cap) {
+      d.k_begin = full * chunk;
+      d.k_end = N;
+      p.items[pos] = d;
+    }
+  }
+  if (list_splits && h == 0 && ns > 1) split_list[atomicAdd(p.plan + 3, 1)] = b;   // (any order: each head merges alone)
+}
+
+// Up to this many (sequence, KV head) pairs the plan kernel writes the
+// descriptors itself; beyond, verify_attn_items spreads them over the GPU (one
+// workgroup's stores would take tens of microseconds).
+constexpr int kPlanWrites = 4096;
 
 __global__ __launch_bounds__(kPlanThreads) void verify_attn_plan(AttnParams p, int fixed_chunk, int slots,
                                                                  int ovh_keys, int list_splits) {
-  __shared__ int s_keys[kPlanThreads];
-  __shared__ int scan[kPlanThreads];
-  __shared__ int fscan[kPlanThreads];
   __shared__ int s_bucket[kLenBuckets];
   __shared__ unsigned long long s_best;
   __shared__ long long s_ksum, s_full;
   __shared__ int s_nmax;
   __shared__ int s_n[kPlanCacheSeqs];      // N_b
-  __shared__ int s_t0[kPlanCacheSeqs];     // q_start[b]
-  __shared__ int s_d[kPlanCacheSeqs];      // drafts of sequence b
-  __shared__ int s_tail[kPlanCacheSeqs];   // tail_pos[b]
+  // the descriptors' fields, for the batches whose descriptors this kernel writes
+  __shared__ int s_t0[kPlanWrites], s_d[kPlanWrites], s_tail[kPlanWrites], s_fbase[kPlanWrites];
   __shared__ int s_wsum[2][kPlanThreads / 64];
   __shared__ int s_hist[kHistBins];        // sequences by ceil(N/64), the last bin N > kMaxChunk
   __shared__ int s_above[kHistBins];       // s_above[x] = sequences with ceil(N/64) > x
   __shared__ int s_long[kLongSeqs];        // ceil(N/64) of the sequences longer than kMaxChunk
-  __shared__ int s_nlong, s_nsplit;
+  __shared__ int s_nlong;
   const int tid = threadIdx.x;
   const int max_keys = p.max_pages * kPage;
   const int cap_chunk = max(kMinChunk, min(kMaxChunk, (max_keys + 63) / 64 * 64));
   const int my_chunk = min(plan_candidate(tid), cap_chunk);
   int* tail_pos = p.plan + kPlanHeader + p.B + 1;
-  int* split_list = p.plan + kPlanHeader + 2 * p.B + 1;   // the sequences with more than one split
   auto keys_of = [&](int b) { return b < kPlanCacheSeqs ? s_n[b] : seq_keys(p, b); };
 
   // (1) the chunk.  Candidates are c = 64 d keys (d >= 4), and ceil(N/c) =
@@ -211,7 +278,8 @@ __global__ __launch_bounds__(kPlanThreads) void verify_attn_plan(AttnParams p, i
   // costs O(B + 256 * long sequences) instead of 256 divisions per sequence.
   // Up to kDirectSeqs sequences every candidate simply divides each length.
   const bool direct = p.B <= kDirectSeqs;
-  if (tid == 0) { s_best = ~0ull; s_ksum = 0; s_full = 0; s_nmax = 0; s_nlong = 0; s_nsplit = 0; }
+  const bool writes = p.B * p.Hkv <= kPlanWrites;   // (then B <= kPlanWrites: the fields fit in LDS)
+  if (tid == 0) { s_best = ~0ull; s_ksum = 0; s_full = 0; s_nmax = 0; s_nlong = 0; }
   if (tid < kLenBuckets) s_bucket[tid] = 0;
   if (!direct) {
     for (int i = tid; i < kHistBins; i += kPlanThreads) s_hist[i] = 0;
@@ -219,24 +287,36 @@ __global__ __launch_bounds__(kPlanThreads) void verify_attn_plan(AttnParams p, i
   }
   long long my_items = 0, ksum = 0;
   int nmax = 0;
-  for (int base = 0; base < p.B; base += kPlanThreads) {
-    const bool in = base + tid < p.B;
-    const int nb = in ? seq_keys(p, base + tid) : 0;
-    if (base + tid < kPlanCacheSeqs) {        // (the descriptors' fields, loaded here alongside N_b)
-      s_n[base + tid] = nb;
-      if (in) {
-        s_t0[base + tid] = p.q_start[base + tid];
-        s_d[base + tid] = seq_drafts(p, base + tid);
-      }
+  constexpr int kLoadGroups = 4;   // groups of sequences whose loads are issued before any is used
+  for (int base0 = 0; base0 < p.B; base0 += kLoadGroups * kPlanThreads) {
+    int nbv[kLoadGroups], t0v[kLoadGroups], dv[kLoadGroups];
+#pragma unroll
+    for (int u = 0; u < kLoadGroups; ++u) {
+      const int b = base0 + u * kPlanThreads + tid;
+      const bool mine = b < p.B && writes;
+      nbv[u] = b < p.B ? seq_keys(p, b) : 0;
+      t0v[u] = mine ? p.q_start[b] : 0;
+      dv[u] = mine ? seq_drafts(p, b) : 0;
     }
-    ksum += nb;
-    nmax = max(nmax, nb);
-    if (in && !direct) {
-      const int n64 = (nb + 63) >> 6;
-      atomicAdd(&s_hist[min(n64, kHistBins - 1)], 1);
-      if (n64 > kHistBins - 2) {
-        const int sl = atomicAdd(&s_nlong, 1);
-        if (sl < kLongSeqs) s_long[sl] = n64;
+#pragma unroll
+    for (int u = 0; u < kLoadGroups; ++u) {
+      const int b = base0 + u * kPlanThreads + tid;
+      const bool in = b < p.B;
+      const int nb = nbv[u];
+      if (b < kPlanCacheSeqs) s_n[b] = nb;
+      if (in && writes) {
+        s_t0[b] = t0v[u];
+        s_d[b] = dv[u];
+      }
+      ksum += nb;
+      nmax = max(nmax, nb);
+      if (!direct) {   // (every lane takes part: the histogram adds are per wave and distinct bin)
+        const int n64 = (nb + 63) >> 6;
+        wave_bucket_add(s_hist, min(n64, kHistBins - 1), in);
+        if (in && n64 > kHistBins - 2) {
+          const int sl = atomicAdd(&s_nlong, 1);
+          if (sl < kLongSeqs) s_long[sl] = n64;
+        }
       }
     }
   }
@@ -314,19 +394,21 @@ __global__ __launch_bounds__(kPlanThreads) void verify_attn_plan(AttnParams p, i
 
   // (2) the shorter items: count per length bucket (bucket 0 = longest), and
   // the number of full-chunk items
+  const float rchunk = 1.f / (float)chunk, rchunk1 = 1.f / (float)(chunk + 1);
   auto split_of = [&](int N, int& full, int& tail_len) {   // full chunks, and the shorter item's length (-1: none)
-    full = N / chunk;
-    tail_len = (N % chunk != 0 || N == 0) ? N - full * chunk : -1;
+    full = floor_div_keys(N, chunk, rchunk);
+    tail_len = (N - full * chunk != 0 || N == 0) ? N - full * chunk : -1;
   };
   auto bucket_of = [&](int len) {   // (len <= chunk <= kMaxChunk: the product fits 32 bits)
-    return kLenBuckets - 1 - (len * kLenBuckets) / (chunk + 1);
+    return kLenBuckets - 1 - floor_div_keys(len * kLenBuckets, chunk + 1, rchunk1);
   };
   long long nfull = 0;
-  for (int b = tid; b < p.B; b += kPlanThreads) {
-    int full, tl;
-    split_of(keys_of(b), full, tl);
+  for (int base = 0; base < p.B; base += kPlanThreads) {   // (uniform trip count: the bucket adds are per wave)
+    const int b = base + tid;
+    int full = 0, tl = -1;
+    if (b < p.B) split_of(keys_of(b), full, tl);
     nfull += (long long)full * p.Hkv;
-    if (tl >= 0) atomicAdd(&s_bucket[bucket_of(tl)], 1);
+    wave_bucket_add(s_bucket, tl >= 0 ? bucket_of(tl) : 0, tl >= 0);
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) nfull += __shfl_xor(nfull, off);
@@ -344,119 +426,85 @@ __global__ __launch_bounds__(kPlanThreads) void verify_attn_plan(AttnParams p, i
     s_bucket[tid] = incl - c;
   }
   __syncthreads();
-  for (int b = tid; b < p.B; b += kPlanThreads) {
-    int full, tl;
-    split_of(keys_of(b), full, tl);
-    const int tp = tl >= 0 ? (int)(s_full + (long long)atomicAdd(&s_bucket[bucket_of(tl)], 1) * p.Hkv) : -1;
-    if (b < kPlanCacheSeqs) s_tail[b] = tp;
-    else tail_pos[b] = tp;
+  for (int base = 0; base < p.B; base += kPlanThreads) {
+    const int b = base + tid;
+    int full = 0, tl = -1;
+    if (b < p.B) split_of(keys_of(b), full, tl);
+    const int slot = wave_bucket_add(s_bucket, tl >= 0 ? bucket_of(tl) : 0, tl >= 0);
+    const int tp = tl >= 0 ? (int)(s_full + (long long)slot * p.Hkv) : -1;
+    if (b < p.B) {
+      if (writes) s_tail[b] = tp;
+      else tail_pos[b] = tp;
+    }
   }
   __syncthreads();
 
-  // (3) descriptors: sequences in groups of kPlanThreads.  Natural index e of
-  // the group's items -> (sequence by binary search over the inclusive scan of
-  // items per sequence, head, split) -> scheduled index.
+  // (3) per-sequence item starts: sequences in groups of kPlanThreads, inclusive
+  // scans of the items and of the full-chunk items (within each wave by
+  // shuffles, then the totals of the waves before it).  verify_attn_items
+  // writes the descriptors from these tables, one thread per sequence, over
+  // many workgroups.
+  int* full_base = p.plan + kPlanHeader + 3 * p.B + 1;
+  if (tid == 0) p.plan[3] = 0;   // split sequences, counted as their descriptors are written
   int carry = 0, fcarry = 0;
   for (int base = 0; base < p.B; base += kPlanThreads) {
     const int b = base + tid;
-    int v = 0, N = 0, ns = 1, full = 0, tl = -1;
+    int v = 0, full = 0, tl = -1;
     if (b < p.B) {
-      N = keys_of(b);
-      ns = max(1, (N + chunk - 1) / chunk);
-      v = ns * p.Hkv;
-      split_of(N, full, tl);
-      if (list_splits && ns > 1) split_list[atomicAdd(&s_nsplit, 1)] = b;   // (any order: each head merges alone)
+      split_of(keys_of(b), full, tl);
+      v = (full + (tl >= 0 ? 1 : 0)) * p.Hkv;
     }
-    // inclusive scans of v and of the full-chunk items: within each wave by
-    // shuffles, then the totals of the waves before it
-    int sv = v, sf = b < p.B ? full * p.Hkv : 0;
+    int sv = v, sf = full * p.Hkv;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int a = __shfl_up(sv, off), f = __shfl_up(sf, off);
       if (lane >= off) { sv += a; sf += f; }
     }
     if (lane == 63) { s_wsum[0][tid >> 6] = sv; s_wsum[1][tid >> 6] = sf; }
-    s_keys[tid] = N;
     __syncthreads();
     for (int w = 0; w < (tid >> 6); ++w) { sv += s_wsum[0][w]; sf += s_wsum[1][w]; }
-    scan[tid] = sv;
-    fscan[tid] = sf;
-    __syncthreads();
-    if (b < p.B) p.plan[kPlanHeader + b] = carry + scan[tid] - v;
-    const int n = min(kPlanThreads, p.B - base);
-    const int group_items = scan[n - 1];
-    // one thread per sequence (no search, no division) unless the group's
-    // longest sequence would keep its thread past kSearchCost times the
-    // per-thread share of a search over the group's items
-    if (!direct && __syncthreads_or(v > kSearchCost * ((group_items + kPlanThreads - 1) / kPlanThreads)) == 0) {
-      if (b < p.B) {
-        const int t0b = b < kPlanCacheSeqs ? s_t0[b] : p.q_start[b];
-        const int Db = b < kPlanCacheSeqs ? s_d[b] : seq_drafts(p, b);
-        const int tpos = b < kPlanCacheSeqs ? s_tail[b] : tail_pos[b];
-        const int fbase = fcarry + fscan[tid] - full * p.Hkv;
-        for (int hj = 0; hj < p.Hkv; ++hj)
-          for (int sj = 0; sj < ns; ++sj) {
-            const int pos = sj < full ? fbase + hj * full + sj : tpos + hj;
-            if (pos < 0 || pos >= p.item_cap) continue;
-            ItemDesc d;
-            d.b = b;
-            d.h = hj;
-            d.k_begin = sj * chunk;
-            d.k_end = min(N, (sj + 1) * chunk);
-            d.t0 = t0b;
-            d.D = Db;
-            d.N = N;
-            d.nsplit = ns;
-            p.items[pos] = d;
-          }
-      }
-    } else {
-      for (int e = tid; e < group_items; e += kPlanThreads) {
-        int lo = 0, hi = n - 1;                 // first j with scan[j] > e
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          if (scan[mid] > e) hi = mid;
-          else lo = mid + 1;
-        }
-        const int bj = base + lo;
-        const int Nj = s_keys[lo];
-        const int r = e - (lo > 0 ? scan[lo - 1] : 0);
-        int nsj = 1, fj = 0, hj = r, sj = 0;    // (one item per head: no division)
-        if (Nj > chunk) {
-          nsj = (Nj + chunk - 1) / chunk;
-          fj = Nj / chunk;
-          hj = r / nsj;
-          sj = r - hj * nsj;
-        } else if (Nj == chunk) {
-          fj = 1;
-        }
-        const int pos = sj < fj ? fcarry + (lo > 0 ? fscan[lo - 1] : 0) + hj * fj + sj
-                                : (bj < kPlanCacheSeqs ? s_tail[bj] : tail_pos[bj]) + hj;
-        if (pos < 0 || pos >= p.item_cap) continue;
-        ItemDesc d;
-        d.b = bj;
-        d.h = hj;
-        d.k_begin = sj * chunk;
-        d.k_end = min(Nj, (sj + 1) * chunk);
-        d.t0 = bj < kPlanCacheSeqs ? s_t0[bj] : p.q_start[bj];
-        d.D = bj < kPlanCacheSeqs ? s_d[bj] : seq_drafts(p, bj);
-        d.N = Nj;
-        d.nsplit = nsj;
-        p.items[pos] = d;
+    if (b < p.B) {
+      p.plan[kPlanHeader + b] = carry + sv - v;
+      if (writes) {
+        s_fbase[b] = fcarry + sf - full * p.Hkv;
+      } else {
+        full_base[b] = fcarry + sf - full * p.Hkv;
       }
     }
-    carry += scan[kPlanThreads - 1];
-    fcarry += fscan[kPlanThreads - 1];
+    if (tid == kPlanThreads - 1) { s_wsum[0][0] = carry + sv; s_wsum[1][0] = fcarry + sf; }
     __syncthreads();
+    carry = s_wsum[0][0];
+    fcarry = s_wsum[1][0];
+    __syncthreads();
+  }
+  if (writes) {
+    for (int idx = tid; idx < p.B * p.Hkv; idx += kPlanThreads) {
+      const int b = idx / p.Hkv;
+      write_item_descs(p, b, idx - b * p.Hkv, chunk, keys_of(b), s_t0[b], s_d[b], s_fbase[b], s_tail[b],
+                       list_splits);
+    }
   }
   if (tid < 8) p.plan[8 + tid] = 0;
   if (tid == 0) {
     p.plan[0] = chunk;
     p.plan[1] = carry;
     p.plan[2] = (int)s_full;
-    p.plan[3] = s_nsplit;
     p.plan[kPlanHeader + p.B] = carry;
   }
+}
+
+
+
+// The descriptors of batches with more than kPlanWrites (sequence, KV head)
+// pairs, one thread per pair.
+__global__ __launch_bounds__(256) void verify_attn_items(AttnParams p, int list_splits) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= p.B * p.Hkv) return;
+  const int chunk = p.plan[0];
+  if (chunk < 64) return;
+  const int b = idx / p.Hkv;
+  write_item_descs(p, b, idx - b * p.Hkv, chunk, seq_keys(p, b), p.q_start[b], seq_drafts(p, b),
+                   p.plan[kPlanHeader + 3 * p.B + 1 + b], p.plan[kPlanHeader + p.B + 1 + b], list_splits);
 }
 
 // ---------------------------------------------------------------------------
@@ -485,9 +533,7 @@ struct FusedPlan {
 // ceil(n / c) for 0 <= n < 2^24 and 64 <= c <= kMaxChunk: the float quotient
 // (relative error far below 1/n) corrected to the exact floor, then rounded up.
 __device__ __forceinline__ int ceil_div_keys(int n, int c, float rc) {
-  int q = (int)((float)n * rc);
-  if (q * c > n) --q;
-  if ((q + 1) * c <= n) ++q;
+  const int q = floor_div_keys(n, c, rc);
   return q + (q * c < n ? 1 : 0);
 }
 
@@ -1984,7 +2030,7 @@ static AttnLayout attn_layout(int B, int Hkv, int G, int HD, int max_pages, int 
   L.item_cap = (int)cap;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += (bytes + 255) / 256 * 256; return o; };
-  L.plan_off = take((size_t)(kPlanHeader + 3 * B + 1) * 4);
+  L.plan_off = take((size_t)(kPlanHeader + 4 * B + 1) * 4);
   L.items_off = take((size_t)cap * sizeof(ItemDesc));
   L.ml_off = take((size_t)cap * L.rpad * 2 * 4);
   L.o_off = take((size_t)cap * L.rpad * HD * 4);
@@ -2072,9 +2118,12 @@ hipError_t sdv_attn_launch(const SdAttnLaunch& a) {
   p.ovh_keys = kItemOverheadBytes / (4 * a.head_dim);
   p.list_splits = cunits > kCombineGrid;
   p.fused = a.B <= kFusedSeqs;   // small batches: the main kernels make the plan themselves
-  if (!p.fused)
+  if (!p.fused) {
     verify_attn_plan<<<1, kPlanThreads, 0, a.stream>>>(p, a.kv_chunk, slots, kItemOverheadBytes / (4 * a.head_dim),
-                                                       cunits > kCombineGrid);
+                                                       p.list_splits);
+    if ((long long)a.B * a.Hkv > kPlanWrites)
+      verify_attn_items<<<(int)(((long long)a.B * a.Hkv + 255) / 256), 256, 0, a.stream>>>(p, p.list_splits);
+  }
   if (a.head_dim == 128) {
     if (a.out_f32) launch_main<128, 1>(L.variant, p, grid, a.stream, a.v_key_major);
     else launch_main<128, 0>(L.variant, p, grid, a.stream, a.v_key_major);

@@ -89,10 +89,11 @@ def run_and_read_plan(inp, kv_chunk=0):
 
 def check_items(ws, inp, chunk, items):
     """The descriptors the plan wrote: 8 int32 each (b, h, k_begin, k_end, t0,
-    D, N, nsplit) in schedule order after the plan header and its 3B+1 ints,
-    rounded up to 256 bytes; item_start[b] at int 16 + b."""
+    D, N, nsplit) in schedule order after the plan header and its 4B+1 ints
+    (item starts, shorter-item positions, split list, full-item bases), rounded
+    up to 256 bytes; item_start[b] at int 16 + b."""
     B, hkv = inp.spec.batch, inp.spec.kv_heads
-    off = -(-(16 + 3 * B + 1) * 4 // 256) * 256 // 4
+    off = -(-(16 + 4 * B + 1) * 4 // 256) * 256 // 4
     words = ws[:4 * (off + 8 * items)].view(torch.int32).cpu().numpy()
     desc = words[off:off + 8 * items].reshape(items, 8)
     kv = np.minimum(inp.kv_len.cpu().numpy().astype(np.int64), inp.block_table.shape[1] * PAGE)
