@@ -897,7 +897,8 @@ def write_batch_profile(bench_json: str, kt_dir: str):
         f.write("# Verify attention against the batch size (H_kv=8, G=8, d=128, D=3; B sequences of N keys):\n"
                 "# median kernel durations per point from a rocprofv3 kernel trace, and the call time with HIP\n"
                 "# events in the same run.  The plan and the combine are the launches whose cost grows with B;\n"
-                "# batches of up to 32 sequences plan inside the main kernel (plan_us 0).\n"
+                "# batches of up to 32 sequences plan inside the main kernel (plan_us 0); plan_us includes the\n"
+                "# descriptor kernel of batches past 4096 sequence-head pairs.\n"
                 "$ cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace -d OUT/kt_batch -o run "
                 "--output-format csv -- python3 REPO/bench.py --batch-sweep\n")
         f.write("batch,kv_len,plan_us,main_us,combine_us,call_us_events,hbm_frac\n")
@@ -905,11 +906,11 @@ def write_batch_profile(bench_json: str, kt_dir: str):
             lo = ends[k * per_point - 1] + 1 if k > 0 else 0
             hi = ends[(k + 1) * per_point - 1] + 1
             med = {}
-            for part, key in (("plan", "verify_attn_plan"), ("main", "verify_attn_main"), ("wide", "verify_attn_wide"),
-                              ("combine", "verify_attn_combine")):
+            for part, key in (("plan", "verify_attn_plan"), ("items", "verify_attn_items"), ("main", "verify_attn_main"),
+                              ("wide", "verify_attn_wide"), ("combine", "verify_attn_combine")):
                 d = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows[lo:hi] if key in r["Kernel_Name"]]
                 med[part] = statistics.median(d) / 1e3 if d else 0.0
-            f.write(f"{pt['batch']},{pt['kv_len']},{med['plan']:.1f},{med['main'] + med['wide']:.1f},"
+            f.write(f"{pt['batch']},{pt['kv_len']},{med['plan'] + med['items']:.1f},{med['main'] + med['wide']:.1f},"
                     f"{med['combine']:.1f},{pt['attention_ms'] * 1e3:.1f},{pt['hbm_frac']:.3f}\n")
     print(f"wrote {path}")
 
