@@ -190,13 +190,25 @@ __global__ __launch_bounds__(256) void verify_gemm(GemmParams p) {
 }
 
 // y = bf16(sum over splits, in split order, of the fp32 partials); 4 columns per thread.
+// The partials come from other XCDs' L2 writebacks, so each load waits a full
+// memory round trip: they are issued 8 at a time, then added in split order.
+constexpr int kReduceBatch = 8;
 __global__ __launch_bounds__(256) void verify_gemm_reduce(GemmParams p) {
   const size_t q = (size_t)blockIdx.x * 256 + threadIdx.x;   // index of a 4-column group
   const size_t total = (size_t)p.m * p.n / 4;
   if (q >= total) return;
   const size_t mn = (size_t)p.m * p.n;
-  f32x4 s = *(const f32x4*)(p.part + q * 4);
-  for (int z = 1; z < p.ksplit; ++z) s += *(const f32x4*)(p.part + (size_t)z * mn + q * 4);
+  const float* src = p.part + q * 4;
+  f32x4 s = *(const f32x4*)src;
+  for (int z0 = 1; z0 < p.ksplit; z0 += kReduceBatch) {
+    f32x4 v[kReduceBatch];
+#pragma unroll
+    for (int j = 0; j < kReduceBatch; ++j)
+      v[j] = z0 + j < p.ksplit ? *(const f32x4*)(src + (size_t)(z0 + j) * mn) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < kReduceBatch; ++j)
+      if (z0 + j < p.ksplit) s += v[j];
+  }
   const bf16x4 t = {(__bf16)s[0], (__bf16)s[1], (__bf16)s[2], (__bf16)s[3]};
   *(u32x2*)(p.y + q * 4) = __builtin_bit_cast(u32x2, t);
 }

@@ -5,7 +5,8 @@ Bound per element: the bf16 rounding of the output (half an ulp, at most
 2^-9 |y|, taken as 2^-8 |y|) plus an fp32 accumulation error of at most
 2 K 2^-24 sum_k |x W| (sum_k |x W| from the oracle).  The cases cover every
 tile height (32, 64, 128 rows), rows that do not fill a tile, split and
-unsplit K, the expert shape N = K = 6144, and sampled rows at 4096 rows."""
+unsplit K, the few-rows path (M <= 32 with 16-row workgroups), the expert
+shape N = K = 6144, and sampled rows at 4096 rows."""
 
 import numpy as np
 import pytest
@@ -47,6 +48,10 @@ def _check(x, w, y, rows=None):
 @pytest.mark.parametrize("m,n,k", [
     (1, 128, 64), (5, 256, 640), (32, 384, 1024), (33, 128, 2048), (64, 256, 6144),
     (100, 512, 1280), (256, 384, 768), (300, 256, 512), (513, 640, 1024),
+    # the few-rows path (M <= 32, at least one 16-row workgroup per CU): two k-steps
+    # for eight waves, a step count that is not a multiple of the waves or of the
+    # load batch, rows that fill one or two 16-row blocks in part
+    (17, 4096, 64), (32, 4096, 1984), (3, 4224, 6208), (16, 4096, 192), (31, 6144, 320),
 ])
 def test_shapes(m, n, k):
     x, w = linear_inputs(m, n, k, seed=m + n + k, device="cuda")
@@ -79,8 +84,9 @@ def test_deterministic_and_ignores_output_contents():
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
 
 
-def test_identity_weight_is_exact():
-    x, _ = linear_inputs(40, 256, 256, seed=9, device="cuda")
-    w = torch.eye(256, dtype=torch.bfloat16, device="cuda")
+@pytest.mark.parametrize("m,n", [(40, 256), (20, 4096), (9, 4096)])
+def test_identity_weight_is_exact(m, n):
+    x, _ = linear_inputs(m, n, n, seed=9, device="cuda")
+    w = torch.eye(n, dtype=torch.bfloat16, device="cuda")
     y = _run(x, w)
     assert torch.equal(y.view(torch.int16), x.view(torch.int16))
