@@ -186,8 +186,10 @@ __device__ __forceinline__ void load_chunk(const float* src, int j0, int V, floa
 
 // ---------------------------------------------------------------------------
 // MODE 0: greedy (lowest-index maximum); 1: stochastic (maximum and sum of
-// exp(x - max)); 2: relaxed acceptance (all of those, and for draft rows the
-// sum of exp(x - max) (x - max), from which the row's entropy follows).
+// exp(x - max)); 2: relaxed greedy acceptance (all of those, and for draft rows
+// the sum of exp(x - max) (x - max), from which the row's entropy follows);
+// 3: relaxed stochastic acceptance (as 2 without the argmax, which only the
+// greedy test reads).
 // Chunk g of the rows x chunks grid: row g / nchunk, chunk g % nchunk, whose
 // logits the caller has loaded into x.
 template <int MODE, int VEC4>
@@ -201,7 +203,7 @@ __device__ __forceinline__ void rowstats_chunk(const AccParams& p, int g, const 
   r.idx = 0;
   r.s = 0.0;
   float m;
-  if (MODE != 1) {
+  if (MODE == 0 || MODE == 2) {
     // lowest-index maximum: strict '>' over increasing indices; a row of -inf
     // still reports a real index (first element inside the vocabulary)
     m = -INFINITY;
@@ -221,16 +223,33 @@ __device__ __forceinline__ void rowstats_chunk(const AccParams& p, int g, const 
   }
   r.m = m;
   if (MODE != 0) {
-    const bool ent = MODE == 2 && row >= p.T;   // (uniform over the workgroup)
+    const bool ent = MODE >= 2 && row >= p.T;   // (uniform over the workgroup)
     double s = 0.0, s1 = 0.0;
     if (m != -INFINITY) {
-      // exp(x - m) as 2^((x - m) log2 e); fp32 terms, fp64 running sums
+      // exp(x - m) as 2^((x - m) log2 e): fp32 terms, fp64 running sums, the
+      // terms summed eight at a time first (MODE 2, whose argmax holds more
+      // registers: one at a time)
       const float ml = m * 1.4426950408889634f;
+      if constexpr (MODE == 2) {
 #pragma unroll
-      for (int k = 0; k < kPerThread; ++k) {
-        const float e = fast_exp2(fmaf(x[k], 1.4426950408889634f, -ml));
-        s += (double)e;
-        if (ent && e > 0.f) s1 += (double)(e * (x[k] - m));
+        for (int k = 0; k < kPerThread; ++k) {
+          const float e = fast_exp2(fmaf(x[k], 1.4426950408889634f, -ml));
+          s += (double)e;
+          if (ent && e > 0.f) s1 += (double)(e * (x[k] - m));
+        }
+      } else {
+#pragma unroll
+        for (int k0 = 0; k0 < kPerThread; k0 += 8) {
+          float a = 0.f, a1 = 0.f;
+#pragma unroll
+          for (int k = k0; k < k0 + 8; ++k) {
+            const float e = fast_exp2(fmaf(x[k], 1.4426950408889634f, -ml));
+            a += e;
+            if (ent) a1 += e > 0.f ? e * (x[k] - m) : 0.f;
+          }
+          s += (double)a;
+          if (ent) s1 += (double)a1;
+        }
       }
       s = block_sum(s, sd);
       if (ent) s1 = block_sum(s1, sd);
@@ -251,9 +270,10 @@ __device__ __forceinline__ void rowstats_load(const AccParams& p, int g, float (
 
 // A persistent grid over the rows x chunks: each workgroup takes chunks
 // blockIdx.x, + gridDim.x, ..., and loads the next one before it reduces the
-// current one, so that its loads stay in flight through the reductions.
+// current one, so that its loads stay in flight through the reductions.  Four
+// waves per SIMD (at most 128 VGPRs) keep every workgroup of the grid resident.
 template <int MODE, int VEC4>
-__global__ __launch_bounds__(kAccThreads) void accept_rowstats(AccParams p, int total) {
+__global__ __launch_bounds__(kAccThreads, 4) void accept_rowstats(AccParams p, int total) {
   __shared__ float sm[4];
   __shared__ int si[4];
   __shared__ double sd[4];
@@ -903,9 +923,14 @@ hipError_t sdv_accept_launch(const SdAccLaunch& a) {
   const size_t rows = need_draft ? (size_t)a.T + drows : (size_t)a.T;
   const unsigned grid1 = (unsigned)(rows * L.nchunk);
   const unsigned rs_grid = std::max(1u, std::min(grid1, (unsigned)kRowstatsWGs));
-  if (a.lossy) {
+  if (a.lossy && a.stochastic) {
+    if (vec4) accept_rowstats<3, 1><<<rs_grid, kAccThreads, 0, a.stream>>>(p, (int)grid1);
+    else accept_rowstats<3, 0><<<rs_grid, kAccThreads, 0, a.stream>>>(p, (int)grid1);
+  } else if (a.lossy) {
     if (vec4) accept_rowstats<2, 1><<<rs_grid, kAccThreads, 0, a.stream>>>(p, (int)grid1);
     else accept_rowstats<2, 0><<<rs_grid, kAccThreads, 0, a.stream>>>(p, (int)grid1);
+  }
+  if (a.lossy) {
     if (drows > 0) {
       const unsigned grid2 = (unsigned)(drows * L.nchunk);
       if (vec4) accept_jsd<1><<<grid2, kAccThreads, 0, a.stream>>>(p);
