@@ -47,6 +47,7 @@ constexpr int kAccThreads = 256;
 #endif
 constexpr int kChunk = SDV_ACC_CHUNK;
 constexpr int kPerThread = kChunk / kAccThreads;  // 32 at the default chunk
+constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kSChunk = 4096;                     // logits per sampling workgroup
 constexpr int kSPerThread = kSChunk / kAccThreads;  // 16: one slice of the sampling search per thread
 static_assert(kSPerThread % 4 == 0 && kSPerThread <= 64, "a slice is scanned by one wave");
@@ -325,7 +326,9 @@ __device__ __forceinline__ double row_lse64(const AccParams& p, int prow) {
 // 443 u^10/604800 - 559 u^12/2721600 + ...) (relative error below 2e-8 for
 // x < 1); for x >= 1, t_j = P ((1 + e^-x) h - x e^-x) with h = ln 2 -
 // ln(1 + e^-x), which has no cancellation there and gives P ln 2 when one side
-// is zero.  Terms in fp32 with the hardware exp2/log2, sums in fp64.
+// is zero.  Both forms come from P and z = e^(-x/2) (sqrt(p_j q_j) = P z,
+// e^-x = z^2), so an element costs three transcendentals and no divergent
+// branch.  Terms in fp32 with the hardware exp2/log2, sums in fp64.
 template <int VEC4>
 __global__ __launch_bounds__(kAccThreads) void accept_jsd(AccParams p) {
   __shared__ double sd[4];
@@ -368,17 +371,15 @@ __global__ __launch_bounds__(kAccThreads) void accept_jsd(AccParams p) {
       const float a = tl[k] - lse_p, bq = dl[k] - lse_q;     // ln p_j, ln q_j
       const float hi = fmaxf(a, bq);
       const float x = fabsf((tl[k] - dl[k]) - dlse);          // |ln p_j - ln q_j| (inf: one side 0)
-      float t;
-      if (x < 1.f) {
-        const float u = 0.5f * x, u2 = u * u;
-        const float poly = u2 * (1.f + u2 * u2 * (1.f / 72.f + u2 * (-1.f / 360.f + u2 * (443.f / 604800.f +
-                                                                       u2 * (-559.f / 2721600.f)))));
-        t = __expf(0.5f * (a + bq)) * poly;
-      } else {
-        const float y = __expf(-x);
-        const float h = 0.69314718f * (1.f - __log2f(1.f + y));
-        t = __expf(hi) * ((1.f + y) * h - (y > 0.f ? y * x : 0.f));
-      }
+      const float P = fast_exp2(hi * kLog2e);
+      const float z = fast_exp2(x * (-0.5f * kLog2e));
+      const float u = 0.5f * x, u2 = u * u;
+      const float poly = u2 * (1.f + u2 * u2 * (1.f / 72.f + u2 * (-1.f / 360.f + u2 * (443.f / 604800.f +
+                                                                     u2 * (-559.f / 2721600.f)))));
+      const float y = z * z;
+      const float h = 0.69314718f * (1.f - __log2f(1.f + y));
+      const float tb = (1.f + y) * h - (y > 0.f ? y * x : 0.f);
+      const float t = P * (x < 1.f ? z * poly : tb);
       if (hi != -INFINITY) part += t;                         // (p_j = q_j = 0: no term)
     }
     acc += (double)part;
