@@ -780,7 +780,7 @@ def write_lossy_profile(bench_json: str, kt_dir: str):
         f.write(f"# rocprofv3 kernel-trace summary of the accept kernels, workload {wl} (tau = "
                 f"{line['config']['js_threshold']}):\n"
                 "# each step runs the lossless call (accept_rowstats<1,...>, accept_finish<false>, accept_draw) and\n"
-                "# the relaxed call (accept_rowstats<2,...>, accept_jsd, accept_finish<true>, accept_draw; the draw\n"
+                "# the relaxed call (accept_rowstats<3,...>, accept_jsd, accept_finish<true>, accept_draw; the draw\n"
                 "# kernel is the same in both, so its line counts two launches per step).  Calls = clock-settle +\n"
                 "# warmup + timed steps.  Durations in ns.\n"
                 "$ cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d OUT/kt_lossy "
@@ -789,9 +789,9 @@ def write_lossy_profile(bench_json: str, kt_dir: str):
         for r in stats:
             f.write(",".join([r["Name"], r["Calls"], r["TotalDurationNs"], r["AverageNs"], r["Percentage"],
                               r["MinNs"], r["MaxNs"], r["StdDev"]]) + "\n")
-        lossy = sum(float(r["AverageNs"]) for r in stats if "<2" in r["Name"] or "jsd" in r["Name"]
+        lossy = sum(float(r["AverageNs"]) for r in stats if "rowstats<3" in r["Name"] or "jsd" in r["Name"]
                     or "finish<true>" in r["Name"] or "accept_draw" in r["Name"])
-        f.write(f"relaxed accept call (rowstats<2> + jsd + finish<true> + draw averages): {lossy / 1e3:.1f} us\n")
+        f.write(f"relaxed accept call (rowstats<3> + jsd + finish<true> + draw averages): {lossy / 1e3:.1f} us\n")
         f.write(f"bench.py in the same call: relaxed accept {line['lossy_accept_ms'] * 1e3:.1f} us/step, lossless "
                 f"{line['lossless_accept_ms'] * 1e3:.1f} us/step (HIP events), HBM {line['roofline']['frac']:.3f} "
                 f"of peak, mean AL {line['mean_accept_len']:.3f} (lossless {line['mean_accept_len_lossless']:.3f})\n")
