@@ -2008,7 +2008,15 @@ static int attn_slots(int cus, int variant) { return cus * (variant == 0 ? 2 : 1
 constexpr int kMaxCus = 256;
 constexpr int kCombineGrid = 32 * kMaxCus;   // combine workgroups: 8 rows of one (sequence, KV head) each
 
+// The chunk the plan is given: the caller's, or for caches no longer than the
+// smallest automatic chunk that chunk itself (the plan would choose it after a
+// search, and no sequence is split).
+static int plan_chunk(int kv_chunk, int max_pages) {
+  return kv_chunk == 0 && (long long)max_pages * kPage <= kMinChunk ? kMinChunk : kv_chunk;
+}
+
 static AttnLayout attn_layout(int B, int Hkv, int G, int HD, int max_pages, int max_draft, int kv_chunk) {
+  kv_chunk = plan_chunk(kv_chunk, max_pages);
   AttnLayout L;
   const int rmax = G * (1 + max_draft);
   L.variant = attn_variant(rmax);
@@ -2113,7 +2121,9 @@ hipError_t sdv_attn_launch(const SdAttnLaunch& a) {
     p.tmask = masks;
   }
   const long long cunits = (long long)a.B * a.Hkv * (L.rpad / 8);   // combine workgroups, one per 8 rows of a head
-  p.fixed_chunk = a.kv_chunk;
+  p.fixed_chunk = plan_chunk(a.kv_chunk, a.max_pages);
+  // no sequence is longer than a fixed chunk: nothing is split, and the combine launch is left out
+  const bool no_split = p.fixed_chunk > 0 && (long long)a.max_pages * kPage <= p.fixed_chunk;
   p.slots = slots;
   p.ovh_keys = kItemOverheadBytes / (4 * a.head_dim);
   p.list_splits = cunits > kCombineGrid;
@@ -2133,6 +2143,7 @@ hipError_t sdv_attn_launch(const SdAttnLaunch& a) {
   }
   // one workgroup per (sequence, KV head, 8 rows), or for large batches a
   // bounded grid over the split sequences only (their number is known on the device)
+  if (no_split) return hipGetLastError();
   if (cunits <= kCombineGrid) {
     const int cgrid = (int)cunits;
     if (a.head_dim == 128) {

@@ -192,6 +192,10 @@ def test_deterministic():
     (8, [31, 20], [700, 1333], 0),                # R <= 256 (row split)
     (8, [19, 12], [700, 1333], 0),                # R = 160 (blocks 4-5 split by tile parity)
     (2, [3, 0, 1, 2] * 40, [37, 900, 5000, 260] * 40, 0),   # short items: counter-driven fetch
+    # caches of at most 256 keys: never split, and no combine launch (plan in the
+    # main kernel for B <= 32, the plan kernel past that)
+    (8, [3, 7, 0, 15], [256, 9, 200, 17], 0),
+    (4, [3, 1, 0, 2] * 12, [256, 129, 64, 250] * 12, 0),
 ])
 def test_workspace_contents_never_matter(G, drafts, kv, kv_chunk):
     """The call initialises every workspace byte it reads: with the workspace
