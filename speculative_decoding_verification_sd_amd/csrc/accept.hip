@@ -415,12 +415,11 @@ __device__ __forceinline__ void row_relaxed_stats(const AccParams& p, int r, dou
 // ---------------------------------------------------------------------------
 // LOSSY: a draft also passes when the JS distance of its rows is at most tau,
 // and the rows' entropy and JS distance are written out.
+// The greedy decision of sequence b (one workgroup); amax: LDS for its D+1 row argmaxes.
 template <bool LOSSY>
-__global__ __launch_bounds__(kAccThreads) void accept_decide(AccParams p) {
-  extern __shared__ int amax[];                 // [D+1] row argmaxes
+__device__ __forceinline__ void decide_seq(const AccParams& p, int b, int* amax) {
   __shared__ RowPart stage[kDecideSlots];
   __shared__ int first_fail;
-  const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int t0 = p.q_start[b];
   const int D = seq_d(p, b);
@@ -466,6 +465,12 @@ __global__ __launch_bounds__(kAccThreads) void accept_decide(AccParams p) {
   const int n = first_fail;
   for (int k = tid; k <= D; k += kAccThreads) p.out_tokens[t0 + k] = k < n ? p.tokens[d0 + k] : k == n ? amax[n] : -1;
   if (tid == 0) p.accept_len[b] = n + 1;
+}
+
+template <bool LOSSY>
+__global__ __launch_bounds__(kAccThreads) void accept_decide(AccParams p) {
+  extern __shared__ int amax[];                 // [D+1] row argmaxes
+  decide_seq<LOSSY>(p, blockIdx.x, amax);
 }
 
 // ---------------------------------------------------------------------------
@@ -599,13 +604,14 @@ __device__ __forceinline__ double row_lse16(const AccParams& p, int prow, int la
 }
 
 // ---------------------------------------------------------------------------
+// The stochastic decision of sequence b and the sums of its chunks c0, c0 +
+// cstep, ... (one workgroup; the workgroup with c0 = 0 writes the decision).
 template <bool LOSSY>
-__global__ __launch_bounds__(kAccThreads) void accept_finish(AccParams p) {
+__device__ __forceinline__ void finish_seq(const AccParams& p, int b, int c0, int cstep) {
   __shared__ double sd[4];
   __shared__ int s_fail, s_have;
   __shared__ double s_lp, s_lq;
-  const int c = blockIdx.x;
-  const int b = blockIdx.y;
+  const int c = c0;
   const int tid = threadIdx.x;
   const int t0 = p.q_start[b];
   const int D = seq_d(p, b);
@@ -646,7 +652,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_finish(AccParams p) {
         // relaxed: the draft also passes when the JS distance of its rows is at most tau
         double H, js;
         row_relaxed_stats(p, d0 + i, H, js);
-        if (blockIdx.x == 0) {
+        if (c0 == 0) {
           if (p.out_ent) p.out_ent[d0 + i] = (float)H;
           if (p.out_js) p.out_js[d0 + i] = (float)js;
         }
@@ -686,7 +692,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_finish(AccParams p) {
   // sums (residual, p) and the workgroup the chunk's, for accept_draw.
   const float* prow = p.target + (size_t)(t0 + n) * p.V;
   const float* qrow = p.draft + (size_t)(d0 + (n < D ? n : 0)) * p.V;
-  for (int c = blockIdx.x; c < p.nschunk; c += gridDim.x) {
+  for (int c = c0; c < p.nschunk; c += cstep) {
     const int j0 = c * kSChunk + tid * kSPerThread;
     float tl[kSPerThread], dl[kSPerThread];
     if (p.vec4 && j0 + kSPerThread <= p.V) {
@@ -724,18 +730,22 @@ __global__ __launch_bounds__(kAccThreads) void accept_finish(AccParams p) {
   }
 }
 
+template <bool LOSSY>
+__global__ __launch_bounds__(kAccThreads) void accept_finish(AccParams p) {
+  finish_seq<LOSSY>(p, blockIdx.y, blockIdx.x, gridDim.x);
+}
+
 // ---------------------------------------------------------------------------
 // (2) one workgroup per stochastic sequence draws the token from the sums
 // accept_finish left: the first token whose inclusive prefix sum of weights
 // exceeds T = u * Z, found in three levels (chunk, 16-token slice, token).
 // Where rounding leaves T past every prefix of a level, the level takes its
 // last element with weight > 0.
-__global__ __launch_bounds__(kAccThreads) void accept_draw(AccParams p) {
+__device__ __forceinline__ void draw_seq(const AccParams& p, int b) {
   __shared__ double s_wtot[4];
   __shared__ int s_chunk, s_usep, s_slice, s_slice_last;
   __shared__ double s_base, s_slice_base, s_T;
   __shared__ float s_tl[kSPerThread], s_dl[kSPerThread];
-  const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   // Two memory round trips.  The first: the sequence's rows, its decision and
@@ -855,6 +865,19 @@ __global__ __launch_bounds__(kAccThreads) void accept_draw(AccParams p) {
   }
 }
 
+__global__ __launch_bounds__(kAccThreads) void accept_draw(AccParams p) { draw_seq(p, blockIdx.x); }
+
+// The stochastic decision and the draw of sequence b in one workgroup, for
+// calls where accept_finish would run a single workgroup per sequence anyway
+// (one sampling chunk, or enough sequences): a workgroup barrier where the
+// two-kernel path has a launch boundary, the same code on the same data.
+template <bool LOSSY>
+__global__ __launch_bounds__(kAccThreads) void accept_finish_draw(AccParams p) {
+  finish_seq<LOSSY>(p, blockIdx.x, 0, 1);
+  __syncthreads();
+  draw_seq(p, blockIdx.x);
+}
+
 struct AccLayout {
   size_t part_off, seqrec_off, rsum_off, rsub_off, ent_off, jsp_off, total;
   int nchunk, nschunk;
@@ -948,9 +971,14 @@ hipError_t sdv_accept_launch(const SdAccLaunch& a) {
     // workgroups per sequence: all chunks, or about kFinishWGs / B in all when
     // that is fewer (each then takes several chunks)
     const int per_seq = std::max(1, std::min(L.nschunk, (kFinishWGs + a.B - 1) / std::max(a.B, 1)));
-    if (a.lossy) accept_finish<true><<<dim3(per_seq, a.B), kAccThreads, 0, a.stream>>>(p);
-    else accept_finish<false><<<dim3(per_seq, a.B), kAccThreads, 0, a.stream>>>(p);
-    accept_draw<<<a.B, kAccThreads, 0, a.stream>>>(p);
+    if (per_seq == 1) {
+      if (a.lossy) accept_finish_draw<true><<<a.B, kAccThreads, 0, a.stream>>>(p);
+      else accept_finish_draw<false><<<a.B, kAccThreads, 0, a.stream>>>(p);
+    } else {
+      if (a.lossy) accept_finish<true><<<dim3(per_seq, a.B), kAccThreads, 0, a.stream>>>(p);
+      else accept_finish<false><<<dim3(per_seq, a.B), kAccThreads, 0, a.stream>>>(p);
+      accept_draw<<<a.B, kAccThreads, 0, a.stream>>>(p);
+    }
   } else {
     const size_t lds = (size_t)(a.max_draft + 1) * sizeof(int);
     if (a.lossy) accept_decide<true><<<a.B, kAccThreads, lds, a.stream>>>(p);
