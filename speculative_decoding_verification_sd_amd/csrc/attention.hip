@@ -1126,10 +1126,9 @@ __global__ __launch_bounds__(64 * NW, WPC) void verify_attn_main(AttnParams p) {
     // recomputed by the safe pass below with a running max.  Below that bound
     // o and l are far from fp32 overflow.
     constexpr float kOverflow = 0x1p64f;   // row sums above this redo the item
-    // Tiles 0..steady-1 run in the unrolled, pipelined loop: each has a next
-    // tile that needs no causal mask.  steady is a multiple of S, so that the
-    // loop carries no per-step guards and tile `steady` starts the tail with
-    // its scores in sc[0].
+    // Tiles 0..plain-1 run as pipelined steps: each has a next tile that needs
+    // no causal mask.  The first `steady` of them (a multiple of S) run in the
+    // unrolled loop with no per-step guards.
     const int plain = max(0, min(ntiles - 1, (N - D - k_begin) / RG::kTile - 1));
     const int steady = plain - plain % S;
 
@@ -1208,9 +1207,39 @@ __global__ __launch_bounds__(64 * NW, WPC) void verify_attn_main(AttnParams p) {
         if constexpr (S > 6) step(ic<6>{});
         if constexpr (S > 7) step(ic<7>{});
       }
-      // tail: the last plain tiles, the masked ones and the last one, one at a
-      // time with run-time ring stages
-      for (int t = steady; t < ntiles; ++t) {
+      // the plain tiles past the last whole block (fewer than S): the same
+      // pipelined steps behind one uniform guard each.  Their ring stages stay
+      // static (steady is a multiple of S); afterwards the next tile's scores
+      // are moved to sc[0], where the tail takes them.
+      {
+        const int extra = plain - steady;
+        auto step = [&](auto uc) {
+          constexpr int u = decltype(uc)::value;
+          if constexpr (u < S - 1) {
+            if (u < extra) {
+              advance(steady + u, (u + S - 1) % S);
+              if constexpr (ACTIVE) body(uc);
+            }
+          }
+        };
+        step(ic<0>{});
+        step(ic<1>{});
+        step(ic<2>{});
+        step(ic<3>{});
+        step(ic<4>{});
+        step(ic<5>{});
+        step(ic<6>{});
+        if constexpr (ACTIVE) {
+          if (extra & 1) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+              for (int rb = 0; rb < NRB; ++rb) sc[0][kb][rb] = sc[1][kb][rb];
+          }
+        }
+      }
+      // tail: the masked tiles and the last one, one at a time with run-time ring stages
+      for (int t = plain; t < ntiles; ++t) {
         const bool has_next = t + 1 < ntiles;
         if (has_next) {
           advance(t, (t + S - 1) % S);
