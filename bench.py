@@ -888,10 +888,20 @@ def write_batch_profile(bench_json: str, kt_dir: str):
         line = json.loads(f.read().strip().splitlines()[-1])
     rows = [r for r in _rocprof_csv(kt_dir, "kernel_trace") if "sdv::" in r["Kernel_Name"]]
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
-    # every attention call ends with one combine launch (batches of up to 32 sequences make
-    # their plan inside the main kernel, so the plan launch does not mark every call)
-    ends = [i for i, r in enumerate(rows) if "verify_attn_combine" in r["Kernel_Name"]]
-    per_point = len(ends) // len(line["points"])
+    # every attention call has exactly one main launch (the plan may run inside it, and caches
+    # that cannot be split have no combine launch): a plan or descriptor launch belongs to the
+    # next main launch's call, a combine launch to the previous one's
+    call_of, mains = [], 0
+    for r in rows:
+        name = r["Kernel_Name"]
+        if "verify_attn_main" in name or "verify_attn_wide" in name:
+            call_of.append(mains)
+            mains += 1
+        elif "verify_attn_combine" in name:
+            call_of.append(mains - 1)
+        else:
+            call_of.append(mains)
+    per_point = mains // len(line["points"])
     path = os.path.join(ROOT, "profiles", "verify_attn_batch_sweep_hkv8_g8_d128_D3.txt")
     with open(path, "w") as f:
         f.write("# Verify attention against the batch size (H_kv=8, G=8, d=128, D=3; B sequences of N keys):\n"
@@ -903,12 +913,12 @@ def write_batch_profile(bench_json: str, kt_dir: str):
                 "--output-format csv -- python3 REPO/bench.py --batch-sweep\n")
         f.write("batch,kv_len,plan_us,main_us,combine_us,call_us_events,hbm_frac\n")
         for k, pt in enumerate(line["points"]):
-            lo = ends[k * per_point - 1] + 1 if k > 0 else 0
-            hi = ends[(k + 1) * per_point - 1] + 1
+            lo, hi = k * per_point, (k + 1) * per_point
+            sel = [r for r, c in zip(rows, call_of) if lo <= c < hi]
             med = {}
             for part, key in (("plan", "verify_attn_plan"), ("items", "verify_attn_items"), ("main", "verify_attn_main"),
                               ("wide", "verify_attn_wide"), ("combine", "verify_attn_combine")):
-                d = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows[lo:hi] if key in r["Kernel_Name"]]
+                d = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in sel if key in r["Kernel_Name"]]
                 med[part] = statistics.median(d) / 1e3 if d else 0.0
             f.write(f"{pt['batch']},{pt['kv_len']},{med['plan'] + med['items']:.1f},{med['main'] + med['wide']:.1f},"
                     f"{med['combine']:.1f},{pt['attention_ms'] * 1e3:.1f},{pt['hbm_frac']:.3f}\n")
