@@ -8,11 +8,14 @@
 // W (N*K*2 bytes); from about 312 rows on (2.5 PFLOP/s over 8 TB/s) it is
 // bound by the bf16 MFMA rate.
 //
-// A workgroup of 4 waves computes a BM x BN tile of y (BM = 32, 64 or 128 and
-// BN = 128 or 256, chosen by M) over a range of K.  x and W tiles of 64 k
-// travel global -> LDS with global_load_lds_dwordx4 into a ring of S stages,
-// and each wave multiplies 32x32 blocks with v_mfma_f32_32x32x16_bf16 (A =
-// rows of x, B = rows of W, both read from LDS as 16-byte chunks).  When M
+// A workgroup computes a BM x BN tile of y (BM = 32, 64, 128 or 256 and
+// BN = 128 or 256, chosen by M) over a range of K: 4 waves for the 32- and
+// 64-row tiles, 8 (two per SIMD, so that one wave's MFMAs run while the other
+// waits at the ring) for the 128- and 256-row tiles, which fill the LDS at one
+// workgroup per CU.  x and W tiles of 64 k travel global -> LDS with global_load_lds_dwordx4
+// into a ring of S stages, and each wave multiplies 32x32 blocks with
+// v_mfma_f32_32x32x16_bf16 (A = rows of x, B = rows of W, both read from LDS
+// as 16-byte chunks).  When M
 // gives too few tiles to fill the GPU, K is split: each split writes an fp32 partial and a second
 // kernel adds the partials in split order (the result does not depend on
 // timing) and rounds to bf16.
@@ -61,26 +64,26 @@ __device__ __forceinline__ bool gemm_tile(const GemmParams& p, int& mt, int& nt,
 // group of 16 lanes the rows then cover all 64 banks once.
 __device__ __forceinline__ int gemm_swz(int r) { return (r >> 1) & 7; }
 
-template <int BM, int BN>
+template <int BM, int BN, int NW>
 struct GemmShape {
-  static constexpr int WAVES_M = BM >= 128 ? 2 : 1;      // the 4 waves as WAVES_M x WAVES_N
-  static constexpr int WAVES_N = 4 / WAVES_M;
+  static constexpr int WAVES_M = BM >= 128 ? 2 : 1;      // the NW waves as WAVES_M x WAVES_N
+  static constexpr int WAVES_N = NW / WAVES_M;
   static constexpr int WM = BM / (32 * WAVES_M);         // 32-row blocks per wave
   static constexpr int WN = BN / (32 * WAVES_N);         // 32-column blocks per wave
   static constexpr int A_BYTES = BM * kGemmRowB;
   static constexpr int STAGE = A_BYTES + BN * kGemmRowB;
   static constexpr int A_LOADS = A_BYTES / 1024;         // one wave-wide DMA instruction moves 1 KB (8 rows)
   static constexpr int B_LOADS = BN * kGemmRowB / 1024;
-  static constexpr int LPW = (A_LOADS + B_LOADS) / 4;    // DMA instructions per wave per stage
-  static_assert(WM >= 1 && WN >= 1 && (A_LOADS + B_LOADS) % 4 == 0, "tile shape");
+  static constexpr int LPW = (A_LOADS + B_LOADS) / NW;   // DMA instructions per wave per stage
+  static_assert(WM >= 1 && WN >= 1 && (A_LOADS + B_LOADS) % NW == 0, "tile shape");
 };
 
 // STREAM_W: W tiles go with the non-temporal hint, for shapes with a single
 // m-tile (each W byte is then read once; with several m-tiles the tiles of W
 // are shared through L2 and stay cached).
-template <int BM, int BN, int S, bool STREAM_W>
-__global__ __launch_bounds__(256) void verify_gemm(GemmParams p) {
-  using SH = GemmShape<BM, BN>;
+template <int BM, int BN, int S, bool STREAM_W, int NW = 4>
+__global__ __launch_bounds__(64 * NW) void verify_gemm(GemmParams p) {
+  using SH = GemmShape<BM, BN, NW>;
   static_assert(S >= 2 && S <= 4 && (S - 2) * SH::LPW < 64, "ring depth");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[S * SH::STAGE];
   const unsigned lds_base = (unsigned)(size_t)(__attribute__((address_space(3))) unsigned char*)smem;
@@ -99,14 +102,14 @@ __global__ __launch_bounds__(256) void verify_gemm(GemmParams p) {
   const int nst = (kb1 - kb0) / kGemmBK;
   const size_t rowg = (size_t)p.k * 2;   // bytes of one row of x or W
 
-  // DMA slots of this wave: instruction j (= wave + 4i) fills rows 8j'..8j'+7
+  // DMA slots of this wave: instruction j (= wave + NW i) fills rows 8j'..8j'+7
   // of the A tile (j < A_LOADS) or of the B tile; lane l takes row 8j' + l/8
   // and physical chunk l % 8, i.e. logical chunk (l % 8) ^ swz(row).
   unsigned src[SH::LPW], dst[SH::LPW];
   bool isb[SH::LPW];
 #pragma unroll
   for (int i = 0; i < SH::LPW; ++i) {
-    const int j = wave + 4 * i;
+    const int j = wave + NW * i;
     isb[i] = j >= SH::A_LOADS;
     const int jr = isb[i] ? j - SH::A_LOADS : j;
     const int row = 8 * jr + lane / 8;
@@ -217,12 +220,19 @@ struct GemmPlan {
   int bm, bn, ksplit, kchunk;
 };
 
-// Tile by M (128 x 256 when that still gives two rounds of workgroups); K
+// Tile by M (256 x 256 or 128 x 256 when that still gives three or two rounds of workgroups); K
 // split so that small M still fills about two workgroups per CU in one round,
 // as long as the fp32 partials (written and read once) stay below the bytes
 // of W.
 static GemmPlan gemm_plan(int m, int n, int k, int cus) {
   GemmPlan g;
+  // 256 x 256 (the most flops per byte of ring fill) when it gives at least three whole rounds
+  if (n % 256 == 0 && (long long)((m + 255) / 256) * (n / 256) >= 3LL * cus) {
+    g.bm = g.bn = 256;
+    g.ksplit = 1;
+    g.kchunk = k;
+    return g;
+  }
   g.bm = m <= 32 ? 32 : m <= 256 ? 64 : 128;
   g.bn = (g.bm == 128 && n % 256 == 0 && (long long)((m + 127) / 128) * (n / 256) >= 2LL * cus) ? 256 : 128;
   const long long tiles = (long long)((m + g.bm - 1) / g.bm) * (n / g.bn);
@@ -278,8 +288,9 @@ hipError_t sdv_gemm_launch(const SdGemmLaunch& a) {
   else if (g.bm == 32) verify_gemm<32, 128, 4, false><<<grid, 256, 0, a.stream>>>(p);
   else if (g.bm == 64 && stream_w) verify_gemm<64, 128, 3, true><<<grid, 256, 0, a.stream>>>(p);
   else if (g.bm == 64) verify_gemm<64, 128, 3, false><<<grid, 256, 0, a.stream>>>(p);
-  else if (g.bn == 128) verify_gemm<128, 128, 4, false><<<grid, 256, 0, a.stream>>>(p);
-  else verify_gemm<128, 256, 3, false><<<grid, 256, 0, a.stream>>>(p);
+  else if (g.bm == 256) verify_gemm<256, 256, 2, false, 8><<<grid, 512, 0, a.stream>>>(p);
+  else if (g.bn == 128) verify_gemm<128, 128, 4, false, 8><<<grid, 512, 0, a.stream>>>(p);
+  else verify_gemm<128, 256, 3, false, 8><<<grid, 512, 0, a.stream>>>(p);
   if (g.ksplit > 1) {
     const size_t groups = (size_t)a.m * a.n / 4;
     verify_gemm_reduce<<<(unsigned)((groups + 255) / 256), 256, 0, a.stream>>>(p);

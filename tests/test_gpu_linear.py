@@ -4,9 +4,9 @@ oracle, through the C ABI.
 Bound per element: the bf16 rounding of the output (half an ulp, at most
 2^-9 |y|, taken as 2^-8 |y|) plus an fp32 accumulation error of at most
 2 K 2^-24 sum_k |x W| (sum_k |x W| from the oracle).  The cases cover every
-tile height (32, 64, 128 rows), rows that do not fill a tile, split and
-unsplit K, the few-rows path (M <= 32 with 16-row workgroups), the expert
-shape N = K = 6144, and sampled rows at 4096 rows."""
+tile height (32, 64, 128, 256 rows), rows that do not fill a tile, split and
+unsplit K, the expert shape N = K = 6144, and sampled rows at 4096 and 8269
+rows (the 256-row tiles)."""
 
 import numpy as np
 import pytest
@@ -48,9 +48,8 @@ def _check(x, w, y, rows=None):
 @pytest.mark.parametrize("m,n,k", [
     (1, 128, 64), (5, 256, 640), (32, 384, 1024), (33, 128, 2048), (64, 256, 6144),
     (100, 512, 1280), (256, 384, 768), (300, 256, 512), (513, 640, 1024),
-    # the few-rows path (M <= 32, at least one 16-row workgroup per CU): two k-steps
-    # for eight waves, a step count that is not a multiple of the waves or of the
-    # load batch, rows that fill one or two 16-row blocks in part
+    # few rows against wide weights (split K with the reduce launch): K of one ring
+    # stage, K that splits unevenly, N not a power of two
     (17, 4096, 64), (32, 4096, 1984), (3, 4224, 6208), (16, 4096, 192), (31, 6144, 320),
 ])
 def test_shapes(m, n, k):
@@ -72,6 +71,16 @@ def test_sampled_rows_at_4096():
     rows = np.random.default_rng(7).choice(4096, size=48, replace=False)
     rows = np.sort(np.concatenate([rows, [0, 4095]]))
     say("case: m=4096 sampled rows")
+    _check(x, w, y, rows=rows)
+
+
+def test_sampled_rows_256_row_tiles():
+    """M = 8269 (not a multiple of 256) at N = K = 6144: enough 256 x 256 tiles for three rounds."""
+    x, w = linear_inputs(8269, seed=11, device="cuda")
+    y = _run(x, w)
+    rows = np.random.default_rng(11).choice(8269, size=40, replace=False)
+    rows = np.sort(np.concatenate([rows, [0, 8191, 8192, 8268]]))
+    say("case: m=8269 sampled rows (256 x 256 tiles)")
     _check(x, w, y, rows=rows)
 
 
