@@ -98,6 +98,15 @@ def test_identical_distributions_accept_everything():
     assert np.all(al == 10)
 
 
+def test_many_sequences_one_decision_workgroup_each():
+    """1100 sequences at V = 20000: the decision takes one workgroup per
+    sequence, so decision and draw share one launch, and that workgroup walks
+    all five 4096-logit sampling chunks itself."""
+    inp = generate(spec(batch=1100, draft_len=(0, 1, 2, 3), vocab=20000, seed=21))
+    say("case: 1100 sequences, V=20000, decision and draw in one launch")
+    _check(inp, "stochastic")
+
+
 def test_deterministic():
     inp = generate(spec(seed=5))
     a = gpu_accept(inp)
