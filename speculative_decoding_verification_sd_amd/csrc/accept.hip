@@ -413,9 +413,9 @@ __device__ __forceinline__ void row_relaxed_stats(const AccParams& p, int r, dou
 }
 
 // ---------------------------------------------------------------------------
-// LOSSY: a draft also passes when the JS distance of its rows is at most tau,
-// and the rows' entropy and JS distance are written out.
-// The greedy decision of sequence b (one workgroup); amax: LDS for its D+1 row argmaxes.
+// The greedy decision of sequence b (one workgroup); amax: LDS for its D+1 row
+// argmaxes.  LOSSY: a draft also passes when the JS distance of its rows is at
+// most tau, and the rows' entropy and JS distance are written out.
 template <bool LOSSY>
 __device__ __forceinline__ void decide_seq(const AccParams& p, int b, int* amax) {
   __shared__ RowPart stage[kDecideSlots];
