@@ -878,6 +878,112 @@ __global__ __launch_bounds__(kAccThreads) void accept_finish_draw(AccParams p) {
   draw_seq(p, blockIdx.x);
 }
 
+// Small vocabularies (V <= kSmallV, so one chunk per row and a whole row in
+// kSmallPL logits per lane): one workgroup per sequence does the whole call.
+// Each wave makes the statistics of whole rows on its own (wave shuffles, no
+// workgroup barrier), the four waves taking the sequence's rows in turn, so
+// the rows run in parallel; then the decision and (stochastic) the draw run as
+// in accept_finish_draw.  The fp64 row sums add the same fp32 terms in another
+// order than accept_rowstats.
+constexpr int kSmallV = 2048;
+constexpr int kSmallPL = kSmallV / 64;
+
+template <int VEC4>
+__device__ __forceinline__ void small_row_load(const float* src, int V, float (&x)[kSmallPL]) {
+  const int lane = threadIdx.x & 63;
+  if (VEC4) {   // lane's logits (i*64 + lane)*4 + e; V % 4 == 0, so a vector lies wholly inside or past the row
+#pragma unroll
+    for (int i = 0; i < kSmallPL / 4; ++i) {
+      const int j = (i * 64 + lane) * 4;
+      const f32x4 v = j < V ? __builtin_nontemporal_load((const f32x4*)(src + j))
+                            : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[i * 4 + e] = v[e];
+    }
+  } else {      // lane's logits i*64 + lane
+#pragma unroll
+    for (int i = 0; i < kSmallPL; ++i) {
+      const int j = i * 64 + lane;
+      x[i] = j < V ? src[j] : -INFINITY;
+    }
+  }
+}
+
+// The row's statistics by one wave (every lane returns them): greedy, the
+// lowest-index maximum; stochastic, the maximum and the fp64 sum of exp(x - m).
+template <bool STOCH, int VEC4>
+__device__ __forceinline__ RowPart small_row_stats(const float (&x)[kSmallPL], int V) {
+  const int lane = threadIdx.x & 63;
+  RowPart r;
+  r.idx = 0;
+  r.s = 0.0;
+  float m = -INFINITY;
+  if constexpr (!STOCH) {
+    int idx = INT_MAX;   // (increasing indices in k; a row of -inf reports its first index)
+#pragma unroll
+    for (int k = 0; k < kSmallPL; ++k) {
+      const int j = VEC4 ? ((k >> 2) * 64 + lane) * 4 + (k & 3) : k * 64 + lane;
+      if (x[k] > m || (idx == INT_MAX && j < V)) { m = x[k]; idx = j; }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const float om = __shfl_xor(m, off);
+      const int oi = __shfl_xor(idx, off);
+      if (better(om, oi, m, idx)) { m = om; idx = oi; }
+    }
+    r.idx = idx;
+  } else {
+#pragma unroll
+    for (int k = 0; k < kSmallPL; ++k) m = fmaxf(m, x[k]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    double sum = 0.0;
+    if (m != -INFINITY) {
+      const float ml = m * kLog2e;
+#pragma unroll
+      for (int k0 = 0; k0 < kSmallPL; k0 += 8) {
+        float a = 0.f;
+#pragma unroll
+        for (int k = k0; k < k0 + 8; ++k) a += fast_exp2(fmaf(x[k], kLog2e, -ml));
+        sum += (double)a;
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+    }
+    r.s = sum;
+  }
+  r.m = m;
+  return r;
+}
+
+template <bool STOCH, int VEC4>
+__global__ __launch_bounds__(kAccThreads) void accept_small(AccParams p) {
+  extern __shared__ int amax[];                 // greedy: [max_draft + 1] row argmaxes
+  const int b = blockIdx.x;
+  const int wave = threadIdx.x >> 6;
+  const int t0 = p.q_start[b], D = seq_d(p, b), d0 = t0 - b;
+  if (seq_ok(p, t0, D, d0)) {                   // (otherwise the decision writes AL = 0)
+    // target rows t0 .. t0+D, then (stochastic) draft rows d0 .. d0+D-1
+    const int nrows = STOCH ? 2 * D + 1 : D + 1;
+    for (int k = wave; k < nrows; k += kAccThreads / 64) {
+      const int row = k <= D ? t0 + k : p.T + d0 + (k - D - 1);
+      const float* src = row < p.T ? p.target + (size_t)row * p.V : p.draft + (size_t)(row - p.T) * p.V;
+      float x[kSmallPL];
+      small_row_load<VEC4>(src, p.V, x);
+      const RowPart r = small_row_stats<STOCH, VEC4>(x, p.V);
+      if ((threadIdx.x & 63) == 0) p.part[row] = r;   // (one chunk per row)
+    }
+  }
+  __syncthreads();
+  if constexpr (STOCH) {
+    finish_seq<false>(p, b, 0, 1);
+    __syncthreads();
+    draw_seq(p, b);
+  } else {
+    decide_seq<false>(p, b, amax);
+  }
+}
+
 struct AccLayout {
   size_t part_off, seqrec_off, rsum_off, rsub_off, ent_off, jsp_off, total;
   int nchunk, nschunk;
@@ -943,6 +1049,17 @@ hipError_t sdv_accept_launch(const SdAccLaunch& a) {
   const bool vec4 = (a.V % 4 == 0) && ((uintptr_t)a.target % 16 == 0) &&
                     (!need_draft || (uintptr_t)a.draft % 16 == 0);
   p.vec4 = vec4;
+  if (!a.lossy && a.V <= kSmallV) {   // small vocabularies: the whole call in one launch
+    if (a.stochastic) {
+      if (vec4) accept_small<true, 1><<<a.B, kAccThreads, 0, a.stream>>>(p);
+      else accept_small<true, 0><<<a.B, kAccThreads, 0, a.stream>>>(p);
+    } else {
+      const size_t lds = (size_t)(a.max_draft + 1) * sizeof(int);
+      if (vec4) accept_small<false, 1><<<a.B, kAccThreads, lds, a.stream>>>(p);
+      else accept_small<false, 0><<<a.B, kAccThreads, lds, a.stream>>>(p);
+    }
+    return hipGetLastError();
+  }
   const size_t drows = (size_t)(a.T - a.B);
   const size_t rows = need_draft ? (size_t)a.T + drows : (size_t)a.T;
   const unsigned grid1 = (unsigned)(rows * L.nchunk);
