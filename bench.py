@@ -1010,8 +1010,9 @@ def write_sweep_profile(sweep_json: str):
         f.write(f"# Verify attention per draft length D on {cfg['workload']} (one MI355X, HIP events, "
                 f"{line['steps']} timed calls per point after {line['clock_settle_s_per_point']} s of clock settle).\n"
                 "# G*(1+D) query rows share each KV head; the kernel variant changes at 64 rows (16x16 MFMA ->\n"
-                "# 32x32 MFMA, the wave sets split the tiles) and at 128 rows (the wave sets split the rows, so\n"
-                "# every wave takes both tiles of a step).\n"
+                "# 32x32 MFMA, the wave sets split the tiles), at 128 rows (rows past 128 one 16-row block of\n"
+                "# 16x16 MFMAs), at 144 rows (one or two 32-row blocks past 128, split by tile parity) and at\n"
+                "# 192 rows (the wave sets split the rows, so every wave takes both tiles of a step).\n"
                 "$ python3 REPO/bench.py --sweep\n")
         f.write("D,rows_per_kv_head,attention_us,accept_us,hbm_frac,mfma_frac,verified_tokens_per_s,mean_AL\n")
         for pt in line["sweep"]:

@@ -23,8 +23,9 @@
 //   * S^T = K * Q^T with Q held in registers, so each lane holds one query row
 //     and the row reductions stay within a lane pair (v_permlane32_swap).
 //     verify_attn_wide (more than 64 rows) uses v_mfma_f32_32x32x16_bf16 with
-//     8 waves in two sets that take alternate tiles; verify_attn_main (up to
-//     64 rows) uses v_mfma_f32_16x16x32_bf16.
+//     8 waves in two sets that take alternate tiles or row blocks (and, from
+//     129 to 144 rows, one 16-row block of 16x16x32 MFMAs for the rows past
+//     128); verify_attn_main (up to 64 rows) uses v_mfma_f32_16x16x32_bf16.
 //   * Softmax: each row's reference max is fixed by the item's first tile, so
 //     later tiles need neither a row max nor a rescale; an item whose row sum
 //     ends above 2^64 (a score far above its reference) is computed again with
@@ -711,6 +712,12 @@ __device__ __forceinline__ float row_max4(float v) {
   auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
+__device__ __forceinline__ float row_sum4(float v) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 // The max a split-KV partial is stored with: the offset its P values were
 // actually computed against.  In the fast pass a row whose first tile of the
@@ -1364,7 +1371,9 @@ __global__ __launch_bounds__(64 * NW, WPC) void verify_attn_main(AttnParams p) {
 // item.  Up to 256 rows (MODE 1), set s takes rows 128s .. 128s+127 over every
 // tile, so the item's pages are streamed once for all its rows.  From 129 to
 // 192 rows (MODE 2) set 0 takes rows 0..127 over every tile and set 1 splits
-// the tiles of the remaining one or two row blocks.  Two waves per SIMD hide
+// the tiles of the remaining one or two row blocks; from 129 to 144 rows
+// (MODE 3) the rows past 128 form one 16-row block of 16x16x32 MFMAs, whose
+// tiles two waves of set 1 split.  Two waves per SIMD hide
 // each other's LDS, barrier and MFMA-dependency latencies.  Operands:
 //   * S^T = K Q^T per 32-key tile: A = K (lane: key row l%32, dims
 //     c*16 + (l/32)*8..+7), B = Q^T (lane: query row l%32, same dims), so each
@@ -1392,7 +1401,19 @@ __device__ __forceinline__ int wide_swz(int k) {
 // rows): waves 0-3 take row blocks 0-3 over both tiles, and waves 4-7 share
 // blocks 4 and 5 two to a block, one tile of every step each, so that no SIMD
 // (it hosts waves s and s+4) carries more than three of the step's 32-row
-// tile products where the row split would give one SIMD four.
+// tile products where the row split would give one SIMD four.  MODE 3 (129 to
+// 144 rows): waves 0-3 as in MODE 2; waves 4 and 5 take rows 128..143 as a
+// 16-row block, one tile of every step each, so the rows past 128 cost a
+// quarter of a 32-row tile product per tile instead of a half; waves 6 and 7
+// only load.
+//
+// The 16-row block (16x16x32 MFMAs, as verify_attn_main): S^T block kb takes
+// key (r/4)*8 + kb*4 + r%4 as its MFMA row r, so lane group g = l/16 holds the
+// eight consecutive keys 8g..8g+7 of the tile (entries kb*4 + e) for query row
+// 128 + l%16, which is the B operand of O^T += V^T P^T over the whole tile.
+// Its registers are those of the 32-row path: Q in qf[0 .. HD/32), the K
+// offsets of block kb in koff[kb*HD/32 ..], the scores in sc[0..7] and the
+// output block db (d = 16db + 4g + 0..3) in entries 4(db%4) .. of o[db/4].
 template <int HD, int OUT_F32, int MODE, bool TREE, bool VKM>
 __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
   constexpr int NW = 8;
@@ -1421,9 +1442,10 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
   // This wave's role: PAIR waves take both tiles of a step, the others the
   // tile of parity `par`; its 32-row block; whether it hands its partial to
   // a partner (same block, other parity) through LDS, and where.
-  const bool pair = MODE == 1 || (MODE == 2 && set == 0);
-  const int par = MODE == 0 ? set : (MODE == 2 && set == 1) ? (w4 & 1) : 0;
-  const int rblock = MODE == 0 ? w4 : MODE == 1 ? wave : set == 0 ? w4 : 4 + (w4 >> 1);
+  const bool pair = MODE == 1 || (MODE >= 2 && set == 0);
+  const bool narrow = MODE == 3 && set == 1;     // the 16-row block (waves 4 and 5; 6 and 7 idle)
+  const int par = MODE == 0 ? set : (MODE >= 2 && set == 1) ? (w4 & 1) : 0;
+  const int rblock = MODE == 0 ? w4 : MODE == 1 ? wave : set == 0 ? w4 : MODE == 3 ? 4 + 2 * (w4 >> 1) : 4 + (w4 >> 1);
   const bool giver = !pair && par == 1;          // hands (O, l, m) to the block's parity-0 wave
   const int xslot = MODE == 0 ? w4 : (w4 >> 1);  // LDS hand-off slot of the block
   __shared__ FusedPlan fp;
@@ -1456,6 +1478,36 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
       voffs[mb] = par * RG::kHalf + S * RG::kHalf + dd * 32 + ((hh ^ ((dd >> 3) & 1)) * 16);
     }
   }
+  // The 16-row block's operands (lane l16 = l % 16, group g4 = l / 16).  K of
+  // S^T block kb: key row (l16/4)*8 + kb*4 + l16%4, logical chunk 4c + g4, in
+  // koff[kb * NKC16 + c].  V^T block db: d-rows 16db + l16, keys 8g4..+7, at
+  // voffs[0] + 512 db (d-major pages) or, key-major, at voffs[0] + 32 (db ^
+  // voffs[1]) (key row 8g4 + l16/4, dims 16db + 4(l16 % 4)..+3, whose chunk
+  // pair 2db.. the row's swizzle permutes).
+  constexpr int NKC16 = HD / 32;   // 32-wide d steps of the 16-row S^T
+  constexpr int NDB16 = HD / 16;   // 16-row d blocks of O^T
+  if constexpr (MODE == 3) {
+    if (narrow) {
+      const int l16 = lane & 15, g4 = lane >> 4;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int key = (l16 >> 2) * 8 + kb * 4 + (l16 & 3);
+#pragma unroll
+        for (int c = 0; c < NKC16; ++c)
+          koff[kb * NKC16 + c] = par * RG::kHalf + key * RG::kRowB + (((c * 4 + g4) ^ wide_swz<HD>(key)) * 16);
+      }
+      if constexpr (VKM) {
+        const int key = 8 * g4 + (l16 >> 2);
+        const int sw = vkm_swz<HD>(key);   // (bit 0 clear: the chunk pair of a d block stays a pair)
+        voffs[0] = par * RG::kHalf + S * RG::kHalf + key * RG::kRowB + ((((l16 & 3) >> 1) ^ (sw & 1)) * 16) +
+                   ((4 * (l16 & 3)) & 7) * 2;
+        voffs[1] = sw >> 1;
+      } else {
+        voffs[0] = par * RG::kHalf + S * RG::kHalf + (g4 >> 1) * HD * 32 + l16 * 32 +
+                   (((g4 & 1) ^ ((l16 >> 3) & 1)) * 16);
+      }
+    }
+  }
   DmaSlot dma[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i)
@@ -1465,6 +1517,7 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
   // items shorter than the chunk and more items than workgroups, the next item
   // of this workgroup's class (index = blockIdx % 8 modulo 8) as workgroups
   // finish, from the class's counter; otherwise a fixed stride.
+  __shared__ int s_votes[NW];    // MODE 3: per-wave votes of the safe-pass test
   __shared__ int s_next;
   const int chunk = __builtin_amdgcn_readfirstlane(p.fused ? fp.chunk : p.plan[0]);
   const bool dyn = !p.fused && gridDim.x >= 8 && total > (int)gridDim.x && p.plan[2] < total;
@@ -1525,8 +1578,15 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
       wait_lds();
     };
 
-    // Query fragments (B operand of S^T): lane holds row r32, dims c*16 + hh*8..+7.
-    const int row = rblock * 32 + r32;
+    // MODE 3: the lane index, opaque to the compiler once per item, so that
+    // the lane terms of the Q and output addresses are formed here, not
+    // hoisted out of the item loop as 64-bit pointers held (or spilled) across
+    // it.
+    int lane_i = lane;
+    if constexpr (MODE == 3) asm volatile("" : "+v"(lane_i));
+    // Query fragments (B operand of S^T): lane holds row r32, dims c*16 + hh*8..+7
+    // (the 16-row block: row 128 + l16, dims c*32 + g4*8..+7 for c < NKC16).
+    const int row = narrow ? 128 + (lane & 15) : rblock * 32 + r32;
     const int i0 = row / p.G;
     const bool valid = row < R && t0 >= 0 && t0 + i0 < p.total_q;
     const int qi = valid ? i0 : 0;
@@ -1535,8 +1595,15 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
     unsigned long long tm = 0ull;   // draft tree: nodes this row sees
     if constexpr (TREE) tm = valid ? p.tmask[t0 + qi] : 0ull;
     bf16x8 qf[NKS];
-    {
-      const uint16_t* qp = p.q + ((size_t)(t0 + qi) * Hq + (size_t)h * p.G + qg) * HD + hh * 8;
+    if (MODE == 3 && narrow) {
+      const uint16_t* qp = p.q + ((size_t)(t0 + qi) * Hq + (size_t)h * p.G + qg) * HD + (lane_i >> 4) * 8;
+#pragma unroll
+      for (int c = 0; c < NKS; ++c) {
+        u32x4 raw = valid && c < NKC16 ? *(const u32x4*)(qp + c * 32) : u32x4{0, 0, 0, 0};
+        qf[c] = __builtin_bit_cast(bf16x8, raw);
+      }
+    } else {
+      const uint16_t* qp = p.q + ((size_t)(t0 + qi) * Hq + (size_t)h * p.G + qg) * HD + (lane_i >> 5) * 8;
 #pragma unroll
       for (int c = 0; c < NKS; ++c) {
         u32x4 raw = valid ? *(const u32x4*)(qp + c * 16) : u32x4{0, 0, 0, 0};
@@ -1570,6 +1637,23 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
     f32x16 sc;
     float mt = -INFINITY;
     auto mask_scores = [&](int tile) {
+      if (MODE == 3 && narrow) {   // entry e: key 8g4 + e
+        const int g4 = lane >> 4;
+        if constexpr (TREE) {
+          const int nb = k_begin + tile * RG::kTile + 8 * g4 - (N - 1 - D);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int node = nb + e;
+            if (!(node < 0 || (node < 64 && ((tm >> node) & 1ull)))) sc[e] = -INFINITY;
+          }
+        } else {
+          const int lim = pos - (k_begin + tile * RG::kTile) - 8 * g4;
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (e > lim) sc[e] = -INFINITY;
+        }
+        return;
+      }
       if constexpr (TREE) {
         const int nb = k_begin + tile * RG::kTile + 8 * hh - (N - 1 - D);   // block node of entry 0
 #pragma unroll
@@ -1586,6 +1670,12 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
     };
     auto row_max = [&](float slack) {
       float m = sc[0];
+      if (MODE == 3 && narrow) {
+#pragma unroll
+        for (int e = 1; e < 8; ++e) m = fmaxf(m, sc[e]);
+        mt = row_max4(m) * p.scale_log2;
+        return mt > m_run + slack;
+      }
 #pragma unroll
       for (int e = 1; e < 16; ++e) m = fmaxf(m, sc[e]);
       auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
@@ -1601,7 +1691,22 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
     // two waves per SIMD the other wave's MFMAs fill the single chain's
     // dependency stalls: measured, one chain with no adds beats two chains by
     // 1-3%.)
+    // The 16-row block's S^T: two 16-key blocks, chains from zero (PRE: from
+    // the reference max, as below).
+    auto narrow_scores = [&](int off, auto prec) {
+      f32x4 s0 = decltype(prec)::value ? f32x4{mneg[0], mneg[1], mneg[2], mneg[3]} : f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 s1 = s0;
+#pragma unroll
+      for (int c = 0; c < NKC16; ++c) {
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(smem + off + koff[c]), qf[c], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(smem + off + koff[NKC16 + c]), qf[c], s1, 0, 0,
+                                                     0);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { sc[e] = s0[e]; sc[4 + e] = s1[e]; }
+    };
     auto scores = [&](int off, auto prec) {
+      if (MODE == 3 && narrow) return narrow_scores(off, prec);
       if constexpr (decltype(prec)::value) {
         f32x16 s0 = mneg;
 #pragma unroll
@@ -1629,7 +1734,28 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
     };
     // P from the scores, then O^T += V^T P^T at stage offset `off`, and the
     // lane's share of l from the same bf16 P (dot products with (1, 1))
+    // The 16-row block's P (keys 8g4..+7), O^T block db += V^T P^T, and l.
+    auto narrow_accumulate = [&](int off, auto prec) {
+      bf16x8 pn;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pn[e] = p_of(sc[e], prec);
+#pragma unroll
+      for (int db = 0; db < NDB16; ++db) {
+        const int vo = VKM ? voffs[0] + 32 * (db ^ voffs[1]) : voffs[0] + 512 * db;
+        const bf16x8 vf = vt_operand<VKM, RG::kRowB>(lds_smem, off + vo);
+        f32x4 acc = {o[db / 4][4 * (db % 4)], o[db / 4][4 * (db % 4) + 1], o[db / 4][4 * (db % 4) + 2],
+                     o[db / 4][4 * (db % 4) + 3]};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pn, acc, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[db / 4][4 * (db % 4) + e] = acc[e];
+      }
+      const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pn[2 * q], pn[2 * q + 1]}, one2, l_run, false);
+    };
     auto accumulate = [&](int off, auto prec) {
+      if (MODE == 3 && narrow) return narrow_accumulate(off, prec);
       bf16x8 pf[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
@@ -1711,6 +1837,11 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
     // P V): in MODE 2 a single-tile wave shares its SIMD with a PAIR wave, and
     // the fences keep its registers within the row-split step's budget.
     auto single_tile = [&](int off) {
+      if constexpr (MODE == 3) {   // (MODE 3: the single-tile waves are the 16-row block's)
+        narrow_scores(off, std::true_type{});
+        narrow_accumulate(off, std::true_type{});
+        return;
+      }
       constexpr int kSlots = NKS + 2 * NMB;
       constexpr int kAhead = SDV_RS_AHEAD;
       auto operand = [&](auto jc) -> bf16x8 {
@@ -1749,6 +1880,7 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
       });
     };
     auto row_sum = [&]() {
+      if (MODE == 3 && narrow) return row_sum4(l_run);
       auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
       return __uint_as_float(a[0]) + __uint_as_float(a[1]);
     };
@@ -1829,7 +1961,7 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
           constexpr int st = (2 * (1 + u)) % S;         // stage of tile 2k (k = kb + u; kb - 1 is a multiple of S/2)
           advance(kb + u, (st + S - 2) % S);
           if constexpr (ROLE == 2) {
-            if constexpr (MODE == 2) {   // (one loop for both roles of MODE 2: the wave's role is uniform)
+            if constexpr (MODE >= 2) {   // (one loop for both roles of MODES 2 and 3: the wave's role is uniform)
               if (pair) rs_pair(st * RG::kHalf, (st + 1) * RG::kHalf);
               else single_tile(st * RG::kHalf);
             } else {
@@ -1860,7 +1992,20 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
 
     // ---- Safe pass (only if some row's max outgrew its reference): the same
     // steps again with a running max.
-    if (__syncthreads_or(over ? 1 : 0)) {
+    // (MODE 3: a vote per wave in LDS, the workgroup OR without a flat thread
+    // index, which would otherwise be held across the item loop; a slot is
+    // rewritten only in the next item, after the item's last barrier)
+    int any_over = 0;
+    if constexpr (MODE == 3) {
+      const bool over_w = __any(over);
+      if (lane == 0) s_votes[wave] = over_w ? 1 : 0;
+      block_sync_lds();
+#pragma unroll
+      for (int w = 0; w < NW; ++w) any_over |= s_votes[w];
+    } else {
+      any_over = __syncthreads_or(over ? 1 : 0);
+    }
+    if (any_over) {
       clear();
 #pragma unroll
       for (int t = 0; t < S - 2; ++t)
@@ -1899,11 +2044,41 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
         lt = lt * wa + lb * wb;
       }
     }
-    if (!giver && wave_active && valid) {
+    if (MODE == 3 && narrow && !giver && wave_active && valid) {
+      // the 16-row block: lane holds query row 128 + l16 and dims 16db + 4g4 + 0..3
+      const int g4 = lane_i >> 4;
+      if (nsplit == 1) {
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        const size_t obase = ((size_t)(t0 + qi) * Hq + (size_t)h * p.G + qg) * HD + g4 * 4;
+#pragma unroll
+        for (int db = 0; db < NDB16; ++db) {
+          const int q = db % 4;
+          const f32x4 v = f32x4{o[db / 4][4 * q], o[db / 4][4 * q + 1], o[db / 4][4 * q + 2], o[db / 4][4 * q + 3]} * inv;
+          if (OUT_F32) {
+            *(f32x4*)((float*)p.out + obase + 16 * db) = v;
+          } else {
+            const bf16x4 t = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+            *(u32x2*)((uint16_t*)p.out + obase + 16 * db) = __builtin_bit_cast(u32x2, t);
+          }
+        }
+      } else {
+        float* slab = p.part_o + ((size_t)pslot * p.rpad + row) * HD + g4 * 4;
+#pragma unroll
+        for (int db = 0; db < NDB16; ++db) {
+          const int q = db % 4;
+          *(f32x4*)(slab + 16 * db) = f32x4{o[db / 4][4 * q], o[db / 4][4 * q + 1], o[db / 4][4 * q + 2], o[db / 4][4 * q + 3]};
+        }
+        if (g4 == 0) {
+          float* ml = p.part_ml + ((size_t)pslot * p.rpad + row) * 2;
+          ml[0] = M;
+          ml[1] = lt;
+        }
+      }
+    } else if (!giver && wave_active && valid) {
       // O^T accumulator: lane holds query row r32 and dims mb*32 + q*8 + 4hh + 0..3 in entries 4q..4q+3.
       if (nsplit == 1) {
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
-        const size_t obase = ((size_t)(t0 + qi) * Hq + (size_t)h * p.G + qg) * HD + hh * 4;
+        const size_t obase = ((size_t)(t0 + qi) * Hq + (size_t)h * p.G + qg) * HD + (lane_i >> 5) * 4;
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
@@ -1918,7 +2093,7 @@ __global__ __launch_bounds__(512, 1) void verify_attn_wide(AttnParams p) {
             }
           }
       } else {
-        float* slab = p.part_o + ((size_t)pslot * p.rpad + row) * HD + hh * 4;
+        float* slab = p.part_o + ((size_t)pslot * p.rpad + row) * HD + (lane_i >> 5) * 4;
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
@@ -2023,10 +2198,13 @@ struct AttnLayout {
   // variant 1: verify_attn_wide, 8 waves, up to 128 rows (the sets split the tiles);
   // variant 2: verify_attn_wide, 8 waves, up to 256 rows (the sets split the rows);
   // variant 3: verify_attn_wide, 8 waves, 129..192 rows (blocks 4-5 split by tile parity);
-  // one workgroup per CU for variants 1 and 2
+  // variant 4: verify_attn_wide, 8 waves, 129..144 rows (a 16-row block split by tile parity);
+  // one workgroup per CU for variants 1 to 4
 };
 
-static int attn_variant(int rmax) { return rmax <= 64 ? 0 : rmax <= 128 ? 1 : rmax <= 192 ? 3 : 2; }
+static int attn_variant(int rmax) {
+  return rmax <= 64 ? 0 : rmax <= 128 ? 1 : rmax <= 144 ? 4 : rmax <= 192 ? 3 : 2;
+}
 
 // Resident workgroups of the persistent grid per CU.
 static int attn_slots(int cus, int variant) { return cus * (variant == 0 ? 2 : 1); }
@@ -2092,6 +2270,7 @@ static void launch_variant(int variant, const AttnParams& p, int grid, hipStream
   if (variant == 0) verify_attn_main<HD, 1, 4, 2, OUTF, TREE, VKM><<<grid, 256, 0, st>>>(p);
   else if (variant == 1) verify_attn_wide<HD, OUTF, 0, TREE, VKM><<<grid, 512, 0, st>>>(p);
   else if (variant == 3) verify_attn_wide<HD, OUTF, 2, TREE, VKM><<<grid, 512, 0, st>>>(p);
+  else if (variant == 4) verify_attn_wide<HD, OUTF, 3, TREE, VKM><<<grid, 512, 0, st>>>(p);
   else verify_attn_wide<HD, OUTF, 1, TREE, VKM><<<grid, 512, 0, st>>>(p);
 }
 

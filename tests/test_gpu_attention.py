@@ -45,7 +45,10 @@ def test_ragged_lengths_and_split_kv(kv_chunk):
     (8, [3, 1], 128),          # R <= 64
     (8, [15, 9], 128),         # R <= 128
     (8, [31, 20], 128),        # R <= 256
-    (8, [16, 9], 128),         # R = 136: rows 128.. split by tile parity
+    (8, [16, 9], 128),         # R = 136: rows 128..143 a 16-row block, split by tile parity
+    (16, [8, 3], 128),         # R = 144: the 16-row block full
+    (5, [27, 3], 128),         # R = 140
+    (4, [35, 20], 64),         # R = 144, d = 64
     (8, [23, 19], 128),        # R = 192
     (12, [15, 10], 64),        # R = 192, d = 64
     (3, [50, 47], 128),        # R = 153
@@ -75,7 +78,9 @@ def _dim_major(inp):
     (4, [3, 2], 64, 256),        # R = 16, d = 64, split
     (8, [7, 5], 128, 0),         # R = 64
     (8, [15, 9], 128, 256),      # R = 128 (the wave sets split the tiles)
-    (8, [16, 9], 128, 0),        # R = 136 (rows past 128 split by tile parity)
+    (8, [16, 9], 128, 0),        # R = 136 (rows past 128: a 16-row block split by tile parity)
+    (8, [16, 9], 128, 256),      # R = 136, split
+    (4, [35, 20], 64, 0),        # R = 144, d = 64
     (8, [31, 20], 128, 256),     # R = 256 (row split)
     (16, [15, 4], 64, 0),        # R = 256, d = 64
 ])
@@ -150,9 +155,10 @@ def test_many_sequences_mixed_lengths(kv_chunk):
     assert err <= ATTN_TOL
 
 
-def test_fp32_output_and_explicit_scale():
-    inp = generate(spec(seed=4))
-    say("case: fp32 output, scale 0.05")
+@pytest.mark.parametrize("drafts", [[15, 3, 7], [16, 3, 7]])
+def test_fp32_output_and_explicit_scale(drafts):
+    inp = generate(spec(seed=4, draft_len=drafts))
+    say(f"case: fp32 output, scale 0.05, drafts {drafts}")
     from oracle import verify_attention
     from tests.oracle_io import attention_args
     ref = verify_attention(**attention_args(inp), scale=0.05)
@@ -191,6 +197,7 @@ def test_deterministic():
     (8, [15, 9], [700, 1333], 0),                 # R <= 128
     (8, [31, 20], [700, 1333], 0),                # R <= 256 (row split)
     (8, [19, 12], [700, 1333], 0),                # R = 160 (blocks 4-5 split by tile parity)
+    (8, [16, 12], [700, 1333], 0),                # R = 136 (a 16-row block split by tile parity)
     (2, [3, 0, 1, 2] * 40, [37, 900, 5000, 260] * 40, 0),   # short items: counter-driven fetch
     # caches of at most 256 keys: never split, and no combine launch (plan in the
     # main kernel for B <= 32, the plan kernel past that)
@@ -265,16 +272,19 @@ def _plant_dominant_key(inp, b, h, key, scale=5.0, negative_prefix=0):
         inp.k_cache[int(bt[j // ps]), h, j % ps, :] = (-scale * v.float()).to(torch.bfloat16)
 
 
-@pytest.mark.parametrize("key,prefix,kv_chunk", [
-    (2000, 0, 0),       # late dominant key, one item per sequence
-    (2000, 0, 256),     # ... in a later split
-    (2497, 0, 0),       # inside the draft block (visible to the last rows only)
-    (1500, 32, 0),      # first tile far below everything after it
+@pytest.mark.parametrize("key,prefix,kv_chunk,D", [
+    (2000, 0, 0, 7),       # late dominant key, one item per sequence
+    (2000, 0, 256, 7),     # ... in a later split
+    (2497, 0, 0, 7),       # inside the draft block (visible to the last rows only)
+    (1500, 32, 0, 7),      # first tile far below everything after it
+    (2000, 0, 256, 16),    # 136 rows: the 16-row block's safe pass too
+    (2497, 0, 0, 16),
+    (1500, 32, 0, 16),
 ])
-def test_score_far_above_the_first_tile_max(key, prefix, kv_chunk):
-    inp = generate(spec(batch=1, kv_len=[2500], draft_len=[7], seed=5))
+def test_score_far_above_the_first_tile_max(key, prefix, kv_chunk, D):
+    inp = generate(spec(batch=1, kv_len=[2500], draft_len=[D], seed=5))
     _plant_dominant_key(inp, 0, 1, key, negative_prefix=prefix)
-    say(f"case: dominant key {key} prefix {prefix} kv_chunk={kv_chunk}")
+    say(f"case: dominant key {key} prefix {prefix} kv_chunk={kv_chunk} D={D}")
     err = compare_attention(inp, gpu_attention(inp, kv_chunk=kv_chunk))
     say(f"max|err| = {err:.3e}")
     assert err <= ATTN_TOL

@@ -43,7 +43,7 @@ def _tree_attention(inp, parents, kv_chunk=0):
 
 
 @pytest.mark.parametrize("G,drafts,d", [(8, [3, 1, 7], 128), (8, [15, 9, 4], 128), (8, [31, 20, 5], 128),
-                                        (4, [63, 30, 0], 64)])
+                                        (4, [63, 30, 0], 64), (8, [16, 9, 4], 128)])
 def test_chain_tree_is_bitwise_the_causal_call(G, drafts, d):
     inp = generate(_spec(group=G, head_dim=d, draft_len=drafts, seed=G + d))
     par = _parents(inp.q_start.cpu().numpy(), "chain", None)
@@ -57,7 +57,8 @@ def test_chain_tree_is_bitwise_the_causal_call(G, drafts, d):
 @pytest.mark.parametrize("G,drafts,d,kv_chunk", [(8, [15, 3, 7], 128, 0), (8, [31, 12, 6], 128, 0),
                                                  (4, [7, 2, 5], 64, 0), (8, [15, 3, 7], 128, 256),
                                                  (2, [40, 63, 1], 64, 0), (3, [50, 20, 7], 128, 0),
-                                                 (3, [50, 20, 7], 128, 256)])
+                                                 (3, [50, 20, 7], 128, 256), (8, [16, 3, 7], 128, 0),
+                                                 (8, [16, 3, 7], 128, 256), (4, [35, 20, 1], 64, 0)])
 def test_tree_attention_matches_oracle(kind, G, drafts, d, kv_chunk):
     inp = generate(_spec(group=G, head_dim=d, draft_len=drafts, seed=3 * G + d + len(kind)))
     rng = np.random.default_rng(G + d)
@@ -95,7 +96,28 @@ def test_split_boundary_inside_the_tree(kind, G, kv_chunk):
     assert err <= ATTN_TOL
 
 
-@pytest.mark.parametrize("G,drafts,kv_chunk", [(1, [63, 40, 2], 64), (8, [15, 9, 4], 0), (4, [63, 31, 1], 128)])
+@pytest.mark.parametrize("kind", ["random", "star"])
+@pytest.mark.parametrize("kv_chunk", [64, 128])
+def test_split_boundary_inside_the_tree_16_row_block(kind, kv_chunk):
+    """36-node trees at G = 4 (144 rows: the rows past 128 are one 16-row
+    block) whose last split begins 1, 10 and 30 nodes into the tree: as above,
+    with the 16-row block's own reference max and partial."""
+    kv = [1059, 1050, 1030]                   # tree starts at key 1023, 1014 and 994; a split starts at 1024
+    inp = generate(_spec(batch=3, group=4, head_dim=128, kv_len=kv, draft_len=[35, 35, 35], seed=60))
+    rng = np.random.default_rng(61)
+    a = attention_args(inp)
+    par = _parents(a["q_start"], kind, rng)
+    say(f"case: split inside the tree, 16-row block, {kind} tree kv_chunk={kv_chunk}")
+    out = _tree_attention(inp, par, kv_chunk)
+    assert not torch.isnan(out.float()).any()
+    ref = verify_tree_attention(parents=par, **a)
+    err = float(np.max(np.abs(out.float().cpu().numpy().astype(np.float64) - ref)))
+    say(f"max|err| = {err:.3e}")
+    assert err <= ATTN_TOL
+
+
+@pytest.mark.parametrize("G,drafts,kv_chunk", [(1, [63, 40, 2], 64), (8, [15, 9, 4], 0), (4, [63, 31, 1], 128),
+                                               (4, [35, 31, 1], 128)])
 def test_tree_dim_major_v_cache(G, drafts, kv_chunk):
     """Tree attention over a d-major V cache equals the key-major call bit for bit."""
     inp = generate(_spec(group=G, draft_len=drafts, kv_len=[1087, 900, 2500], seed=50 + G))
