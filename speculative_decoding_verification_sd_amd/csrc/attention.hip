@@ -2197,7 +2197,7 @@ struct AttnLayout {
   // variant 0: verify_attn_main, 4 waves x 16 rows (64 rows), two workgroups per CU;
   // variant 1: verify_attn_wide, 8 waves, up to 128 rows (the sets split the tiles);
   // variant 2: verify_attn_wide, 8 waves, up to 256 rows (the sets split the rows);
-  // variant 3: verify_attn_wide, 8 waves, 129..192 rows (blocks 4-5 split by tile parity);
+  // variant 3: verify_attn_wide, 8 waves, 145..192 rows (blocks 4-5 split by tile parity);
   // variant 4: verify_attn_wide, 8 waves, 129..144 rows (a 16-row block split by tile parity);
   // one workgroup per CU for variants 1 to 4
 };
