@@ -388,18 +388,22 @@ __global__ __launch_bounds__(kAccThreads) void accept_jsd(AccParams p) {
   if (tid == 0) p.jsp[(size_t)r * p.nchunk + c] = acc;
 }
 
-// Entropy (nats) and JS distance of drafted row r, from the chunk sums, by one
-// thread: H = log S0 - S1/S0 with S0 = sum_c exp(m_c - M) s_c and S1 = sum_c
-// exp(m_c - M) (e_c + (m_c - M) s_c); JS = sqrt(JSD) with JSD half the sum of
-// the chunk sums of the divergence terms.
-__device__ __forceinline__ void row_relaxed_stats(const AccParams& p, int r, double& H, double& js) {
+// Entropy (nats) and JS distance of drafted row r, from the chunk sums, by the
+// 16 lanes of a group (lane k takes chunks k, k+16, ...; every lane of the
+// group must call it, and each gets the result): H = log S0 - S1/S0 with
+// S0 = sum_c exp(m_c - M) s_c and S1 = sum_c exp(m_c - M) (e_c + (m_c - M) s_c);
+// JS = sqrt(JSD) with JSD half the sum of the chunk sums of the divergence
+// terms.
+__device__ __forceinline__ void row_relaxed_stats16(const AccParams& p, int r, int lane16, double& H, double& js) {
   const RowPart* pr = p.part + (size_t)(p.T + r) * p.nchunk;
   const double* e = p.ent + (size_t)r * p.nchunk;
   const double* jp = p.jsp + (size_t)r * p.nchunk;
   float M = -INFINITY;
-  for (int k = 0; k < p.nchunk; ++k) M = fmaxf(M, pr[k].m);
+  for (int k = lane16; k < p.nchunk; k += 16) M = fmaxf(M, pr[k].m);
+#pragma unroll
+  for (int off = 8; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   double S0 = 0.0, S1 = 0.0, J = 0.0;
-  for (int k = 0; k < p.nchunk; ++k) {
+  for (int k = lane16; k < p.nchunk; k += 16) {
     const RowPart q = pr[k];
     if (q.m != -INFINITY) {
       const double w = exp((double)q.m - (double)M);
@@ -407,6 +411,12 @@ __device__ __forceinline__ void row_relaxed_stats(const AccParams& p, int r, dou
       S1 += w * (e[k] + ((double)q.m - (double)M) * q.s);
     }
     J += jp[k];
+  }
+#pragma unroll
+  for (int off = 8; off > 0; off >>= 1) {
+    S0 += __shfl_xor(S0, off);
+    S1 += __shfl_xor(S1, off);
+    J += __shfl_xor(J, off);
   }
   H = log(S0) - S1 / S0;
   js = sqrt(fmax(0.0, 0.5 * J));
@@ -449,17 +459,30 @@ __device__ __forceinline__ void decide_seq(const AccParams& p, int b, int* amax)
   if (tid == 0) first_fail = D;
   __syncthreads();
 
-  for (int i = tid; i < D; i += kAccThreads) {
-    const int x = p.tokens[d0 + i];
-    bool pass = x >= 0 && x < p.V && x == amax[i];
-    if constexpr (LOSSY) {
-      double H, js;
-      row_relaxed_stats(p, d0 + i, H, js);
-      if (p.out_ent) p.out_ent[d0 + i] = (float)H;
-      if (p.out_js) p.out_js[d0 + i] = (float)js;
-      pass = x >= 0 && x < p.V && (x == amax[i] || js <= (double)p.tau);
+  if constexpr (LOSSY) {
+    // relaxed: a group of 16 lanes per draft, which also passes when the JS
+    // distance of its rows is at most tau
+    const int lane16 = tid & 15, grp = tid >> 4;
+    for (int i0 = 0; i0 < D; i0 += kAccThreads / 16) {
+      const int i = i0 + grp;
+      if (i < D) {   // (uniform over the group's 16 lanes)
+        double H, js;
+        row_relaxed_stats16(p, d0 + i, lane16, H, js);
+        if (lane16 == 0) {
+          const int x = p.tokens[d0 + i];
+          if (p.out_ent) p.out_ent[d0 + i] = (float)H;
+          if (p.out_js) p.out_js[d0 + i] = (float)js;
+          const bool pass = x >= 0 && x < p.V && (x == amax[i] || js <= (double)p.tau);
+          if (!pass) atomicMin(&first_fail, i);
+        }
+      }
     }
-    if (!pass) atomicMin(&first_fail, i);
+  } else {
+    for (int i = tid; i < D; i += kAccThreads) {
+      const int x = p.tokens[d0 + i];
+      const bool pass = x >= 0 && x < p.V && x == amax[i];
+      if (!pass) atomicMin(&first_fail, i);
+    }
   }
   __syncthreads();
   const int n = first_fail;
@@ -645,13 +668,16 @@ __device__ __forceinline__ void finish_seq(const AccParams& p, int b, int c0, in
     // (draft rows d0 .. d0+D-1 exist only for D > 0, a condition uniform over the workgroup)
     const double lq = D > 0 ? row_lse16(p, p.T + d0 + min(i, D - 1), lane16) : 0.0;
     if (live) { my_lp = lp; my_lq = lq; my_i = i; }
+    // relaxed: the drafted row's entropy and JS distance, by every lane of the group
+    double H = 0.0, js = 0.0;
+    if constexpr (LOSSY) {
+      if (D > 0) row_relaxed_stats16(p, d0 + min(i, D - 1), lane16, H, js);
+    }
     if (test) {
       const double r = exp(((double)tl - lp) - ((double)dl - lq));
       bool pass = inv && (double)ut < r;
       if constexpr (LOSSY) {
-        // relaxed: the draft also passes when the JS distance of its rows is at most tau
-        double H, js;
-        row_relaxed_stats(p, d0 + i, H, js);
+        // the draft also passes when the JS distance of its rows is at most tau
         if (c0 == 0) {
           if (p.out_ent) p.out_ent[d0 + i] = (float)H;
           if (p.out_js) p.out_js[d0 + i] = (float)js;
