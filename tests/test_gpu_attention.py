@@ -290,11 +290,13 @@ def test_score_far_above_the_first_tile_max(key, prefix, kv_chunk, D):
     assert err <= ATTN_TOL
 
 
-@pytest.mark.parametrize("group,kv_chunk", [(8, 0), (8, 512), (16, 512)])
-def test_dynamic_schedule_many_items_per_workgroup(group, kv_chunk):
+@pytest.mark.parametrize("group,kv_chunk,D", [(8, 0, 7), (8, 512, 7), (16, 512, 7), (8, 512, 16)])
+def test_dynamic_schedule_many_items_per_workgroup(group, kv_chunk, D):
     """1100 sequences of 600..2000 keys with D=7 (64 rows per KV head: every wave
-    of the R <= 64 kernel has rows; group 16: the wide kernel), several items
-    per workgroup handed out by the work counters.  Each wave must take the
+    of the R <= 64 kernel has rows; group 16: the wide kernel) or D=16 (136
+    rows: the 16-row block, whose safe-pass votes go through LDS slots reused
+    item after item), several items per workgroup handed out by the work
+    counters.  Each wave must take the
     item index the counter gave its workgroup: the index passes through LDS,
     and a barrier does not wait for LDS stores by itself (a wave that read the
     old index redid the previous item and left its rows of the new one
@@ -304,11 +306,11 @@ def test_dynamic_schedule_many_items_per_workgroup(group, kv_chunk):
     rng = np.random.default_rng(37)
     B = 1100
     kv = [int(x) for x in rng.integers(600, 2000, size=B)]
-    inp = generate(spec(batch=B, kv_heads=1, group=group, head_dim=64, kv_len=kv, draft_len=7, seed=37))
+    inp = generate(spec(batch=B, kv_heads=1, group=group, head_dim=64, kv_len=kv, draft_len=D, seed=37))
     x = on_gpu(inp)
     desc = sdv.attn_desc(x.q, x.k_cache, x.block_table, group, inp.max_draft, kv_chunk=kv_chunk)
     n = sdv.sd_verify_attention_workspace_size(desc, x.q.shape[0])
-    say(f"case: dynamic schedule B={B} G={group} kv_chunk={kv_chunk}")
+    say(f"case: dynamic schedule B={B} G={group} D={D} kv_chunk={kv_chunk}")
     outs = []
     for fill in ("zeros", "ones", "random"):
         ws = torch.empty(n, dtype=torch.uint8, device="cuda")
