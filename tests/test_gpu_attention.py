@@ -30,7 +30,7 @@ def test_tiny_workload_full_parity():
     assert err <= ATTN_TOL
 
 
-@pytest.mark.parametrize("kv_chunk", [0, 256, 64])
+@pytest.mark.parametrize("kv_chunk", [0, 256, 64, 8192])
 def test_ragged_lengths_and_split_kv(kv_chunk):
     inp = generate(spec())
     say(f"case: ragged G=8 d=128 kv_chunk={kv_chunk}")
@@ -53,6 +53,7 @@ def test_ragged_lengths_and_split_kv(kv_chunk):
     (12, [15, 10], 64),        # R = 192, d = 64
     (3, [50, 47], 128),        # R = 153
     (32, [3, 1], 128),         # G = 32, R = 128
+    (32, [7, 2], 128),         # G = 32, R = 256
     (16, [15, 4], 64),         # R = 256, d = 64
     (1, [0, 7], 128),          # G = 1
 ])
@@ -63,6 +64,16 @@ def test_row_block_variants(G, drafts, d):
     say(f"max|err| = {err:.3e}")
     assert err <= ATTN_TOL
     err = compare_attention(inp, gpu_attention(inp))
+    assert err <= ATTN_TOL
+
+
+def test_maximum_fixed_chunk_splits():
+    """kv_chunk at its maximum (8192 keys) on caches of 20000 and 8193 keys:
+    three and two splits merged by the combine, and a short cache unsplit."""
+    inp = generate(spec(kv_len=[20000, 8193, 300], seed=11))
+    say("case: kv_chunk=8192 with splits")
+    err = compare_attention(inp, gpu_attention(inp, kv_chunk=8192))
+    say(f"max|err| = {err:.3e}")
     assert err <= ATTN_TOL
 
 
